@@ -1,0 +1,243 @@
+/*
+ * collider.h - C ABI of libcollider: the backward pass of a transformer layer under token
+ * filtering, in which the activations of filtered tokens are dropped in every layer and each
+ * linear / attention backward runs as dense work over the kept tokens only.  MI355X (gfx950).
+ *
+ * Method: "Enhancing Token Filtering Efficiency in Large Language Model Training with Collider"
+ * (arXiv 2502.00340).  Its abstract states the two parts built here: activations of filtered
+ * tokens are filtered across all layers, and sparse GEMMs become dimension-reduced dense GEMMs.
+ * Figure 2(b) defines backward token filtering (the loss of filtered tokens is dropped), Figure 3
+ * why the attention softmax activation must be filtered too, Figure 5 that the Q/K backward
+ * activations are filtered with it.
+ *
+ * Conventions shared by every entry point
+ *  - Tokens are flattened t = b*S + s (B sequences of S tokens, M = B*S); tensors are row-major,
+ *    one row per token; heads are interleaved in columns (q is [rows, nq*head_dim]).
+ *  - Linear weights use the [out, in] layout, y = x @ w^T; weight gradients are [out, in] float32.
+ *  - bf16 = bfloat16 (uint16 storage).  Every pointer is a device pointer unless said otherwise.
+ *  - Ownership: the caller owns every buffer.  The library never allocates device memory; calls
+ *    that need scratch space take a workspace sized by the matching *_workspace_bytes function.
+ *  - Execution: every call enqueues work on `stream` and returns without waiting, except
+ *    collider_index_count_host, which waits for one 4-byte copy.
+ *  - Errors: arguments are checked on the host before anything is enqueued; a failed check returns
+ *    a non-zero status and enqueues nothing.  A failed launch returns COLLIDER_ERR_HIP and leaves
+ *    the outputs undefined.  Nothing throws across this interface.
+ *  - Alignment: every bf16 tensor pointer must be 16-byte aligned and every bf16 leading dimension
+ *    a multiple of 8 elements (COLLIDER_ERR_ALIGN otherwise).
+ */
+#ifndef COLLIDER_H
+#define COLLIDER_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  COLLIDER_OK = 0,
+  COLLIDER_ERR_NULL = 1,        /* a required pointer is NULL */
+  COLLIDER_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  COLLIDER_ERR_ALIGN = 3,       /* pointer / leading-dimension alignment violated */
+  COLLIDER_ERR_UNSUPPORTED = 4, /* valid but not implemented (head_dim, dtype, ...) */
+  COLLIDER_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+  COLLIDER_ERR_HIP = 6          /* a HIP runtime call failed */
+} collider_status;
+
+typedef enum { COLLIDER_F32 = 0, COLLIDER_BF16 = 1 } collider_dtype;
+
+/* Softmax-backward row term of the filtered attention backward.  The pages do not fix it.
+ *  FILTERED: D~_i = sum_j P~_ij dP_ij over kept keys j (P~ = P with filtered-token columns
+ *            removed) - the ordinary softmax backward run on the filtered activation; needs an
+ *            extra pass over the kept pairs.
+ *  FULL:     D_i = dO_i . O_i with the forward output O (the full softmax's identity). */
+typedef enum { COLLIDER_ATTN_D_FILTERED = 0, COLLIDER_ATTN_D_FULL = 1 } collider_dmode;
+
+/* Compacted index of a keep mask, produced by collider_build_index.  All arrays device-resident. */
+typedef struct {
+  const int32_t* idx;        /* [M]: idx[c], c < count, = c-th kept position (ascending);
+                                entries c >= count list the filtered positions ascending */
+  const int32_t* inv;        /* [M]: inv[t] = c if token t is kept, else -1 */
+  const int32_t* cu_seqlens; /* [B+1]: kept tokens before sequence b; cu_seqlens[B] = count */
+  const int32_t* count;      /* [1]: number of kept tokens M_kept */
+  int32_t B, S;              /* batch and sequence length, M = B*S */
+  int32_t M_kept;            /* host copy of *count (collider_index_count_host) */
+} collider_index;
+
+/* ---------------------------------------------------------------------------------------------
+ * Mask -> index.  Backward token filtering selects tokens one by one (Figure 2(b)); the kept
+ * tokens are what the dimension-reduced GEMMs run over (abstract).
+ * keep: [B*S] bytes, non-zero = kept.  Outputs idx, inv [B*S], cu_seqlens [B+1], count [1] int32.
+ * Deterministic; bit-exact.  B >= 1, S >= 1, B*S <= 2^30.
+ * ------------------------------------------------------------------------------------------- */
+collider_status collider_build_index(const uint8_t* keep, int32_t B, int32_t S, int32_t* idx,
+                                     int32_t* inv, int32_t* cu_seqlens, int32_t* count,
+                                     hipStream_t stream);
+
+/* Copies *count_dev to *count_host (host pointer) and waits for it: the one host sync of a step. */
+collider_status collider_index_count_host(const int32_t* count_dev, int32_t* count_host,
+                                          hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Row gather (dimension reduction, abstract): dst[c, :] = src[idx[c], :] for c < n_rows.
+ * row_elems elements of type dt per row; ld_* are row strides in elements.  Bit-exact copy.
+ * ------------------------------------------------------------------------------------------- */
+collider_status collider_gather_rows(const void* src, int64_t ld_src, void* dst, int64_t ld_dst,
+                                     const int32_t* idx, int32_t n_rows, int32_t row_elems,
+                                     collider_dtype dt, hipStream_t stream);
+
+/* Row scatter back to the full token layout, for t < M:
+ *   dst[t, :] = src[inv[t], :] if inv[t] >= 0; else +0.0 (zero_fill_filtered != 0) or untouched.
+ * The rows of filtered tokens therefore stay exactly zero (abstract: sparsity is maintained). */
+collider_status collider_scatter_rows(const void* src, int64_t ld_src, void* dst, int64_t ld_dst,
+                                      const int32_t* inv, int32_t M, int32_t row_elems,
+                                      int32_t zero_fill_filtered, collider_dtype dt,
+                                      hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Linear-layer backward as dimension-reduced dense GEMMs (abstract) over M_kept compacted rows:
+ *   dx = dy @ w        [M_kept, K]  (dtype dt; skipped when dx == NULL)
+ *   dw = dy^T @ x      [N, K] float32 (overwritten, or added to when accumulate != 0)
+ *   db = colsum(dy)    [N] float32 (optional, NULL to skip; same accumulate rule)
+ * x [M_kept, K] (row stride ld_x), dy [M_kept, N] (ld_dy), w [N, K] dense, all of dtype dt
+ * (COLLIDER_BF16: bf16 operands, fp32 accumulation; COLLIDER_F32: fp32 throughout).
+ * M_kept = 0 gives dw = 0, db = 0.
+ * ------------------------------------------------------------------------------------------- */
+size_t collider_linear_workspace_bytes(collider_dtype dt, int32_t M_kept, int32_t K, int32_t N);
+collider_status collider_linear_bwd_reduced(collider_dtype dt, int32_t M_kept, int32_t K, int32_t N,
+                                            const void* x, int64_t ld_x, const void* dy,
+                                            int64_t ld_dy, const void* w, void* dx, float* dw,
+                                            float* db, int32_t accumulate, void* ws,
+                                            size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Filtered attention backward (Figures 3 and 5), causal, grouped-query, over compacted rows.
+ * For each sequence b (rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of the compacted tensors) and
+ * query head h (KV head g = h / (nq/nkv)), with tau = softmax scale, for kept i >= j:
+ *   P_ij = exp(tau q_i.k_j - lse_i)  (lse from the forward, over ALL causal keys, filtered too)
+ *   dV_j = sum_i P_ij dO_i,  dP_ij = dO_i.v_j,  dS_ij = P_ij (dP_ij - D_i)  (D per dmode)
+ *   dq_i = tau sum_j dS_ij k_j,  dk_j = tau sum_i dS_ij q_i, dK/dV summed over each KV group,
+ * then the rotary-embedding backward on dq, dk (rotate-half on the first rot_dims dims of each
+ * head, angle = pos * rope_base^(-2m/rot_dims), pos = idx[c] mod S).  Filtered keys never enter:
+ * that is the removal of their softmax-activation columns.  q, k are post-rotary.
+ * Inputs bf16 (lse float32 [M_kept, nq] natural-log); outputs bf16, each with its row stride.
+ * ------------------------------------------------------------------------------------------- */
+typedef struct {
+  int32_t n_q_heads, n_kv_heads, head_dim; /* head_dim 64 or 128; n_q_heads % n_kv_heads == 0 */
+  int32_t rot_dims;                        /* 0 = no rotary; even, <= head_dim */
+  float rope_base;
+  float softmax_scale;                     /* 0 = 1/sqrt(head_dim) */
+  int32_t dmode;                           /* collider_dmode */
+} collider_attn_cfg;
+
+typedef struct {
+  const void* q; int64_t ld_q;     /* [M_kept, nq*d]  */
+  const void* k; int64_t ld_k;     /* [M_kept, nkv*d] */
+  const void* v; int64_t ld_v;     /* [M_kept, nkv*d] */
+  const void* o; int64_t ld_o;     /* [M_kept, nq*d]; read only with COLLIDER_ATTN_D_FULL */
+  const float* lse; int64_t ld_lse;/* [M_kept, nq] float32 */
+  const void* dout; int64_t ld_do; /* [M_kept, nq*d] gradient of o */
+  void* dq; int64_t ld_dq;         /* [M_kept, nq*d] out */
+  void* dk; int64_t ld_dk;         /* [M_kept, nkv*d] out */
+  void* dv; int64_t ld_dv;         /* [M_kept, nkv*d] out */
+} collider_attn_io;
+
+size_t collider_attn_workspace_bytes(const collider_attn_cfg* cfg, const collider_index* ix);
+collider_status collider_attn_bwd_filtered(const collider_attn_cfg* cfg, const collider_index* ix,
+                                           const collider_attn_io* io, void* ws, size_t ws_bytes,
+                                           hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Whole-layer filtered backward (abstract: activations of filtered tokens filtered in every layer).
+ * LLAMA: x -> RMSNorm(gamma1) -> QKV -> rotary -> causal GQA attention -> O; h = x + attn;
+ *        h -> RMSNorm(gamma2) -> [gate|up] -> silu(gate)*up -> down; y = h + mlp.
+ * PHI:   xn = LayerNorm(x; gamma, beta); y = x + O(attn(QKV(xn))) + fc2(gelu_tanh(fc1(xn))).
+ * The upstream gradient rows of filtered tokens are never read (their loss is dropped, Figure
+ * 2(b)); every GEMM runs over the M_kept kept rows; weight / gain gradients are sums over kept
+ * tokens only; dx rows of filtered tokens are +0.0 (or absent when dx_compact != 0).
+ * ------------------------------------------------------------------------------------------- */
+typedef enum { COLLIDER_LAYER_LLAMA = 0, COLLIDER_LAYER_PHI = 1 } collider_layer_kind;
+
+typedef struct {
+  int32_t kind;                 /* collider_layer_kind */
+  int32_t hidden;               /* H, multiple of 8 */
+  int32_t n_q_heads, n_kv_heads, head_dim, rot_dims;
+  int32_t inter;                /* I, multiple of 8 */
+  float rope_base;
+  int32_t dmode;                /* collider_dmode */
+  int32_t accumulate;           /* != 0: weight / gain gradients are added to, not overwritten */
+} collider_layer_cfg;
+
+typedef struct {                /* bf16 weights [out, in]; float32 norm parameters */
+  const void* w_qkv;            /* [(nq+2nkv)*d, H]: q rows, then k, then v */
+  const void* w_o;              /* [H, nq*d] */
+  const void* w_gateup;         /* LLAMA [2I, H]: gate rows then up rows */
+  const void* w_down;           /* LLAMA [H, I] */
+  const void* w_fc1;            /* PHI [I, H] */
+  const void* w_fc2;            /* PHI [H, I] */
+  const float* gamma1;          /* LLAMA first RMSNorm gain [H] */
+  const float* gamma2;          /* LLAMA second RMSNorm gain [H] */
+  const float* ln_gamma;        /* PHI LayerNorm gain [H] */
+  const float* ln_beta;         /* PHI LayerNorm bias [H] */
+} collider_layer_weights;
+
+typedef struct {                /* forward activations, full token layout [M, ...] */
+  const void* x;                /* bf16 [M, H] layer input */
+  const void* q;                /* bf16 [M, nq*d] post-rotary */
+  const void* k;                /* bf16 [M, nkv*d] post-rotary */
+  const void* v;                /* bf16 [M, nkv*d] */
+  const void* o;                /* bf16 [M, nq*d] attention output (input of w_o) */
+  const float* lse;             /* [M, nq] */
+  const float* rstd1;           /* LLAMA: first RMSNorm 1/rms [M]; PHI: LayerNorm 1/std [M] */
+  const float* mean;            /* PHI LayerNorm mean [M] */
+  const void* h;                /* LLAMA bf16 [M, H] = x + attention output */
+  const float* rstd2;           /* LLAMA second RMSNorm [M] */
+  const void* gate;             /* LLAMA bf16 [M, I] */
+  const void* up;               /* LLAMA bf16 [M, I] */
+  const void* f;                /* PHI bf16 [M, I] fc1 pre-activation */
+} collider_layer_saved;
+
+typedef struct {                /* outputs */
+  void* dx;                     /* bf16 [M, H] (dx_compact = 0) or [M_kept, H] (dx_compact != 0) */
+  float* dw_qkv;                /* [(nq+2nkv)*d, H] */
+  float* dw_o;                  /* [H, nq*d] */
+  float* dw_gateup;             /* LLAMA [2I, H] */
+  float* dw_down;               /* LLAMA [H, I] */
+  float* dw_fc1;                /* PHI [I, H] */
+  float* dw_fc2;                /* PHI [H, I] */
+  float* dgamma1;               /* LLAMA [H] */
+  float* dgamma2;               /* LLAMA [H] */
+  float* dln_gamma;             /* PHI [H] */
+  float* dln_beta;              /* PHI [H] */
+} collider_layer_grads;
+
+/* dy: bf16 [M, H] (dy_compact = 0) or already compacted [M_kept, H] (dy_compact != 0, e.g. the
+ * dx of the layer above produced with dx_compact != 0).  The workspace must not alias any input
+ * or output. */
+size_t collider_layer_workspace_bytes(const collider_layer_cfg* cfg, int32_t B, int32_t S,
+                                      int32_t M_kept);
+collider_status collider_layer_bwd(const collider_layer_cfg* cfg, const collider_layer_weights* w,
+                                   const collider_layer_saved* saved, const void* dy,
+                                   int32_t dy_compact, const collider_index* ix,
+                                   collider_layer_grads* grads, int32_t dx_compact, void* ws,
+                                   size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Measurement and diagnostics.
+ * collider_profile_enable(1): from then on every kernel the library enqueues is bracketed by a
+ * pair of HIP events recorded on the same stream.  collider_profile_collect waits for them and,
+ * for each kernel name, returns the summed duration (ms) and the number of launches; it then
+ * clears the record.  names receives up to max_kernels NUL-separated names (name_cap bytes).
+ * Returns the number of distinct kernels, or -1 on error.
+ * ------------------------------------------------------------------------------------------- */
+collider_status collider_profile_enable(int32_t on);
+int32_t collider_profile_collect(char* names, int32_t name_cap, double* total_ms, int32_t* launches,
+                                 int32_t max_kernels);
+const char* collider_status_string(collider_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* COLLIDER_H */

@@ -1,0 +1,105 @@
+"""The C ABI library loads, exports every function include/collider.h declares, and rejects bad
+arguments on the host before touching the GPU (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import synth
+import token_filtered_backward_amd as tfb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "collider.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(tfb.LIB_PATH), reason="libcollider.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(collider_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("collider_build_index", "collider_index_count_host", "collider_gather_rows",
+              "collider_scatter_rows", "collider_linear_bwd_reduced", "collider_attn_bwd_filtered",
+              "collider_layer_bwd"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(tfb.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_status_strings():
+    L = tfb.lib()
+    for s in range(7):
+        assert L.collider_status_string(s)
+    assert L.collider_status_string(5).decode() == "workspace missing or too small"
+
+
+def test_host_validation_errors():
+    L = tfb.lib()
+    p = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    assert L.collider_build_index(None, 1, 1, p, p, p, p, None) == 1
+    assert L.collider_build_index(p, 0, 1, p, p, p, p, None) == 2
+    assert L.collider_gather_rows(p, 8, p, 8, p, 1, 8, 7, None) == 4          # bad dtype
+    assert L.collider_gather_rows(p, 4, p, 8, p, 1, 8, 1, None) == 2          # ld < row
+    assert L.collider_gather_rows(None, 8, p, 8, p, 1, 8, 1, None) == 1
+    assert L.collider_scatter_rows(p, 8, None, 8, p, 4, 8, 1, 1, None) == 1
+    # linear: K not a multiple of 8 for bf16, missing workspace
+    assert L.collider_linear_bwd_reduced(1, 4, 12, 8, p, 12, p, 8, p, p, p, None, 0, None, 0, None) == 3
+    a16 = ctypes.c_void_p(0x10000)
+    assert L.collider_linear_bwd_reduced(1, 4096, 2048, 2048, a16, 2048, a16, 2048, a16, a16, a16, None, 0,
+                                         None, 0, None) == 5                  # workspace missing
+    cfg = tfb.AttnCfg(8, 2, 96, 0, 0.0, 0.0, 0)
+    ix = tfb.CollIndex(p, p, p, p, 1, 8, 8)
+    io = tfb.AttnIO()
+    assert L.collider_attn_bwd_filtered(ctypes.byref(cfg), ctypes.byref(ix), ctypes.byref(io), None, 0, None) == 4
+    cfg = tfb.AttnCfg(6, 4, 64, 0, 0.0, 0.0, 0)                                # nq % nkv != 0
+    assert L.collider_attn_bwd_filtered(ctypes.byref(cfg), ctypes.byref(ix), ctypes.byref(io), None, 0, None) == 2
+    cfg = tfb.AttnCfg(8, 2, 64, 24, 1e4, 0.0, 0)                               # rot not multiple of 16
+    assert L.collider_attn_bwd_filtered(ctypes.byref(cfg), ctypes.byref(ix), ctypes.byref(io), None, 0, None) == 4
+    cfg = tfb.AttnCfg(8, 2, 64, 64, 1e4, 0.0, 0)
+    ix_bad = tfb.CollIndex(p, p, p, p, 1, 8, 9)                                # M_kept > M
+    assert L.collider_attn_bwd_filtered(ctypes.byref(cfg), ctypes.byref(ix_bad), ctypes.byref(io), None, 0, None) == 2
+    io.q = io.k = io.v = io.lse = io.dout = io.dq = io.dk = io.dv = 0x10008    # misaligned
+    io.ld_q = io.ld_do = io.ld_dq = 512
+    io.ld_k = io.ld_v = io.ld_dk = io.ld_dv = 128
+    io.ld_lse = 8
+    assert L.collider_attn_bwd_filtered(ctypes.byref(cfg), ctypes.byref(ix), ctypes.byref(io), None, 0, None) == 3
+    io.q = io.k = io.v = io.lse = io.dout = io.dq = io.dk = io.dv = 0x10000
+    assert L.collider_attn_bwd_filtered(ctypes.byref(cfg), ctypes.byref(ix), ctypes.byref(io), None, 0, None) == 5
+
+
+def test_layer_validation_and_workspace_sizes():
+    L = tfb.lib()
+    for name in ("tinyllama", "qwen25", "phi15", "small_llama", "small_phi"):
+        shape = synth.get_config(name)
+        cfg = tfb.layer_cfg(shape)
+        mk = shape.M - synth.n_filtered(shape.M, 40)
+        need = L.collider_layer_workspace_bytes(ctypes.byref(cfg), shape.B, shape.S, mk)
+        assert need > 0
+        # more kept tokens never needs less workspace; M_kept > M is rejected
+        assert L.collider_layer_workspace_bytes(ctypes.byref(cfg), shape.B, shape.S, shape.M) >= need
+        assert L.collider_layer_workspace_bytes(ctypes.byref(cfg), shape.B, shape.S, shape.M + 1) == 0
+    shape = synth.get_config("tinyllama")
+    bad = tfb.layer_cfg(shape.with_(H=5000))
+    assert L.collider_layer_workspace_bytes(ctypes.byref(bad), 1, 8, 8) == 0
+    cfg = tfb.layer_cfg(shape)
+    ix = tfb.CollIndex(0x1000, 0x1000, 0x1000, 0x1000, 4, 2048, 4916)
+    w, sv, g = tfb.LayerWeights(), tfb.LayerSaved(), tfb.LayerGrads()
+    assert L.collider_layer_bwd(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(sv), ctypes.c_void_p(0x1000),
+                                0, ctypes.byref(ix), ctypes.byref(g), 0, None, 0, None) == 1
+    cfg.kind = 7
+    assert L.collider_layer_bwd(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(sv), ctypes.c_void_p(0x1000),
+                                0, ctypes.byref(ix), ctypes.byref(g), 0, None, 0, None) == 4
+
+
+def test_linear_workspace_size_is_host_only():
+    assert tfb.collider_linear_workspace_bytes(tfb.BF16, 4916, 2048, 2048) > 0
+    assert tfb.collider_linear_workspace_bytes(tfb.F32, 154, 256, 256) > 0

@@ -1,0 +1,304 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Bars: bit-exact for index / gather / scatter; max|d|/max|ref| <= 2e-2 for bf16 outputs and <= 1e-4
+for the fp32 linear layer; rows of filtered tokens exactly zero in full-layout outputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import token_filtered_backward_amd as tfb
+from tests.helpers import BF16_TOL, F32_TOL, bf16_dev, f32_dev, rel_err, to64, upcast
+
+pytestmark = pytest.mark.gpu
+
+
+def _keep(M, pattern, seed=0, r=40):
+    rng = np.random.default_rng(seed)
+    if pattern == "all":
+        return np.ones(M, np.uint8)
+    if pattern == "none":
+        return np.zeros(M, np.uint8)
+    if pattern == "rand":
+        return (rng.random(M) < 0.6).astype(np.uint8) * rng.integers(1, 256, M).astype(np.uint8)
+    return synth.make_keep(M, r, seed)
+
+
+def _dev_keep(keep):
+    return torch.from_numpy(np.ascontiguousarray(keep, np.uint8)).cuda()
+
+
+# ------------------------------------------------------------------------------------------------
+# index, gather, scatter: bit-exact
+# ------------------------------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("B,S,pattern", [(1, 1, "all"), (1, 1, "none"), (1, 7, "none"), (3, 11, "rand"),
+                                         (4, 2048, "topk"), (2, 4096, "topk"), (1, 8192, "topk"),
+                                         (5, 3001, "rand"), (1, 70000, "rand"), (2, 5, "all")])
+def test_build_index_bit_exact(B, S, pattern):
+    keep = _keep(B * S, pattern, seed=B + S)
+    ix = tfb.build_index(_dev_keep(keep), B, S)
+    torch.cuda.synchronize()
+    ref = oracle.build_index(keep, B, S)
+    assert ix.M_kept == ref["count"]
+    assert np.array_equal(ix.idx.cpu().numpy(), ref["partition"])
+    assert np.array_equal(ix.inv.cpu().numpy(), ref["inv"])
+    assert np.array_equal(ix.cu_seqlens.cpu().numpy(), ref["cu_seqlens"])
+    assert int(ix.count.cpu()[0]) == ref["count"]
+
+
+@pytest.mark.parametrize("cols,dtype", [(2048, torch.bfloat16), (256, torch.bfloat16), (32, torch.float32),
+                                        (12, torch.bfloat16), (5, torch.float32), (4096, torch.float32)])
+def test_gather_scatter_bit_exact(cols, dtype):
+    B, S = 3, 517
+    M = B * S
+    keep = _keep(M, "topk", seed=cols)
+    ix = tfb.build_index(_dev_keep(keep), B, S)
+    rng = np.random.default_rng(cols)
+    if dtype == torch.bfloat16:
+        bits = rng.integers(0, 2 ** 16, size=(M, cols), dtype=np.uint16)
+        src = bf16_dev(bits)
+        src_np = bits
+    else:
+        src_np = rng.standard_normal((M, cols)).astype(np.float32)
+        src = f32_dev(src_np)
+    mk = ix.M_kept
+    dst = torch.empty((mk, cols), dtype=dtype, device="cuda")
+    tfb.collider_gather_rows(src, dst, ix.idx, mk)
+    ref_idx = oracle.build_index(keep, B, S)["idx"]
+    got = dst.cpu().view(torch.int16).numpy().view(np.uint16) if dtype == torch.bfloat16 else dst.cpu().numpy()
+    assert np.array_equal(got, oracle.gather_rows(src_np, ref_idx))
+    # scatter back with zero fill over a poisoned destination
+    full = torch.full((M, cols), float("nan"), dtype=dtype, device="cuda")
+    tfb.collider_scatter_rows(dst, full, ix.inv, M, zero_fill_filtered=True)
+    back = full.cpu().view(torch.int16).numpy().view(np.uint16) if dtype == torch.bfloat16 else full.cpu().numpy()
+    assert np.array_equal(back, oracle.scatter_rows(got, ref_idx, M))
+    # without zero fill the filtered rows are untouched
+    full2 = torch.full((M, cols), 7.0, dtype=dtype, device="cuda")
+    tfb.collider_scatter_rows(dst, full2, ix.inv, M, zero_fill_filtered=False)
+    f2 = full2.float().cpu().numpy()
+    assert np.all(f2[keep == 0] == 7.0)
+
+
+# ------------------------------------------------------------------------------------------------
+# linear layer
+# ------------------------------------------------------------------------------------------------
+
+
+def test_linear_fp32_single_layer():
+    cfg = synth.get_config("linear_fp32")
+    inp = synth.make_linear_inputs(cfg)
+    keep = inp["keep"]
+    ix = tfb.build_index(_dev_keep(keep), cfg.B, cfg.S)
+    assert ix.M_kept == 154
+    x, dy, w = f32_dev(inp["x"]), f32_dev(inp["dy"]), f32_dev(inp["w"])
+    mk = ix.M_kept
+    x_c = torch.empty((mk, cfg.K), device="cuda")
+    dy_c = torch.empty((mk, cfg.N), device="cuda")
+    tfb.collider_gather_rows(x, x_c, ix.idx, mk)
+    tfb.collider_gather_rows(dy, dy_c, ix.idx, mk)
+    dx_c = torch.empty((mk, cfg.K), device="cuda")
+    dw = torch.empty((cfg.N, cfg.K), device="cuda")
+    db = torch.empty(cfg.N, device="cuda")
+    tfb.collider_linear_bwd_reduced(x_c, dy_c, w, dx_c, dw, db)
+    dx = torch.empty((cfg.M, cfg.K), device="cuda")
+    tfb.collider_scatter_rows(dx_c, dx, ix.inv, cfg.M)
+    ref = oracle.linear_bwd(inp["x"], inp["dy"], inp["w"], keep, bias=True)
+    assert rel_err(to64(dx), ref["dx"]) <= F32_TOL
+    assert rel_err(to64(dw), ref["dw"]) <= F32_TOL
+    assert rel_err(to64(db), ref["db"]) <= F32_TOL
+    assert np.all(to64(dx)[keep == 0] == 0.0)
+
+
+@pytest.mark.parametrize("Mk,K,N", [(1, 8, 8), (77, 64, 136), (300, 256, 512), (1000, 520, 264),
+                                    (4916, 2048, 2048), (4916, 2048, 5632), (4916, 5632, 2048),
+                                    (4916, 1536, 8960), (0, 64, 64)])
+def test_linear_bf16(Mk, K, N):
+    rng = np.random.default_rng(Mk + K + N)
+    xb = synth.f32_to_bf16_bits(rng.standard_normal((Mk, K)).astype(np.float32))
+    dyb = synth.f32_to_bf16_bits(rng.standard_normal((Mk, N)).astype(np.float32))
+    wb = synth.f32_to_bf16_bits(0.02 * rng.standard_normal((N, K)).astype(np.float32))
+    x, dy, w = bf16_dev(xb), bf16_dev(dyb), bf16_dev(wb)
+    dx = torch.empty((Mk, K), dtype=torch.bfloat16, device="cuda")
+    dw = torch.full((N, K), float("nan"), device="cuda")
+    db = torch.full((N,), float("nan"), device="cuda")
+    tfb.collider_linear_bwd_reduced(x, dy, w, dx, dw, db)
+    ref = oracle.linear_bwd(synth.bf16_bits_to_f32(xb), synth.bf16_bits_to_f32(dyb),
+                            synth.bf16_bits_to_f32(wb), np.ones(Mk, np.uint8), bias=True)
+    if Mk == 0:
+        assert np.all(to64(dw) == 0.0) and np.all(to64(db) == 0.0)
+        return
+    assert rel_err(to64(dx), ref["dx"]) <= 1e-2
+    assert rel_err(to64(dw), ref["dw"]) <= 1e-3
+    assert rel_err(to64(db), ref["db"]) <= 1e-3
+    # accumulate adds onto the previous contents
+    tfb.collider_linear_bwd_reduced(x, dy, w, None, dw, None, accumulate=True)
+    assert rel_err(to64(dw), 2 * ref["dw"]) <= 1e-3
+
+
+# ------------------------------------------------------------------------------------------------
+# attention
+# ------------------------------------------------------------------------------------------------
+
+
+def _attn_case(name, r, dmode, seed=0):
+    cfg = synth.get_config(name)
+    inp = synth.make_layer_inputs(cfg, seed=seed, r_pct=r)
+    keep = inp["keep"]
+    sv = upcast(inp["saved"])
+    rng = np.random.default_rng(seed + 1)
+    dob = synth.f32_to_bf16_bits(rng.standard_normal((cfg.M, cfg.nq * cfg.d)).astype(np.float32))
+    mode = "filtered" if dmode == 0 else "full_d"
+    dq, dk, dv = oracle.attention_bwd(sv["q"], sv["k"], sv["v"], sv["o"], sv["lse"],
+                                      synth.bf16_bits_to_f32(dob), keep, cfg.B, cfg.S, cfg.nq, cfg.nkv,
+                                      cfg.d, mode=mode)
+    pos = np.arange(cfg.M) % cfg.S
+    dq = oracle.rope_bwd(dq, pos, cfg.nq, cfg.d, cfg.rot, cfg.rope_base)
+    dk = oracle.rope_bwd(dk, pos, cfg.nkv, cfg.d, cfg.rot, cfg.rope_base)
+    return cfg, inp, dob, (dq, dk, dv)
+
+
+@pytest.mark.parametrize("name", ["small_llama", "small_llama_d128", "small_phi"])
+@pytest.mark.parametrize("dmode", [0, 1])
+@pytest.mark.parametrize("r", [0, 40, 90])
+def test_attention_parity(name, dmode, r):
+    cfg, inp, dob, ref = _attn_case(name, r, dmode)
+    keep = inp["keep"]
+    ix = tfb.build_index(_dev_keep(keep), cfg.B, cfg.S)
+    mk = ix.M_kept
+    nqd, nkvd = cfg.nq * cfg.d, cfg.nkv * cfg.d
+    full = {k: bf16_dev(inp["saved"][k]) for k in ("q", "k", "v", "o")}
+    full["lse"] = f32_dev(inp["saved"]["lse"])
+    full["do"] = bf16_dev(dob)
+    comp = {}
+    for k, t in full.items():
+        comp[k] = torch.empty((mk, t.shape[1]), dtype=t.dtype, device="cuda")
+        tfb.collider_gather_rows(t, comp[k], ix.idx, mk)
+    out = {k: torch.empty((mk, n), dtype=torch.bfloat16, device="cuda") for k, n in
+           (("dq", nqd), ("dk", nkvd), ("dv", nkvd))}
+    acfg = tfb.AttnCfg(cfg.nq, cfg.nkv, cfg.d, cfg.rot, cfg.rope_base, 0.0, dmode)
+    io = tfb.AttnIO(comp["q"].data_ptr(), nqd, comp["k"].data_ptr(), nkvd, comp["v"].data_ptr(), nkvd,
+                    comp["o"].data_ptr(), nqd, comp["lse"].data_ptr(), cfg.nq, comp["do"].data_ptr(), nqd,
+                    out["dq"].data_ptr(), nqd, out["dk"].data_ptr(), nkvd, out["dv"].data_ptr(), nkvd)
+    cix = ix.c()
+    ws = torch.empty(max(1, tfb.collider_attn_workspace_bytes(acfg, cix)), dtype=torch.uint8, device="cuda")
+    tfb.collider_attn_bwd_filtered(acfg, cix, io, ws)
+    idx = ix.idx[:mk].cpu().numpy()
+    for name_, r_ in zip(("dq", "dk", "dv"), ref):
+        e = rel_err(to64(out[name_]), r_[idx])
+        assert e <= BF16_TOL, (name_, e)
+
+
+# ------------------------------------------------------------------------------------------------
+# whole layer
+# ------------------------------------------------------------------------------------------------
+
+
+def _upload_layer(inp):
+    cfg = inp["cfg"]
+    W = {}
+    for k, v in inp["weights"].items():
+        W[k] = bf16_dev(v) if v.dtype == np.uint16 else f32_dev(v)
+    S = {}
+    for k, v in inp["saved"].items():
+        S[k] = bf16_dev(v) if v.dtype == np.uint16 else f32_dev(v)
+    if cfg.kind == "llama":
+        weights = dict(w_qkv=W["w_qkv"], w_o=W["w_o"], w_gateup=W["w_gateup"], w_down=W["w_down"],
+                       gamma1=W["gamma1"], gamma2=W["gamma2"])
+        saved = dict(x=S["x"], q=S["q"], k=S["k"], v=S["v"], o=S["o"], lse=S["lse"], rstd1=S["rstd1"],
+                     h=S["h"], rstd2=S["rstd2"], gate=S["gate"], up=S["up"])
+    else:
+        weights = dict(w_qkv=W["w_qkv"], w_o=W["w_o"], w_fc1=W["w_fc1"], w_fc2=W["w_fc2"],
+                       ln_gamma=W["gamma"], ln_beta=W["beta"])
+        saved = dict(x=S["x"], q=S["q"], k=S["k"], v=S["v"], o=S["o"], lse=S["lse"], rstd1=S["rstd"],
+                     mean=S["mean"], f=S["f"])
+    return weights, saved, bf16_dev(inp["dy"])
+
+
+GRAD_NAMES = {"llama": {"dx": "dx", "dw_qkv": "dw_qkv", "dw_o": "dw_o", "dw_gateup": "dw_gateup",
+                        "dw_down": "dw_down", "dgamma1": "dgamma1", "dgamma2": "dgamma2"},
+              "phi": {"dx": "dx", "dw_qkv": "dw_qkv", "dw_o": "dw_o", "dw_fc1": "dw_fc1", "dw_fc2": "dw_fc2",
+                      "dln_gamma": "dgamma", "dln_beta": "dbeta"}}
+
+
+def run_layer_and_compare(inp, dmode, tol=BF16_TOL):
+    cfg = inp["cfg"]
+    keep = inp["keep"]
+    weights, saved, dy = _upload_layer(inp)
+    ix = tfb.build_index(_dev_keep(keep), cfg.B, cfg.S)
+    lcfg = tfb.layer_cfg(cfg, dmode=dmode)
+    grads = tfb.make_grads(lcfg, cfg.M, ix.M_kept, "cuda")
+    for g in grads.values():
+        g.fill_(float("nan"))
+    tfb.layer_bwd(lcfg, weights, saved, dy, ix, grads)
+    torch.cuda.synchronize()
+    ref = oracle.layer_bwd(cfg, upcast(inp["weights"]), upcast(inp["saved"]),
+                           synth.bf16_bits_to_f32(inp["dy"]), keep,
+                           "filtered" if dmode == 0 else "full_d")
+    errs = {}
+    for gname, oname in GRAD_NAMES[cfg.kind].items():
+        errs[gname] = rel_err(to64(grads[gname]), ref[oname])
+    assert np.all(to64(grads["dx"])[keep == 0] == 0.0)
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, errs
+    return errs
+
+
+@pytest.mark.parametrize("name", ["small_llama", "small_llama_d128", "small_phi"])
+@pytest.mark.parametrize("dmode", [0, 1])
+@pytest.mark.parametrize("r", [0, 40, 75])
+def test_layer_parity_small(name, dmode, r):
+    inp = synth.make_layer_inputs(synth.get_config(name), r_pct=r)
+    run_layer_and_compare(inp, dmode)
+
+
+@pytest.mark.parametrize("name", ["small_llama", "small_phi"])
+def test_layer_all_filtered(name):
+    cfg = synth.get_config(name)
+    inp = synth.make_layer_inputs(cfg, keep=np.zeros(cfg.M, np.uint8))
+    weights, saved, dy = _upload_layer(inp)
+    ix = tfb.build_index(_dev_keep(inp["keep"]), cfg.B, cfg.S)
+    assert ix.M_kept == 0
+    lcfg = tfb.layer_cfg(cfg)
+    grads = tfb.make_grads(lcfg, cfg.M, 0, "cuda")
+    for g in grads.values():
+        g.fill_(float("nan"))
+    tfb.layer_bwd(lcfg, weights, saved, dy, ix, grads)
+    for k, g in grads.items():
+        assert torch.all(g == 0).item(), k
+
+
+def test_layer_compact_chain_matches_full_layout():
+    """dx_compact of the upper layer feeding dy_compact of the lower one equals the full-layout path."""
+    cfg = synth.get_config("small_llama")
+    inp = synth.make_layer_inputs(cfg)
+    weights, saved, dy = _upload_layer(inp)
+    ix = tfb.build_index(_dev_keep(inp["keep"]), cfg.B, cfg.S)
+    lcfg = tfb.layer_cfg(cfg)
+    g_full = tfb.make_grads(lcfg, cfg.M, ix.M_kept, "cuda")
+    tfb.layer_bwd(lcfg, weights, saved, dy, ix, g_full)
+    g_c = tfb.make_grads(lcfg, cfg.M, ix.M_kept, "cuda", dx_compact=True)
+    tfb.layer_bwd(lcfg, weights, saved, dy, ix, g_c, dx_compact=True)
+    idx = ix.idx[: ix.M_kept].long()
+    assert torch.equal(g_c["dx"], g_full["dx"][idx])
+    # feed the compact dx down as a compact dy: equals feeding the full-layout dx
+    g1 = tfb.make_grads(lcfg, cfg.M, ix.M_kept, "cuda")
+    tfb.layer_bwd(lcfg, weights, saved, g_full["dx"], ix, g1)
+    g2 = tfb.make_grads(lcfg, cfg.M, ix.M_kept, "cuda")
+    tfb.layer_bwd(lcfg, weights, saved, g_c["dx"], ix, g2, dy_compact=True)
+    for k in g1:
+        assert torch.equal(g1[k], g2[k]), k
+
+
+def test_layer_repeat_is_deterministic():
+    cfg = synth.get_config("small_llama")
+    inp = synth.make_layer_inputs(cfg)
+    weights, saved, dy = _upload_layer(inp)
+    ix = tfb.build_index(_dev_keep(inp["keep"]), cfg.B, cfg.S)
+    lcfg = tfb.layer_cfg(cfg)
+    a = tfb.layer_bwd(lcfg, weights, saved, dy, ix)
+    b = tfb.layer_bwd(lcfg, weights, saved, dy, ix)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k

@@ -1,0 +1,319 @@
+"""Python binding of libcollider (filtered transformer-layer backward on MI355X).
+
+Argument marshalling only: every step runs in the HIP kernels of libcollider.so.  Torch tensors
+supply device memory and the current HIP stream.  Functions named collider_* mirror the C entry
+points of include/collider.h one to one; build_index / layer_bwd are conveniences on top of them.
+There is no CPU fallback: if the library is missing or a call fails, an exception is raised.
+
+Method: "Enhancing Token Filtering Efficiency in Large Language Model Training with Collider"
+(arXiv 2502.00340), abstract and Figures 2, 3, 5.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcollider.so")
+
+F32, BF16 = 0, 1
+ATTN_D_FILTERED, ATTN_D_FULL = 0, 1
+LAYER_LLAMA, LAYER_PHI = 0, 1
+
+_c_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+
+
+class CollIndex(ctypes.Structure):
+    _fields_ = [("idx", _c_p), ("inv", _c_p), ("cu_seqlens", _c_p), ("count", _c_p),
+                ("B", _i32), ("S", _i32), ("M_kept", _i32)]
+
+
+class AttnCfg(ctypes.Structure):
+    _fields_ = [("n_q_heads", _i32), ("n_kv_heads", _i32), ("head_dim", _i32), ("rot_dims", _i32),
+                ("rope_base", ctypes.c_float), ("softmax_scale", ctypes.c_float), ("dmode", _i32)]
+
+
+class AttnIO(ctypes.Structure):
+    _fields_ = [("q", _c_p), ("ld_q", _i64), ("k", _c_p), ("ld_k", _i64), ("v", _c_p), ("ld_v", _i64),
+                ("o", _c_p), ("ld_o", _i64), ("lse", _c_p), ("ld_lse", _i64), ("dout", _c_p),
+                ("ld_do", _i64), ("dq", _c_p), ("ld_dq", _i64), ("dk", _c_p), ("ld_dk", _i64),
+                ("dv", _c_p), ("ld_dv", _i64)]
+
+
+class LayerCfg(ctypes.Structure):
+    _fields_ = [("kind", _i32), ("hidden", _i32), ("n_q_heads", _i32), ("n_kv_heads", _i32),
+                ("head_dim", _i32), ("rot_dims", _i32), ("inter", _i32),
+                ("rope_base", ctypes.c_float), ("dmode", _i32), ("accumulate", _i32)]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, _c_p) for n in ("w_qkv", "w_o", "w_gateup", "w_down", "w_fc1", "w_fc2",
+                                    "gamma1", "gamma2", "ln_gamma", "ln_beta")]
+
+
+class LayerSaved(ctypes.Structure):
+    _fields_ = [(n, _c_p) for n in ("x", "q", "k", "v", "o", "lse", "rstd1", "mean", "h", "rstd2",
+                                    "gate", "up", "f")]
+
+
+class LayerGrads(ctypes.Structure):
+    _fields_ = [(n, _c_p) for n in ("dx", "dw_qkv", "dw_o", "dw_gateup", "dw_down", "dw_fc1",
+                                    "dw_fc2", "dgamma1", "dgamma2", "dln_gamma", "dln_beta")]
+
+
+_lib = None
+
+
+def lib():
+    """Load libcollider.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m token_filtered_backward_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    st = _i32
+    sz = ctypes.c_size_t
+    P = ctypes.POINTER
+    sig = {
+        "collider_status_string": (ctypes.c_char_p, [_i32]),
+        "collider_build_index": (st, [_c_p, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _c_p]),
+        "collider_index_count_host": (st, [_c_p, P(_i32), _c_p]),
+        "collider_gather_rows": (st, [_c_p, _i64, _c_p, _i64, _c_p, _i32, _i32, _i32, _c_p]),
+        "collider_scatter_rows": (st, [_c_p, _i64, _c_p, _i64, _c_p, _i32, _i32, _i32, _i32, _c_p]),
+        "collider_linear_workspace_bytes": (sz, [_i32, _i32, _i32, _i32]),
+        "collider_linear_bwd_reduced": (st, [_i32, _i32, _i32, _i32, _c_p, _i64, _c_p, _i64, _c_p,
+                                             _c_p, _c_p, _c_p, _i32, _c_p, sz, _c_p]),
+        "collider_attn_workspace_bytes": (sz, [P(AttnCfg), P(CollIndex)]),
+        "collider_attn_bwd_filtered": (st, [P(AttnCfg), P(CollIndex), P(AttnIO), _c_p, sz, _c_p]),
+        "collider_layer_workspace_bytes": (sz, [P(LayerCfg), _i32, _i32, _i32]),
+        "collider_layer_bwd": (st, [P(LayerCfg), P(LayerWeights), P(LayerSaved), _c_p, _i32,
+                                    P(CollIndex), P(LayerGrads), _i32, _c_p, sz, _c_p]),
+        "collider_profile_enable": (st, [_i32]),
+        "collider_profile_collect": (_i32, [ctypes.c_char_p, _i32, P(ctypes.c_double), P(_i32), _i32]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+class ColliderError(RuntimeError):
+    pass
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = lib().collider_status_string(status).decode()
+        raise ColliderError(f"{what}: status {status} ({msg})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ld(t):
+    """Row stride in elements of a 2-D tensor with unit column stride (shape-derived when the
+    stride is not meaningful: empty or single-row tensors)."""
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    if t.shape[0] <= 1 or t.numel() == 0:
+        return t.shape[1]
+    if t.stride(1) != 1:
+        raise ValueError("columns must be contiguous")
+    return t.stride(0)
+
+
+def _dt(t):
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+# ------------------------------------------------------------------------------------------------
+# one-to-one wrappers of the C entry points
+# ------------------------------------------------------------------------------------------------
+
+
+def collider_build_index(keep, B, S, idx, inv, cu_seqlens, count, stream=None):
+    _check(lib().collider_build_index(_ptr(keep), B, S, _ptr(idx), _ptr(inv), _ptr(cu_seqlens),
+                                      _ptr(count), _stream(stream)), "collider_build_index")
+
+
+def collider_index_count_host(count, stream=None) -> int:
+    out = _i32(0)
+    _check(lib().collider_index_count_host(_ptr(count), ctypes.byref(out), _stream(stream)),
+           "collider_index_count_host")
+    return int(out.value)
+
+
+def collider_gather_rows(src, dst, idx, n_rows, stream=None):
+    """dst[c, :] = src[idx[c], :] for c < n_rows (2-D tensors with unit column stride)."""
+    _check(lib().collider_gather_rows(_ptr(src), _ld(src), _ptr(dst), _ld(dst), _ptr(idx),
+                                      n_rows, src.shape[1], _dt(src), _stream(stream)),
+           "collider_gather_rows")
+
+
+def collider_scatter_rows(src, dst, inv, M, zero_fill_filtered=True, stream=None):
+    _check(lib().collider_scatter_rows(_ptr(src), _ld(src), _ptr(dst), _ld(dst), _ptr(inv),
+                                       M, dst.shape[1], int(zero_fill_filtered), _dt(dst),
+                                       _stream(stream)), "collider_scatter_rows")
+
+
+def collider_linear_workspace_bytes(dt, M_kept, K, N) -> int:
+    return int(lib().collider_linear_workspace_bytes(dt, M_kept, K, N))
+
+
+def collider_linear_bwd_reduced(x, dy, w, dx, dw, db=None, accumulate=False, ws=None, stream=None):
+    """dx = dy @ w, dw = dy^T @ x, db = colsum(dy) over the M_kept = x.shape[0] compacted rows."""
+    Mk, K = x.shape
+    N = w.shape[0]
+    dt = _dt(w)
+    if ws is None:
+        nbytes = collider_linear_workspace_bytes(dt, Mk, K, N)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=w.device)
+    _check(lib().collider_linear_bwd_reduced(dt, Mk, K, N, _ptr(x), _ld(x), _ptr(dy), _ld(dy),
+                                             _ptr(w), _ptr(dx), _ptr(dw), _ptr(db), int(accumulate),
+                                             _ptr(ws), ws.numel(), _stream(stream)),
+           "collider_linear_bwd_reduced")
+
+
+def collider_attn_workspace_bytes(cfg: AttnCfg, ix: CollIndex) -> int:
+    return int(lib().collider_attn_workspace_bytes(ctypes.byref(cfg), ctypes.byref(ix)))
+
+
+def collider_attn_bwd_filtered(cfg: AttnCfg, ix: CollIndex, io: AttnIO, ws, stream=None):
+    _check(lib().collider_attn_bwd_filtered(ctypes.byref(cfg), ctypes.byref(ix), ctypes.byref(io),
+                                            _ptr(ws), ws.numel(), _stream(stream)),
+           "collider_attn_bwd_filtered")
+
+
+def collider_layer_workspace_bytes(cfg: LayerCfg, B, S, M_kept) -> int:
+    return int(lib().collider_layer_workspace_bytes(ctypes.byref(cfg), B, S, M_kept))
+
+
+def collider_layer_bwd(cfg: LayerCfg, w: LayerWeights, saved: LayerSaved, dy, dy_compact,
+                       ix: CollIndex, grads: LayerGrads, dx_compact, ws, stream=None):
+    _check(lib().collider_layer_bwd(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(saved), _ptr(dy),
+                                    int(dy_compact), ctypes.byref(ix), ctypes.byref(grads),
+                                    int(dx_compact), _ptr(ws), ws.numel(), _stream(stream)),
+           "collider_layer_bwd")
+
+
+def collider_profile_enable(on: bool):
+    _check(lib().collider_profile_enable(int(on)), "collider_profile_enable")
+
+
+def collider_profile_collect(max_kernels=64):
+    """{kernel name: (total ms, launches)} recorded since the last collect."""
+    cap = 64 * max_kernels
+    names = ctypes.create_string_buffer(cap)
+    ms = (ctypes.c_double * max_kernels)()
+    cnt = (_i32 * max_kernels)()
+    n = lib().collider_profile_collect(names, cap, ms, cnt, max_kernels)
+    if n < 0:
+        raise ColliderError("collider_profile_collect failed")
+    out, parts = {}, names.raw.split(b"\0")
+    for i in range(n):
+        out[parts[i].decode()] = (float(ms[i]), int(cnt[i]))
+    return out
+
+
+# ------------------------------------------------------------------------------------------------
+# conveniences
+# ------------------------------------------------------------------------------------------------
+
+
+@dataclass
+class Index:
+    idx: torch.Tensor
+    inv: torch.Tensor
+    cu_seqlens: torch.Tensor
+    count: torch.Tensor
+    B: int
+    S: int
+    M_kept: int
+
+    def c(self) -> CollIndex:
+        return CollIndex(self.idx.data_ptr(), self.inv.data_ptr(), self.cu_seqlens.data_ptr(),
+                         self.count.data_ptr(), self.B, self.S, self.M_kept)
+
+
+def build_index(keep: torch.Tensor, B: int, S: int, stream=None) -> Index:
+    """Compact a [B*S] uint8 keep mask on the device; waits once for the kept count."""
+    dev = keep.device
+    M = B * S
+    idx = torch.empty(M, dtype=torch.int32, device=dev)
+    inv = torch.empty(M, dtype=torch.int32, device=dev)
+    cu = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    count = torch.empty(1, dtype=torch.int32, device=dev)
+    collider_build_index(keep, B, S, idx, inv, cu, count, stream)
+    mk = collider_index_count_host(count, stream)
+    return Index(idx, inv, cu, count, B, S, mk)
+
+
+def layer_cfg(shape, dmode=ATTN_D_FILTERED, accumulate=False) -> LayerCfg:
+    """LayerCfg from any object with kind/H/nq/nkv/d/rot/I/rope_base attributes."""
+    return LayerCfg(LAYER_LLAMA if shape.kind == "llama" else LAYER_PHI, shape.H, shape.nq, shape.nkv,
+                    shape.d, shape.rot, shape.I, float(shape.rope_base), dmode, int(accumulate))
+
+
+def _struct(cls, tensors: dict):
+    return cls(**{k: (v.data_ptr() if v is not None else None) for k, v in tensors.items()})
+
+
+def make_grads(cfg: LayerCfg, M: int, M_kept: int, device, dx_compact=False) -> dict:
+    H, I, d = cfg.hidden, cfg.inter, cfg.head_dim
+    nqkv = (cfg.n_q_heads + 2 * cfg.n_kv_heads) * d
+    f32 = dict(dtype=torch.float32, device=device)
+    g = {"dx": torch.empty((M_kept if dx_compact else M, H), dtype=torch.bfloat16, device=device),
+         "dw_qkv": torch.empty((nqkv, H), **f32), "dw_o": torch.empty((H, cfg.n_q_heads * d), **f32)}
+    if cfg.kind == LAYER_LLAMA:
+        g.update(dw_gateup=torch.empty((2 * I, H), **f32), dw_down=torch.empty((H, I), **f32),
+                 dgamma1=torch.empty(H, **f32), dgamma2=torch.empty(H, **f32))
+    else:
+        g.update(dw_fc1=torch.empty((I, H), **f32), dw_fc2=torch.empty((H, I), **f32),
+                 dln_gamma=torch.empty(H, **f32), dln_beta=torch.empty(H, **f32))
+    return g
+
+
+class LayerBackward:
+    """Reusable filtered layer backward: holds the workspace; call with an Index per step."""
+
+    def __init__(self, cfg: LayerCfg, B: int, S: int, device="cuda"):
+        self.cfg, self.B, self.S, self.device = cfg, B, S, device
+        self.ws = None
+
+    def workspace(self, M_kept: int):
+        need = collider_layer_workspace_bytes(self.cfg, self.B, self.S, M_kept)
+        if need == 0:
+            raise ColliderError("invalid layer configuration")
+        if self.ws is None or self.ws.numel() < need:
+            self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self.ws
+
+    def __call__(self, weights: dict, saved: dict, dy, index: Index, grads: dict, dy_compact=False,
+                 dx_compact=False, stream=None):
+        ws = self.workspace(index.M_kept)
+        collider_layer_bwd(self.cfg, _struct(LayerWeights, weights), _struct(LayerSaved, saved), dy,
+                           dy_compact, index.c(), _struct(LayerGrads, grads), dx_compact, ws, stream)
+        return grads
+
+
+def layer_bwd(cfg: LayerCfg, weights: dict, saved: dict, dy, index: Index, grads=None, **kw):
+    """One filtered layer backward: returns the dict of gradients (allocated if not given)."""
+    if grads is None:
+        grads = make_grads(cfg, index.B * index.S, index.M_kept, dy.device, kw.get("dx_compact", False))
+    return LayerBackward(cfg, index.B, index.S, dy.device)(weights, saved, dy, index, grads, **kw)

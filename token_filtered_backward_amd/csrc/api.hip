@@ -1,0 +1,350 @@
+// extern "C" entry points of libcollider: argument validation on the host, then launches.
+// Nothing here allocates device memory; nothing throws across the interface.
+#include <algorithm>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace collider {
+
+collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weights* w,
+                          const collider_layer_saved* sv, const void* dy, int dy_compact,
+                          const collider_index& ix, collider_layer_grads* gr, int dx_compact,
+                          void* ws, size_t ws_bytes, hipStream_t s, size_t* need);
+
+// ------------------------------------------------------------------------------------------
+// per-kernel event timing (measurement only; off by default)
+// ------------------------------------------------------------------------------------------
+namespace {
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t pool_get() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
+
+ProfScope::ProfScope(const char* n, hipStream_t s) : name(n), stream(s), slot(-1) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on) return;
+  hipEvent_t a = pool_get(), b = pool_get();
+  if (!a || !b) return;
+  (void)hipEventRecord(a, s);
+  g_prof_recs.push_back(ProfRec{n, a, b});
+  slot = (int)g_prof_recs.size() - 1;
+}
+
+ProfScope::~ProfScope() {
+  if (slot < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  (void)hipEventRecord(g_prof_recs[slot].b, stream);
+}
+
+}  // namespace collider
+
+using namespace collider;
+
+// ------------------------------------------------------------------------------------------
+// validation helpers
+// ------------------------------------------------------------------------------------------
+static bool bad_ptr16(const void* p) { return p == nullptr || !aligned16(p); }
+
+static collider_status check_index(const collider_index* ix) {
+  if (!ix || !ix->idx || !ix->inv || !ix->cu_seqlens || !ix->count) return COLLIDER_ERR_NULL;
+  if (ix->B < 1 || ix->S < 1 || (int64_t)ix->B * ix->S > (1 << 30)) return COLLIDER_ERR_SHAPE;
+  if (ix->M_kept < 0 || ix->M_kept > ix->B * ix->S) return COLLIDER_ERR_SHAPE;
+  return COLLIDER_OK;
+}
+
+static collider_status check_attn_cfg(const collider_attn_cfg* c) {
+  if (!c) return COLLIDER_ERR_NULL;
+  if (c->n_q_heads < 1 || c->n_kv_heads < 1 || c->n_q_heads % c->n_kv_heads) return COLLIDER_ERR_SHAPE;
+  if (c->head_dim != 64 && c->head_dim != 128) return COLLIDER_ERR_UNSUPPORTED;
+  if (c->n_q_heads % 4) return COLLIDER_ERR_UNSUPPORTED;  // lse rows are moved as 16-byte vectors
+  if (c->rot_dims < 0 || c->rot_dims > c->head_dim || c->rot_dims % 16) return COLLIDER_ERR_UNSUPPORTED;
+  if (c->rot_dims > 0 && !(c->rope_base > 1.f)) return COLLIDER_ERR_SHAPE;
+  if (c->softmax_scale < 0.f) return COLLIDER_ERR_SHAPE;
+  if (c->dmode != COLLIDER_ATTN_D_FILTERED && c->dmode != COLLIDER_ATTN_D_FULL) return COLLIDER_ERR_SHAPE;
+  return COLLIDER_OK;
+}
+
+extern "C" {
+
+const char* collider_status_string(collider_status s) {
+  switch (s) {
+    case COLLIDER_OK: return "ok";
+    case COLLIDER_ERR_NULL: return "null pointer argument";
+    case COLLIDER_ERR_SHAPE: return "invalid or inconsistent size";
+    case COLLIDER_ERR_ALIGN: return "pointer or leading dimension not 16-byte aligned";
+    case COLLIDER_ERR_UNSUPPORTED: return "unsupported configuration";
+    case COLLIDER_ERR_WORKSPACE: return "workspace missing or too small";
+    case COLLIDER_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+collider_status collider_build_index(const uint8_t* keep, int32_t B, int32_t S, int32_t* idx,
+                                     int32_t* inv, int32_t* cu_seqlens, int32_t* count,
+                                     hipStream_t stream) {
+  if (!keep || !idx || !inv || !cu_seqlens || !count) return COLLIDER_ERR_NULL;
+  if (B < 1 || S < 1 || (int64_t)B * S > (1 << 30)) return COLLIDER_ERR_SHAPE;
+  return launch_build_index(keep, B, S, idx, inv, cu_seqlens, count, stream);
+}
+
+collider_status collider_index_count_host(const int32_t* count_dev, int32_t* count_host,
+                                          hipStream_t stream) {
+  if (!count_dev || !count_host) return COLLIDER_ERR_NULL;
+  if (hipMemcpyAsync(count_host, count_dev, sizeof(int32_t), hipMemcpyDeviceToHost, stream) !=
+      hipSuccess)
+    return COLLIDER_ERR_HIP;
+  return hipStreamSynchronize(stream) == hipSuccess ? COLLIDER_OK : COLLIDER_ERR_HIP;
+}
+
+static int dt_size(collider_dtype dt) { return dt == COLLIDER_F32 ? 4 : (dt == COLLIDER_BF16 ? 2 : 0); }
+
+collider_status collider_gather_rows(const void* src, int64_t ld_src, void* dst, int64_t ld_dst,
+                                     const int32_t* idx, int32_t n_rows, int32_t row_elems,
+                                     collider_dtype dt, hipStream_t stream) {
+  const int es = dt_size(dt);
+  if (!es) return COLLIDER_ERR_UNSUPPORTED;
+  if (n_rows < 0 || row_elems < 0 || ld_src < row_elems || ld_dst < row_elems) return COLLIDER_ERR_SHAPE;
+  if (n_rows == 0 || row_elems == 0) return COLLIDER_OK;
+  if (!src || !dst || !idx) return COLLIDER_ERR_NULL;
+  if (((uintptr_t)src | (uintptr_t)dst) & (es - 1)) return COLLIDER_ERR_ALIGN;
+  return launch_gather_bytes(src, ld_src * es, dst, ld_dst * es, idx, n_rows, row_elems * es, stream);
+}
+
+collider_status collider_scatter_rows(const void* src, int64_t ld_src, void* dst, int64_t ld_dst,
+                                      const int32_t* inv, int32_t M, int32_t row_elems,
+                                      int32_t zero_fill_filtered, collider_dtype dt,
+                                      hipStream_t stream) {
+  const int es = dt_size(dt);
+  if (!es) return COLLIDER_ERR_UNSUPPORTED;
+  if (M < 0 || row_elems < 0 || ld_src < row_elems || ld_dst < row_elems) return COLLIDER_ERR_SHAPE;
+  if (M == 0 || row_elems == 0) return COLLIDER_OK;
+  if (!src || !dst || !inv) return COLLIDER_ERR_NULL;
+  if (((uintptr_t)src | (uintptr_t)dst) & (es - 1)) return COLLIDER_ERR_ALIGN;
+  return launch_scatter_bytes(src, ld_src * es, dst, ld_dst * es, inv, M, row_elems * es,
+                              zero_fill_filtered, stream);
+}
+
+static void linear_problems(collider_dtype dt, int32_t Mk, int32_t K, int32_t N, const void* x,
+                            int64_t ld_x, const void* dy, int64_t ld_dy, const void* w, void* dx,
+                            float* dw, int32_t accumulate, GemmProblem* pdx, GemmProblem* pdw) {
+  *pdx = GemmProblem{};
+  pdx->M = Mk; pdx->N = K; pdx->K = N;
+  pdx->A = dy; pdx->lda = ld_dy; pdx->a_kmajor = true;
+  pdx->B0 = w; pdx->ldb = K; pdx->b_kmajor = false;
+  pdx->epi = dt == COLLIDER_F32 ? EPI_F32 : EPI_BF16;
+  pdx->C = dx; pdx->ldc = K;
+  *pdw = GemmProblem{};
+  pdw->M = N; pdw->N = K; pdw->K = Mk;
+  pdw->A = dy; pdw->lda = ld_dy; pdw->a_kmajor = false;
+  pdw->B0 = x; pdw->ldb = ld_x; pdw->b_kmajor = false;
+  pdw->epi = EPI_F32; pdw->C = dw; pdw->ldc = K; pdw->accumulate = accumulate;
+}
+
+size_t collider_linear_workspace_bytes(collider_dtype dt, int32_t M_kept, int32_t K, int32_t N) {
+  if (M_kept < 0 || K < 1 || N < 1) return 0;
+  GemmProblem a, b;
+  linear_problems(dt, M_kept, K, N, nullptr, K, nullptr, N, nullptr, nullptr, nullptr, 0, &a, &b);
+  Carver cv(nullptr);
+  cv.take<float>((size_t)norm_bwd_parts(M_kept) * N);  // bias column-sum partials
+  if (dt == COLLIDER_BF16)
+    cv.take<char>(std::max(gemm_bf16_workspace_bytes(a), gemm_bf16_workspace_bytes(b)));
+  return cv.bytes();
+}
+
+collider_status collider_linear_bwd_reduced(collider_dtype dt, int32_t M_kept, int32_t K, int32_t N,
+                                            const void* x, int64_t ld_x, const void* dy,
+                                            int64_t ld_dy, const void* w, void* dx, float* dw,
+                                            float* db, int32_t accumulate, void* ws,
+                                            size_t ws_bytes, hipStream_t stream) {
+  if (dt != COLLIDER_F32 && dt != COLLIDER_BF16) return COLLIDER_ERR_UNSUPPORTED;
+  if (M_kept < 0 || K < 1 || N < 1 || ld_x < K || ld_dy < N) return COLLIDER_ERR_SHAPE;
+  if (!w || !dw || (M_kept > 0 && (!x || !dy))) return COLLIDER_ERR_NULL;
+  if (dt == COLLIDER_BF16) {
+    if (K % 8 || N % 8 || ld_x % 8 || ld_dy % 8) return COLLIDER_ERR_ALIGN;
+    if (!aligned16(w) || (M_kept > 0 && (!aligned16(x) || !aligned16(dy))) || (dx && !aligned16(dx)))
+      return COLLIDER_ERR_ALIGN;
+  }
+  const size_t need = collider_linear_workspace_bytes(dt, M_kept, K, N);
+  if (need > 0 && (!ws || ws_bytes < need)) return COLLIDER_ERR_WORKSPACE;
+  GemmProblem pdx, pdw;
+  linear_problems(dt, M_kept, K, N, x, ld_x, dy, ld_dy, w, dx, dw, accumulate, &pdx, &pdw);
+  Carver cv(ws);
+  float* parts = cv.take<float>((size_t)norm_bwd_parts(M_kept) * N);
+  char* gws = cv.take<char>(0);
+  const size_t gws_bytes = ws_bytes > (size_t)(gws - (char*)ws) ? ws_bytes - (gws - (char*)ws) : 0;
+  collider_status st = COLLIDER_OK;
+  if (dt == COLLIDER_F32) {
+    if (dx) st = gemm_f32(pdx, stream);
+    if (st == COLLIDER_OK) st = gemm_f32(pdw, stream);
+  } else {
+    if (dx) st = gemm_bf16(pdx, gws, gws_bytes, stream);
+    if (st == COLLIDER_OK) st = gemm_bf16(pdw, gws, gws_bytes, stream);
+  }
+  if (st == COLLIDER_OK && db) {
+    if (M_kept > 0)
+      st = launch_colsum(dy, ld_dy, M_kept, N, dt == COLLIDER_BF16, db, accumulate, parts, stream);
+    else if (!accumulate)
+      st = launch_fill_f32(db, N, 0.f, stream);
+  }
+  return st;
+}
+
+size_t collider_attn_workspace_bytes(const collider_attn_cfg* cfg, const collider_index* ix) {
+  if (check_attn_cfg(cfg) != COLLIDER_OK || !ix || ix->B < 1 || ix->S < 1 || ix->M_kept < 0) return 0;
+  return attn_workspace_bytes(*cfg, ix->B, ix->S, ix->M_kept);
+}
+
+collider_status collider_attn_bwd_filtered(const collider_attn_cfg* cfg, const collider_index* ix,
+                                           const collider_attn_io* io, void* ws, size_t ws_bytes,
+                                           hipStream_t stream) {
+  collider_status st = check_attn_cfg(cfg);
+  if (st != COLLIDER_OK) return st;
+  if ((st = check_index(ix)) != COLLIDER_OK) return st;
+  if (!io) return COLLIDER_ERR_NULL;
+  if (ix->M_kept == 0) return COLLIDER_OK;
+  const int d = cfg->head_dim, nqd = cfg->n_q_heads * d, nkvd = cfg->n_kv_heads * d;
+  if (!io->q || !io->k || !io->v || !io->lse || !io->dout || !io->dq || !io->dk || !io->dv)
+    return COLLIDER_ERR_NULL;
+  if (cfg->dmode == COLLIDER_ATTN_D_FULL && !io->o) return COLLIDER_ERR_NULL;
+  if (io->ld_q < nqd || io->ld_k < nkvd || io->ld_v < nkvd || io->ld_do < nqd || io->ld_dq < nqd ||
+      io->ld_dk < nkvd || io->ld_dv < nkvd || io->ld_lse < cfg->n_q_heads ||
+      (cfg->dmode == COLLIDER_ATTN_D_FULL && io->ld_o < nqd))
+    return COLLIDER_ERR_SHAPE;
+  const void* p16[] = {io->q, io->k, io->v, io->dout, io->dq, io->dk, io->dv};
+  for (const void* p : p16)
+    if (bad_ptr16(p)) return COLLIDER_ERR_ALIGN;
+  if ((io->ld_q | io->ld_k | io->ld_v | io->ld_do | io->ld_dq | io->ld_dk | io->ld_dv) % 8)
+    return COLLIDER_ERR_ALIGN;
+  if (cfg->dmode == COLLIDER_ATTN_D_FULL && (bad_ptr16(io->o) || io->ld_o % 8)) return COLLIDER_ERR_ALIGN;
+  const size_t need = attn_workspace_bytes(*cfg, ix->B, ix->S, ix->M_kept);
+  if (!ws || ws_bytes < need) return COLLIDER_ERR_WORKSPACE;
+  return attn_bwd(*cfg, *ix, *io, ws, ws_bytes, stream);
+}
+
+static collider_status check_layer(const collider_layer_cfg* c) {
+  if (!c) return COLLIDER_ERR_NULL;
+  if (c->kind != COLLIDER_LAYER_LLAMA && c->kind != COLLIDER_LAYER_PHI) return COLLIDER_ERR_UNSUPPORTED;
+  if (c->hidden < 8 || c->inter < 8 || c->hidden % 8 || c->inter % 8) return COLLIDER_ERR_SHAPE;
+  if (c->hidden > 4096) return COLLIDER_ERR_UNSUPPORTED;  // norm backward keeps a row in registers
+  collider_attn_cfg ac{c->n_q_heads, c->n_kv_heads, c->head_dim, c->rot_dims, c->rope_base, 0.f, c->dmode};
+  collider_status st = check_attn_cfg(&ac);
+  if (st != COLLIDER_OK) return st;
+  if (c->kind == COLLIDER_LAYER_PHI && ((c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim) % 64)
+    return COLLIDER_ERR_UNSUPPORTED;
+  return COLLIDER_OK;
+}
+
+size_t collider_layer_workspace_bytes(const collider_layer_cfg* cfg, int32_t B, int32_t S,
+                                      int32_t M_kept) {
+  if (check_layer(cfg) != COLLIDER_OK || B < 1 || S < 1 || M_kept < 0 || M_kept > B * S) return 0;
+  collider_index ix{};
+  ix.B = B;
+  ix.S = S;
+  ix.M_kept = M_kept;
+  size_t need = 0;
+  layer_run(*cfg, nullptr, nullptr, nullptr, 0, ix, nullptr, 0, nullptr, 0, nullptr, &need);
+  // dy_compact / dx_compact only remove buffers, so this bound covers every variant
+  return need;
+}
+
+collider_status collider_layer_bwd(const collider_layer_cfg* cfg, const collider_layer_weights* w,
+                                   const collider_layer_saved* sv, const void* dy,
+                                   int32_t dy_compact, const collider_index* ix,
+                                   collider_layer_grads* g, int32_t dx_compact, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+  collider_status st = check_layer(cfg);
+  if (st != COLLIDER_OK) return st;
+  if ((st = check_index(ix)) != COLLIDER_OK) return st;
+  if (!w || !sv || !g || !dy) return COLLIDER_ERR_NULL;
+  const bool llama = cfg->kind == COLLIDER_LAYER_LLAMA;
+  const void* wp[] = {w->w_qkv, w->w_o, llama ? w->w_gateup : w->w_fc1, llama ? w->w_down : w->w_fc2};
+  const void* sp16[] = {sv->x, sv->q, sv->k, sv->v, sv->o, llama ? sv->h : sv->f,
+                        llama ? sv->gate : sv->f, llama ? sv->up : sv->f, dy, g->dx};
+  for (const void* p : wp)
+    if (!p) return COLLIDER_ERR_NULL;
+  for (const void* p : sp16)
+    if (!p) return COLLIDER_ERR_NULL;
+  if (!sv->lse || !sv->rstd1 || (!llama && !sv->mean) || (llama && !sv->rstd2)) return COLLIDER_ERR_NULL;
+  if (llama && (!w->gamma1 || !w->gamma2 || !g->dgamma1 || !g->dgamma2 || !g->dw_gateup || !g->dw_down))
+    return COLLIDER_ERR_NULL;
+  if (!llama && (!w->ln_gamma || !w->ln_beta || !g->dln_gamma || !g->dln_beta || !g->dw_fc1 || !g->dw_fc2))
+    return COLLIDER_ERR_NULL;
+  if (!g->dw_qkv || !g->dw_o) return COLLIDER_ERR_NULL;
+  for (const void* p : wp)
+    if (!aligned16(p)) return COLLIDER_ERR_ALIGN;
+  for (const void* p : sp16)
+    if (!aligned16(p)) return COLLIDER_ERR_ALIGN;
+  const float* f16[] = {sv->lse, llama ? w->gamma1 : w->ln_gamma, llama ? w->gamma2 : w->ln_beta};
+  for (const float* p : f16)
+    if (!aligned16(p)) return COLLIDER_ERR_ALIGN;
+  size_t need = 0;
+  layer_run(*cfg, nullptr, nullptr, nullptr, dy_compact, *ix, nullptr, dx_compact, nullptr, 0,
+            nullptr, &need);
+  if (!ws || ws_bytes < need) return COLLIDER_ERR_WORKSPACE;
+  return layer_run(*cfg, w, sv, dy, dy_compact, *ix, g, dx_compact, ws, ws_bytes, stream, nullptr);
+}
+
+collider_status collider_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return COLLIDER_OK;
+}
+
+int32_t collider_profile_collect(char* names, int32_t name_cap, double* total_ms, int32_t* launches,
+                                 int32_t max_kernels) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  std::vector<std::string> order;
+  std::map<std::string, std::pair<double, int>> agg;
+  for (const ProfRec& r : g_prof_recs) {
+    if (hipEventSynchronize(r.b) != hipSuccess) return -1;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return -1;
+    auto it = agg.find(r.name);
+    if (it == agg.end()) {
+      order.push_back(r.name);
+      agg[r.name] = {ms, 1};
+    } else {
+      it->second.first += ms;
+      it->second.second += 1;
+    }
+    g_prof_pool.push_back(r.a);
+    g_prof_pool.push_back(r.b);
+  }
+  g_prof_recs.clear();
+  int n = 0, off = 0;
+  for (const std::string& nm : order) {
+    if (n >= max_kernels) break;
+    if (names) {
+      if (off + (int)nm.size() + 1 > name_cap) break;
+      std::memcpy(names + off, nm.c_str(), nm.size() + 1);
+      off += (int)nm.size() + 1;
+    }
+    if (total_ms) total_ms[n] = agg[nm].first;
+    if (launches) launches[n] = agg[nm].second;
+    ++n;
+  }
+  return n;
+}
+
+}  // extern "C"

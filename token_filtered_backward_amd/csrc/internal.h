@@ -1,0 +1,151 @@
+// Internal declarations of libcollider (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/collider.h"
+
+namespace collider {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------------------------------
+// bf16 helpers (uint16 storage)
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  __bf16 h = (__bf16)f;  // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+__device__ __forceinline__ float bflo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bfhi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ------------------------------------------------------------------------------------------
+// launch bookkeeping: error check + optional per-kernel event timing
+// ------------------------------------------------------------------------------------------
+struct ProfScope {
+  const char* name;
+  hipStream_t stream;
+  int slot;
+  ProfScope(const char* n, hipStream_t s);
+  ~ProfScope();
+};
+
+#define COLLIDER_LAUNCH(name, stream, ...)                  \
+  do {                                                      \
+    ::collider::ProfScope _ps(name, stream);                \
+    __VA_ARGS__;                                            \
+  } while (0)
+
+inline collider_status last_hip_status() {
+  return hipGetLastError() == hipSuccess ? COLLIDER_OK : COLLIDER_ERR_HIP;
+}
+
+inline bool aligned16(const void* p) { return (((uintptr_t)p) & 15u) == 0; }
+
+// ------------------------------------------------------------------------------------------
+// workspace carving (256-byte aligned sub-buffers)
+// ------------------------------------------------------------------------------------------
+struct Carver {
+  char* base;
+  size_t off;
+  explicit Carver(void* b) : base((char*)b), off(0) {}
+  template <class T>
+  T* take(size_t n) {
+    off = (off + 255) & ~(size_t)255;
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += n * sizeof(T);
+    return p;
+  }
+  size_t bytes() const { return (off + 255) & ~(size_t)255; }
+};
+
+// ------------------------------------------------------------------------------------------
+// kernel launchers (each returns the launch status)
+// ------------------------------------------------------------------------------------------
+
+// mask -> index (index.hip)
+collider_status launch_build_index(const uint8_t* keep, int B, int S, int32_t* idx, int32_t* inv,
+                                   int32_t* cu, int32_t* count, hipStream_t s);
+
+// rows.hip
+struct GatherDesc {
+  const void* src;
+  void* dst;
+  int64_t ld_src, ld_dst;  // in 16-byte units
+  int32_t row_vec16;       // 16-byte vectors per row
+  int32_t tail_bytes;      // bytes after the last whole vector (0, 4, 8, 12 allowed)
+};
+collider_status launch_gather_rows(const GatherDesc* d, int n_desc, const int32_t* idx, int n_rows,
+                                   hipStream_t s);
+collider_status launch_gather_bytes(const void* src, int64_t ld_src_b, void* dst, int64_t ld_dst_b,
+                                    const int32_t* idx, int n_rows, int row_bytes, hipStream_t s);
+collider_status launch_scatter_bytes(const void* src, int64_t ld_src_b, void* dst, int64_t ld_dst_b,
+                                     const int32_t* inv, int M, int row_bytes, int zero_fill,
+                                     hipStream_t s);
+
+// xn = norm(x[rowmap[c]]) as bf16 (RMSNorm when mean == nullptr, else LayerNorm with beta)
+collider_status launch_norm_recompute(const uint16_t* x, const float* mean, const float* rstd,
+                                      const float* gamma, const float* beta, const int32_t* rowmap,
+                                      int rows, int H, uint16_t* xn, hipStream_t s);
+// a = act(gate/f [rowmap[c]]) as bf16: SwiGLU (up != nullptr) or GELU-tanh (up == nullptr)
+collider_status launch_act_recompute(const uint16_t* g, const uint16_t* up, const int32_t* rowmap,
+                                     int rows, int I, uint16_t* a, hipStream_t s);
+// dx = dres + norm_bwd(dxn; x[rowmap], stats) ; per-block partial sums for dgamma (and dbeta)
+collider_status launch_norm_bwd(const uint16_t* dxn, const uint16_t* dres, const uint16_t* x,
+                                const float* mean, const float* rstd, const float* gamma,
+                                const int32_t* rowmap, int rows, int H, uint16_t* dx,
+                                float* part_dgamma, float* part_dbeta, int n_part, hipStream_t s);
+int norm_bwd_parts(int rows);
+collider_status launch_colsum_parts(const float* parts, int n_part, int H, float* out,
+                                    int accumulate, hipStream_t s);
+// column sums of a bf16 / f32 matrix (bias gradient)
+collider_status launch_colsum(const void* x, int64_t ld, int rows, int cols, bool bf16, float* out,
+                              int accumulate, float* ws, hipStream_t s);
+collider_status launch_fill_f32(float* p, size_t n, float v, hipStream_t s);
+// rotary tables cos/sin [S, rot/2] float32
+collider_status launch_rope_table(float* cs, int S, int rot, float base, hipStream_t s);
+
+// gemm.hip
+enum EpiKind { EPI_BF16 = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_GELU = 3 };
+struct GemmProblem {
+  // C[M, N] = sum_k A(m, k) B(k, n)
+  int M, N, K;
+  const void* A;
+  int64_t lda;
+  bool a_kmajor;  // A(m,k) = A[m*lda + k] (true) or A[k*lda + m] (false)
+  const void* B0;
+  const void* B1;  // k >= kseg reads B1 at k - kseg (nullptr: single segment)
+  int kseg;
+  int64_t ldb;
+  bool b_kmajor;  // B(k,n) = B[n*ldb + k] (true) or B[k*ldb + n] (false)
+  // epilogue
+  int epi;
+  void* C;
+  int64_t ldc;
+  int accumulate;
+  // SwiGLU / GELU epilogue: saved tensors read at row rowmap[m] (nullptr: row m)
+  const uint16_t* g;   // gate (SwiGLU) or f (GELU)
+  const uint16_t* up;  // SwiGLU only
+  int64_t ld_g;
+  const int32_t* rowmap;
+  uint16_t* out2;      // SwiGLU: dup written at out2 (C gets dgate); GELU: unused
+  int64_t ld_out2;
+};
+size_t gemm_bf16_workspace_bytes(const GemmProblem& p);
+collider_status gemm_bf16(const GemmProblem& p, void* ws, size_t ws_bytes, hipStream_t s);
+collider_status gemm_f32(const GemmProblem& p, hipStream_t s);
+
+// attn.hip
+size_t attn_workspace_bytes(const collider_attn_cfg& c, int B, int S, int M_kept);
+collider_status attn_bwd(const collider_attn_cfg& c, const collider_index& ix,
+                         const collider_attn_io& io, void* ws, size_t ws_bytes, hipStream_t s);
+
+}  // namespace collider

@@ -1,0 +1,222 @@
+// Whole-layer filtered backward (Collider paper, abstract: the activations of filtered tokens are
+// filtered across all layers; every linear backward becomes a dense GEMM over the kept tokens).
+//
+// The sequence of launches for one layer, all on one stream, no host synchronisation:
+//   gather   dY', O', Q', K', V', lse' (one multi-tensor launch; saved tensors are full-layout)
+//   LLAMA                                         PHI (parallel block)
+//   a'  = silu(gate')*up'   (recompute)           g' = gelu_tanh(f')       (recompute)
+//   dA  = dY' w_down   -> SwiGLU bwd epilogue     dF = dY' w_fc2 -> GELU bwd epilogue
+//   dw_down = dY'^T a'                            dw_fc2 = dY'^T g'
+//   dXn2 = [dgate|dup] w_gateup                   dO = dY' w_o;  dw_o = dY'^T O'
+//   dw_gateup = [dgate|dup]^T xn2'                attention bwd -> [dq|dk|dv]
+//   dh = dY' + RMSNorm2 bwd(dXn2)                 dXn = [dq|dk|dv|dF] [w_qkv; w_fc1]
+//   dO = dh w_o;  dw_o = dh^T O'                  dw_qkv, dw_fc1 = (...)^T xn'
+//   attention bwd -> [dq|dk|dv]                   dx = dY' + LayerNorm bwd(dXn)
+//   dXn1 = [dq|dk|dv] w_qkv; dw_qkv = (...)^T xn1'
+//   dx = dh + RMSNorm1 bwd(dXn1)
+//   scatter dx to the full layout (filtered rows +0.0) unless the caller keeps it compact.
+// Normalised inputs (xn1', xn2') and activations (a', g') are recomputed from saved tensors read
+// through the index; the SwiGLU / GELU backward is fused into the epilogue of the GEMM producing dA.
+#include <algorithm>
+
+#include "internal.h"
+
+namespace collider {
+
+namespace {
+
+struct LayerBufs {
+  uint16_t *dy_c, *o_c, *q_c, *k_c, *v_c;
+  float* lse_c;
+  uint16_t *act_c, *xn_c, *dmid, *dxn, *dh, *do_c, *dx_c;
+  float *part_g, *part_b;
+  void* gemm_ws;
+  void* attn_ws;
+  size_t gemm_ws_bytes, attn_ws_bytes;
+};
+
+}  // namespace
+
+collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weights* w,
+                          const collider_layer_saved* sv, const void* dy, int dy_compact,
+                          const collider_index& ix, collider_layer_grads* gr, int dx_compact,
+                          void* ws, size_t ws_bytes, hipStream_t s, size_t* need) {
+  const bool llama = c.kind == COLLIDER_LAYER_LLAMA;
+  const int B = ix.B, S = ix.S, M = B * S, Mk = ix.M_kept;
+  const int H = c.hidden, I = c.inter, d = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
+  const int nqd = nq * d, nkvd = nkv * d, nqkv = nqd + 2 * nkvd;
+  const int mid = llama ? 2 * I : nqkv + I;  // width of [dgate|dup] or [dq|dk|dv|dF]
+  const int parts = norm_bwd_parts(Mk);
+  const bool dry = need != nullptr;
+
+  Carver cv(dry ? nullptr : ws);
+  LayerBufs b{};
+  b.dy_c = dy_compact ? (uint16_t*)dy : cv.take<uint16_t>((size_t)Mk * H);
+  b.o_c = cv.take<uint16_t>((size_t)Mk * nqd);
+  b.q_c = cv.take<uint16_t>((size_t)Mk * nqd);
+  b.k_c = cv.take<uint16_t>((size_t)Mk * nkvd);
+  b.v_c = cv.take<uint16_t>((size_t)Mk * nkvd);
+  b.lse_c = cv.take<float>((size_t)Mk * nq);
+  b.act_c = cv.take<uint16_t>((size_t)Mk * I);
+  b.xn_c = cv.take<uint16_t>((size_t)Mk * H);
+  b.dmid = cv.take<uint16_t>((size_t)Mk * mid);
+  b.dxn = cv.take<uint16_t>((size_t)Mk * H);
+  b.dh = llama ? cv.take<uint16_t>((size_t)Mk * H) : nullptr;
+  b.do_c = cv.take<uint16_t>((size_t)Mk * nqd);
+  b.dx_c = dx_compact ? (uint16_t*)(gr ? gr->dx : nullptr) : cv.take<uint16_t>((size_t)Mk * H);
+  b.part_g = cv.take<float>((size_t)parts * H);
+  b.part_b = cv.take<float>((size_t)parts * H);
+
+  // GEMM problems (pointers are only meaningful when not dry)
+  const int32_t* idx = ix.idx;
+  GemmProblem g_dA{}, g_dw2{}, g_dXmid{}, g_dwmid{}, g_dO{}, g_dwo{}, g_dXin{}, g_dwqkv{}, g_dwfc1{};
+  auto dx_gemm = [&](GemmProblem& p, int n, int k, const void* A, int64_t lda, const void* Bm,
+                     int64_t ldb, int epi, void* C, int64_t ldc) {
+    p.M = Mk; p.N = n; p.K = k;
+    p.A = A; p.lda = lda; p.a_kmajor = true;
+    p.B0 = Bm; p.ldb = ldb; p.b_kmajor = false;
+    p.epi = epi; p.C = C; p.ldc = ldc;
+  };
+  auto dw_gemm = [&](GemmProblem& p, int m, int n, const void* A, int64_t lda, const void* Bm,
+                     int64_t ldb, float* C) {
+    p.M = m; p.N = n; p.K = Mk;
+    p.A = A; p.lda = lda; p.a_kmajor = false;
+    p.B0 = Bm; p.ldb = ldb; p.b_kmajor = false;
+    p.epi = EPI_F32; p.C = C; p.ldc = n; p.accumulate = c.accumulate;
+  };
+  if (llama) {
+    dx_gemm(g_dA, I, H, b.dy_c, H, w ? w->w_down : nullptr, I, EPI_SWIGLU, b.dmid, mid);
+    g_dA.g = sv ? (const uint16_t*)sv->gate : nullptr;
+    g_dA.up = sv ? (const uint16_t*)sv->up : nullptr;
+    g_dA.ld_g = I;
+    g_dA.rowmap = idx;
+    g_dA.out2 = b.dmid ? b.dmid + I : nullptr;
+    g_dA.ld_out2 = mid;
+    dw_gemm(g_dw2, H, I, b.dy_c, H, b.act_c, I, gr ? gr->dw_down : nullptr);
+    dx_gemm(g_dXmid, H, 2 * I, b.dmid, mid, w ? w->w_gateup : nullptr, H, EPI_BF16, b.dxn, H);
+    dw_gemm(g_dwmid, 2 * I, H, b.dmid, mid, b.xn_c, H, gr ? gr->dw_gateup : nullptr);
+    dx_gemm(g_dO, nqd, H, b.dh, H, w ? w->w_o : nullptr, nqd, EPI_BF16, b.do_c, nqd);
+    dw_gemm(g_dwo, H, nqd, b.dh, H, b.o_c, nqd, gr ? gr->dw_o : nullptr);
+    dx_gemm(g_dXin, H, nqkv, b.dmid, mid, w ? w->w_qkv : nullptr, H, EPI_BF16, b.dxn, H);
+    dw_gemm(g_dwqkv, nqkv, H, b.dmid, mid, b.xn_c, H, gr ? gr->dw_qkv : nullptr);
+  } else {
+    uint16_t* dF = b.dmid ? b.dmid + nqkv : nullptr;
+    dx_gemm(g_dA, I, H, b.dy_c, H, w ? w->w_fc2 : nullptr, I, EPI_GELU, dF, mid);
+    g_dA.g = sv ? (const uint16_t*)sv->f : nullptr;
+    g_dA.ld_g = I;
+    g_dA.rowmap = idx;
+    dw_gemm(g_dw2, H, I, b.dy_c, H, b.act_c, I, gr ? gr->dw_fc2 : nullptr);
+    dx_gemm(g_dO, nqd, H, b.dy_c, H, w ? w->w_o : nullptr, nqd, EPI_BF16, b.do_c, nqd);
+    dw_gemm(g_dwo, H, nqd, b.dy_c, H, b.o_c, nqd, gr ? gr->dw_o : nullptr);
+    dx_gemm(g_dXin, H, nqkv + I, b.dmid, mid, w ? w->w_qkv : nullptr, H, EPI_BF16, b.dxn, H);
+    g_dXin.B1 = w ? w->w_fc1 : nullptr;
+    g_dXin.kseg = nqkv;
+    dw_gemm(g_dwqkv, nqkv, H, b.dmid, mid, b.xn_c, H, gr ? gr->dw_qkv : nullptr);
+    dw_gemm(g_dwfc1, I, H, dF, mid, b.xn_c, H, gr ? gr->dw_fc1 : nullptr);
+  }
+  const GemmProblem* gl[] = {&g_dA, &g_dw2, &g_dXmid, &g_dwmid, &g_dO, &g_dwo, &g_dXin, &g_dwqkv,
+                             &g_dwfc1};
+  size_t gemm_need = 0;
+  for (const GemmProblem* p : gl)
+    if (p->M > 0) gemm_need = std::max(gemm_need, gemm_bf16_workspace_bytes(*p));
+  b.gemm_ws = cv.take<char>(gemm_need);
+  b.gemm_ws_bytes = gemm_need;
+
+  collider_attn_cfg ac{};
+  ac.n_q_heads = nq;
+  ac.n_kv_heads = nkv;
+  ac.head_dim = d;
+  ac.rot_dims = c.rot_dims;
+  ac.rope_base = c.rope_base;
+  ac.softmax_scale = 0.f;
+  ac.dmode = c.dmode;
+  b.attn_ws_bytes = attn_workspace_bytes(ac, B, S, Mk);
+  b.attn_ws = cv.take<char>(b.attn_ws_bytes);
+
+  if (dry) {
+    *need = cv.bytes();
+    return COLLIDER_OK;
+  }
+  if (ws_bytes < cv.bytes()) return COLLIDER_ERR_WORKSPACE;
+
+  collider_status st;
+#define CHECK(x)                       \
+  do {                                 \
+    st = (x);                          \
+    if (st != COLLIDER_OK) return st;  \
+  } while (0)
+
+  if (Mk > 0) {
+    // 1. gathers of the saved tensors the dense GEMMs / attention read as compacted operands
+    GatherDesc gd[6];
+    int nd = 0;
+    auto add = [&](const void* src, void* dst, int row_bytes) {
+      gd[nd++] = GatherDesc{src, dst, row_bytes / 16, row_bytes / 16, row_bytes / 16, 0};
+    };
+    if (!dy_compact) add(dy, b.dy_c, H * 2);
+    add(sv->o, b.o_c, nqd * 2);
+    add(sv->q, b.q_c, nqd * 2);
+    add(sv->k, b.k_c, nkvd * 2);
+    add(sv->v, b.v_c, nkvd * 2);
+    add(sv->lse, b.lse_c, nq * 4);
+    CHECK(launch_gather_rows(gd, nd, idx, Mk, s));
+  }
+  if (llama) {
+    CHECK(launch_act_recompute((const uint16_t*)sv->gate, (const uint16_t*)sv->up, idx, Mk, I,
+                               b.act_c, s));
+    CHECK(gemm_bf16(g_dA, b.gemm_ws, b.gemm_ws_bytes, s));
+    CHECK(gemm_bf16(g_dw2, b.gemm_ws, b.gemm_ws_bytes, s));
+    CHECK(launch_norm_recompute((const uint16_t*)sv->h, nullptr, sv->rstd2, w->gamma2, nullptr, idx,
+                                Mk, H, b.xn_c, s));
+    CHECK(gemm_bf16(g_dXmid, b.gemm_ws, b.gemm_ws_bytes, s));
+    CHECK(gemm_bf16(g_dwmid, b.gemm_ws, b.gemm_ws_bytes, s));
+    CHECK(launch_norm_bwd(b.dxn, b.dy_c, (const uint16_t*)sv->h, nullptr, sv->rstd2, w->gamma2, idx,
+                          Mk, H, b.dh, b.part_g, nullptr, parts, s));
+    CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dgamma2, c.accumulate, s));
+    CHECK(gemm_bf16(g_dO, b.gemm_ws, b.gemm_ws_bytes, s));
+    CHECK(gemm_bf16(g_dwo, b.gemm_ws, b.gemm_ws_bytes, s));
+  } else {
+    CHECK(launch_act_recompute((const uint16_t*)sv->f, nullptr, idx, Mk, I, b.act_c, s));
+    CHECK(gemm_bf16(g_dA, b.gemm_ws, b.gemm_ws_bytes, s));
+    CHECK(gemm_bf16(g_dw2, b.gemm_ws, b.gemm_ws_bytes, s));
+    CHECK(gemm_bf16(g_dO, b.gemm_ws, b.gemm_ws_bytes, s));
+    CHECK(gemm_bf16(g_dwo, b.gemm_ws, b.gemm_ws_bytes, s));
+  }
+  // attention backward -> [dq | dk | dv] columns of dmid
+  collider_attn_io io{};
+  io.q = b.q_c; io.ld_q = nqd;
+  io.k = b.k_c; io.ld_k = nkvd;
+  io.v = b.v_c; io.ld_v = nkvd;
+  io.o = b.o_c; io.ld_o = nqd;
+  io.lse = b.lse_c; io.ld_lse = nq;
+  io.dout = b.do_c; io.ld_do = nqd;
+  io.dq = b.dmid; io.ld_dq = mid;
+  io.dk = b.dmid + nqd; io.ld_dk = mid;
+  io.dv = b.dmid + nqd + nkvd; io.ld_dv = mid;
+  CHECK(attn_bwd(ac, ix, io, b.attn_ws, b.attn_ws_bytes, s));
+  if (llama) {
+    CHECK(launch_norm_recompute((const uint16_t*)sv->x, nullptr, sv->rstd1, w->gamma1, nullptr, idx,
+                                Mk, H, b.xn_c, s));
+    CHECK(gemm_bf16(g_dXin, b.gemm_ws, b.gemm_ws_bytes, s));
+    CHECK(gemm_bf16(g_dwqkv, b.gemm_ws, b.gemm_ws_bytes, s));
+    CHECK(launch_norm_bwd(b.dxn, b.dh, (const uint16_t*)sv->x, nullptr, sv->rstd1, w->gamma1, idx, Mk,
+                          H, b.dx_c, b.part_g, nullptr, parts, s));
+    CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dgamma1, c.accumulate, s));
+  } else {
+    CHECK(launch_norm_recompute((const uint16_t*)sv->x, sv->mean, sv->rstd1, w->ln_gamma, w->ln_beta,
+                                idx, Mk, H, b.xn_c, s));
+    CHECK(gemm_bf16(g_dXin, b.gemm_ws, b.gemm_ws_bytes, s));
+    CHECK(gemm_bf16(g_dwqkv, b.gemm_ws, b.gemm_ws_bytes, s));
+    CHECK(gemm_bf16(g_dwfc1, b.gemm_ws, b.gemm_ws_bytes, s));
+    CHECK(launch_norm_bwd(b.dxn, b.dy_c, (const uint16_t*)sv->x, sv->mean, sv->rstd1, w->ln_gamma,
+                          idx, Mk, H, b.dx_c, b.part_g, b.part_b, parts, s));
+    CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dln_gamma, c.accumulate, s));
+    CHECK(launch_colsum_parts(b.part_b, Mk > 0 ? parts : 0, H, gr->dln_beta, c.accumulate, s));
+  }
+  if (!dx_compact) CHECK(launch_scatter_bytes(b.dx_c, (int64_t)H * 2, gr->dx, (int64_t)H * 2, ix.inv,
+                                              M, H * 2, 1, s));
+#undef CHECK
+  return COLLIDER_OK;
+}
+
+}  // namespace collider

@@ -1,0 +1,438 @@
+// Row-wise kernels: gather / scatter of token rows, activation and norm recomputation, norm
+// backward, column sums and rotary tables.  All are HBM-bound streaming kernels: rows are moved in
+// 16-byte vectors, one wavefront (or workgroup) per row, consecutive lanes on consecutive vectors.
+//
+// Dimension reduction (Collider paper, abstract): the rows of kept tokens are gathered into dense
+// [M_kept, C] operands; the scatter puts results back with filtered rows exactly zero.
+#include "internal.h"
+
+namespace collider {
+
+// ------------------------------------------------------------------------------------------
+// gather: dst[c] = src[idx[c]], several tensors per launch (blockIdx.y = descriptor)
+// ------------------------------------------------------------------------------------------
+struct GatherBatch {
+  GatherDesc d[8];
+};
+
+static constexpr int kRowsPerBlock = 16;
+
+__global__ __launch_bounds__(256) void gather_rows_kernel(GatherBatch batch,
+                                                          const int32_t* __restrict__ idx,
+                                                          int n_rows) {
+  const GatherDesc& d = batch.d[blockIdx.y];
+  const int r0 = blockIdx.x * kRowsPerBlock;
+  const int nr = min(kRowsPerBlock, n_rows - r0);
+  if (nr <= 0) return;
+  const int per_row = d.row_vec16;
+  const int items = nr * per_row;
+  const uint4* __restrict__ src = (const uint4*)d.src;
+  uint4* __restrict__ dst = (uint4*)d.dst;
+  for (int i = threadIdx.x; i < items; i += 256) {
+    const int rr = i / per_row, v = i - rr * per_row;
+    const int c = r0 + rr;
+    const int64_t t = idx[c];
+    dst[(int64_t)c * d.ld_dst + v] = src[t * d.ld_src + v];
+  }
+  if (d.tail_bytes) {  // 4-byte tail words (row bytes not a multiple of 16)
+    const int tw = d.tail_bytes >> 2;
+    for (int i = threadIdx.x; i < nr * tw; i += 256) {
+      const int rr = i / tw, w = i - rr * tw;
+      const int c = r0 + rr;
+      const int64_t t = idx[c];
+      const uint32_t* s32 = (const uint32_t*)(src + t * d.ld_src + per_row);
+      uint32_t* d32 = (uint32_t*)(dst + (int64_t)c * d.ld_dst + per_row);
+      d32[w] = s32[w];
+    }
+  }
+}
+
+collider_status launch_gather_rows(const GatherDesc* d, int n_desc, const int32_t* idx, int n_rows,
+                                   hipStream_t s) {
+  if (n_rows <= 0 || n_desc <= 0) return COLLIDER_OK;
+  for (int base = 0; base < n_desc; base += 8) {
+    GatherBatch b;
+    const int n = n_desc - base < 8 ? n_desc - base : 8;
+    for (int i = 0; i < n; ++i) b.d[i] = d[base + i];
+    dim3 grid((n_rows + kRowsPerBlock - 1) / kRowsPerBlock, n);
+    COLLIDER_LAUNCH("gather_rows", s,
+                    hipLaunchKernelGGL(gather_rows_kernel, grid, dim3(256), 0, s, b, idx, n_rows));
+  }
+  return last_hip_status();
+}
+
+// Generic byte-granular gather / scatter (2-byte units) for rows that are not 16-byte multiples.
+__global__ void gather_u16_kernel(const uint16_t* __restrict__ src, int64_t ld_src,
+                                  uint16_t* __restrict__ dst, int64_t ld_dst,
+                                  const int32_t* __restrict__ idx, int n_rows, int row_u16) {
+  const int c = blockIdx.x;
+  if (c >= n_rows) return;
+  const int64_t t = idx[c];
+  for (int j = threadIdx.x; j < row_u16; j += blockDim.x) dst[c * ld_dst + j] = src[t * ld_src + j];
+}
+
+collider_status launch_gather_bytes(const void* src, int64_t ld_src_b, void* dst, int64_t ld_dst_b,
+                                    const int32_t* idx, int n_rows, int row_bytes, hipStream_t s) {
+  if (n_rows <= 0) return COLLIDER_OK;
+  if (row_bytes % 16 == 0 && ld_src_b % 16 == 0 && ld_dst_b % 16 == 0 && aligned16(src) &&
+      aligned16(dst)) {
+    GatherDesc d{src, dst, ld_src_b / 16, ld_dst_b / 16, row_bytes / 16, 0};
+    return launch_gather_rows(&d, 1, idx, n_rows, s);
+  }
+  COLLIDER_LAUNCH("gather_rows_u16", s,
+                  hipLaunchKernelGGL(gather_u16_kernel, dim3(n_rows), dim3(128), 0, s,
+                                     (const uint16_t*)src, ld_src_b / 2, (uint16_t*)dst,
+                                     ld_dst_b / 2, idx, n_rows, row_bytes / 2));
+  return last_hip_status();
+}
+
+// ------------------------------------------------------------------------------------------
+// scatter: dst[t] = inv[t] >= 0 ? src[inv[t]] : 0 (or untouched), for every t < M
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4* __restrict__ src,
+                                                           int64_t ld_src, uint4* __restrict__ dst,
+                                                           int64_t ld_dst,
+                                                           const int32_t* __restrict__ inv, int M,
+                                                           int per_row, int zero_fill) {
+  const int r0 = blockIdx.x * kRowsPerBlock;
+  const int nr = min(kRowsPerBlock, M - r0);
+  if (nr <= 0) return;
+  const int items = nr * per_row;
+  for (int i = threadIdx.x; i < items; i += 256) {
+    const int rr = i / per_row, v = i - rr * per_row;
+    const int t = r0 + rr;
+    const int c = inv[t];
+    if (c >= 0) {
+      dst[(int64_t)t * ld_dst + v] = src[(int64_t)c * ld_src + v];
+    } else if (zero_fill) {
+      dst[(int64_t)t * ld_dst + v] = make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+__global__ void scatter_u16_kernel(const uint16_t* __restrict__ src, int64_t ld_src,
+                                   uint16_t* __restrict__ dst, int64_t ld_dst,
+                                   const int32_t* __restrict__ inv, int M, int row_u16,
+                                   int zero_fill) {
+  const int t = blockIdx.x;
+  if (t >= M) return;
+  const int c = inv[t];
+  if (c < 0 && !zero_fill) return;
+  for (int j = threadIdx.x; j < row_u16; j += blockDim.x)
+    dst[(int64_t)t * ld_dst + j] = c >= 0 ? src[(int64_t)c * ld_src + j] : (uint16_t)0;
+}
+
+collider_status launch_scatter_bytes(const void* src, int64_t ld_src_b, void* dst, int64_t ld_dst_b,
+                                     const int32_t* inv, int M, int row_bytes, int zero_fill,
+                                     hipStream_t s) {
+  if (M <= 0) return COLLIDER_OK;
+  if (row_bytes % 16 == 0 && ld_src_b % 16 == 0 && ld_dst_b % 16 == 0 && aligned16(src) &&
+      aligned16(dst)) {
+    dim3 grid((M + kRowsPerBlock - 1) / kRowsPerBlock);
+    COLLIDER_LAUNCH("scatter_rows", s,
+                    hipLaunchKernelGGL(scatter_rows_kernel, grid, dim3(256), 0, s,
+                                       (const uint4*)src, ld_src_b / 16, (uint4*)dst,
+                                       ld_dst_b / 16, inv, M, row_bytes / 16, zero_fill));
+  } else {
+    COLLIDER_LAUNCH("scatter_rows_u16", s,
+                    hipLaunchKernelGGL(scatter_u16_kernel, dim3(M), dim3(128), 0, s,
+                                       (const uint16_t*)src, ld_src_b / 2, (uint16_t*)dst,
+                                       ld_dst_b / 2, inv, M, row_bytes / 2, zero_fill));
+  }
+  return last_hip_status();
+}
+
+// ------------------------------------------------------------------------------------------
+// norm recompute: xn[c] = bf16(norm(x[rowmap[c]])), RMSNorm (mean == nullptr) or LayerNorm
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void norm_recompute_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ mean, const float* __restrict__ rstd,
+    const float* __restrict__ gamma, const float* __restrict__ beta,
+    const int32_t* __restrict__ rowmap, int rows, int H, uint16_t* __restrict__ xn) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 4 + wave;
+  if (c >= rows) return;
+  const int64_t r = rowmap ? rowmap[c] : c;
+  const float mu = mean ? mean[r] : 0.f;
+  const float rs = rstd[r];
+  const uint4* xr = (const uint4*)(x + r * H);
+  uint4* out = (uint4*)(xn + (int64_t)c * H);
+  for (int v = lane; v < H / 8; v += 64) {
+    const uint4 xv = xr[v];
+    const float4 g0 = ((const float4*)gamma)[2 * v], g1 = ((const float4*)gamma)[2 * v + 1];
+    float4 b0 = make_float4(0, 0, 0, 0), b1 = b0;
+    if (beta) {
+      b0 = ((const float4*)beta)[2 * v];
+      b1 = ((const float4*)beta)[2 * v + 1];
+    }
+    uint4 o;
+    o.x = pack2bf((bflo(xv.x) - mu) * rs * g0.x + b0.x, (bfhi(xv.x) - mu) * rs * g0.y + b0.y);
+    o.y = pack2bf((bflo(xv.y) - mu) * rs * g0.z + b0.z, (bfhi(xv.y) - mu) * rs * g0.w + b0.w);
+    o.z = pack2bf((bflo(xv.z) - mu) * rs * g1.x + b1.x, (bfhi(xv.z) - mu) * rs * g1.y + b1.y);
+    o.w = pack2bf((bflo(xv.w) - mu) * rs * g1.z + b1.z, (bfhi(xv.w) - mu) * rs * g1.w + b1.w);
+    out[v] = o;
+  }
+}
+
+collider_status launch_norm_recompute(const uint16_t* x, const float* mean, const float* rstd,
+                                      const float* gamma, const float* beta, const int32_t* rowmap,
+                                      int rows, int H, uint16_t* xn, hipStream_t s) {
+  if (rows <= 0) return COLLIDER_OK;
+  COLLIDER_LAUNCH("norm_recompute", s,
+                  hipLaunchKernelGGL(norm_recompute_kernel, dim3((rows + 3) / 4), dim3(256), 0, s,
+                                     x, mean, rstd, gamma, beta, rowmap, rows, H, xn));
+  return last_hip_status();
+}
+
+// ------------------------------------------------------------------------------------------
+// activation recompute: a[c] = bf16(silu(g)*up) or bf16(gelu_tanh(g)), rows rowmap[c]
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
+__device__ __forceinline__ float gelu_f(float f) {
+  const float c = 0.7978845608028654f, a = 0.044715f;
+  const float u = c * (f + a * f * f * f);
+  return 0.5f * f * (1.f + tanhf(u));
+}
+
+__global__ __launch_bounds__(256) void act_recompute_kernel(const uint16_t* __restrict__ g,
+                                                            const uint16_t* __restrict__ up,
+                                                            const int32_t* __restrict__ rowmap,
+                                                            int rows, int I,
+                                                            uint16_t* __restrict__ a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 4 + wave;
+  if (c >= rows) return;
+  const int64_t r = rowmap ? rowmap[c] : c;
+  const uint4* gr = (const uint4*)(g + r * I);
+  const uint4* ur = up ? (const uint4*)(up + r * I) : nullptr;
+  uint4* out = (uint4*)(a + (int64_t)c * I);
+  for (int v = lane; v < I / 8; v += 64) {
+    const uint4 gv = gr[v];
+    uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+    uint32_t ow[4];
+    if (ur) {
+      const uint4 uv = ur[v];
+      uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        ow[i] = pack2bf(silu_f(bflo(gw[i])) * bflo(uw[i]), silu_f(bfhi(gw[i])) * bfhi(uw[i]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ow[i] = pack2bf(gelu_f(bflo(gw[i])), gelu_f(bfhi(gw[i])));
+    }
+    out[v] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+  }
+}
+
+collider_status launch_act_recompute(const uint16_t* g, const uint16_t* up, const int32_t* rowmap,
+                                     int rows, int I, uint16_t* a, hipStream_t s) {
+  if (rows <= 0) return COLLIDER_OK;
+  COLLIDER_LAUNCH("act_recompute", s,
+                  hipLaunchKernelGGL(act_recompute_kernel, dim3((rows + 3) / 4), dim3(256), 0, s,
+                                     g, up, rowmap, rows, I, a));
+  return last_hip_status();
+}
+
+// ------------------------------------------------------------------------------------------
+// norm backward + residual:
+//   xhat = (x - mean) * rstd (mean = 0 for RMSNorm), g = dxn * gamma,
+//   RMSNorm:   dx = rstd * (g - xhat * mean(g * xhat))
+//   LayerNorm: dx = rstd * (g - mean(g) - xhat * mean(g * xhat))
+//   out = dres + dx (bf16); per-block partial column sums of dxn * xhat (and dxn)
+// One wavefront per row, the row held in registers (NV 8-element vectors per lane, H <= 512*NV).
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+template <int NV>
+__global__ __launch_bounds__(256) void norm_bwd_kernel(
+    const uint16_t* __restrict__ dxn, const uint16_t* __restrict__ dres,
+    const uint16_t* __restrict__ x, const float* __restrict__ mean, const float* __restrict__ rstd,
+    const float* __restrict__ gamma, const int32_t* __restrict__ rowmap, int rows, int H,
+    uint16_t* __restrict__ dx, float* __restrict__ part_dgamma, float* __restrict__ part_dbeta,
+    int rows_per_part) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nvec = H >> 3;
+  float acc_g[NV][8], acc_b[NV][8];
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc_g[i][j] = acc_b[i][j] = 0.f;
+  const int c_begin = blockIdx.x * rows_per_part;
+  const int c_end = min(rows, c_begin + rows_per_part);
+  for (int c = c_begin + wave; c < c_end; c += 4) {
+    const int64_t r = rowmap ? rowmap[c] : c;
+    const float mu = mean ? mean[r] : 0.f;
+    const float rs = rstd[r];
+    float gv[NV][8], xh[NV][8];
+    float s_g = 0.f, s_gx = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int v = lane + 64 * i;
+      if (v < nvec) {
+        const uint4 dv = ((const uint4*)(dxn + (int64_t)c * H))[v];
+        const uint4 xv = ((const uint4*)(x + r * H))[v];
+        const float4 g0 = ((const float4*)gamma)[2 * v], g1 = ((const float4*)gamma)[2 * v + 1];
+        const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w}, xw[4] = {xv.x, xv.y, xv.z, xv.w};
+        const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float d = (j & 1) ? bfhi(dw[j >> 1]) : bflo(dw[j >> 1]);
+          const float xx = (j & 1) ? bfhi(xw[j >> 1]) : bflo(xw[j >> 1]);
+          xh[i][j] = (xx - mu) * rs;
+          gv[i][j] = d * gm[j];
+          s_g += gv[i][j];
+          s_gx += gv[i][j] * xh[i][j];
+          acc_g[i][j] += d * xh[i][j];
+          acc_b[i][j] += d;
+        }
+      }
+    }
+    s_g = wave_sum(s_g) / (float)H;
+    s_gx = wave_sum(s_gx) / (float)H;
+    if (!mean) s_g = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int v = lane + 64 * i;
+      if (v < nvec) {
+        const uint4 rv = ((const uint4*)(dres + (int64_t)c * H))[v];
+        const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
+        uint32_t ow[4];
+#pragma unroll
+        for (int j2 = 0; j2 < 4; ++j2) {
+          const float a0 = bflo(rw[j2]) + rs * (gv[i][2 * j2] - s_g - xh[i][2 * j2] * s_gx);
+          const float a1 = bfhi(rw[j2]) + rs * (gv[i][2 * j2 + 1] - s_g - xh[i][2 * j2 + 1] * s_gx);
+          ow[j2] = pack2bf(a0, a1);
+        }
+        ((uint4*)(dx + (int64_t)c * H))[v] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+      }
+    }
+  }
+  // combine the 4 wavefronts' column partials through LDS, in a fixed order
+  __shared__ float red[4][512];
+  for (int i = 0; i < NV; ++i) {
+    for (int which = 0; which < (part_dbeta ? 2 : 1); ++which) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) red[wave][lane * 8 + j] = which ? acc_b[i][j] : acc_g[i][j];
+      __syncthreads();
+      for (int e = threadIdx.x; e < 512; e += 256) {
+        const int col = i * 512 + e;
+        if (col < H) {
+          const float sum = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+          float* dst = which ? part_dbeta : part_dgamma;
+          dst[(int64_t)blockIdx.x * H + col] = sum;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+static constexpr int kNormParts = 256;
+int norm_bwd_parts(int rows) { return rows <= 0 ? 1 : (rows < kNormParts ? rows : kNormParts); }
+
+collider_status launch_norm_bwd(const uint16_t* dxn, const uint16_t* dres, const uint16_t* x,
+                                const float* mean, const float* rstd, const float* gamma,
+                                const int32_t* rowmap, int rows, int H, uint16_t* dx,
+                                float* part_dgamma, float* part_dbeta, int n_part, hipStream_t s) {
+  const int rpp = rows <= 0 ? 1 : (rows + n_part - 1) / n_part;
+  const int nv = (H / 8 + 63) / 64;
+  dim3 grid(n_part), block(256);
+#define NB_CASE(N)                                                                              \
+  case N:                                                                                       \
+    COLLIDER_LAUNCH("norm_bwd", s,                                                              \
+                    hipLaunchKernelGGL(norm_bwd_kernel<N>, grid, block, 0, s, dxn, dres, x, mean, \
+                                       rstd, gamma, rowmap, rows, H, dx, part_dgamma,           \
+                                       part_dbeta, rpp));                                       \
+    break;
+  switch (nv) {
+    NB_CASE(1) NB_CASE(2) NB_CASE(3) NB_CASE(4) NB_CASE(5) NB_CASE(6) NB_CASE(7) NB_CASE(8)
+    default:
+      return COLLIDER_ERR_UNSUPPORTED;
+  }
+#undef NB_CASE
+  return last_hip_status();
+}
+
+// out[col] (+)= sum_p parts[p, col], p ascending
+__global__ void colsum_parts_kernel(const float* __restrict__ parts, int n_part, int H,
+                                    float* __restrict__ out, int accumulate) {
+  const int col = blockIdx.x * blockDim.x + threadIdx.x;
+  if (col >= H) return;
+  float s = 0.f;
+  for (int p = 0; p < n_part; ++p) s += parts[(int64_t)p * H + col];
+  out[col] = accumulate ? out[col] + s : s;
+}
+
+collider_status launch_colsum_parts(const float* parts, int n_part, int H, float* out,
+                                    int accumulate, hipStream_t s) {
+  COLLIDER_LAUNCH("colsum_parts", s,
+                  hipLaunchKernelGGL(colsum_parts_kernel, dim3((H + 255) / 256), dim3(256), 0, s,
+                                     parts, n_part, H, out, accumulate));
+  return last_hip_status();
+}
+
+// column sums of a [rows, cols] matrix (bias gradient): per-block partials then colsum_parts
+__global__ void colsum_partial_kernel(const void* __restrict__ x, int64_t ld, int rows, int cols,
+                                      int is_bf16, int rows_per_part, float* __restrict__ parts) {
+  const int col = blockIdx.y * blockDim.x + threadIdx.x;
+  if (col >= cols) return;
+  const int r0 = blockIdx.x * rows_per_part, r1 = min(rows, r0 + rows_per_part);
+  float s = 0.f;
+  for (int r = r0; r < r1; ++r)
+    s += is_bf16 ? bf2f(((const uint16_t*)x)[(int64_t)r * ld + col])
+                 : ((const float*)x)[(int64_t)r * ld + col];
+  parts[(int64_t)blockIdx.x * cols + col] = s;
+}
+
+collider_status launch_colsum(const void* x, int64_t ld, int rows, int cols, bool bf16, float* out,
+                              int accumulate, float* ws, hipStream_t s) {
+  const int n_part = norm_bwd_parts(rows);
+  const int rpp = rows <= 0 ? 1 : (rows + n_part - 1) / n_part;
+  COLLIDER_LAUNCH("colsum_partial", s,
+                  hipLaunchKernelGGL(colsum_partial_kernel, dim3(n_part, (cols + 255) / 256),
+                                     dim3(256), 0, s, x, ld, rows, cols, (int)bf16, rpp, ws));
+  return launch_colsum_parts(ws, n_part, cols, out, accumulate, s);
+}
+
+__global__ void fill_f32_kernel(float* p, size_t n, float v) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+collider_status launch_fill_f32(float* p, size_t n, float v, hipStream_t s) {
+  if (n == 0) return COLLIDER_OK;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  COLLIDER_LAUNCH("fill_f32", s,
+                  hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p,
+                                     n, v));
+  return last_hip_status();
+}
+
+// cs[s][m] = (cos(s*theta_m), sin(s*theta_m)), theta_m = base^(-2m/rot); angles in double
+__global__ void rope_table_kernel(float2* cs, int S, int half, double log_base, int rot) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= S * half) return;
+  const int p = i / half, m = i - p * half;
+  const double theta = exp(-2.0 * (double)m / (double)rot * log_base);
+  double sn, cn;
+  sincos((double)p * theta, &sn, &cn);
+  cs[i] = make_float2((float)cn, (float)sn);
+}
+
+collider_status launch_rope_table(float* cs, int S, int rot, float base, hipStream_t s) {
+  const int half = rot / 2;
+  if (half == 0) return COLLIDER_OK;
+  const int n = S * half;
+  COLLIDER_LAUNCH("rope_table", s,
+                  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s,
+                                     (float2*)cs, S, half, log((double)base), rot));
+  return last_hip_status();
+}
+
+}  // namespace collider
