@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Filtered transformer-layer backward on one MI355X.
+
+One step = the whole filtered path for one batch: keep mask -> index (one host wait for the kept
+count), gathers, every reduced GEMM, the filtered attention backward, norm / activation backward and
+the scatter of dx, for one TinyLlama-shaped layer (B 4 x S 2048, hidden 2048, 32/4 heads x 64,
+SwiGLU 5632) with 40% of the tokens filtered by top-k on a LogNormal score.  Inputs are synthetic
+(seeded generator, random-init weights) and resident in HBM before timing starts.
+
+Prints one JSON line: value = ms per filtered layer backward (back-to-back steps), the speedup over
+the unfiltered dense backward of the same layer (same kernels on all tokens, no index / gather /
+scatter, D = dO . O), the reduced-GEMM roofline (bf16 MFMA) from per-kernel HIP events, and the
+CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config tinyllama] [--r 40]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "filtered layer-bwd ms, MFMA util & speedup vs unfiltered at 40% filter"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(cfg, M_kept, seq_counts):
+    """Algorithmic work of one filtered layer backward (never the dense work avoided)."""
+    H, I, d, nq, nkv = cfg.H, cfg.I, cfg.d, cfg.nq, cfg.nkv
+    nqkv = (nq + 2 * nkv) * d
+    if cfg.kind == "llama":
+        proj = H * nqkv + H * nq * d + 2 * I * H + H * I
+    else:
+        proj = H * nqkv + H * nq * d + I * H + H * I
+    gemm_flops = 4.0 * M_kept * proj                      # dX and dW: 2 * M' * K * N each
+    pairs = sum(n * (n + 1) // 2 for n in seq_counts)     # causal kept (query, key) pairs per head
+    attn_flops = 10.0 * d * nq * pairs                    # S, dP, dV, dK, dQ
+    attn_dt_flops = 4.0 * d * nq * pairs                  # the filtered softmax-backward row term
+    gather_bytes = 2.0 * M_kept * (2 * H + 2 * 2 * nq * d + 2 * 2 * nkv * d + 4 * nq)
+    return {"gemm_flops": gemm_flops, "attn_flops": attn_flops, "attn_dt_flops": attn_dt_flops,
+            "pairs": pairs, "gather_bytes": gather_bytes}
+
+
+def cpu_baseline(cfg, inp, min_seconds=8.0):
+    """The oracle as it stands on whole sequences of the same workload, scaled to one layer."""
+    import numpy as np
+
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    S = cfg.S
+    one = cfg.with_(B=1)
+    w = synth.floats(inp["weights"])
+    done, t_total = 0, 0.0
+    for b in range(cfg.B):
+        rows = slice(b * S, (b + 1) * S)
+        sv = {k: v[rows] for k, v in synth.floats(inp["saved"]).items()}
+        dy = synth.bf16_bits_to_f32(inp["dy"][rows])
+        keep = inp["keep"][rows]
+        t0 = time.perf_counter()
+        oracle.layer_bwd(one, w, sv, dy, keep, "filtered")
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= min_seconds:
+            break
+    ms = t_total * 1e3 * cfg.B / done
+    return {"value": round(ms, 1), "unit": "ms", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {cfg.B} sequences (S={S}) of the same layer, float64 NumPy, "
+                      f"scaled x{cfg.B / done:g} (the layer's work is linear in the sequence count)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="tinyllama")
+    ap.add_argument("--r", type=int, default=40, help="filtered percentage")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-unfiltered", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); the filtered layer backward "
+              "is data-parallel and needs no second GPU to measure", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import token_filtered_backward_amd as tfb
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda"
+    cfg = synth.get_config(args.config)
+    log(f"[bench] generating inputs for {cfg.name} (B={cfg.B} S={cfg.S} r={args.r}%) ...")
+    t0 = time.perf_counter()
+    inp = synth.make_layer_inputs(cfg, seed=args.seed, r_pct=args.r)
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s")
+
+    def up(v):
+        if v.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(dev)
+
+    W = {k: up(v) for k, v in inp["weights"].items()}
+    Sv = {k: up(v) for k, v in inp["saved"].items()}
+    if cfg.kind == "llama":
+        weights = {k: W[k] for k in ("w_qkv", "w_o", "w_gateup", "w_down", "gamma1", "gamma2")}
+        saved = {k: Sv[k] for k in ("x", "q", "k", "v", "o", "lse", "rstd1", "h", "rstd2", "gate", "up")}
+    else:
+        weights = dict(w_qkv=W["w_qkv"], w_o=W["w_o"], w_fc1=W["w_fc1"], w_fc2=W["w_fc2"],
+                       ln_gamma=W["gamma"], ln_beta=W["beta"])
+        saved = dict(x=Sv["x"], q=Sv["q"], k=Sv["k"], v=Sv["v"], o=Sv["o"], lse=Sv["lse"],
+                     rstd1=Sv["rstd"], mean=Sv["mean"], f=Sv["f"])
+    dy = up(inp["dy"])
+    keep = torch.from_numpy(inp["keep"]).to(dev)
+    B, S, M = cfg.B, cfg.S, cfg.M
+
+    lcfg = tfb.layer_cfg(cfg)
+    lb = tfb.LayerBackward(lcfg, B, S, dev)
+    ix0 = tfb.build_index(keep, B, S)
+    grads = tfb.make_grads(lcfg, M, ix0.M_kept, dev)
+    lb.workspace(ix0.M_kept)
+
+    def step_filtered():
+        ix = tfb.build_index(keep, B, S)
+        lb(weights, saved, dy, ix, grads)
+
+    ucfg = tfb.layer_cfg(cfg, unfiltered=True)
+    ub = tfb.LayerBackward(ucfg, B, S, dev)
+    uix = tfb.dense_index(B, S)
+    ugrads = tfb.make_grads(ucfg, M, M, dev)
+
+    def step_unfiltered():
+        ub(weights, saved, dy, uix, ugrads)
+
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)  # > 256 MB MALL
+
+    def timed(fn, K, W_):
+        for _ in range(W_):
+            fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(K):
+            fn()
+        torch.cuda.synchronize()
+        warm = (time.perf_counter() - t) * 1e3 / K
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cold = []
+        for _ in range(K):
+            flush.fill_(1)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        return warm, float(np.median(cold))
+
+    log(f"[bench] timing filtered step: warmup {args.warmup}, steps {args.steps}")
+    ms_f, ms_f_cold = timed(step_filtered, args.steps, args.warmup)
+    log(f"[bench] filtered: {ms_f:.3f} ms/step (cold median {ms_f_cold:.3f})")
+    ms_u = ms_u_cold = None
+    if not args.no_unfiltered:
+        ms_u, ms_u_cold = timed(step_unfiltered, args.steps, args.warmup)
+        log(f"[bench] unfiltered: {ms_u:.3f} ms/step (cold median {ms_u_cold:.3f})")
+
+    # per-kernel durations from HIP events recorded by the library on its launch stream
+    n_prof = max(3, min(args.steps, 10))
+    torch.cuda.synchronize()
+    tfb.collider_profile_collect()
+    tfb.collider_profile_enable(True)
+    for _ in range(n_prof):
+        step_filtered()
+    torch.cuda.synchronize()
+    prof = tfb.collider_profile_collect()
+    tfb.collider_profile_enable(False)
+    kernels = {k: round(v[0] / n_prof, 4) for k, v in sorted(prof.items(), key=lambda kv: -kv[1][0])}
+    gemm_names = [k for k in prof if k.startswith("gemm_") and k != "gemm_splitk_reduce"]
+    gemm_ms = sum(prof[k][0] for k in gemm_names) / n_prof
+    gemm_launches = sum(prof[k][1] for k in gemm_names) / n_prof
+
+    ix = tfb.build_index(keep, B, S)
+    cu = ix.cu_seqlens.cpu().numpy()
+    seq_counts = [int(cu[b + 1] - cu[b]) for b in range(B)]
+    work = algorithmic_work(cfg, ix.M_kept, seq_counts)
+    gemm_tflops = work["gemm_flops"] / (gemm_ms * 1e-3) / 1e12
+    attn_ms = sum(prof[k][0] for k in prof if k.startswith("attn_")) / n_prof
+    attn_tflops = (work["attn_flops"] + work["attn_dt_flops"]) / (attn_ms * 1e-3) / 1e12 if attn_ms else None
+    gather_ms = prof.get("gather_rows", (0.0, 1))[0] / n_prof
+    gather_gbs = work["gather_bytes"] / (gather_ms * 1e-3) / 1e9 if gather_ms else None
+
+    out = {
+        "metric": METRIC,
+        "value": round(ms_f, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_f, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}-shaped layer backward, B{B}xS{S}, {args.r}% filtered",
+                   "B": B, "S": S, "hidden": cfg.H, "heads": f"{cfg.nq}/{cfg.nkv}x{cfg.d}",
+                   "inter": cfg.I, "M": M, "M_kept": ix.M_kept, "parallelism": "single GPU"},
+        "ms_filtered_cold": round(ms_f_cold, 4),
+        "ms_unfiltered": None if ms_u is None else round(ms_u, 4),
+        "ms_unfiltered_cold": None if ms_u_cold is None else round(ms_u_cold, 4),
+        "speedup_vs_unfiltered": None if ms_u is None else round(ms_u / ms_f, 3),
+        "speedup_vs_unfiltered_cold": None if ms_u is None else round(ms_u_cold / ms_f_cold, 3),
+        "mfma_util_gemm": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+        "gemm_tflops": round(gemm_tflops, 1),
+        "attn_tflops": None if attn_tflops is None else round(attn_tflops, 1),
+        "gather_gbs": None if gather_gbs is None else round(gather_gbs, 1),
+        "kernel_ms_per_step": kernels,
+        "roofline": {
+            "kernel": f"gemm_bf16 (all {int(gemm_launches)} reduced-GEMM launches of one layer)",
+            "bound": "mfma",
+            "achieved": round(gemm_tflops, 1),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "flops_per_launch": work["gemm_flops"] / max(gemm_launches, 1),
+            "avg_launch_ms": round(gemm_ms / max(gemm_launches, 1), 5),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(cfg, inp)
+        log(f"[bench] cpu oracle: {out['cpu_baseline']['value']} ms per layer")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -168,6 +168,10 @@ typedef struct {
   float rope_base;
   int32_t dmode;                /* collider_dmode */
   int32_t accumulate;           /* != 0: weight / gain gradients are added to, not overwritten */
+  int32_t unfiltered;           /* != 0: the ordinary dense backward over all M tokens, the baseline
+                                   the method is measured against: the index arrays are not read
+                                   (only B, S), nothing is gathered or scattered, every GEMM and
+                                   the attention run on the full layout, dmode is taken as FULL */
 } collider_layer_cfg;
 
 typedef struct {                /* bf16 weights [out, in]; float32 norm parameters */

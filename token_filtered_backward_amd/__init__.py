@@ -46,7 +46,8 @@ class AttnIO(ctypes.Structure):
 class LayerCfg(ctypes.Structure):
     _fields_ = [("kind", _i32), ("hidden", _i32), ("n_q_heads", _i32), ("n_kv_heads", _i32),
                 ("head_dim", _i32), ("rot_dims", _i32), ("inter", _i32),
-                ("rope_base", ctypes.c_float), ("dmode", _i32), ("accumulate", _i32)]
+                ("rope_base", ctypes.c_float), ("dmode", _i32), ("accumulate", _i32),
+                ("unfiltered", _i32)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -264,10 +265,18 @@ def build_index(keep: torch.Tensor, B: int, S: int, stream=None) -> Index:
     return Index(idx, inv, cu, count, B, S, mk)
 
 
-def layer_cfg(shape, dmode=ATTN_D_FILTERED, accumulate=False) -> LayerCfg:
-    """LayerCfg from any object with kind/H/nq/nkv/d/rot/I/rope_base attributes."""
+def layer_cfg(shape, dmode=ATTN_D_FILTERED, accumulate=False, unfiltered=False) -> LayerCfg:
+    """LayerCfg from any object with kind/H/nq/nkv/d/rot/I/rope_base attributes.
+    unfiltered=True selects the ordinary dense backward over all tokens (the baseline)."""
     return LayerCfg(LAYER_LLAMA if shape.kind == "llama" else LAYER_PHI, shape.H, shape.nq, shape.nkv,
-                    shape.d, shape.rot, shape.I, float(shape.rope_base), dmode, int(accumulate))
+                    shape.d, shape.rot, shape.I, float(shape.rope_base), dmode, int(accumulate),
+                    int(unfiltered))
+
+
+def dense_index(B: int, S: int) -> Index:
+    """Index placeholder for the unfiltered baseline (only B and S are read)."""
+    z = torch.empty(0, dtype=torch.int32)
+    return Index(z, z, z, z, B, S, B * S)
 
 
 def _struct(cls, tensors: dict):

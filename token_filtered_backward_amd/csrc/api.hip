@@ -275,7 +275,13 @@ collider_status collider_layer_bwd(const collider_layer_cfg* cfg, const collider
                                    size_t ws_bytes, hipStream_t stream) {
   collider_status st = check_layer(cfg);
   if (st != COLLIDER_OK) return st;
-  if ((st = check_index(ix)) != COLLIDER_OK) return st;
+  if (cfg->unfiltered) {  // only B and S of the index are read
+    if (!ix) return COLLIDER_ERR_NULL;
+    if (ix->B < 1 || ix->S < 1 || (int64_t)ix->B * ix->S > (1 << 30)) return COLLIDER_ERR_SHAPE;
+    if (dy_compact || dx_compact) return COLLIDER_ERR_UNSUPPORTED;
+  } else if ((st = check_index(ix)) != COLLIDER_OK) {
+    return st;
+  }
   if (!w || !sv || !g || !dy) return COLLIDER_ERR_NULL;
   const bool llama = cfg->kind == COLLIDER_LAYER_LLAMA;
   const void* wp[] = {w->w_qkv, w->w_o, llama ? w->w_gateup : w->w_fc1, llama ? w->w_down : w->w_fc2};

@@ -104,8 +104,8 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnParams p) {
   uint16_t* Vs = smem + BKV * LDR;
   uint16_t* Kt = smem + 2 * BKV * LDR;
   const int b = blockIdx.z, h = blockIdx.y, g = h / p.G;
-  const int cs = min(p.cu[b], p.M_kept);
-  const int nb = max(0, min(p.cu[b + 1], p.M_kept) - cs);
+  const int cs = p.cu ? min(p.cu[b], p.M_kept) : b * p.S;
+  const int nb = p.cu ? max(0, min(p.cu[b + 1], p.M_kept) - cs) : p.S;
   const int nqb = (nb + BQ - 1) / BQ;
   if ((int)blockIdx.x >= nqb) return;
   const int q0 = (nqb - 1 - (int)blockIdx.x) * BQ;
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnParams p) {
     float out[8];
     const float* er = E + row * LDE;
     if (c0 < p.rot) {
-      const int pos = p.idx[cs + i] % p.S;
+      const int pos = (p.idx ? p.idx[cs + i] : cs + i) % p.S;
       const bool lower = c0 < half;
       const int m0 = lower ? c0 : c0 - half;
       const int pc = lower ? c0 + half : c0 - half;
@@ -266,8 +266,8 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnParams p) {
   __shared__ __align__(16) float Ls[BQ];
   __shared__ __align__(16) float Ds[BQ];
   const int b = blockIdx.z, g = blockIdx.y / p.HS, hs = blockIdx.y % p.HS;
-  const int cs = min(p.cu[b], p.M_kept);
-  const int nb = max(0, min(p.cu[b + 1], p.M_kept) - cs);
+  const int cs = p.cu ? min(p.cu[b], p.M_kept) : b * p.S;
+  const int nb = p.cu ? max(0, min(p.cu[b + 1], p.M_kept) - cs) : p.S;
   const int nkb = (nb + BKV - 1) / BKV;
   if ((int)blockIdx.x >= nkb) return;
   const int k0 = blockIdx.x * BKV;
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(256) void attn_dkv_finalize_kernel(AttnParams p) {
   const int64_t slice = (int64_t)p.M_kept * p.nkv * D;
   const int64_t base = ((int64_t)c * p.nkv + g) * D;
   int pos = 0;
-  if (p.rot) pos = p.idx[c] % p.S;
+  if (p.rot) pos = (p.idx ? p.idx[c] : c) % p.S;
   for (int m = lane; m < D; m += 64) {
     float xk = 0.f, yk = 0.f, xv = 0.f;
     const bool rotated = m < p.rot;

@@ -313,7 +313,8 @@ Plan make_plan(const GemmProblem& p) {
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI>
-collider_status launch_cfg(const GemmParams& gp, const Plan& pl, bool ak, bool bk, hipStream_t s) {
+collider_status launch_cfg(const GemmParams& gp, const Plan& pl, bool ak, bool bk, const char* name,
+                           hipStream_t s) {
   constexpr int BK = 64;
   const int T = gp.tiles_m * gp.tiles_n;
   dim3 grid(T, 1, pl.splits), block(64 * WAVES_M * WAVES_N);
@@ -322,7 +323,7 @@ collider_status launch_cfg(const GemmParams& gp, const Plan& pl, bool ak, bool b
   {                                                                                             \
     auto kern = gemm_bf16_kernel<BM, BN, BK, WAVES_M, WAVES_N, AKV, BKV, EPI>;                  \
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
-    COLLIDER_LAUNCH("gemm_bf16", s, hipLaunchKernelGGL(kern, grid, block, lds, s, gp));         \
+    COLLIDER_LAUNCH(name, s, hipLaunchKernelGGL(kern, grid, block, lds, s, gp));                \
   }
   if (ak && !bk) GEMM_LAUNCH(true, false)
   else if (!ak && !bk) GEMM_LAUNCH(false, false)
@@ -335,10 +336,11 @@ collider_status launch_cfg(const GemmParams& gp, const Plan& pl, bool ak, bool b
 template <int EPI>
 collider_status run(const GemmProblem& prob, GemmParams gp, const Plan& pl, hipStream_t s) {
   collider_status st;
+  const char* name = prob.name ? prob.name : "gemm_bf16";
   if (pl.cfg == 0)
-    st = launch_cfg<256, 256, 2, 4, EPI>(gp, pl, prob.a_kmajor, prob.b_kmajor, s);
+    st = launch_cfg<256, 256, 2, 4, EPI>(gp, pl, prob.a_kmajor, prob.b_kmajor, name, s);
   else
-    st = launch_cfg<128, 128, 2, 2, EPI>(gp, pl, prob.a_kmajor, prob.b_kmajor, s);
+    st = launch_cfg<128, 128, 2, 2, EPI>(gp, pl, prob.a_kmajor, prob.b_kmajor, name, s);
   if (st != COLLIDER_OK || pl.splits == 1) return st;
   const int64_t total = (int64_t)prob.M * prob.N;
   int64_t blocks = (total + 255) / 256;

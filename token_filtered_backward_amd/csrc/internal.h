@@ -138,6 +138,7 @@ struct GemmProblem {
   const int32_t* rowmap;
   uint16_t* out2;      // SwiGLU: dup written at out2 (C gets dgate); GELU: unused
   int64_t ld_out2;
+  const char* name;    // label for per-kernel timing (static string)
 };
 size_t gemm_bf16_workspace_bytes(const GemmProblem& p);
 collider_status gemm_bf16(const GemmProblem& p, void* ws, size_t ws_bytes, hipStream_t s);

@@ -42,7 +42,8 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
                           const collider_index& ix, collider_layer_grads* gr, int dx_compact,
                           void* ws, size_t ws_bytes, hipStream_t s, size_t* need) {
   const bool llama = c.kind == COLLIDER_LAYER_LLAMA;
-  const int B = ix.B, S = ix.S, M = B * S, Mk = ix.M_kept;
+  const bool unf = c.unfiltered != 0;  // dense baseline: full layout, no index
+  const int B = ix.B, S = ix.S, M = B * S, Mk = unf ? M : ix.M_kept;
   const int H = c.hidden, I = c.inter, d = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
   const int nqd = nq * d, nkvd = nkv * d, nqkv = nqd + 2 * nkvd;
   const int mid = llama ? 2 * I : nqkv + I;  // width of [dgate|dup] or [dq|dk|dv|dF]
@@ -51,24 +52,33 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
 
   Carver cv(dry ? nullptr : ws);
   LayerBufs b{};
-  b.dy_c = dy_compact ? (uint16_t*)dy : cv.take<uint16_t>((size_t)Mk * H);
-  b.o_c = cv.take<uint16_t>((size_t)Mk * nqd);
-  b.q_c = cv.take<uint16_t>((size_t)Mk * nqd);
-  b.k_c = cv.take<uint16_t>((size_t)Mk * nkvd);
-  b.v_c = cv.take<uint16_t>((size_t)Mk * nkvd);
-  b.lse_c = cv.take<float>((size_t)Mk * nq);
+  if (unf) {  // saved tensors are read in place
+    b.dy_c = (uint16_t*)dy;
+    b.o_c = sv ? (uint16_t*)sv->o : nullptr;
+    b.q_c = sv ? (uint16_t*)sv->q : nullptr;
+    b.k_c = sv ? (uint16_t*)sv->k : nullptr;
+    b.v_c = sv ? (uint16_t*)sv->v : nullptr;
+    b.lse_c = sv ? (float*)sv->lse : nullptr;
+  } else {
+    b.dy_c = dy_compact ? (uint16_t*)dy : cv.take<uint16_t>((size_t)Mk * H);
+    b.o_c = cv.take<uint16_t>((size_t)Mk * nqd);
+    b.q_c = cv.take<uint16_t>((size_t)Mk * nqd);
+    b.k_c = cv.take<uint16_t>((size_t)Mk * nkvd);
+    b.v_c = cv.take<uint16_t>((size_t)Mk * nkvd);
+    b.lse_c = cv.take<float>((size_t)Mk * nq);
+  }
   b.act_c = cv.take<uint16_t>((size_t)Mk * I);
   b.xn_c = cv.take<uint16_t>((size_t)Mk * H);
   b.dmid = cv.take<uint16_t>((size_t)Mk * mid);
   b.dxn = cv.take<uint16_t>((size_t)Mk * H);
   b.dh = llama ? cv.take<uint16_t>((size_t)Mk * H) : nullptr;
   b.do_c = cv.take<uint16_t>((size_t)Mk * nqd);
-  b.dx_c = dx_compact ? (uint16_t*)(gr ? gr->dx : nullptr) : cv.take<uint16_t>((size_t)Mk * H);
+  b.dx_c = (dx_compact || unf) ? (uint16_t*)(gr ? gr->dx : nullptr) : cv.take<uint16_t>((size_t)Mk * H);
   b.part_g = cv.take<float>((size_t)parts * H);
   b.part_b = cv.take<float>((size_t)parts * H);
 
   // GEMM problems (pointers are only meaningful when not dry)
-  const int32_t* idx = ix.idx;
+  const int32_t* idx = unf ? nullptr : ix.idx;  // row map of the saved tensors (null: identity)
   GemmProblem g_dA{}, g_dw2{}, g_dXmid{}, g_dwmid{}, g_dO{}, g_dwo{}, g_dXin{}, g_dwqkv{}, g_dwfc1{};
   auto dx_gemm = [&](GemmProblem& p, int n, int k, const void* A, int64_t lda, const void* Bm,
                      int64_t ldb, int epi, void* C, int64_t ldc) {
@@ -114,6 +124,15 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     dw_gemm(g_dwqkv, nqkv, H, b.dmid, mid, b.xn_c, H, gr ? gr->dw_qkv : nullptr);
     dw_gemm(g_dwfc1, I, H, dF, mid, b.xn_c, H, gr ? gr->dw_fc1 : nullptr);
   }
+  g_dA.name = llama ? "gemm_dA_swiglu" : "gemm_dA_gelu";
+  g_dw2.name = llama ? "gemm_dw_down" : "gemm_dw_fc2";
+  g_dXmid.name = "gemm_dX_gateup";
+  g_dwmid.name = "gemm_dw_gateup";
+  g_dO.name = "gemm_dO";
+  g_dwo.name = "gemm_dw_o";
+  g_dXin.name = llama ? "gemm_dX_qkv" : "gemm_dX_qkv_fc1";
+  g_dwqkv.name = "gemm_dw_qkv";
+  g_dwfc1.name = "gemm_dw_fc1";
   const GemmProblem* gl[] = {&g_dA, &g_dw2, &g_dXmid, &g_dwmid, &g_dO, &g_dwo, &g_dXin, &g_dwqkv,
                              &g_dwfc1};
   size_t gemm_need = 0;
@@ -129,7 +148,15 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
   ac.rot_dims = c.rot_dims;
   ac.rope_base = c.rope_base;
   ac.softmax_scale = 0.f;
-  ac.dmode = c.dmode;
+  ac.dmode = unf ? COLLIDER_ATTN_D_FULL : c.dmode;
+  collider_index aix = ix;
+  if (unf) {  // every token kept: the attention kernels take cs = b*S and position = row mod S
+    aix.idx = nullptr;
+    aix.inv = nullptr;
+    aix.cu_seqlens = nullptr;
+    aix.count = nullptr;
+    aix.M_kept = M;
+  }
   b.attn_ws_bytes = attn_workspace_bytes(ac, B, S, Mk);
   b.attn_ws = cv.take<char>(b.attn_ws_bytes);
 
@@ -146,7 +173,7 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     if (st != COLLIDER_OK) return st;  \
   } while (0)
 
-  if (Mk > 0) {
+  if (Mk > 0 && !unf) {
     // 1. gathers of the saved tensors the dense GEMMs / attention read as compacted operands
     GatherDesc gd[6];
     int nd = 0;
@@ -193,7 +220,7 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
   io.dq = b.dmid; io.ld_dq = mid;
   io.dk = b.dmid + nqd; io.ld_dk = mid;
   io.dv = b.dmid + nqd + nkvd; io.ld_dv = mid;
-  CHECK(attn_bwd(ac, ix, io, b.attn_ws, b.attn_ws_bytes, s));
+  CHECK(attn_bwd(ac, aix, io, b.attn_ws, b.attn_ws_bytes, s));
   if (llama) {
     CHECK(launch_norm_recompute((const uint16_t*)sv->x, nullptr, sv->rstd1, w->gamma1, nullptr, idx,
                                 Mk, H, b.xn_c, s));
@@ -213,7 +240,7 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dln_gamma, c.accumulate, s));
     CHECK(launch_colsum_parts(b.part_b, Mk > 0 ? parts : 0, H, gr->dln_beta, c.accumulate, s));
   }
-  if (!dx_compact) CHECK(launch_scatter_bytes(b.dx_c, (int64_t)H * 2, gr->dx, (int64_t)H * 2, ix.inv,
+  if (!dx_compact && !unf) CHECK(launch_scatter_bytes(b.dx_c, (int64_t)H * 2, gr->dx, (int64_t)H * 2, ix.inv,
                                               M, H * 2, 1, s));
 #undef CHECK
   return COLLIDER_OK;
