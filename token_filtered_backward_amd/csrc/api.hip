@@ -159,6 +159,8 @@ static void linear_problems(collider_dtype dt, int32_t Mk, int32_t K, int32_t N,
   pdw->A = dy; pdw->lda = ld_dy; pdw->a_kmajor = false;
   pdw->B0 = x; pdw->ldb = ld_x; pdw->b_kmajor = false;
   pdw->epi = EPI_F32; pdw->C = dw; pdw->ldc = K; pdw->accumulate = accumulate;
+  pdx->name = "linear_dx";
+  pdw->name = "linear_dw";
 }
 
 size_t collider_linear_workspace_bytes(collider_dtype dt, int32_t M_kept, int32_t K, int32_t N) {

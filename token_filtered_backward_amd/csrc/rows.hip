@@ -357,20 +357,30 @@ collider_status launch_norm_bwd(const uint16_t* dxn, const uint16_t* dres, const
   return last_hip_status();
 }
 
-// out[col] (+)= sum_p parts[p, col], p ascending
-__global__ void colsum_parts_kernel(const float* __restrict__ parts, int n_part, int H,
-                                    float* __restrict__ out, int accumulate) {
-  const int col = blockIdx.x * blockDim.x + threadIdx.x;
-  if (col >= H) return;
+// out[col] (+)= sum_p parts[p, col]: 64 columns per workgroup, 4 interleaved part streams per
+// column summed in a fixed order (deterministic), so the dependent-load chain is n_part / 4 long.
+__global__ __launch_bounds__(256) void colsum_parts_kernel(const float* __restrict__ parts,
+                                                           int n_part, int H,
+                                                           float* __restrict__ out,
+                                                           int accumulate) {
+  __shared__ float red[4][64];
+  const int cl = threadIdx.x & 63, ps = threadIdx.x >> 6;
+  const int col = blockIdx.x * 64 + cl;
   float s = 0.f;
-  for (int p = 0; p < n_part; ++p) s += parts[(int64_t)p * H + col];
-  out[col] = accumulate ? out[col] + s : s;
+  if (col < H)
+    for (int p = ps; p < n_part; p += 4) s += parts[(int64_t)p * H + col];
+  red[ps][cl] = s;
+  __syncthreads();
+  if (ps == 0 && col < H) {
+    const float t = ((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl];
+    out[col] = accumulate ? out[col] + t : t;
+  }
 }
 
 collider_status launch_colsum_parts(const float* parts, int n_part, int H, float* out,
                                     int accumulate, hipStream_t s) {
   COLLIDER_LAUNCH("colsum_parts", s,
-                  hipLaunchKernelGGL(colsum_parts_kernel, dim3((H + 255) / 256), dim3(256), 0, s,
+                  hipLaunchKernelGGL(colsum_parts_kernel, dim3((H + 63) / 64), dim3(256), 0, s,
                                      parts, n_part, H, out, accumulate));
   return last_hip_status();
 }
