@@ -15,8 +15,13 @@
 //     over a slice of the query heads sharing its KV head; slices go to fp32 partial buffers.
 //  3. attn_dkv_finalize: sums the slices in a fixed order, applies the rotary backward to dK and
 //     stores bf16 dk, dv.
-// Operands that need the token index as the MFMA reduction index (K in dS K, Q and dO in the key
-// kernel) are kept twice in LDS: row-major and transposed.
+// Token tiles [64 rows x D] live in LDS once, row-major with padded rows.  Operands that need the
+// token index as the MFMA reduction index (K in dS K; Q and dO in P^T dO and dS^T Q) are read with
+// ds_read_b64_tr_b16: within a group of 16 lanes, lane j addresses row k0 + j/4 at columns
+// n + 4*(j%4) and lane i receives rows k0 .. k0+3 of column n + i.  The row order of the two
+// transpose reads per fragment follows the 32x32 accumulator layout (rows 8*(r/4) + 4*(lane/32) +
+// r%4), so the P / dS registers feed the MFMA without any data movement.  The next tile is fetched
+// into registers while the MFMAs of the current one run (two LDS buffers, one barrier per tile).
 #include "internal.h"
 
 namespace collider {
@@ -47,6 +52,9 @@ struct AttnParams {
 
 static constexpr float kLog2e = 1.4426950408889634f;
 
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+
 __device__ __forceinline__ int acc_row(int r, int lane) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
@@ -65,44 +73,90 @@ __device__ __forceinline__ bf16x8 to_frag(const float* v8) {
   return a;
 }
 
-// 8 values of a transposed LDS tile: row `d`, token columns base+4h+{0..3} and base+8+4h+{0..3}
-__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* T, int ldt, int d, int base, int hl) {
-  const uint2 lo = *(const uint2*)(T + d * ldt + base + 4 * hl);
-  const uint2 hi = *(const uint2*)(T + d * ldt + base + 8 + 4 * hl);
-  uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-  return __builtin_bit_cast(bf16x8, u);
-}
+// [64 x D] bf16 token tile in LDS, row-major with padded rows.  Pitch (in 4-byte banks) is 36 for
+// D = 64 and 76 for D = 128: 16 consecutive rows of a 16-byte fragment read start on distinct
+// 4-bank groups, and the 4 consecutive rows of a transpose-read group on distinct 8-bank groups.
+template <int D>
+struct TokTile {
+  static constexpr int PITCH = D == 64 ? 144 : 304;  // bytes
+  static constexpr int BYTES = 64 * PITCH;
+  static constexpr int NV = 64 * (D / 8) / 256;       // 16-byte chunks per thread
+};
 
-// Cooperative copy of a [64 x D] token tile into LDS (row-major, and transposed if T != nullptr).
-template <int D, int ROWS, int LDR, int LDT>
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ src, int64_t ld, int col0,
-                                          int row0, int nrows, uint16_t* R, uint16_t* T) {
-  constexpr int CPR = D / 8;
-  for (int c = threadIdx.x; c < ROWS * CPR; c += 256) {
-    const int r = c / CPR, dc = c % CPR;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row0 + r < nrows) v = *(const uint4*)(src + (int64_t)(row0 + r) * ld + col0 + dc * 8);
-    *(uint4*)(R + r * LDR + dc * 8) = v;
-    if (T) {
-      const uint16_t* e = (const uint16_t*)&v;
+template <int D>
+struct TileRegs {
+  uint4 v[TokTile<D>::NV];
+  // rows row0 .. row0+63 of `src` (row stride ld elements), columns col0 .. col0+D-1
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int64_t ld, int col0,
+                                       int row0, int nrows) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) T[(dc * 8 + i) * LDT + r] = e[i];
+    for (int i = 0; i < TokTile<D>::NV; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int r = c / (D / 8), dc = c % (D / 8);
+      v[i] = (row0 + r < nrows) ? *(const uint4*)(src + (int64_t)(row0 + r) * ld + col0 + dc * 8)
+                                : make_uint4(0, 0, 0, 0);
     }
   }
+  __device__ __forceinline__ void store(char* T) const {
+#pragma unroll
+    for (int i = 0; i < TokTile<D>::NV; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int r = c / (D / 8), dc = c % (D / 8);
+      *(uint4*)(T + r * TokTile<D>::PITCH + dc * 16) = v[i];
+    }
+  }
+};
+
+// A/B operand with the head dimension as the reduction index: rows rbase .. rbase+31,
+// d = kk*16 .. kk*16+15 (16-byte read per lane)
+template <int D>
+__device__ __forceinline__ bf16x8 frag_rows(const char* T, int rbase, int kk, int lane) {
+  return *(const bf16x8*)(T + (rbase + (lane & 31)) * TokTile<D>::PITCH + (kk * 16 + (lane >> 5) * 8) * 2);
+}
+
+// B operand with the token index as the reduction index: 16 tokens tbase .. tbase+15 in the
+// accumulator row order (lane half h, element 4c+e <-> token tbase + 8c + 4h + e), columns
+// dbase .. dbase+31 (lane & 31)
+template <int D>
+__device__ __forceinline__ bf16x8 frag_tr(const char* T, int tbase, int dbase, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int col = dbase + 16 * (g & 1) + 4 * (j & 3);
+  const int row = tbase + 4 * (g >> 1) + (j >> 2);
+  const char* a0 = T + row * TokTile<D>::PITCH + col * 2;
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s __attribute__((address_space(3)))*)a0);
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (v4s __attribute__((address_space(3)))*)(a0 + 8 * TokTile<D>::PITCH));
+  const v8s both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, both);
 }
 
 // ------------------------------------------------------------------------------------------
 // 1. dQ (and D) kernel
 // ------------------------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void score_tiles(const char* Ks, const char* Vs, const bf16x8* qf,
+                                            const bf16x8* dof, int jt, int lane, f32x16& st,
+                                            f32x16& dpt) {
+  constexpr int KK = D / 16;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) st[r] = dpt[r] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const bf16x8 ka = frag_rows<D>(Ks, jt * 32, kk, lane);
+    const bf16x8 va = frag_rows<D>(Vs, jt * 32, kk, lane);
+    st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], st, 0, 0, 0);
+    dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dof[kk], dpt, 0, 0, 0);
+  }
+}
+
 template <int D, bool FULLD>
 __global__ __launch_bounds__(256) void attn_dq_kernel(AttnParams p) {
-  constexpr int BQ = 128, BKV = 64, LDR = D + 8, LDT = BKV + 8, KK = D / 16, DT = D / 32;
+  constexpr int BQ = 128, BKV = 64, KK = D / 16, DT = D / 32;
+  constexpr int TB = TokTile<D>::BYTES;
   constexpr int LDE = D + 4;  // fp32 epilogue tile [BQ][LDE] reuses the same LDS
-  constexpr int KV_ELEMS = 2 * BKV * LDR + D * LDT, EPI_ELEMS = BQ * LDE * 2;
-  __shared__ __align__(16) uint16_t smem[KV_ELEMS > EPI_ELEMS ? KV_ELEMS : EPI_ELEMS];
-  uint16_t* Ks = smem;
-  uint16_t* Vs = smem + BKV * LDR;
-  uint16_t* Kt = smem + 2 * BKV * LDR;
+  constexpr int KV_BYTES = 4 * TB, EPI_BYTES = BQ * LDE * 4;
+  __shared__ __align__(16) char smem[KV_BYTES > EPI_BYTES ? KV_BYTES : EPI_BYTES];
+  // buffers: K in smem + buf*2*TB, V right after it
   const int b = blockIdx.z, h = blockIdx.y, g = h / p.G;
   const int cs = p.cu ? min(p.cu[b], p.M_kept) : b * p.S;
   const int nb = p.cu ? max(0, min(p.cu[b + 1], p.M_kept) - cs) : p.S;
@@ -129,6 +183,7 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnParams p) {
   const float lse2 = qvalid ? p.lse[(int64_t)(cs + iq) * p.ld_lse + h] * kLog2e : 0.f;
   const int kv_end = min(nb, q0 + BQ);
   const int nkvb = (kv_end + BKV - 1) / BKV;
+  TileRegs<D> rk, rv;
 
   float Dv = 0.f;
   if constexpr (FULLD) {
@@ -145,23 +200,21 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnParams p) {
   } else {
     // pass 1: D~_i = sum over kept keys j <= i of P_ij dP_ij
     float dacc = 0.f;
+    rk.load(kseq, p.ld_k, g * D, 0, nb);
+    rv.load(vseq, p.ld_v, g * D, 0, nb);
+    rk.store(smem);
+    rv.store(smem + TB);
+    __syncthreads();
     for (int kb = 0; kb < nkvb; ++kb) {
-      __syncthreads();
-      load_tile<D, BKV, LDR, LDT>(kseq, p.ld_k, g * D, kb * BKV, nb, Ks, nullptr);
-      load_tile<D, BKV, LDR, LDT>(vseq, p.ld_v, g * D, kb * BKV, nb, Vs, nullptr);
-      __syncthreads();
+      const char* Ks = smem + (kb & 1) * 2 * TB;
+      if (kb + 1 < nkvb) {
+        rk.load(kseq, p.ld_k, g * D, (kb + 1) * BKV, nb);
+        rv.load(vseq, p.ld_v, g * D, (kb + 1) * BKV, nb);
+      }
 #pragma unroll
       for (int jt = 0; jt < BKV / 32; ++jt) {
         f32x16 st, dpt;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st[r] = dpt[r] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8 ka = *(const bf16x8*)(Ks + (jt * 32 + l32) * LDR + kk * 16 + hl * 8);
-          const bf16x8 va = *(const bf16x8*)(Vs + (jt * 32 + l32) * LDR + kk * 16 + hl * 8);
-          st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], st, 0, 0, 0);
-          dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dof[kk], dpt, 0, 0, 0);
-        }
+        score_tiles<D>(Ks, Ks + TB, qf, dof, jt, lane, st, dpt);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = kb * BKV + jt * 32 + acc_row(r, lane);
@@ -169,6 +222,12 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnParams p) {
           dacc += pr * dpt[r];
         }
       }
+      if (kb + 1 < nkvb) {
+        char* nx = smem + ((kb + 1) & 1) * 2 * TB;
+        rk.store(nx);
+        rv.store(nx + TB);
+      }
+      __syncthreads();
     }
     Dv = dacc + __shfl_xor(dacc, 32, 64);
   }
@@ -180,23 +239,21 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnParams p) {
   for (int t = 0; t < DT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqa[t][r] = 0.f;
+  rk.load(kseq, p.ld_k, g * D, 0, nb);
+  rv.load(vseq, p.ld_v, g * D, 0, nb);
+  rk.store(smem);
+  rv.store(smem + TB);
+  __syncthreads();
   for (int kb = 0; kb < nkvb; ++kb) {
-    __syncthreads();
-    load_tile<D, BKV, LDR, LDT>(kseq, p.ld_k, g * D, kb * BKV, nb, Ks, Kt);
-    load_tile<D, BKV, LDR, LDT>(vseq, p.ld_v, g * D, kb * BKV, nb, Vs, nullptr);
-    __syncthreads();
+    const char* Ks = smem + (kb & 1) * 2 * TB;
+    if (kb + 1 < nkvb) {
+      rk.load(kseq, p.ld_k, g * D, (kb + 1) * BKV, nb);
+      rv.load(vseq, p.ld_v, g * D, (kb + 1) * BKV, nb);
+    }
 #pragma unroll
     for (int jt = 0; jt < BKV / 32; ++jt) {
       f32x16 st, dpt;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[r] = dpt[r] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const bf16x8 ka = *(const bf16x8*)(Ks + (jt * 32 + l32) * LDR + kk * 16 + hl * 8);
-        const bf16x8 va = *(const bf16x8*)(Vs + (jt * 32 + l32) * LDR + kk * 16 + hl * 8);
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], st, 0, 0, 0);
-        dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dof[kk], dpt, 0, 0, 0);
-      }
+      score_tiles<D>(Ks, Ks + TB, qf, dof, jt, lane, st, dpt);
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -209,15 +266,20 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnParams p) {
         const bf16x8 a = to_frag(ds + 8 * step);
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
-          const bf16x8 bk = tr_frag(Kt, LDT, t * 32 + l32, jt * 32 + 16 * step, hl);
+          const bf16x8 bk = frag_tr<D>(Ks, jt * 32 + 16 * step, t * 32, lane);
           dqa[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bk, dqa[t], 0, 0, 0);
         }
       }
     }
+    if (kb + 1 < nkvb) {
+      char* nx = smem + ((kb + 1) & 1) * 2 * TB;
+      rk.store(nx);
+      rv.store(nx + TB);
+    }
+    __syncthreads();
   }
 
   // epilogue: tau * dQ through LDS (fp32), rotary backward, bf16 store
-  __syncthreads();
   float* E = (float*)smem;
 #pragma unroll
   for (int t = 0; t < DT; ++t)
@@ -258,13 +320,10 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnParams p) {
 // ------------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnParams p) {
-  constexpr int BKV = 128, BQ = 64, LDR = D + 8, LDT = BQ + 8, KK = D / 16, DT = D / 32;
-  __shared__ __align__(16) uint16_t Qs[BQ * LDR];
-  __shared__ __align__(16) uint16_t Qt[D * LDT];
-  __shared__ __align__(16) uint16_t Os[BQ * LDR];
-  __shared__ __align__(16) uint16_t Ot[D * LDT];
-  __shared__ __align__(16) float Ls[BQ];
-  __shared__ __align__(16) float Ds[BQ];
+  constexpr int BKV = 128, BQ = 64, KK = D / 16, DT = D / 32;
+  constexpr int TB = TokTile<D>::BYTES;
+  constexpr int BUF = 2 * TB + 2 * BQ * 4;  // Q tile, dO tile, lse*log2e, D
+  __shared__ __align__(16) char smem[2 * BUF];
   const int b = blockIdx.z, g = blockIdx.y / p.HS, hs = blockIdx.y % p.HS;
   const int cs = p.cu ? min(p.cu[b], p.M_kept) : b * p.S;
   const int nb = p.cu ? max(0, min(p.cu[b + 1], p.M_kept) - cs) : p.S;
@@ -296,61 +355,89 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnParams p) {
 
   const int GH = p.G / p.HS;
   const int nqb = (nb + BQ - 1) / BQ;
-  for (int hh = 0; hh < GH; ++hh) {
-    const int h = g * p.G + hs * GH + hh;
-    for (int qb = k0 / BQ; qb < nqb; ++qb) {
-      const int i0 = qb * BQ;
-      __syncthreads();
-      load_tile<D, BQ, LDR, LDT>(qseq, p.ld_q, h * D, i0, nb, Qs, Qt);
-      load_tile<D, BQ, LDR, LDT>(doseq, p.ld_do, h * D, i0, nb, Os, Ot);
-      if (threadIdx.x < BQ) {
-        const int i = i0 + threadIdx.x;
-        Ls[threadIdx.x] = i < nb ? p.lse[(int64_t)(cs + i) * p.ld_lse + h] * kLog2e : 0.f;
-        Ds[threadIdx.x] = i < nb ? p.Dbuf[(int64_t)(cs + i) * p.nq + h] : 0.f;
+  const int qb0 = k0 / BQ;
+  const int per_head = nqb - qb0;
+  const int n_iter = GH * per_head;  // (head, query block) pairs, head-major
+  TileRegs<D> rq, ro;
+  float sl = 0.f, sd = 0.f;
+
+  auto fetch = [&](int it) {
+    const int h = g * p.G + hs * GH + it / per_head;
+    const int i0 = (qb0 + it % per_head) * BQ;
+    rq.load(qseq, p.ld_q, h * D, i0, nb);
+    ro.load(doseq, p.ld_do, h * D, i0, nb);
+    if (threadIdx.x < BQ) {
+      const int i = i0 + threadIdx.x;
+      sl = i < nb ? p.lse[(int64_t)(cs + i) * p.ld_lse + h] * kLog2e : 0.f;
+      sd = i < nb ? p.Dbuf[(int64_t)(cs + i) * p.nq + h] : 0.f;
+    }
+  };
+  auto put = [&](int buf) {
+    char* base = smem + buf * BUF;
+    rq.store(base);
+    ro.store(base + TB);
+    if (threadIdx.x < BQ) {
+      ((float*)(base + 2 * TB))[threadIdx.x] = sl;
+      ((float*)(base + 2 * TB + BQ * 4))[threadIdx.x] = sd;
+    }
+  };
+
+  if (n_iter > 0) {
+    fetch(0);
+    put(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < n_iter; ++it) {
+    const char* base = smem + (it & 1) * BUF;
+    const char* Qs = base;
+    const char* Os = base + TB;
+    const float* Ls = (const float*)(base + 2 * TB);
+    const float* Ds = Ls + BQ;
+    const int i0 = (qb0 + it % per_head) * BQ;
+    if (it + 1 < n_iter) fetch(it + 1);
+#pragma unroll
+    for (int t2 = 0; t2 < BQ / 32; ++t2) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const bf16x8 qa = frag_rows<D>(Qs, t2 * 32, kk, lane);
+        const bf16x8 oa = frag_rows<D>(Os, t2 * 32, kk, lane);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kk], dp, 0, 0, 0);
       }
-      __syncthreads();
+      float pr[16], ds[16];
 #pragma unroll
-      for (int it = 0; it < BQ / 32; ++it) {
-        f32x16 s, dp;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int ib = t2 * 32 + 8 * r4 + 4 * hl;  // 4 consecutive queries
+        const float4 l4 = *(const float4*)(Ls + ib);
+        const float4 d4 = *(const float4*)(Ds + ib);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8 qa = *(const bf16x8*)(Qs + (it * 32 + l32) * LDR + kk * 16 + hl * 8);
-          const bf16x8 oa = *(const bf16x8*)(Os + (it * 32 + l32) * LDR + kk * 16 + hl * 8);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], s, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kk], dp, 0, 0, 0);
+        for (int q = 0; q < 4; ++q) {
+          const int r = 4 * r4 + q;
+          const int i = i0 + ib + q;
+          const float pv = (kvalid && i < nb && jk <= i) ? exp2f(s[r] * p.scale_log2 - lv[q]) : 0.f;
+          pr[r] = pv;
+          ds[r] = pv * (dp[r] - dvv[q]);
         }
-        float pr[16], ds[16];
+      }
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int ib = it * 32 + 8 * r4 + 4 * hl;  // 4 consecutive queries
-          const float4 l4 = *(const float4*)(Ls + ib);
-          const float4 d4 = *(const float4*)(Ds + ib);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+      for (int step = 0; step < 2; ++step) {
+        const bf16x8 ap = to_frag(pr + 8 * step);
+        const bf16x8 as = to_frag(ds + 8 * step);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = 4 * r4 + q;
-            const int i = i0 + ib + q;
-            const float pv = (kvalid && i < nb && jk <= i) ? exp2f(s[r] * p.scale_log2 - lv[q]) : 0.f;
-            pr[r] = pv;
-            ds[r] = pv * (dp[r] - dvv[q]);
-          }
-        }
-#pragma unroll
-        for (int step = 0; step < 2; ++step) {
-          const bf16x8 ap = to_frag(pr + 8 * step);
-          const bf16x8 as = to_frag(ds + 8 * step);
-#pragma unroll
-          for (int t = 0; t < DT; ++t) {
-            const bf16x8 bo = tr_frag(Ot, LDT, t * 32 + l32, it * 32 + 16 * step, hl);
-            const bf16x8 bq = tr_frag(Qt, LDT, t * 32 + l32, it * 32 + 16 * step, hl);
-            dva[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap, bo, dva[t], 0, 0, 0);
-            dka[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as, bq, dka[t], 0, 0, 0);
-          }
+        for (int t = 0; t < DT; ++t) {
+          const bf16x8 bo = frag_tr<D>(Os, t2 * 32 + 16 * step, t * 32, lane);
+          const bf16x8 bq = frag_tr<D>(Qs, t2 * 32 + 16 * step, t * 32, lane);
+          dva[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap, bo, dva[t], 0, 0, 0);
+          dka[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as, bq, dka[t], 0, 0, 0);
         }
       }
     }
+    if (it + 1 < n_iter) put((it + 1) & 1);
+    __syncthreads();
   }
   // partial slices: [HS][M_kept][nkv][D]
 #pragma unroll

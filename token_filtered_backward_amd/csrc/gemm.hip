@@ -12,6 +12,8 @@
 // barrier per k-tile).  Long reductions with few output tiles (the weight gradients reduce over
 // all kept tokens) are split over K; the partials are summed in a fixed order by a second kernel
 // that also applies the epilogue, so results are deterministic.
+#include <cstdio>
+#include <cstdlib>
 #include <type_traits>
 
 #include "internal.h"
@@ -359,19 +361,33 @@ __device__ __forceinline__ int mnmaj_off(int k, int c) {
   return k * (2 * R) + ((c ^ ((k & 3) << 2)) << 4);
 }
 
-struct OperandRsrc {
-  __amdgpu_buffer_rsrc_t r;
-};
+// Buffer resource of a raw byte buffer (stride 0): base, num_records = bytes, gfx9 dword 3.
+typedef int rsrc_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  return rsrc_t{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+
+// 16-byte buffer load of each lane straight into LDS (M0 = LDS base of the wave, lane i lands at
+// M0 + 16*i).  Issued as inline assembly: the compiler then inserts no waits for it of its own
+// (it cannot tell which LDS bytes the copy writes and would wait for every outstanding load at
+// each LDS read); completion is tracked explicitly with s_waitcnt vmcnt in the k-loop.
+__device__ __forceinline__ void dma16(rsrc_t rs, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rs)
+               : "memory", "m0");
 }
 
 // Issue the direct loads of one [R x 64] (K-major) or [64 x R] (MN-major) tile; wave w issues
 // instructions w, w+4, ...  `row0` is the first tile row (token or feature index of the operand
 // rows), `col0` the first column.  Byte offsets are relative to the buffer base.
 template <int R, bool KMAJ>
-__device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rs, int64_t ld, int row0, int col0,
+__device__ __forceinline__ void issue_tile(rsrc_t rs, int64_t ld, int row0, int col0,
                                            char* lds_tile, int wave, int lane) {
   constexpr int NI = R * 64 * 2 / 1024;
 #pragma unroll
@@ -387,7 +403,7 @@ __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rs, int64_t ld
       const int c = pos ^ ((k & 3) << 2);
       off = (uint32_t)(((int64_t)(row0 + k) * ld + col0 + 8 * c) * 2);
     }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_tile + q * 1024), 16, off, 0, 0, 0);
+    dma16(rs, lds_addr(lds_tile + q * 1024), off);
   }
 }
 
@@ -415,8 +431,7 @@ __device__ __forceinline__ bf16x8 read_frag(const char* lds_tile, int rbase, int
 // Loads of one k-tile (A then B) into one LDS stage.  B may come in two row segments (B0 for
 // k < kseg, B1 after); a 64-row k-tile never straddles them.
 template <int BM, int BN, bool AK, bool BKM>
-__device__ __forceinline__ void issue_stage(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0,
-                                            __amdgpu_buffer_rsrc_t rb1, int64_t lda, int64_t ldb,
+__device__ __forceinline__ void issue_stage(rsrc_t ra, rsrc_t rb0, rsrc_t rb1, int64_t lda, int64_t ldb,
                                             int kseg, bool two_seg, int m0, int n0, int k0,
                                             char* stage, int wave, int lane) {
   if constexpr (AK)
@@ -443,6 +458,40 @@ __device__ __forceinline__ void issue_stage(__amdgpu_buffer_rsrc_t ra, __amdgpu_
 #define VMCNT_WAIT(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 0xf) | (((n) >> 4) << 14) | (0x7 << 4) | (0xf << 8))
 
+// MFMAs of one k-tile (4 steps of k = 16) from one LDS stage; fragments of step kk+1 are read
+// while the MFMAs of step kk run (two register sets).
+template <int BM, int BN, bool AK, bool BKM>
+__device__ __forceinline__ void mma_ktile(const char* As, const char* Bs,
+                                          f32x16 (&acc)[BM / 64][BN / 64], int wm, int wn,
+                                          int lane) {
+  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  bf16x8 af[2][TM], bfv[2][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) af[0][i] = read_frag<BM, AK>(As, wm * WM + i * 32, 0, lane);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) bfv[0][j] = read_frag<BN, BKM>(Bs, wn * WN + j * 32, 0, lane);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int cur = kk & 1;
+    if (kk + 1 < 4) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[cur ^ 1][i] = read_frag<BM, AK>(As, wm * WM + i * 32, kk + 1, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bfv[cur ^ 1][j] = read_frag<BN, BKM>(Bs, wn * WN + j * 32, kk + 1, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfv[cur][j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 template <int BM, int BN, bool AK, bool BKM, int EPI, int NS>
 __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
   constexpr int BK = 64;
@@ -458,11 +507,11 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
   const int total = T * p.splits;
   const bool partial = p.splits > 1;
   // operand buffers: rows of A are tokens (K-major A: M rows; MN-major A: K rows)
-  const __amdgpu_buffer_rsrc_t ra =
-      make_rsrc(p.A, (uint32_t)((int64_t)(AK ? p.M : p.K) * p.lda * 2));
+  const rsrc_t ra = make_rsrc(p.A, (uint32_t)((int64_t)(AK ? p.M : p.K) * p.lda * 2));
   const int kseg = p.B1 ? p.kseg : p.K;
-  const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(p.B0, (uint32_t)((int64_t)kseg * p.ldb * 2));
-  const __amdgpu_buffer_rsrc_t rb1 =
+  const bool two_seg = p.B1 != nullptr;
+  const rsrc_t rb0 = make_rsrc(p.B0, (uint32_t)((int64_t)kseg * p.ldb * 2));
+  const rsrc_t rb1 =
       make_rsrc(p.B1 ? p.B1 : p.B0, (uint32_t)((int64_t)(p.B1 ? p.K - kseg : 0) * p.ldb * 2));
 
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
@@ -487,7 +536,7 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
       if (s < nk)
-        issue_stage<BM, BN, AK, BKM>(ra, rb0, rb1, p.lda, p.ldb, kseg, p.B1 != nullptr, m0, n0,
+        issue_stage<BM, BN, AK, BKM>(ra, rb0, rb1, p.lda, p.ldb, kseg, two_seg, m0, n0,
                                      kbeg + s * BK, lds + s * STAGE, wave, lane);
     for (int kt = 0; kt < nk; ++kt) {
       // tile kt complete (for this wave), then visible to all waves
@@ -497,66 +546,48 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
         VMCNT_WAIT(0);
       }
       __syncthreads();
-      if (kt + NS - 1 < nk)  // overwrites the stage read in iteration kt-1
-        issue_stage<BM, BN, AK, BKM>(ra, rb0, rb1, p.lda, p.ldb, kseg, p.B1 != nullptr, m0, n0,
+      if (kt + NS - 1 < nk)  // refills the stage read in iteration kt-1
+        issue_stage<BM, BN, AK, BKM>(ra, rb0, rb1, p.lda, p.ldb, kseg, two_seg, m0, n0,
                                      kbeg + (kt + NS - 1) * BK, lds + ((kt + NS - 1) % NS) * STAGE,
                                      wave, lane);
       const char* As = lds + (kt % NS) * STAGE;
-      const char* Bs = As + A_BYTES;
-      // fragments of step kk+1 are read while the MFMAs of step kk run (two register sets)
-      bf16x8 af[2][TM], bfv[2][TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) af[0][i] = read_frag<BM, AK>(As, wm * WM + i * 32, 0, lane);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bfv[0][j] = read_frag<BN, BKM>(Bs, wn * WN + j * 32, 0, lane);
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        const int cur = kk & 1;
-        if (kk + 1 < BK / 16) {
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-            af[cur ^ 1][i] = read_frag<BM, AK>(As, wm * WM + i * 32, kk + 1, lane);
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            bfv[cur ^ 1][j] = read_frag<BN, BKM>(Bs, wn * WN + j * 32, kk + 1, lane);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfv[cur][j], acc[i][j],
-                                                                0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      mma_ktile<BM, BN, AK, BKM>(As, As + A_BYTES, acc, wm, wn, lane);
     }
 
-    // epilogue through LDS: the fp32 tile is staged row-major, then every thread finishes
-    // 8 consecutive columns of a row with 16-byte loads / stores (one row lookup per 8 outputs)
+    // epilogue through LDS: the fp32 tile is staged row-major in passes of EROWS rows, then every
+    // thread finishes 8 consecutive columns of a row with 16-byte loads / stores (one row lookup
+    // per 8 outputs)
     constexpr int LDE = BN + 8;  // +8 floats: the two lane halves' rows land 32 banks apart
-    static_assert(BM * LDE * 4 <= NS * STAGE, "epilogue tile must fit in the stage buffers");
-    __syncthreads();
+    constexpr int EROWS = (BM * LDE * 4 <= NS * STAGE) ? BM : ((64 * LDE * 4 <= NS * STAGE) ? 64 : 32);
+    static_assert(EROWS * LDE * 4 <= NS * STAGE, "epilogue pass must fit in the stage buffers");
     float* E = (float*)lds;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int pass = 0; pass < BM / EROWS; ++pass) {
+      __syncthreads();
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+      for (int i = 0; i < TM; ++i) {
+        const int rb = wm * WM + i * 32;  // first tile row of this 32-row accumulator block
+        if (rb / EROWS != pass) continue;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          E[(wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * LDE + wn * WN + j * 32 +
-            (lane & 31)] = acc[i][j][r];
-    __syncthreads();
-    for (int c = threadIdx.x; c < BM * (BN / 8); c += 256) {
-      const int row = c / (BN / 8), col = (c % (BN / 8)) * 8;
-      const int m = m0 + row, n = n0 + col;
-      if (m >= p.M || n >= p.N) continue;
-      const float4 lo = *(const float4*)(E + row * LDE + col);
-      const float4 hi = *(const float4*)(E + row * LDE + col + 4);
-      const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      if (partial)
-        store8_partial(p, split, m, n, v);
-      else
-        epi_store8<EPI>(p, m, n, v);
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            E[(rb - pass * EROWS + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * LDE + wn * WN +
+              j * 32 + (lane & 31)] = acc[i][j][r];
+      }
+      __syncthreads();
+      for (int c = threadIdx.x; c < EROWS * (BN / 8); c += 256) {
+        const int row = c / (BN / 8), col = (c % (BN / 8)) * 8;
+        const int m = m0 + pass * EROWS + row, n = n0 + col;
+        if (m >= p.M || n >= p.N) continue;
+        const float4 lo = *(const float4*)(E + row * LDE + col);
+        const float4 hi = *(const float4*)(E + row * LDE + col + 4);
+        const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        if (partial)
+          store8_partial(p, split, m, n, v);
+        else
+          epi_store8<EPI>(p, m, n, v);
+      }
     }
   }
 }
@@ -616,8 +647,8 @@ Plan make_plan(const GemmProblem& p) {
   Plan best{3, 128, 128, 1, kBK, lds};
   if (p.K <= 0) return best;  // empty reduction: the kernel stores zeros (or leaves C + 0)
   double best_cost = 1e300;
-  // 256 x 256 needs more than 512 registers per lane (both kernels spill): not used
-  for (int c = 1; c < 4; ++c) {
+  // 256 x 256 only in the direct-to-LDS kernel (staged through registers it would spill)
+  for (int c = lds ? 0 : 1; c < 4; ++c) {
     TileCfg tc = kCfgs[c];
     if (lds && c == 3) tc.per_cu = 1;  // three 32 KB stages
     if (lds && (c == 1 || c == 2)) tc.eff = 0.85;
@@ -688,6 +719,22 @@ collider_status launch_cfg(const GemmParams& gp, const GemmProblem& pr, bool lds
   return COLLIDER_ERR_UNSUPPORTED;
 }
 
+// 256 x 256 exists only as a direct-to-LDS kernel (the register-staged one would spill)
+template <int BM, int BN>
+collider_status launch_cfg_lds(const GemmParams& gp, const GemmProblem& pr, const char* name,
+                               hipStream_t s) {
+  if (pr.a_kmajor && !pr.b_kmajor) {
+    switch (pr.epi) {
+      case EPI_BF16: return launch_lds<BM, BN, EPI_BF16, true, false>(gp, name, s);
+      case EPI_SWIGLU: return launch_lds<BM, BN, EPI_SWIGLU, true, false>(gp, name, s);
+      case EPI_GELU: return launch_lds<BM, BN, EPI_GELU, true, false>(gp, name, s);
+    }
+  } else if (!pr.a_kmajor && !pr.b_kmajor && pr.epi == EPI_F32) {
+    return launch_lds<BM, BN, EPI_F32, false, false>(gp, name, s);
+  }
+  return COLLIDER_ERR_UNSUPPORTED;
+}
+
 template <int EPI>
 collider_status launch_reduce(const GemmParams& gp, const GemmProblem& prob, int splits,
                               hipStream_t s) {
@@ -740,8 +787,16 @@ collider_status gemm_bf16(const GemmProblem& prob, void* ws, size_t ws_bytes, hi
     gp.partial = (float*)ws;
   }
   const char* name = prob.name ? prob.name : "gemm_bf16";
+  static const bool verbose = getenv("COLLIDER_GEMM_PLANS") != nullptr;
+  if (verbose)
+    fprintf(stderr, "[collider] %s M=%d N=%d K=%d tile=%dx%d splits=%d %s\n", name, prob.M, prob.N,
+            prob.K, pl.bm, pl.bn, pl.splits, pl.lds ? "lds" : "staged");
   collider_status st;
   switch (pl.cfg) {
+    case 0:
+      if (!pl.lds) return COLLIDER_ERR_UNSUPPORTED;
+      st = launch_cfg_lds<256, 256>(gp, prob, name, s);
+      break;
     case 1: st = launch_cfg<256, 128>(gp, prob, pl.lds, name, s); break;
     case 2: st = launch_cfg<128, 256>(gp, prob, pl.lds, name, s); break;
     default: st = launch_cfg<128, 128>(gp, prob, pl.lds, name, s); break;
