@@ -55,6 +55,10 @@ static constexpr float kLog2e = 1.4426950408889634f;
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));
 
+// 2^x with the hardware instruction alone: results below the smallest normal flush to 0, which is
+// what a softmax probability that small should be.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ int acc_row(int r, int lane) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
@@ -150,7 +154,7 @@ __device__ __forceinline__ void score_tiles(const char* Ks, const char* Vs, cons
 }
 
 template <int D, bool FULLD>
-__global__ __launch_bounds__(256) void attn_dq_kernel(AttnParams p) {
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_dq_kernel(AttnParams p) {
   constexpr int BQ = 128, BKV = 64, KK = D / 16, DT = D / 32;
   constexpr int TB = TokTile<D>::BYTES;
   constexpr int LDE = D + 4;  // fp32 epilogue tile [BQ][LDE] reuses the same LDS
@@ -163,9 +167,12 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnParams p) {
   const int nqb = (nb + BQ - 1) / BQ;
   if ((int)blockIdx.x >= nqb) return;
   const int q0 = (nqb - 1 - (int)blockIdx.x) * BQ;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hl = lane >> 5, l32 = lane & 31;
+  const int lane = threadIdx.x & 63, hl = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int iq = q0 + wave * 32 + l32;
   const bool qvalid = iq < nb;
+  const int qw = q0 + wave * 32;     // first query of this wave
+  const bool qall = qw + 31 < nb;    // all 32 queries of the wave exist
   const uint16_t* kseq = p.k + (int64_t)cs * p.ld_k;  // rows of this sequence
   const uint16_t* vseq = p.v + (int64_t)cs * p.ld_v;
 
@@ -215,11 +222,16 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnParams p) {
       for (int jt = 0; jt < BKV / 32; ++jt) {
         f32x16 st, dpt;
         score_tiles<D>(Ks, Ks + TB, qf, dof, jt, lane, st, dpt);
+        if (kb * BKV + jt * 32 + 31 <= qw && qall) {  // below the diagonal: no mask
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = kb * BKV + jt * 32 + acc_row(r, lane);
-          const float pr = (qvalid && j <= iq) ? exp2f(st[r] * p.scale_log2 - lse2) : 0.f;
-          dacc += pr * dpt[r];
+          for (int r = 0; r < 16; ++r) dacc += fast_exp2(fmaf(st[r], p.scale_log2, -lse2)) * dpt[r];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = kb * BKV + jt * 32 + acc_row(r, lane);
+            const float pr = (qvalid && j <= iq) ? fast_exp2(fmaf(st[r], p.scale_log2, -lse2)) : 0.f;
+            dacc += pr * dpt[r];
+          }
         }
       }
       if (kb + 1 < nkvb) {
@@ -255,11 +267,17 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnParams p) {
       f32x16 st, dpt;
       score_tiles<D>(Ks, Ks + TB, qf, dof, jt, lane, st, dpt);
       float ds[16];
+      if (kb * BKV + jt * 32 + 31 <= qw && qall) {  // below the diagonal: no mask
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = kb * BKV + jt * 32 + acc_row(r, lane);
-        const float pr = (qvalid && j <= iq) ? exp2f(st[r] * p.scale_log2 - lse2) : 0.f;
-        ds[r] = pr * (dpt[r] - Dv);
+        for (int r = 0; r < 16; ++r)
+          ds[r] = fast_exp2(fmaf(st[r], p.scale_log2, -lse2)) * (dpt[r] - Dv);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = kb * BKV + jt * 32 + acc_row(r, lane);
+          const float pr = (qvalid && j <= iq) ? fast_exp2(fmaf(st[r], p.scale_log2, -lse2)) : 0.f;
+          ds[r] = pr * (dpt[r] - Dv);
+        }
       }
 #pragma unroll
       for (int step = 0; step < 2; ++step) {
@@ -319,7 +337,7 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnParams p) {
 // 2. dK / dV kernel
 // ------------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void attn_dkv_kernel(AttnParams p) {
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_dkv_kernel(AttnParams p) {
   constexpr int BKV = 128, BQ = 64, KK = D / 16, DT = D / 32;
   constexpr int TB = TokTile<D>::BYTES;
   constexpr int BUF = 2 * TB + 2 * BQ * 4;  // Q tile, dO tile, lse*log2e, D
@@ -330,9 +348,12 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnParams p) {
   const int nkb = (nb + BKV - 1) / BKV;
   if ((int)blockIdx.x >= nkb) return;
   const int k0 = blockIdx.x * BKV;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hl = lane >> 5, l32 = lane & 31;
+  const int lane = threadIdx.x & 63, hl = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int jk = k0 + wave * 32 + l32;  // this lane's key (S column)
   const bool kvalid = jk < nb;
+  const int kw = k0 + wave * 32;     // first key of this wave
+  const bool kall = kw + 31 < nb;    // all 32 keys of the wave exist
   const uint16_t* qseq = p.q + (int64_t)cs * p.ld_q;  // rows of this sequence
   const uint16_t* doseq = p.dout + (int64_t)cs * p.ld_do;
 
@@ -408,19 +429,30 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(AttnParams p) {
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kk], dp, 0, 0, 0);
       }
       float pr[16], ds[16];
+      // every query of this 32-block is valid and after every key of the wave: no mask
+      const bool interior = (i0 + t2 * 32 >= kw + 31) && (i0 + t2 * 32 + 31 < nb) && kall;
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int ib = t2 * 32 + 8 * r4 + 4 * hl;  // 4 consecutive queries
         const float4 l4 = *(const float4*)(Ls + ib);
         const float4 d4 = *(const float4*)(Ds + ib);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+        if (interior) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = 4 * r4 + q;
-          const int i = i0 + ib + q;
-          const float pv = (kvalid && i < nb && jk <= i) ? exp2f(s[r] * p.scale_log2 - lv[q]) : 0.f;
-          pr[r] = pv;
-          ds[r] = pv * (dp[r] - dvv[q]);
+          for (int q = 0; q < 4; ++q) {
+            const int r = 4 * r4 + q;
+            pr[r] = fast_exp2(fmaf(s[r], p.scale_log2, -lv[q]));
+            ds[r] = pr[r] * (dp[r] - dvv[q]);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = 4 * r4 + q;
+            const int i = i0 + ib + q;
+            const float pv = (kvalid && i < nb && jk <= i) ? fast_exp2(fmaf(s[r], p.scale_log2, -lv[q])) : 0.f;
+            pr[r] = pv;
+            ds[r] = pv * (dp[r] - dvv[q]);
+          }
         }
       }
 #pragma unroll
