@@ -190,6 +190,16 @@ def main():
     prof = tfb.collider_profile_collect()
     tfb.collider_profile_enable(False)
     kernels = {k: round(v[0] / n_prof, 4) for k, v in sorted(prof.items(), key=lambda kv: -kv[1][0])}
+    kernels_unf = None
+    if not args.no_unfiltered:
+        tfb.collider_profile_enable(True)
+        for _ in range(n_prof):
+            step_unfiltered()
+        torch.cuda.synchronize()
+        prof_u = tfb.collider_profile_collect()
+        tfb.collider_profile_enable(False)
+        kernels_unf = {k: round(v[0] / n_prof, 4)
+                       for k, v in sorted(prof_u.items(), key=lambda kv: -kv[1][0])}
     gemm_names = [k for k in prof if k.startswith("gemm_") and k != "gemm_splitk_reduce"]
     gemm_ms = sum(prof[k][0] for k in gemm_names) / n_prof
     gemm_launches = sum(prof[k][1] for k in gemm_names) / n_prof
@@ -230,6 +240,7 @@ def main():
         "attn_tflops": None if attn_tflops is None else round(attn_tflops, 1),
         "gather_gbs": None if gather_gbs is None else round(gather_gbs, 1),
         "kernel_ms_per_step": kernels,
+        "kernel_ms_per_step_unfiltered": kernels_unf,
         "roofline": {
             "kernel": f"gemm_bf16 (all {int(gemm_launches)} reduced-GEMM launches of one layer)",
             "bound": "mfma",

@@ -41,6 +41,11 @@ hipEvent_t pool_get() {
 }
 }  // namespace
 
+bool profiling_on() {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  return g_prof_on;
+}
+
 ProfScope::ProfScope(const char* n, hipStream_t s) : name(n), stream(s), slot(-1) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (!g_prof_on) return;

@@ -30,6 +30,9 @@ __device__ __forceinline__ float bfhi(uint32_t w) { return __uint_as_float(w & 0
 // ------------------------------------------------------------------------------------------
 // launch bookkeeping: error check + optional per-kernel event timing
 // ------------------------------------------------------------------------------------------
+// true while per-kernel event timing is enabled (collider_profile_enable)
+bool profiling_on();
+
 struct ProfScope {
   const char* name;
   hipStream_t stream;

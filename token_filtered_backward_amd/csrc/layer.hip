@@ -18,6 +18,7 @@
 // Normalised inputs (xn1', xn2') and activations (a', g') are recomputed from saved tensors read
 // through the index; the SwiGLU / GELU backward is fused into the epilogue of the GEMM producing dA.
 #include <algorithm>
+#include <cstdlib>
 
 #include "internal.h"
 
@@ -25,14 +26,45 @@ namespace collider {
 
 namespace {
 
+// One side stream (default priority) and its fork / join events per host thread and device,
+// created on first use and kept for the life of the process.  Everything runs on the caller's
+// stream with COLLIDER_SINGLE_STREAM=1 set, and while per-kernel timing is on (so that each
+// kernel's events bracket it alone).
+struct Side {
+  hipStream_t s = nullptr;
+  hipEvent_t ev[5] = {};
+};
+
+collider_status side_stream(Side** out) {
+  static const bool single = getenv("COLLIDER_SINGLE_STREAM") != nullptr;
+  *out = nullptr;
+  if (single || profiling_on()) return COLLIDER_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return COLLIDER_ERR_HIP;
+  thread_local Side sides[64];
+  Side& sd = sides[dev];
+  if (!sd.s) {
+    for (hipEvent_t& e : sd.ev)
+      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return COLLIDER_ERR_HIP;
+    if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess) {
+      sd.s = nullptr;
+      return COLLIDER_ERR_HIP;
+    }
+  }
+  *out = &sd;
+  return COLLIDER_OK;
+}
+
 struct LayerBufs {
+
   uint16_t *dy_c, *o_c, *q_c, *k_c, *v_c;
   float* lse_c;
-  uint16_t *act_c, *xn_c, *dmid, *dxn, *dh, *do_c, *dx_c;
+  uint16_t *act_c, *xn_c, *dmid, *dqkv, *dxn, *dh, *do_c, *dx_c;
   float *part_g, *part_b;
-  void* gemm_ws;
+  void* gemm_ws;   // split-K partials of the GEMMs on the caller's stream
+  void* gemm_ws2;  // ... and of the weight-gradient GEMMs on the side stream
   void* attn_ws;
-  size_t gemm_ws_bytes, attn_ws_bytes;
+  size_t gemm_ws_bytes, gemm_ws2_bytes, attn_ws_bytes;
 };
 
 }  // namespace
@@ -70,6 +102,10 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
   b.act_c = cv.take<uint16_t>((size_t)Mk * I);
   b.xn_c = cv.take<uint16_t>((size_t)Mk * H);
   b.dmid = cv.take<uint16_t>((size_t)Mk * mid);
+  // [dq|dk|dv]: its own buffer for LLAMA (attention must not overwrite [dgate|dup] while the
+  // side stream's dw_gateup GEMM may still read it); for PHI the first columns of dmid
+  b.dqkv = llama ? cv.take<uint16_t>((size_t)Mk * nqkv) : b.dmid;
+  const int ldq = llama ? nqkv : mid;
   b.dxn = cv.take<uint16_t>((size_t)Mk * H);
   b.dh = llama ? cv.take<uint16_t>((size_t)Mk * H) : nullptr;
   b.do_c = cv.take<uint16_t>((size_t)Mk * nqd);
@@ -107,8 +143,8 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     dw_gemm(g_dwmid, 2 * I, H, b.dmid, mid, b.xn_c, H, gr ? gr->dw_gateup : nullptr);
     dx_gemm(g_dO, nqd, H, b.dh, H, w ? w->w_o : nullptr, nqd, EPI_BF16, b.do_c, nqd);
     dw_gemm(g_dwo, H, nqd, b.dh, H, b.o_c, nqd, gr ? gr->dw_o : nullptr);
-    dx_gemm(g_dXin, H, nqkv, b.dmid, mid, w ? w->w_qkv : nullptr, H, EPI_BF16, b.dxn, H);
-    dw_gemm(g_dwqkv, nqkv, H, b.dmid, mid, b.xn_c, H, gr ? gr->dw_qkv : nullptr);
+    dx_gemm(g_dXin, H, nqkv, b.dqkv, ldq, w ? w->w_qkv : nullptr, H, EPI_BF16, b.dxn, H);
+    dw_gemm(g_dwqkv, nqkv, H, b.dqkv, ldq, b.xn_c, H, gr ? gr->dw_qkv : nullptr);
   } else {
     uint16_t* dF = b.dmid ? b.dmid + nqkv : nullptr;
     dx_gemm(g_dA, I, H, b.dy_c, H, w ? w->w_fc2 : nullptr, I, EPI_GELU, dF, mid);
@@ -135,11 +171,16 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
   g_dwfc1.name = "gemm_dw_fc1";
   const GemmProblem* gl[] = {&g_dA, &g_dw2, &g_dXmid, &g_dwmid, &g_dO, &g_dwo, &g_dXin, &g_dwqkv,
                              &g_dwfc1};
-  size_t gemm_need = 0;
-  for (const GemmProblem* p : gl)
-    if (p->M > 0) gemm_need = std::max(gemm_need, gemm_bf16_workspace_bytes(*p));
+  size_t gemm_need = 0, gemm_need2 = 0;
+  for (const GemmProblem* p : gl) {
+    if (p->M <= 0) continue;
+    size_t& need_s = p->epi == EPI_F32 ? gemm_need2 : gemm_need;  // dW GEMMs: side stream
+    need_s = std::max(need_s, gemm_bf16_workspace_bytes(*p));
+  }
   b.gemm_ws = cv.take<char>(gemm_need);
   b.gemm_ws_bytes = gemm_need;
+  b.gemm_ws2 = cv.take<char>(gemm_need2);
+  b.gemm_ws2_bytes = gemm_need2;
 
   collider_attn_cfg ac{};
   ac.n_q_heads = nq;
@@ -188,28 +229,17 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     add(sv->lse, b.lse_c, nq * 4);
     CHECK(launch_gather_rows(gd, nd, idx, Mk, s));
   }
-  if (llama) {
-    CHECK(launch_act_recompute((const uint16_t*)sv->gate, (const uint16_t*)sv->up, idx, Mk, I,
-                               b.act_c, s));
-    CHECK(gemm_bf16(g_dA, b.gemm_ws, b.gemm_ws_bytes, s));
-    CHECK(gemm_bf16(g_dw2, b.gemm_ws, b.gemm_ws_bytes, s));
-    CHECK(launch_norm_recompute((const uint16_t*)sv->h, nullptr, sv->rstd2, w->gamma2, nullptr, idx,
-                                Mk, H, b.xn_c, s));
-    CHECK(gemm_bf16(g_dXmid, b.gemm_ws, b.gemm_ws_bytes, s));
-    CHECK(gemm_bf16(g_dwmid, b.gemm_ws, b.gemm_ws_bytes, s));
-    CHECK(launch_norm_bwd(b.dxn, b.dy_c, (const uint16_t*)sv->h, nullptr, sv->rstd2, w->gamma2, idx,
-                          Mk, H, b.dh, b.part_g, nullptr, parts, s));
-    CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dgamma2, c.accumulate, s));
-    CHECK(gemm_bf16(g_dO, b.gemm_ws, b.gemm_ws_bytes, s));
-    CHECK(gemm_bf16(g_dwo, b.gemm_ws, b.gemm_ws_bytes, s));
-  } else {
-    CHECK(launch_act_recompute((const uint16_t*)sv->f, nullptr, idx, Mk, I, b.act_c, s));
-    CHECK(gemm_bf16(g_dA, b.gemm_ws, b.gemm_ws_bytes, s));
-    CHECK(gemm_bf16(g_dw2, b.gemm_ws, b.gemm_ws_bytes, s));
-    CHECK(gemm_bf16(g_dO, b.gemm_ws, b.gemm_ws_bytes, s));
-    CHECK(gemm_bf16(g_dwo, b.gemm_ws, b.gemm_ws_bytes, s));
-  }
-  // attention backward -> [dq | dk | dv] columns of dmid
+  // Weight-gradient GEMMs (and the normalised inputs only they read) run on a side stream,
+  // forked from and joined back to the caller's stream with events; the critical path
+  // dA -> dX -> norm bwd -> dO -> attention -> dX -> norm bwd -> scatter stays on `s`.
+  Side* side = nullptr;
+  CHECK(side_stream(&side));
+  hipStream_t s1 = side ? side->s : s;
+  auto handoff = [&](int e, hipStream_t from, hipStream_t to) -> collider_status {
+    if (!side) return COLLIDER_OK;
+    if (hipEventRecord(side->ev[e], from) != hipSuccess) return COLLIDER_ERR_HIP;
+    return hipStreamWaitEvent(to, side->ev[e], 0) == hipSuccess ? COLLIDER_OK : COLLIDER_ERR_HIP;
+  };
   collider_attn_io io{};
   io.q = b.q_c; io.ld_q = nqd;
   io.k = b.k_c; io.ld_k = nkvd;
@@ -217,24 +247,49 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
   io.o = b.o_c; io.ld_o = nqd;
   io.lse = b.lse_c; io.ld_lse = nq;
   io.dout = b.do_c; io.ld_do = nqd;
-  io.dq = b.dmid; io.ld_dq = mid;
-  io.dk = b.dmid + nqd; io.ld_dk = mid;
-  io.dv = b.dmid + nqd + nkvd; io.ld_dv = mid;
-  CHECK(attn_bwd(ac, aix, io, b.attn_ws, b.attn_ws_bytes, s));
+  io.dq = b.dqkv; io.ld_dq = ldq;
+  io.dk = b.dqkv + nqd; io.ld_dk = ldq;
+  io.dv = b.dqkv + nqd + nkvd; io.ld_dv = ldq;
   if (llama) {
+    CHECK(launch_act_recompute((const uint16_t*)sv->gate, (const uint16_t*)sv->up, idx, Mk, I,
+                               b.act_c, s));
+    CHECK(handoff(0, s, s1));  // gathered dY', O' and a' ready
+    CHECK(launch_norm_recompute((const uint16_t*)sv->h, nullptr, sv->rstd2, w->gamma2, nullptr, idx,
+                                Mk, H, b.xn_c, s1));
+    CHECK(gemm_bf16(g_dw2, b.gemm_ws2, b.gemm_ws2_bytes, s1));
+    CHECK(gemm_bf16(g_dA, b.gemm_ws, b.gemm_ws_bytes, s));
+    CHECK(handoff(1, s, s1));  // [dgate|dup] ready
+    CHECK(gemm_bf16(g_dwmid, b.gemm_ws2, b.gemm_ws2_bytes, s1));
+    CHECK(gemm_bf16(g_dXmid, b.gemm_ws, b.gemm_ws_bytes, s));
+    CHECK(launch_norm_bwd(b.dxn, b.dy_c, (const uint16_t*)sv->h, nullptr, sv->rstd2, w->gamma2, idx,
+                          Mk, H, b.dh, b.part_g, nullptr, parts, s));
+    CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dgamma2, c.accumulate, s));
+    CHECK(handoff(2, s, s1));  // dh ready
+    CHECK(gemm_bf16(g_dwo, b.gemm_ws2, b.gemm_ws2_bytes, s1));
+    CHECK(gemm_bf16(g_dO, b.gemm_ws, b.gemm_ws_bytes, s));
+    CHECK(attn_bwd(ac, aix, io, b.attn_ws, b.attn_ws_bytes, s));
+    CHECK(handoff(3, s, s1));  // [dq|dk|dv] ready
     CHECK(launch_norm_recompute((const uint16_t*)sv->x, nullptr, sv->rstd1, w->gamma1, nullptr, idx,
-                                Mk, H, b.xn_c, s));
+                                Mk, H, b.xn_c, s1));
+    CHECK(gemm_bf16(g_dwqkv, b.gemm_ws2, b.gemm_ws2_bytes, s1));
     CHECK(gemm_bf16(g_dXin, b.gemm_ws, b.gemm_ws_bytes, s));
-    CHECK(gemm_bf16(g_dwqkv, b.gemm_ws, b.gemm_ws_bytes, s));
     CHECK(launch_norm_bwd(b.dxn, b.dh, (const uint16_t*)sv->x, nullptr, sv->rstd1, w->gamma1, idx, Mk,
                           H, b.dx_c, b.part_g, nullptr, parts, s));
     CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dgamma1, c.accumulate, s));
   } else {
+    CHECK(launch_act_recompute((const uint16_t*)sv->f, nullptr, idx, Mk, I, b.act_c, s));
+    CHECK(handoff(0, s, s1));  // gathered dY', O' and gelu(f') ready
     CHECK(launch_norm_recompute((const uint16_t*)sv->x, sv->mean, sv->rstd1, w->ln_gamma, w->ln_beta,
-                                idx, Mk, H, b.xn_c, s));
+                                idx, Mk, H, b.xn_c, s1));
+    CHECK(gemm_bf16(g_dw2, b.gemm_ws2, b.gemm_ws2_bytes, s1));
+    CHECK(gemm_bf16(g_dwo, b.gemm_ws2, b.gemm_ws2_bytes, s1));
+    CHECK(gemm_bf16(g_dA, b.gemm_ws, b.gemm_ws_bytes, s));
+    CHECK(gemm_bf16(g_dO, b.gemm_ws, b.gemm_ws_bytes, s));
+    CHECK(attn_bwd(ac, aix, io, b.attn_ws, b.attn_ws_bytes, s));
+    CHECK(handoff(1, s, s1));  // [dq|dk|dv|dF] ready
+    CHECK(gemm_bf16(g_dwqkv, b.gemm_ws2, b.gemm_ws2_bytes, s1));
+    CHECK(gemm_bf16(g_dwfc1, b.gemm_ws2, b.gemm_ws2_bytes, s1));
     CHECK(gemm_bf16(g_dXin, b.gemm_ws, b.gemm_ws_bytes, s));
-    CHECK(gemm_bf16(g_dwqkv, b.gemm_ws, b.gemm_ws_bytes, s));
-    CHECK(gemm_bf16(g_dwfc1, b.gemm_ws, b.gemm_ws_bytes, s));
     CHECK(launch_norm_bwd(b.dxn, b.dy_c, (const uint16_t*)sv->x, sv->mean, sv->rstd1, w->ln_gamma,
                           idx, Mk, H, b.dx_c, b.part_g, b.part_b, parts, s));
     CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dln_gamma, c.accumulate, s));
@@ -242,6 +297,7 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
   }
   if (!dx_compact && !unf) CHECK(launch_scatter_bytes(b.dx_c, (int64_t)H * 2, gr->dx, (int64_t)H * 2, ix.inv,
                                               M, H * 2, 1, s));
+  CHECK(handoff(4, s1, s));  // join: every weight gradient is complete on the caller's stream
 #undef CHECK
   return COLLIDER_OK;
 }
