@@ -46,8 +46,50 @@ def algorithmic_work(cfg, M_kept, seq_counts):
     attn_flops = 10.0 * d * nq * pairs                    # S, dP, dV, dK, dQ
     attn_dt_flops = 4.0 * d * nq * pairs                  # the filtered softmax-backward row term
     gather_bytes = 2.0 * M_kept * (2 * H + 2 * 2 * nq * d + 2 * 2 * nkv * d + 4 * nq)
+    # reduced-GEMM bytes: bf16 operands read once, outputs written once (bf16 dX, fp32 dW), plus
+    # the activation-backward epilogue's reads of the saved pre-activations
+    Mk, nqd = M_kept, nq * d
+    if cfg.kind == "llama":
+        gemm_bytes = [2 * (Mk * H + H * I) + 8 * Mk * I,                  # dA (SwiGLU epilogue)
+                      2 * Mk * H + 2 * Mk * I + 4 * H * I,                 # dW down
+                      2 * (2 * Mk * I + 2 * I * H + Mk * H),               # dX gate/up
+                      4 * Mk * I + 2 * Mk * H + 8 * I * H,                 # dW gate/up
+                      2 * (Mk * H + H * nqd + Mk * nqd),                   # dO
+                      2 * Mk * H + 2 * Mk * nqd + 4 * H * nqd,             # dW o
+                      2 * (Mk * nqkv + nqkv * H + Mk * H),                 # dX qkv
+                      2 * Mk * nqkv + 2 * Mk * H + 4 * nqkv * H]           # dW qkv
+    else:
+        gemm_bytes = [2 * (Mk * H + H * I) + 4 * Mk * I,                  # dF (GELU epilogue)
+                      2 * Mk * H + 2 * Mk * I + 4 * H * I,                 # dW fc2
+                      2 * (Mk * H + H * nqd + Mk * nqd),                   # dO
+                      2 * Mk * H + 2 * Mk * nqd + 4 * H * nqd,             # dW o
+                      2 * (Mk * (nqkv + I) + (nqkv + I) * H + Mk * H),     # dX (qkv and fc1)
+                      2 * Mk * nqkv + 2 * Mk * H + 4 * nqkv * H,           # dW qkv
+                      2 * Mk * I + 2 * Mk * H + 4 * I * H]                 # dW fc1
     return {"gemm_flops": gemm_flops, "attn_flops": attn_flops, "attn_dt_flops": attn_dt_flops,
-            "pairs": pairs, "gather_bytes": gather_bytes}
+            "pairs": pairs, "gather_bytes": gather_bytes, "gemm_bytes": float(sum(gemm_bytes)),
+            "gemm_launches": len(gemm_bytes)}
+
+
+def measured_traffic(cfg, r_pct):
+    """HBM bytes per reduced-GEMM launch from the committed counter runs, or None when they were
+    taken on another workload or on a GEMM source other than the one built here."""
+    import hashlib
+    import re
+    if (cfg.name, r_pct) != ("tinyllama", 40):
+        return None
+    path = os.path.join(ROOT, "profiles", "gemm_bf16_tinyllama_b4s2048_r40_traffic.md")
+    src = os.path.join(ROOT, "token_filtered_backward_amd", "csrc", "gemm.hip")
+    try:
+        text = open(path).read()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    h = re.search(r"gemm_source_sha256: ([0-9a-f]+)", text)
+    if not m or not h or h.group(1) != sha:
+        return None
+    return float(m.group(1))
 
 
 def cpu_baseline(cfg, inp, min_seconds=8.0):
@@ -92,6 +134,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfiltered", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="first run one device-to-device copy of this many MiB (a plain copy of "
+                         "known size, to calibrate HBM byte counters in a profiler run)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); the filtered layer backward "
@@ -150,6 +195,15 @@ def main():
         ub(weights, saved, dy, uix, ugrads)
 
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)  # > 256 MB MALL
+    if args.copy_calibration_mb > 0:
+        n = args.copy_calibration_mb << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)  # one elementwise kernel: reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] calibration copy of {args.copy_calibration_mb} MiB done")
 
     def timed(fn, K, W_):
         for _ in range(W_):
@@ -248,7 +302,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(cfg, args.r),
+            "algorithmic_bytes_per_launch": work["gemm_bytes"] / work["gemm_launches"],
             "flops_per_launch": work["gemm_flops"] / max(gemm_launches, 1),
             "avg_launch_ms": round(gemm_ms / max(gemm_launches, 1), 5),
         },
