@@ -254,7 +254,7 @@ def main():
         tfb.collider_profile_enable(False)
         kernels_unf = {k: round(v[0] / n_prof, 4)
                        for k, v in sorted(prof_u.items(), key=lambda kv: -kv[1][0])}
-    gemm_names = [k for k in prof if k.startswith("gemm_") and k != "gemm_splitk_reduce"]
+    gemm_names = [k for k in prof if k.startswith("gemm_") and k not in ("gemm_splitk_reduce", "gemm_sk_fixup")]
     gemm_ms = sum(prof[k][0] for k in gemm_names) / n_prof
     gemm_launches = sum(prof[k][1] for k in gemm_names) / n_prof
 

@@ -237,6 +237,15 @@ collider_status collider_layer_bwd(const collider_layer_cfg* cfg, const collider
  * Returns the number of distinct kernels, or -1 on error.
  * ------------------------------------------------------------------------------------------- */
 collider_status collider_profile_enable(int32_t on);
+
+/* Work decomposition of the bf16 GEMMs (a tuning and test control; results of every policy meet
+ * the same tolerance, and each policy is deterministic):
+ *   0  default: a cost model picks the tile shape and whole tiles, K-splits or stream-K;
+ *   1  whole tiles and K-splits only;   2  stream-K wherever the direct-to-LDS kernel applies;
+ *   3  whole tiles only.
+ * Process-wide.  Workspace sizes depend on it: query *_workspace_bytes after setting it.  Returns
+ * COLLIDER_ERR_SHAPE for any other value. */
+collider_status collider_gemm_set_policy(int32_t policy);
 int32_t collider_profile_collect(char* names, int32_t name_cap, double* total_ms, int32_t* launches,
                                  int32_t max_kernels);
 const char* collider_status_string(collider_status s);

@@ -103,3 +103,10 @@ def test_layer_validation_and_workspace_sizes():
 def test_linear_workspace_size_is_host_only():
     assert tfb.collider_linear_workspace_bytes(tfb.BF16, 4916, 2048, 2048) > 0
     assert tfb.collider_linear_workspace_bytes(tfb.F32, 154, 256, 256) > 0
+
+
+def test_gemm_policy_values():
+    L = tfb.lib()
+    assert L.collider_gemm_set_policy(7) == 2 and L.collider_gemm_set_policy(-1) == 2
+    for p in (1, 2, 3, 0):
+        assert L.collider_gemm_set_policy(p) == 0

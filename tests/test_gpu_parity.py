@@ -138,6 +138,41 @@ def test_linear_bf16(Mk, K, N):
     assert rel_err(to64(dw), 2 * ref["dw"]) <= 1e-3
 
 
+@pytest.fixture
+def gemm_policy():
+    """Sets a GEMM work-decomposition policy for one test and restores the cost model after it."""
+    def set_(policy):
+        tfb.collider_gemm_set_policy(policy)
+    yield set_
+    tfb.collider_gemm_set_policy(tfb.GEMM_POLICY_AUTO)
+
+
+@pytest.mark.parametrize("policy", [tfb.GEMM_POLICY_SPLITK, tfb.GEMM_POLICY_STREAMK, tfb.GEMM_POLICY_TILES])
+@pytest.mark.parametrize("Mk,K,N", [(77, 64, 136), (300, 256, 512), (1000, 520, 264), (2500, 768, 1280),
+                                    (4916, 2048, 5632), (4916, 5632, 2048)])
+def test_linear_bf16_policies(gemm_policy, policy, Mk, K, N):
+    """Every work decomposition (whole tiles, K-splits, stream-K with its fix-up pass) meets the
+    bar, and repeating a call reproduces it bitwise."""
+    gemm_policy(policy)
+    rng = np.random.default_rng(Mk * 7 + K + N)
+    xb = synth.f32_to_bf16_bits(rng.standard_normal((Mk, K)).astype(np.float32))
+    dyb = synth.f32_to_bf16_bits(rng.standard_normal((Mk, N)).astype(np.float32))
+    wb = synth.f32_to_bf16_bits(0.02 * rng.standard_normal((N, K)).astype(np.float32))
+    x, dy, w = bf16_dev(xb), bf16_dev(dyb), bf16_dev(wb)
+    dx = torch.full((Mk, K), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dw = torch.full((N, K), float("nan"), device="cuda")
+    tfb.collider_linear_bwd_reduced(x, dy, w, dx, dw)
+    ref = oracle.linear_bwd(synth.bf16_bits_to_f32(xb), synth.bf16_bits_to_f32(dyb),
+                            synth.bf16_bits_to_f32(wb), np.ones(Mk, np.uint8))
+    assert rel_err(to64(dx), ref["dx"]) <= 1e-2
+    assert rel_err(to64(dw), ref["dw"]) <= 1e-3
+    dx2, dw2 = torch.empty_like(dx), torch.empty_like(dw)
+    tfb.collider_linear_bwd_reduced(x, dy, w, dx2, dw2)
+    assert torch.equal(dx.view(torch.int16), dx2.view(torch.int16)) and torch.equal(dw, dw2)
+    tfb.collider_linear_bwd_reduced(x, dy, w, None, dw, accumulate=True)
+    assert rel_err(to64(dw), 2 * ref["dw"]) <= 1e-3
+
+
 # ------------------------------------------------------------------------------------------------
 # attention
 # ------------------------------------------------------------------------------------------------
@@ -252,6 +287,16 @@ def run_layer_and_compare(inp, dmode, tol=BF16_TOL):
 def test_layer_parity_small(name, dmode, r):
     inp = synth.make_layer_inputs(synth.get_config(name), r_pct=r)
     run_layer_and_compare(inp, dmode)
+
+
+@pytest.mark.parametrize("policy", [tfb.GEMM_POLICY_SPLITK, tfb.GEMM_POLICY_STREAMK, tfb.GEMM_POLICY_TILES])
+@pytest.mark.parametrize("name", ["small_llama", "small_phi"])
+def test_layer_parity_gemm_policies(gemm_policy, policy, name):
+    """The fused SwiGLU / GELU / fp32 epilogues give the same gradients through every GEMM work
+    decomposition, including the stream-K fix-up pass."""
+    gemm_policy(policy)
+    inp = synth.make_layer_inputs(synth.get_config(name), r_pct=40)
+    run_layer_and_compare(inp, 0)
 
 
 @pytest.mark.parametrize("name", ["small_llama", "small_phi"])

@@ -94,6 +94,7 @@ def lib():
         "collider_layer_bwd": (st, [P(LayerCfg), P(LayerWeights), P(LayerSaved), _c_p, _i32,
                                     P(CollIndex), P(LayerGrads), _i32, _c_p, sz, _c_p]),
         "collider_profile_enable": (st, [_i32]),
+        "collider_gemm_set_policy": (st, [_i32]),
         "collider_profile_collect": (_i32, [ctypes.c_char_p, _i32, P(ctypes.c_double), P(_i32), _i32]),
     }
     for name, (res, args) in sig.items():
@@ -211,6 +212,15 @@ def collider_layer_bwd(cfg: LayerCfg, w: LayerWeights, saved: LayerSaved, dy, dy
                                     int(dy_compact), ctypes.byref(ix), ctypes.byref(grads),
                                     int(dx_compact), _ptr(ws), ws.numel(), _stream(stream)),
            "collider_layer_bwd")
+
+
+GEMM_POLICY_AUTO, GEMM_POLICY_SPLITK, GEMM_POLICY_STREAMK, GEMM_POLICY_TILES = 0, 1, 2, 3
+
+
+def collider_gemm_set_policy(policy: int):
+    """Process-wide GEMM work decomposition (0 cost model, 1 tiles + K-splits, 2 stream-K,
+    3 whole tiles only).  Query workspace sizes after changing it."""
+    _check(lib().collider_gemm_set_policy(int(policy)), "collider_gemm_set_policy")
 
 
 def collider_profile_enable(on: bool):

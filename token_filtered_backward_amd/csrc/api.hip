@@ -318,6 +318,12 @@ collider_status collider_layer_bwd(const collider_layer_cfg* cfg, const collider
   return layer_run(*cfg, w, sv, dy, dy_compact, *ix, g, dx_compact, ws, ws_bytes, stream, nullptr);
 }
 
+collider_status collider_gemm_set_policy(int32_t policy) {
+  if (policy < 0 || policy > 3) return COLLIDER_ERR_SHAPE;
+  gemm_set_policy(policy);
+  return COLLIDER_OK;
+}
+
 collider_status collider_profile_enable(int32_t on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = on != 0;

@@ -161,12 +161,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_dq_kernel(AttnParam
   constexpr int KV_BYTES = 4 * TB, EPI_BYTES = BQ * LDE * 4;
   __shared__ __align__(16) char smem[KV_BYTES > EPI_BYTES ? KV_BYTES : EPI_BYTES];
   // buffers: K in smem + buf*2*TB, V right after it
-  const int b = blockIdx.z, h = blockIdx.y, g = h / p.G;
+  // grid (head, sequence, block rank): blocks are dispatched x-fastest, so every sequence's and
+  // head's largest query block (the last one, which sees the most keys) starts first
+  const int b = blockIdx.y, h = blockIdx.x, g = h / p.G;
   const int cs = p.cu ? min(p.cu[b], p.M_kept) : b * p.S;
   const int nb = p.cu ? max(0, min(p.cu[b + 1], p.M_kept) - cs) : p.S;
   const int nqb = (nb + BQ - 1) / BQ;
-  if ((int)blockIdx.x >= nqb) return;
-  const int q0 = (nqb - 1 - (int)blockIdx.x) * BQ;
+  if ((int)blockIdx.z >= nqb) return;
+  const int q0 = (nqb - 1 - (int)blockIdx.z) * BQ;
   const int lane = threadIdx.x & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int iq = q0 + wave * 32 + l32;
@@ -342,12 +344,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_dkv_kernel(AttnPara
   constexpr int TB = TokTile<D>::BYTES;
   constexpr int BUF = 2 * TB + 2 * BQ * 4;  // Q tile, dO tile, lse*log2e, D
   __shared__ __align__(16) char smem[2 * BUF];
-  const int b = blockIdx.z, g = blockIdx.y / p.HS, hs = blockIdx.y % p.HS;
+  // grid (kv head x head slice, sequence, key block): the first key blocks, which see the most
+  // queries, are dispatched first
+  const int b = blockIdx.y, g = blockIdx.x / p.HS, hs = blockIdx.x % p.HS;
   const int cs = p.cu ? min(p.cu[b], p.M_kept) : b * p.S;
   const int nb = p.cu ? max(0, min(p.cu[b + 1], p.M_kept) - cs) : p.S;
   const int nkb = (nb + BKV - 1) / BKV;
-  if ((int)blockIdx.x >= nkb) return;
-  const int k0 = blockIdx.x * BKV;
+  if ((int)blockIdx.z >= nkb) return;
+  const int k0 = blockIdx.z * BKV;
   const int lane = threadIdx.x & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int jk = k0 + wave * 32 + l32;  // this lane's key (S column)
@@ -602,7 +606,7 @@ collider_status attn_bwd(const collider_attn_cfg& c, const collider_index& ix,
     if (st != COLLIDER_OK) return st;
   }
   const bool full = c.dmode == COLLIDER_ATTN_D_FULL;
-  dim3 gq((S + 127) / 128, c.n_q_heads, B), gk((S + 127) / 128, c.n_kv_heads * p.HS, B);
+  dim3 gq(c.n_q_heads, B, (S + 127) / 128), gk(c.n_kv_heads * p.HS, B, (S + 127) / 128);
   const int fin_blocks = (Mk * c.n_kv_heads + 3) / 4;
   if (c.head_dim == 64) {
     if (full)

@@ -12,6 +12,7 @@
 // barrier per k-tile).  Long reductions with few output tiles (the weight gradients reduce over
 // all kept tokens) are split over K; the partials are summed in a fixed order by a second kernel
 // that also applies the epilogue, so results are deterministic.
+#include <atomic>
 #include <cstdio>
 #include <cstdlib>
 #include <type_traits>
@@ -31,6 +32,13 @@ struct GemmParams {
   int k_split;  // reduction length handled by one split (multiple of the k-tile)
   int splits;
   int tiles_m, tiles_n;
+  // work decomposition of the direct-to-LDS kernel: tiles [0, dp_tiles) are whole work items
+  // (times `splits` K-splits); tiles [dp_tiles, dp_tiles + sk_tiles) are shared out as one
+  // stream-K range of k-tiles per workgroup
+  int ipt;       // k-tiles per output tile
+  int dp_tiles;
+  int sk_tiles;
+  float* skp;    // stream-K partial tiles: [2 * gridDim.x][BM * BN], two slots per workgroup
   // epilogue
   void* C;
   int64_t ldc;
@@ -59,14 +67,14 @@ __device__ __forceinline__ void epi_store(const GemmParams& p, int m, int n, flo
     const int64_t r = p.rowmap ? p.rowmap[m] : m;
     const float g = bf2f(p.g[r * p.ld_g + n]);
     const float u = bf2f(p.up[r * p.ld_g + n]);
-    const float s = 1.f / (1.f + __expf(-g));
+    const float s = fast_sigmoid(g);
     ((uint16_t*)p.C)[(int64_t)m * p.ldc + n] = f2bf(v * u * s * (1.f + g * (1.f - s)));
     p.out2[(int64_t)m * p.ld_out2 + n] = f2bf(v * g * s);
   } else {  // EPI_GELU: dF = dA * d/df gelu_tanh(f)
     const int64_t r = p.rowmap ? p.rowmap[m] : m;
     const float f = bf2f(p.g[r * p.ld_g + n]);
     const float c = 0.7978845608028654f, a = 0.044715f;
-    const float t = tanhf(c * (f + a * f * f * f));
+    const float t = fast_tanh(c * (f + a * f * f * f));
     const float d = 0.5f * (1.f + t) + 0.5f * f * (1.f - t * t) * c * (1.f + 3.f * a * f * f);
     ((uint16_t*)p.C)[(int64_t)m * p.ldc + n] = f2bf(v * d);
   }
@@ -108,7 +116,7 @@ __device__ __forceinline__ void epi_store8(const GemmParams& p, int m, int n, co
     unpack8(*(const uint4*)(p.up + r * p.ld_g + n), u);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float s = 1.f / (1.f + __expf(-g[e]));
+      const float s = fast_sigmoid(g[e]);
       dg[e] = v[e] * u[e] * s * (1.f + g[e] * (1.f - s));
       du[e] = v[e] * g[e] * s;
     }
@@ -121,7 +129,7 @@ __device__ __forceinline__ void epi_store8(const GemmParams& p, int m, int n, co
     const float c = 0.7978845608028654f, a = 0.044715f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float t = tanhf(c * (f[e] + a * f[e] * f[e] * f[e]));
+      const float t = fast_tanh(c * (f[e] + a * f[e] * f[e] * f[e]));
       o[e] = v[e] * (0.5f * (1.f + t) + 0.5f * f[e] * (1.f - t * t) * c * (1.f + 3.f * a * f[e] * f[e]));
     }
     *(uint4*)((uint16_t*)p.C + (int64_t)m * p.ldc + n) = pack8(o);
@@ -133,6 +141,82 @@ __device__ __forceinline__ void store8_partial(const GemmParams& p, int split, i
   float4* d = (float4*)(p.partial + ((int64_t)split * p.M + m) * p.N + n);
   d[0] = make_float4(v[0], v[1], v[2], v[3]);
   d[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// The epilogue's other inputs for GPT groups of 8 outputs (rows mfirst + i * mstep, columns
+// n .. n+7): the saved pre-activations (SwiGLU: gate in sa, up in sb; GELU: f in sa) or the fp32
+// values being accumulated into (sa, sb = columns n .. n+3, n+4 .. n+7).  All loads of a call are
+// issued before any is used, so one memory latency covers the whole batch.
+template <int EPI, int GPT>
+__device__ __forceinline__ void prefetch_side(const GemmParams& p, int mfirst, int mstep, int n,
+                                              uint4 (&sa)[GPT], uint4 (&sb)[GPT]) {
+  if constexpr (EPI == EPI_BF16) return;
+  if constexpr (EPI == EPI_F32) {
+    if (!p.accumulate) return;
+  }
+  int64_t r[GPT];
+#pragma unroll
+  for (int i = 0; i < GPT; ++i) {
+    const int m = mfirst + i * mstep;
+    const bool ok = m < p.M && n < p.N;
+    if constexpr (EPI == EPI_F32)
+      r[i] = ok ? m : -1;
+    else
+      r[i] = ok ? (p.rowmap ? (int64_t)p.rowmap[m] : (int64_t)m) : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < GPT; ++i) {
+    if (r[i] < 0) continue;
+    if constexpr (EPI == EPI_F32) {
+      const uint4* c = (const uint4*)((const float*)p.C + r[i] * p.ldc + n);
+      sa[i] = c[0];
+      sb[i] = c[1];
+    } else {
+      sa[i] = *(const uint4*)(p.g + r[i] * p.ld_g + n);
+      if constexpr (EPI == EPI_SWIGLU) sb[i] = *(const uint4*)(p.up + r[i] * p.ld_g + n);
+    }
+  }
+}
+
+// Final epilogue of 8 outputs with the side inputs already in registers.
+template <int EPI>
+__device__ __forceinline__ void epi_finish8(const GemmParams& p, int m, int n, const float* v,
+                                            uint4 sa, uint4 sb) {
+  if constexpr (EPI == EPI_BF16) {
+    *(uint4*)((uint16_t*)p.C + (int64_t)m * p.ldc + n) = pack8(v);
+  } else if constexpr (EPI == EPI_F32) {
+    float4 a = make_float4(v[0], v[1], v[2], v[3]), b = make_float4(v[4], v[5], v[6], v[7]);
+    if (p.accumulate) {
+      const float4 a0 = __builtin_bit_cast(float4, sa), b0 = __builtin_bit_cast(float4, sb);
+      a.x += a0.x; a.y += a0.y; a.z += a0.z; a.w += a0.w;
+      b.x += b0.x; b.y += b0.y; b.z += b0.z; b.w += b0.w;
+    }
+    float4* c = (float4*)((float*)p.C + (int64_t)m * p.ldc + n);
+    c[0] = a;
+    c[1] = b;
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    float g[8], u[8], dg[8], du[8];
+    unpack8(sa, g);
+    unpack8(sb, u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float s = fast_sigmoid(g[e]);
+      dg[e] = v[e] * u[e] * s * (1.f + g[e] * (1.f - s));
+      du[e] = v[e] * g[e] * s;
+    }
+    *(uint4*)((uint16_t*)p.C + (int64_t)m * p.ldc + n) = pack8(dg);
+    *(uint4*)(p.out2 + (int64_t)m * p.ld_out2 + n) = pack8(du);
+  } else {
+    float f[8], o[8];
+    unpack8(sa, f);
+    const float c = 0.7978845608028654f, a = 0.044715f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float t = fast_tanh(c * (f[e] + a * f[e] * f[e] * f[e]));
+      o[e] = v[e] * (0.5f * (1.f + t) + 0.5f * f[e] * (1.f - t * t) * c * (1.f + 3.f * a * f[e] * f[e]));
+    }
+    *(uint4*)((uint16_t*)p.C + (int64_t)m * p.ldc + n) = pack8(o);
+  }
 }
 
 
@@ -342,20 +426,24 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
 
 // ------------------------------------------------------------------------------------------
 // Direct-to-LDS GEMM (gfx950).  Tiles travel global -> LDS with 16-byte buffer loads that write
-// LDS directly (no staging registers), so 3 k-tiles can be in flight.  Buffer loads are range
-// checked: rows past the end of an operand (the ragged token dimension) arrive as zeros.
+// LDS directly (no staging registers), so NS - 1 k-tiles of depth KT (32 or 64) are in flight
+// while one is consumed.  Buffer loads are range checked: rows past the end of an operand (the
+// ragged token dimension) arrive as zeros.
 // Each operand keeps its global orientation in LDS, XOR-swizzled instead of padded:
-//   K-major tile  [R][64]  128-byte rows, 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7)
-//   MN-major tile [64][R]  2R-byte rows,  chunk c of row k stored at c ^ (4 * (k & 3))
+//   K-major tile  [R][KT]  2KT-byte rows, 16-byte chunk c of row r stored at c ^ ((r >> 1) & (KT/8 - 1))
+//   MN-major tile [KT][R]  2R-byte rows,  chunk c of row k stored at c ^ (4 * (k & 3))
 // MFMA fragments come from ds_read_b128 (K-major) or two ds_read_b64_tr_b16 (MN-major): within a
 // group of 16 lanes, lane j addresses row k0 + j/4, columns n + 4*(j%4) .. +3, and lane i receives
 // rows k0 .. k0+3 of column n + i - exactly the k-contiguous operand layout the MFMA expects.
-// Both swizzles make the 16-lane (K-major) and 32-lane (MN-major) read groups bank-conflict free.
+// Both swizzles make the lane groups the LDS serves together bank-conflict free.
 // ------------------------------------------------------------------------------------------
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ int kmaj_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+template <int KT>
+__device__ __forceinline__ int kmaj_off(int r, int c) {
+  return r * (2 * KT) + ((c ^ ((r >> 1) & (KT / 8 - 1))) << 4);
+}
 template <int R>
 __device__ __forceinline__ int mnmaj_off(int k, int c) {
   return k * (2 * R) + ((c ^ ((k & 3) << 2)) << 4);
@@ -368,51 +456,65 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return rsrc_t{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xffffu), (int)bytes, 0x00020000};
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const char* p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
-}
 
 // 16-byte buffer load of each lane straight into LDS (M0 = LDS base of the wave, lane i lands at
-// M0 + 16*i).  Issued as inline assembly: the compiler then inserts no waits for it of its own
-// (it cannot tell which LDS bytes the copy writes and would wait for every outstanding load at
-// each LDS read); completion is tracked explicitly with s_waitcnt vmcnt in the k-loop.
-__device__ __forceinline__ void dma16(rsrc_t rs, uint32_t lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+// M0 + 16*i; address = base + voff + soff).  Issued as inline assembly: the compiler then inserts no
+// waits for it of its own (it cannot tell which LDS bytes the copy writes and would wait for every
+// outstanding load at each LDS read); completion is tracked explicitly with s_waitcnt vmcnt in the
+// k-loop.
+__device__ __forceinline__ void dma16(rsrc_t rs, uint32_t m0, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rs)
+               : "s"(m0), "v"(voff), "s"(rs), "s"(soff)
                : "memory", "m0");
 }
 
-// Issue the direct loads of one [R x 64] (K-major) or [64 x R] (MN-major) tile; wave w issues
-// instructions w, w+4, ...  `row0` is the first tile row (token or feature index of the operand
-// rows), `col0` the first column.  Byte offsets are relative to the buffer base.
-template <int R, bool KMAJ>
-__device__ __forceinline__ void issue_tile(rsrc_t rs, int64_t ld, int row0, int col0,
-                                           char* lds_tile, int wave, int lane) {
-  constexpr int NI = R * 64 * 2 / 1024;
+// Direct loads of one operand tile, [R x KT] (K-major) or [KT x R] (MN-major) in LDS.  Wave w
+// issues loads q = w, w + 4, ...; load q fills LDS bytes [1024 q, 1024 q + 1024) of the tile.  The
+// per-lane byte offsets are computed once per output tile.  K-major: the k offset of a k-tile goes
+// into the scalar offset, and the vector offset holds the row part, which alone decides whether the
+// range check zero-fills a row past the end of the operand.  MN-major: rows are k, so the k offset
+// goes into the vector offset.
+template <int R, bool KMAJ, int KT>
+struct TileDMA {
+  static constexpr int NI = R * KT * 2 / 1024, PW = NI / 4;
+  static_assert(NI % 4 == 0, "every wave issues the same number of loads");
+  uint32_t off[PW];
+  // mn0: first row (K-major) or first column (MN-major) of the tile in the operand
+  __device__ __forceinline__ void init(int64_t ld, int mn0, int wave, int lane) {
 #pragma unroll
-  for (int q = wave; q < NI; q += 4) {
-    const int b = q * 1024 + lane * 16;
-    uint32_t off;
-    if constexpr (KMAJ) {
-      const int r = b >> 7, pos = (b >> 4) & 7;
-      const int c = pos ^ ((r >> 1) & 7);
-      off = (uint32_t)(((int64_t)(row0 + r) * ld + col0 + 8 * c) * 2);
-    } else {
-      const int k = b / (2 * R), pos = (b % (2 * R)) >> 4;
-      const int c = pos ^ ((k & 3) << 2);
-      off = (uint32_t)(((int64_t)(row0 + k) * ld + col0 + 8 * c) * 2);
+    for (int i = 0; i < PW; ++i) {
+      const int b = (wave + 4 * i) * 1024 + lane * 16;
+      if constexpr (KMAJ) {
+        const int r = b / (2 * KT), pos = (b >> 4) & (KT / 8 - 1);
+        const int c = pos ^ ((r >> 1) & (KT / 8 - 1));
+        off[i] = (uint32_t)(((int64_t)(mn0 + r) * ld + 8 * c) * 2);
+      } else {
+        const int k = b / (2 * R), pos = (b % (2 * R)) >> 4;
+        const int c = pos ^ ((k & 3) << 2);
+        off[i] = (uint32_t)(((int64_t)k * ld + mn0 + 8 * c) * 2);
+      }
     }
-    dma16(rs, lds_addr(lds_tile + q * 1024), off);
   }
-}
+  // the k-tile starting at reduction index k0 of this buffer, into the LDS tile at byte m0
+  __device__ __forceinline__ void issue(rsrc_t rs, int64_t ld, int k0, uint32_t m0, int wave) const {
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      const uint32_t lq = m0 + (uint32_t)(wave + 4 * i) * 1024u;
+      if constexpr (KMAJ)
+        dma16(rs, lq, off[i], (uint32_t)k0 * 2u);
+      else
+        dma16(rs, lq, off[i] + (uint32_t)((int64_t)k0 * ld * 2), 0u);
+    }
+  }
+};
 
 // 32x32x16 operand fragment: rows rbase .. rbase+31 (M or N index), k = kk*16 .. +15
-template <int R, bool KMAJ>
+template <int R, bool KMAJ, int KT>
 __device__ __forceinline__ bf16x8 read_frag(const char* lds_tile, int rbase, int kk, int lane) {
   if constexpr (KMAJ) {
     const int r = rbase + (lane & 31), c = kk * 2 + (lane >> 5);
-    return *(const bf16x8*)(lds_tile + kmaj_off(r, c));
+    return *(const bf16x8*)(lds_tile + kmaj_off<KT>(r, c));
   } else {
     const int g = lane >> 4, j = lane & 15;
     const int col = rbase + 16 * (g & 1) + 4 * (j & 3);
@@ -428,58 +530,43 @@ __device__ __forceinline__ bf16x8 read_frag(const char* lds_tile, int rbase, int
   }
 }
 
-// Loads of one k-tile (A then B) into one LDS stage.  B may come in two row segments (B0 for
-// k < kseg, B1 after); a 64-row k-tile never straddles them.
-template <int BM, int BN, bool AK, bool BKM>
-__device__ __forceinline__ void issue_stage(rsrc_t ra, rsrc_t rb0, rsrc_t rb1, int64_t lda, int64_t ldb,
-                                            int kseg, bool two_seg, int m0, int n0, int k0,
-                                            char* stage, int wave, int lane) {
-  if constexpr (AK)
-    issue_tile<BM, true>(ra, lda, m0, k0, stage, wave, lane);
-  else
-    issue_tile<BM, false>(ra, lda, k0, m0, stage, wave, lane);
+// Loads of one k-tile (A then B) into the LDS stage at byte m0.  B may come in two row segments
+// (B0 for k < kseg, B1 after); kseg is a multiple of 64, so a k-tile never straddles them.
+template <int BM, int BN, bool AK, bool BKM, int KT>
+__device__ __forceinline__ void issue_stage(const TileDMA<BM, AK, KT>& da, const TileDMA<BN, BKM, KT>& db,
+                                            rsrc_t ra, rsrc_t rb0, rsrc_t rb1, int64_t lda, int64_t ldb,
+                                            int kseg, bool two_seg, int k0, uint32_t m0, int wave) {
+  da.issue(ra, lda, k0, m0, wave);
   const bool seg1 = two_seg && k0 >= kseg;
-  const int kb = seg1 ? k0 - kseg : k0;
-  char* bst = stage + BM * 64 * 2;
-  if (seg1) {
-    if constexpr (BKM)
-      issue_tile<BN, true>(rb1, ldb, n0, kb, bst, wave, lane);
-    else
-      issue_tile<BN, false>(rb1, ldb, kb, n0, bst, wave, lane);
-  } else {
-    if constexpr (BKM)
-      issue_tile<BN, true>(rb0, ldb, n0, kb, bst, wave, lane);
-    else
-      issue_tile<BN, false>(rb0, ldb, kb, n0, bst, wave, lane);
-  }
+  db.issue(seg1 ? rb1 : rb0, ldb, seg1 ? k0 - kseg : k0, m0 + BM * KT * 2, wave);
 }
 
 // s_waitcnt vmcnt(n), other counters unconstrained (gfx9 encoding)
 #define VMCNT_WAIT(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 0xf) | (((n) >> 4) << 14) | (0x7 << 4) | (0xf << 8))
 
-// MFMAs of one k-tile (4 steps of k = 16) from one LDS stage; fragments of step kk+1 are read
+// MFMAs of one k-tile (KT / 16 steps of k = 16) from one LDS stage; fragments of step kk+1 are read
 // while the MFMAs of step kk run (two register sets).
-template <int BM, int BN, bool AK, bool BKM>
+template <int BM, int BN, bool AK, bool BKM, int KT>
 __device__ __forceinline__ void mma_ktile(const char* As, const char* Bs,
                                           f32x16 (&acc)[BM / 64][BN / 64], int wm, int wn,
                                           int lane) {
-  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32, KS = KT / 16;
   bf16x8 af[2][TM], bfv[2][TN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) af[0][i] = read_frag<BM, AK>(As, wm * WM + i * 32, 0, lane);
+  for (int i = 0; i < TM; ++i) af[0][i] = read_frag<BM, AK, KT>(As, wm * WM + i * 32, 0, lane);
 #pragma unroll
-  for (int j = 0; j < TN; ++j) bfv[0][j] = read_frag<BN, BKM>(Bs, wn * WN + j * 32, 0, lane);
+  for (int j = 0; j < TN; ++j) bfv[0][j] = read_frag<BN, BKM, KT>(Bs, wn * WN + j * 32, 0, lane);
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
+  for (int kk = 0; kk < KS; ++kk) {
     const int cur = kk & 1;
-    if (kk + 1 < 4) {
+    if (kk + 1 < KS) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        af[cur ^ 1][i] = read_frag<BM, AK>(As, wm * WM + i * 32, kk + 1, lane);
+        af[cur ^ 1][i] = read_frag<BM, AK, KT>(As, wm * WM + i * 32, kk + 1, lane);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        bfv[cur ^ 1][j] = read_frag<BN, BKM>(Bs, wn * WN + j * 32, kk + 1, lane);
+        bfv[cur ^ 1][j] = read_frag<BN, BKM, KT>(Bs, wn * WN + j * 32, kk + 1, lane);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -492,20 +579,29 @@ __device__ __forceinline__ void mma_ktile(const char* As, const char* Bs,
   }
 }
 
-template <int BM, int BN, bool AK, bool BKM, int EPI, int NS>
+// Work decomposition.  Whole tiles (optionally split over K, partials summed by
+// splitk_reduce_kernel) are walked with a grid stride.  When the tile count leaves the last wave of
+// workgroups partly idle, the remaining tiles are instead shared out as one contiguous range of
+// (tile, k-tile) iterations per workgroup ("stream-K"): every workgroup gets the same number of
+// k-tiles.  A tile whose k-range one workgroup covers entirely is finished in place; the pieces of
+// a tile shared by several workgroups go to per-workgroup fp32 slots (slot 0: the first piece of a
+// workgroup's range, slot 1: its last) and sk_fixup_kernel adds them in k order and runs the
+// epilogue.  No workgroup waits on another, and every sum has a fixed order, so results are
+// deterministic.
+template <int BM, int BN, int KT, bool AK, bool BKM, int EPI, int NS>
 __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
-  constexpr int BK = 64;
+  constexpr int BK = KT;
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
   constexpr int LPW = (A_BYTES + B_BYTES) / 1024 / 4;  // load instructions per wave per k-tile
   extern __shared__ __align__(16) char lds[];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int T = p.tiles_m * p.tiles_n;
-  const int total = T * p.splits;
-  const bool partial = p.splits > 1;
+  // LDS byte address of the dynamic LDS block (the low half of its flat address)
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
   // operand buffers: rows of A are tokens (K-major A: M rows; MN-major A: K rows)
   const rsrc_t ra = make_rsrc(p.A, (uint32_t)((int64_t)(AK ? p.M : p.K) * p.lda * 2));
   const int kseg = p.B1 ? p.kseg : p.K;
@@ -514,14 +610,47 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
   const rsrc_t rb1 =
       make_rsrc(p.B1 ? p.B1 : p.B0, (uint32_t)((int64_t)(p.B1 ? p.K - kseg : 0) * p.ldb * 2));
 
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    const int li = xcd_remap(item, total);
-    const int split = li / T, t = li % T;
+  const int dp_items = p.dp_tiles * p.splits;
+  const int kts = p.k_split / BK;  // k-tiles per K-split
+  // this workgroup's stream-K range; neighbouring ranges (which share tiles and operand panels)
+  // go to workgroups on the same XCD
+  const int v = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t n_it = (int64_t)p.sk_tiles * p.ipt;
+  const int64_t it_first = (int64_t)v * n_it / gridDim.x;
+  const int64_t it_end = (int64_t)(v + 1) * n_it / gridDim.x;
+  int64_t it = it_first;
+  int item = blockIdx.x;
+
+  for (;;) {
+    int t, kt0, kt1, mode, oidx;  // mode 0: final epilogue, 1: K-split partial, 2: stream-K slot
+    if (item < dp_items) {
+      const int li = xcd_remap(item, dp_items);
+      const int split = li / p.dp_tiles;
+      t = li % p.dp_tiles;
+      kt0 = split * kts;
+      kt1 = min(p.ipt, kt0 + kts);
+      mode = p.splits > 1 ? 1 : 0;
+      oidx = split;
+      item += gridDim.x;
+    } else if (it < it_end) {
+      const int st = (int)(it / p.ipt);
+      t = p.dp_tiles + st;
+      kt0 = (int)(it - (int64_t)st * p.ipt);
+      kt1 = (int)min((int64_t)p.ipt, (int64_t)kt0 + (it_end - it));
+      mode = (kt0 == 0 && kt1 == p.ipt) ? 0 : 2;
+      oidx = 2 * v + (it == it_first ? 0 : 1);
+      it += kt1 - kt0;
+    } else {
+      break;
+    }
     const int tm = t / p.tiles_n, tn = t % p.tiles_n;
     const int m0 = tm * BM, n0 = tn * BN;
-    const int kbeg = split * p.k_split;
-    const int kend = min(p.K, kbeg + p.k_split);
-    const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+    const int nk = kt1 - kt0;
+    const int kbeg = kt0 * BK;
+    TileDMA<BM, AK, KT> da;
+    TileDMA<BN, BKM, KT> db;
+    da.init(p.lda, m0, wave, lane);
+    db.init(p.ldb, n0, wave, lane);
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -536,8 +665,8 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
       if (s < nk)
-        issue_stage<BM, BN, AK, BKM>(ra, rb0, rb1, p.lda, p.ldb, kseg, two_seg, m0, n0,
-                                     kbeg + s * BK, lds + s * STAGE, wave, lane);
+        issue_stage<BM, BN, AK, BKM, KT>(da, db, ra, rb0, rb1, p.lda, p.ldb, kseg, two_seg,
+                                         kbeg + s * BK, lds0 + s * STAGE, wave);
     for (int kt = 0; kt < nk; ++kt) {
       // tile kt complete (for this wave), then visible to all waves
       if (kt + NS - 2 < nk) {
@@ -547,22 +676,30 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
       }
       __syncthreads();
       if (kt + NS - 1 < nk)  // refills the stage read in iteration kt-1
-        issue_stage<BM, BN, AK, BKM>(ra, rb0, rb1, p.lda, p.ldb, kseg, two_seg, m0, n0,
-                                     kbeg + (kt + NS - 1) * BK, lds + ((kt + NS - 1) % NS) * STAGE,
-                                     wave, lane);
+        issue_stage<BM, BN, AK, BKM, KT>(da, db, ra, rb0, rb1, p.lda, p.ldb, kseg, two_seg,
+                                         kbeg + (kt + NS - 1) * BK,
+                                         lds0 + ((kt + NS - 1) % NS) * STAGE, wave);
       const char* As = lds + (kt % NS) * STAGE;
-      mma_ktile<BM, BN, AK, BKM>(As, As + A_BYTES, acc, wm, wn, lane);
+      mma_ktile<BM, BN, AK, BKM, KT>(As, As + A_BYTES, acc, wm, wn, lane);
     }
 
     // epilogue through LDS: the fp32 tile is staged row-major in passes of EROWS rows, then every
-    // thread finishes 8 consecutive columns of a row with 16-byte loads / stores (one row lookup
-    // per 8 outputs)
+    // thread finishes 8 consecutive columns of GPT rows with 16-byte loads / stores
     constexpr int LDE = BN + 8;  // +8 floats: the two lane halves' rows land 32 banks apart
-    constexpr int EROWS = (BM * LDE * 4 <= NS * STAGE) ? BM : ((64 * LDE * 4 <= NS * STAGE) ? 64 : 32);
+    constexpr int EROWS_FIT = (BM * LDE * 4 <= NS * STAGE) ? BM : ((64 * LDE * 4 <= NS * STAGE) ? 64 : 32);
+    // epilogues with two 16-byte side inputs per 8 outputs take shorter passes (registers)
+    constexpr int EROWS_REG = (EPI == EPI_SWIGLU || EPI == EPI_F32) ? 32 : 64;
+    constexpr int EROWS = EROWS_FIT < EROWS_REG ? EROWS_FIT : EROWS_REG;
     static_assert(EROWS * LDE * 4 <= NS * STAGE, "epilogue pass must fit in the stage buffers");
+    constexpr int CPR = BN / 8, RSTEP = 256 / CPR, GPT = EROWS / RSTEP;
+    static_assert(EROWS % RSTEP == 0, "epilogue rows per pass");
+    const int cg = threadIdx.x % CPR, rsub = threadIdx.x / CPR;
+    const int n = n0 + cg * 8;
     float* E = (float*)lds;
 #pragma unroll
     for (int pass = 0; pass < BM / EROWS; ++pass) {
+      uint4 sa[GPT], sb[GPT];
+      if (mode == 0) prefetch_side<EPI, GPT>(p, m0 + pass * EROWS + rsub, RSTEP, n, sa, sb);
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
@@ -576,19 +713,68 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
               j * 32 + (lane & 31)] = acc[i][j][r];
       }
       __syncthreads();
-      for (int c = threadIdx.x; c < EROWS * (BN / 8); c += 256) {
-        const int row = c / (BN / 8), col = (c % (BN / 8)) * 8;
-        const int m = m0 + pass * EROWS + row, n = n0 + col;
-        if (m >= p.M || n >= p.N) continue;
-        const float4 lo = *(const float4*)(E + row * LDE + col);
-        const float4 hi = *(const float4*)(E + row * LDE + col + 4);
-        const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        if (partial)
-          store8_partial(p, split, m, n, v);
-        else
-          epi_store8<EPI>(p, m, n, v);
+#pragma unroll
+      for (int i = 0; i < GPT; ++i) {
+        const int row = rsub + i * RSTEP;
+        const int m = m0 + pass * EROWS + row;
+        const float4 lo = *(const float4*)(E + row * LDE + cg * 8);
+        const float4 hi = *(const float4*)(E + row * LDE + cg * 8 + 4);
+        if (mode == 2) {
+          float4* d = (float4*)(p.skp + (int64_t)oidx * (BM * BN) + (pass * EROWS + row) * BN + cg * 8);
+          d[0] = lo;
+          d[1] = hi;
+        } else if (m < p.M && n < p.N) {
+          const float vv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          if (mode == 1)
+            store8_partial(p, oidx, m, n, vv);
+          else
+            epi_finish8<EPI>(p, m, n, vv, sa[i], sb[i]);
+        }
       }
     }
+  }
+}
+
+// Stream-K tiles shared by several workgroups: add their slots in k order (workgroup order) and
+// run the epilogue.  Grid: (stream-K tiles, BM / 32 row bands); G = the main kernel's grid size.
+template <int BM, int BN, int EPI>
+__global__ __launch_bounds__(256) void sk_fixup_kernel(GemmParams p, int G) {
+  constexpr int ROWS = 32, CPR = BN / 8, RSTEP = 256 / CPR, GPT = ROWS / RSTEP;
+  const int st = blockIdx.x;
+  const int64_t n_it = (int64_t)p.sk_tiles * p.ipt;
+  const int64_t b = (int64_t)st * p.ipt, e = b + p.ipt;
+  // owner(i) = the workgroup whose range [v * n_it / G, (v + 1) * n_it / G) holds iteration i
+  const int g0 = (int)(((b + 1) * G + n_it - 1) / n_it - 1);
+  const int g1 = (int)((e * G + n_it - 1) / n_it - 1);
+  if (g0 == g1) return;  // one workgroup covered the whole tile and finished it
+  const int t = p.dp_tiles + st;
+  const int m0 = (t / p.tiles_n) * BM, n0 = (t % p.tiles_n) * BN;
+  const int cg = threadIdx.x % CPR, rsub = threadIdx.x / CPR;
+  const int n = n0 + cg * 8;
+  const int rfirst = blockIdx.y * ROWS + rsub;
+  uint4 sa[GPT], sb[GPT];
+  prefetch_side<EPI, GPT>(p, m0 + rfirst, RSTEP, n, sa, sb);
+  float acc[GPT][8];
+#pragma unroll
+  for (int i = 0; i < GPT; ++i)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[i][q] = 0.f;
+  for (int g = g0; g <= g1; ++g) {
+    // the tile is slot 1 (last piece) of a range that began in an earlier tile, else slot 0
+    const int slot = 2 * g + (((int64_t)g * n_it / G) < b ? 1 : 0);
+    const float* src = p.skp + (int64_t)slot * (BM * BN) + cg * 8;
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+      const float4 lo = *(const float4*)(src + (rfirst + i * RSTEP) * BN);
+      const float4 hi = *(const float4*)(src + (rfirst + i * RSTEP) * BN + 4);
+      acc[i][0] += lo.x; acc[i][1] += lo.y; acc[i][2] += lo.z; acc[i][3] += lo.w;
+      acc[i][4] += hi.x; acc[i][5] += hi.y; acc[i][6] += hi.z; acc[i][7] += hi.w;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < GPT; ++i) {
+    const int m = m0 + rfirst + i * RSTEP;
+    if (m < p.M && n < p.N) epi_finish8<EPI>(p, m, n, acc[i], sa[i], sb[i]);
   }
 }
 
@@ -617,19 +803,46 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p, int sp
 // ------------------------------------------------------------------------------------------
 namespace {
 
-constexpr int kCUs = 256;
 constexpr int kBK = 64;
+constexpr int kMaxDevices = 64;
 
+std::atomic<int> g_policy{0};
+
+// Compute units of the current device, read once per device.
+int cu_count() {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Tile shapes and the time one workgroup (alone on its CU) spends per 64-deep k-tile on MI355X,
+// in microseconds: 256 x 256 measured at 1.35 us, the others scaled by their flops and their
+// lower MFMA-per-LDS-byte efficiency.
 struct TileCfg {
-  int bm, bn, per_cu;  // workgroups resident per CU (LDS-limited)
-  double eff;          // relative MFMA efficiency of the tile shape (LDS bytes per MFMA)
+  int bm, bn;
+  double t_iter;
 };
-constexpr TileCfg kCfgs[] = {{256, 256, 1, 1.00}, {256, 128, 1, 0.80}, {128, 256, 1, 0.80},
-                             {128, 128, 2, 0.55}};
+constexpr TileCfg kCfgs[] = {{256, 256, 1.35}, {256, 128, 0.80}, {128, 256, 0.80}, {128, 128, 0.62}};
+
+// Direct-to-LDS pipeline of each tile shape: k-tile depth KT and stage count NS, within the
+// 160 KB of LDS a workgroup may hold (NS * (BM + BN) * KT * 2 bytes).  Deeper pipelines hide more
+// memory latency; 32-deep k-tiles buy the extra stages for the large tiles.
+constexpr int lds_kt(int, int) { return 64; }
+constexpr int lds_ns(int bm, int bn) { return (bm == 256 && bn == 256) ? 2 : 3; }
 
 struct Plan {
-  int cfg, bm, bn, splits, k_split;
-  bool lds;  // direct-to-LDS kernel (gemm_lds_kernel) or the register-staged one
+  int cfg, bm, bn;
+  bool lds;        // direct-to-LDS kernel (gemm_lds_kernel) or the register-staged one
+  int splits, k_split;
+  int dp_tiles, sk_tiles, ipt, grid;
+  double cost;     // estimated microseconds
 };
 
 // The direct-to-LDS kernel needs whole 64-wide k-tiles along every K-contiguous operand row
@@ -642,46 +855,91 @@ bool lds_eligible(const GemmProblem& p) {
   return a_rows * p.lda * 2 < (1ll << 31) && b_rows * p.ldb * 2 < (1ll << 31);
 }
 
+// HBM bytes the epilogue moves per output element besides the accumulator.  The plan must not
+// depend on `accumulate` (workspace sizes are queried without it), so its extra read is left out.
+double epi_bytes(const GemmProblem& p) {
+  switch (p.epi) {
+    case EPI_BF16: return 2.0;
+    case EPI_F32: return 4.0;
+    case EPI_SWIGLU: return 8.0;  // gate, up in; dgate, dup out
+    default: return 4.0;          // f in, dF out
+  }
+}
+
+// Cost model (microseconds): waves of workgroups, each running its k-tiles and its epilogue at an
+// equal share of HBM bandwidth; K-split partials cost a write and a read-back; stream-K costs two
+// partial tiles per workgroup, a fix-up pass over them and one more launch.
 Plan make_plan(const GemmProblem& p) {
+  const int ncu = cu_count();
   const bool lds = lds_eligible(p);
-  Plan best{3, 128, 128, 1, kBK, lds};
-  if (p.K <= 0) return best;  // empty reduction: the kernel stores zeros (or leaves C + 0)
-  double best_cost = 1e300;
+  int policy = g_policy.load(std::memory_order_relaxed);
+  if (policy == 0 && p.concurrent) policy = 3;
+  const double bw = 8.0e6, bw_cu = bw / ncu;  // bytes per microsecond
+  const double eb = epi_bytes(p);
+  Plan best{};
+  best.cost = 1e300;
+  if (p.K <= 0) {  // empty reduction: the kernel stores zeros (or leaves C + 0)
+    const int T = ((p.M + 127) / 128) * ((p.N + 127) / 128);
+    return Plan{3, 128, 128, lds, 1, kBK, T, 0, 0, T, 0.0};
+  }
   // 256 x 256 only in the direct-to-LDS kernel (staged through registers it would spill)
   for (int c = lds ? 0 : 1; c < 4; ++c) {
-    TileCfg tc = kCfgs[c];
-    if (lds && c == 3) tc.per_cu = 1;  // three 32 KB stages
-    if (lds && (c == 1 || c == 2)) tc.eff = 0.85;
+    const TileCfg tc = kCfgs[c];
+    const int kt = lds ? lds_kt(tc.bm, tc.bn) : kBK;
+    const int ipt = (p.K + kt - 1) / kt;  // k-tiles per output tile, in the kernel's k-tile depth
+    const double t_it = tc.t_iter * (lds ? 1.0 : 1.5);
+    const int per_cu = (!lds && c == 3) ? 2 : 1;  // LDS-limited residency
     const long tiles = (long)((p.M + tc.bm - 1) / tc.bm) * ((p.N + tc.bn - 1) / tc.bn);
-    for (int splits = 1; splits <= 8; ++splits) {
-      int ks = (p.K + splits - 1) / splits;
-      ks = (ks + kBK - 1) / kBK * kBK;
-      if ((p.K + ks - 1) / ks != splits) continue;
-      const long items = tiles * splits;
-      const long slots = (long)kCUs * tc.per_cu;
-      const long waves = (items + slots - 1) / slots;
-      // one wave: every resident workgroup computes a bm x bn x ks tile; a CU shares its
-      // throughput between its per_cu workgroups
-      double cost = (double)waves * tc.per_cu * tc.bm * tc.bn * ks / tc.eff;
-      // split partials: written once, read once by the reduction (in MFMA-time units)
-      if (splits > 1) cost += (double)splits * p.M * p.N * 8.0 * 64.0 / kCUs;
-      if (cost < best_cost * 0.98) {
-        best_cost = cost;
-        best = Plan{c, tc.bm, tc.bn, splits, ks, lds};
+    const double epi_tile = tc.bm * tc.bn * eb / bw_cu, part_tile = tc.bm * tc.bn * 4.0 / bw_cu;
+    if (policy != 2 || !lds) {
+      for (int splits = 1; splits <= (policy == 3 ? 1 : 8); ++splits) {
+        int ks = (p.K + splits - 1) / splits;
+        ks = (ks + kBK - 1) / kBK * kBK;
+        if ((p.K + ks - 1) / ks != splits) continue;
+        const long items = tiles * splits;
+        const long slots = (long)ncu * per_cu;
+        const long waves = (items + slots - 1) / slots;
+        double cost = (double)waves * per_cu * ((ks / kBK) * t_it + (splits > 1 ? part_tile : epi_tile));
+        if (splits > 1) cost += ((double)splits * p.M * p.N * 4.0 + (double)p.M * p.N * eb) / bw + 4.0;
+        if (cost < best.cost * 0.98)
+          best = Plan{c, tc.bm, tc.bn, lds, splits, ks, (int)tiles, 0, ipt, (int)items, cost};
       }
+    }
+    if (lds && policy != 1 && policy != 3 && (tiles % ncu != 0 || policy == 2)) {
+      const long dp = tiles >= 2L * ncu ? (tiles / ncu - 1) * ncu : 0;
+      const long sk = tiles - dp;
+      const long n_it = sk * ipt;
+      const long grid = n_it < ncu ? n_it : ncu;
+      const double per_wg = (double)((n_it + grid - 1) / grid) * kt / kBK;
+      const double cost = (double)dp / grid * ((double)ipt * kt / kBK * t_it + epi_tile) + per_wg * t_it +
+                          (double)sk / grid * epi_tile + 2.0 * part_tile +
+                          2.0 * grid * tc.bm * tc.bn * 4.0 / bw + 4.0;
+      if (cost < best.cost * 0.98 || policy == 2)
+        best = Plan{c, tc.bm, tc.bn, lds, 1, ipt * kt, (int)dp, (int)sk, ipt, (int)grid, cost};
     }
   }
   return best;
 }
 
+size_t plan_workspace(const GemmProblem& p, const Plan& pl) {
+  if (pl.sk_tiles > 0) return (size_t)2 * pl.grid * pl.bm * pl.bn * sizeof(float);
+  if (pl.splits > 1) return (size_t)pl.splits * p.M * p.N * sizeof(float);
+  return 0;
+}
+
 template <int BM, int BN, int EPI, bool AK, bool BKM>
-collider_status launch_lds(const GemmParams& gp, const char* name, hipStream_t s) {
-  constexpr int NS = (BM == 256 && BN == 256) ? 2 : 3;
-  const int total = gp.tiles_m * gp.tiles_n * gp.splits;
-  const size_t lds = (size_t)NS * (BM + BN) * kBK * sizeof(uint16_t);
-  auto kern = gemm_lds_kernel<BM, BN, AK, BKM, EPI, NS>;
+collider_status launch_lds(const GemmParams& gp, int grid, const char* name, hipStream_t s) {
+  constexpr int KT = lds_kt(BM, BN), NS = lds_ns(BM, BN);
+  const size_t lds = (size_t)NS * (BM + BN) * KT * sizeof(uint16_t);
+  static_assert(NS * (BM + BN) * KT * 2 <= 160 * 1024, "LDS budget");
+  auto kern = gemm_lds_kernel<BM, BN, KT, AK, BKM, EPI, NS>;
   (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  COLLIDER_LAUNCH(name, s, hipLaunchKernelGGL(kern, dim3(total), dim3(256), lds, s, gp));
+  COLLIDER_LAUNCH(name, s, hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, gp));
+  collider_status st = last_hip_status();
+  if (st != COLLIDER_OK || gp.sk_tiles == 0) return st;
+  COLLIDER_LAUNCH("gemm_sk_fixup", s,
+                  hipLaunchKernelGGL((sk_fixup_kernel<BM, BN, EPI>), dim3(gp.sk_tiles, BM / 32),
+                                     dim3(256), 0, s, gp, grid));
   return last_hip_status();
 }
 
@@ -698,39 +956,27 @@ collider_status launch_one(const GemmParams& gp, const char* name, hipStream_t s
 // Layout / epilogue combinations the linear backward uses: dX GEMMs (A K-major, B N-major) with a
 // bf16 / SwiGLU / GELU epilogue; dW GEMMs (both operands token-major) with an fp32 epilogue.
 template <int BM, int BN>
-collider_status launch_cfg(const GemmParams& gp, const GemmProblem& pr, bool lds, const char* name,
-                           hipStream_t s) {
+collider_status launch_cfg(const GemmParams& gp, const GemmProblem& pr, const Plan& pl,
+                           const char* name, hipStream_t s) {
+  constexpr bool kStaged = !(BM == 256 && BN == 256);  // 256 x 256 would spill staged
   if (pr.a_kmajor && !pr.b_kmajor) {
     switch (pr.epi) {
       case EPI_BF16:
-        return lds ? launch_lds<BM, BN, EPI_BF16, true, false>(gp, name, s)
-                   : launch_one<BM, BN, EPI_BF16, true, false>(gp, name, s);
+        if (pl.lds) return launch_lds<BM, BN, EPI_BF16, true, false>(gp, pl.grid, name, s);
+        if constexpr (kStaged) return launch_one<BM, BN, EPI_BF16, true, false>(gp, name, s);
+        break;
       case EPI_SWIGLU:
-        return lds ? launch_lds<BM, BN, EPI_SWIGLU, true, false>(gp, name, s)
-                   : launch_one<BM, BN, EPI_SWIGLU, true, false>(gp, name, s);
+        if (pl.lds) return launch_lds<BM, BN, EPI_SWIGLU, true, false>(gp, pl.grid, name, s);
+        if constexpr (kStaged) return launch_one<BM, BN, EPI_SWIGLU, true, false>(gp, name, s);
+        break;
       case EPI_GELU:
-        return lds ? launch_lds<BM, BN, EPI_GELU, true, false>(gp, name, s)
-                   : launch_one<BM, BN, EPI_GELU, true, false>(gp, name, s);
+        if (pl.lds) return launch_lds<BM, BN, EPI_GELU, true, false>(gp, pl.grid, name, s);
+        if constexpr (kStaged) return launch_one<BM, BN, EPI_GELU, true, false>(gp, name, s);
+        break;
     }
   } else if (!pr.a_kmajor && !pr.b_kmajor && pr.epi == EPI_F32) {
-    return lds ? launch_lds<BM, BN, EPI_F32, false, false>(gp, name, s)
-               : launch_one<BM, BN, EPI_F32, false, false>(gp, name, s);
-  }
-  return COLLIDER_ERR_UNSUPPORTED;
-}
-
-// 256 x 256 exists only as a direct-to-LDS kernel (the register-staged one would spill)
-template <int BM, int BN>
-collider_status launch_cfg_lds(const GemmParams& gp, const GemmProblem& pr, const char* name,
-                               hipStream_t s) {
-  if (pr.a_kmajor && !pr.b_kmajor) {
-    switch (pr.epi) {
-      case EPI_BF16: return launch_lds<BM, BN, EPI_BF16, true, false>(gp, name, s);
-      case EPI_SWIGLU: return launch_lds<BM, BN, EPI_SWIGLU, true, false>(gp, name, s);
-      case EPI_GELU: return launch_lds<BM, BN, EPI_GELU, true, false>(gp, name, s);
-    }
-  } else if (!pr.a_kmajor && !pr.b_kmajor && pr.epi == EPI_F32) {
-    return launch_lds<BM, BN, EPI_F32, false, false>(gp, name, s);
+    if (pl.lds) return launch_lds<BM, BN, EPI_F32, false, false>(gp, pl.grid, name, s);
+    if constexpr (kStaged) return launch_one<BM, BN, EPI_F32, false, false>(gp, name, s);
   }
   return COLLIDER_ERR_UNSUPPORTED;
 }
@@ -749,10 +995,11 @@ collider_status launch_reduce(const GemmParams& gp, const GemmProblem& prob, int
 
 }  // namespace
 
+void gemm_set_policy(int policy) { g_policy.store(policy, std::memory_order_relaxed); }
+
 size_t gemm_bf16_workspace_bytes(const GemmProblem& p) {
   if (p.M <= 0 || p.N <= 0 || p.K <= 0) return 0;
-  const Plan pl = make_plan(p);
-  return pl.splits > 1 ? (size_t)pl.splits * p.M * p.N * sizeof(float) : 0;
+  return plan_workspace(p, make_plan(p));
 }
 
 collider_status gemm_bf16(const GemmProblem& prob, void* ws, size_t ws_bytes, hipStream_t s) {
@@ -772,6 +1019,9 @@ collider_status gemm_bf16(const GemmProblem& prob, void* ws, size_t ws_bytes, hi
   gp.splits = pl.splits;
   gp.tiles_m = (prob.M + pl.bm - 1) / pl.bm;
   gp.tiles_n = (prob.N + pl.bn - 1) / pl.bn;
+  gp.ipt = pl.ipt;
+  gp.dp_tiles = pl.dp_tiles;
+  gp.sk_tiles = pl.sk_tiles;
   gp.C = prob.C;
   gp.ldc = prob.ldc;
   gp.accumulate = prob.accumulate;
@@ -781,25 +1031,36 @@ collider_status gemm_bf16(const GemmProblem& prob, void* ws, size_t ws_bytes, hi
   gp.rowmap = prob.rowmap;
   gp.out2 = prob.out2;
   gp.ld_out2 = prob.ld_out2;
-  if (pl.splits > 1) {
-    if (!ws || ws_bytes < (size_t)pl.splits * prob.M * prob.N * sizeof(float))
-      return COLLIDER_ERR_WORKSPACE;
-    gp.partial = (float*)ws;
+  const size_t need = plan_workspace(prob, pl);
+  if (need) {
+    if (!ws || ws_bytes < need) return COLLIDER_ERR_WORKSPACE;
+    if (pl.sk_tiles > 0)
+      gp.skp = (float*)ws;
+    else
+      gp.partial = (float*)ws;
   }
+  // every stream-K workgroup must own at least one k-tile (the fix-up reads each owner's slot),
+  // and the work items must cover every tile exactly once
+  if (pl.sk_tiles > 0 && ((int64_t)pl.sk_tiles * pl.ipt < pl.grid || pl.splits != 1))
+    return COLLIDER_ERR_UNSUPPORTED;
+  if (pl.dp_tiles + pl.sk_tiles != gp.tiles_m * gp.tiles_n) return COLLIDER_ERR_UNSUPPORTED;
   const char* name = prob.name ? prob.name : "gemm_bf16";
   static const bool verbose = getenv("COLLIDER_GEMM_PLANS") != nullptr;
   if (verbose)
-    fprintf(stderr, "[collider] %s M=%d N=%d K=%d tile=%dx%d splits=%d %s\n", name, prob.M, prob.N,
-            prob.K, pl.bm, pl.bn, pl.splits, pl.lds ? "lds" : "staged");
+    fprintf(stderr,
+            "[collider] %s M=%d N=%d K=%d tile=%dx%d splits=%d dp_tiles=%d sk_tiles=%d grid=%d "
+            "est=%.1fus %s\n",
+            name, prob.M, prob.N, prob.K, pl.bm, pl.bn, pl.splits, pl.dp_tiles, pl.sk_tiles,
+            pl.grid, pl.cost, pl.lds ? "lds" : "staged");
   collider_status st;
   switch (pl.cfg) {
     case 0:
       if (!pl.lds) return COLLIDER_ERR_UNSUPPORTED;
-      st = launch_cfg_lds<256, 256>(gp, prob, name, s);
+      st = launch_cfg<256, 256>(gp, prob, pl, name, s);
       break;
-    case 1: st = launch_cfg<256, 128>(gp, prob, pl.lds, name, s); break;
-    case 2: st = launch_cfg<128, 256>(gp, prob, pl.lds, name, s); break;
-    default: st = launch_cfg<128, 128>(gp, prob, pl.lds, name, s); break;
+    case 1: st = launch_cfg<256, 128>(gp, prob, pl, name, s); break;
+    case 2: st = launch_cfg<128, 256>(gp, prob, pl, name, s); break;
+    default: st = launch_cfg<128, 128>(gp, prob, pl, name, s); break;
   }
   if (st != COLLIDER_OK || pl.splits == 1) return st;
   switch (prob.epi) {

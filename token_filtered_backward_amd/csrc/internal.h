@@ -16,6 +16,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // ------------------------------------------------------------------------------------------
 // bf16 helpers (uint16 storage)
 // ------------------------------------------------------------------------------------------
+// Activation helpers on the hardware transcendental units: v_exp_f32 (2^x) and v_rcp_f32 (1/x,
+// about 1 ulp).  Their error is far below the bf16 resolution of every value they feed.
+__device__ __forceinline__ float fast_sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
+// tanh(x) = 1 - 2 / (e^(2x) + 1): exact limits +-1 for large |x| (e^(2x) -> inf or 0)
+__device__ __forceinline__ float fast_tanh(float x) {
+  return 1.f - 2.f * __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(x * 2.8853900817779268f) + 1.f);
+}
+
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 __device__ __forceinline__ uint16_t f2bf(float f) {
   __bf16 h = (__bf16)f;  // v_cvt_pk_bf16_f32: round to nearest even
@@ -142,7 +152,13 @@ struct GemmProblem {
   uint16_t* out2;      // SwiGLU: dup written at out2 (C gets dgate); GELU: unused
   int64_t ld_out2;
   const char* name;    // label for per-kernel timing (static string)
+  // runs beside work on another stream: the default plan then takes whole tiles only (persistent
+  // stream-K grids and K-split waves would hold every CU the other stream could use)
+  bool concurrent;
 };
+// Work decomposition of the bf16 GEMMs: 0 = cost model, 1 = whole tiles and K-splits only,
+// 2 = stream-K wherever the direct-to-LDS kernel applies, 3 = whole tiles only.
+void gemm_set_policy(int policy);
 size_t gemm_bf16_workspace_bytes(const GemmProblem& p);
 collider_status gemm_bf16(const GemmProblem& p, void* ws, size_t ws_bytes, hipStream_t s);
 collider_status gemm_f32(const GemmProblem& p, hipStream_t s);

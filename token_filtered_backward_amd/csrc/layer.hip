@@ -169,8 +169,10 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
   g_dXin.name = llama ? "gemm_dX_qkv" : "gemm_dX_qkv_fc1";
   g_dwqkv.name = "gemm_dw_qkv";
   g_dwfc1.name = "gemm_dw_fc1";
-  const GemmProblem* gl[] = {&g_dA, &g_dw2, &g_dXmid, &g_dwmid, &g_dO, &g_dwo, &g_dXin, &g_dwqkv,
-                             &g_dwfc1};
+  // the two streams run side by side: every layer GEMM takes the plan for concurrent work (the
+  // same plan in single-stream mode, so per-kernel timings measure the kernels the layer runs)
+  GemmProblem* gl[] = {&g_dA, &g_dw2, &g_dXmid, &g_dwmid, &g_dO, &g_dwo, &g_dXin, &g_dwqkv, &g_dwfc1};
+  for (GemmProblem* p : gl) p->concurrent = true;
   size_t gemm_need = 0, gemm_need2 = 0;
   for (const GemmProblem* p : gl) {
     if (p->M <= 0) continue;

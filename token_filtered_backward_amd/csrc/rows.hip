@@ -187,11 +187,11 @@ collider_status launch_norm_recompute(const uint16_t* x, const float* mean, cons
 // ------------------------------------------------------------------------------------------
 // activation recompute: a[c] = bf16(silu(g)*up) or bf16(gelu_tanh(g)), rows rowmap[c]
 // ------------------------------------------------------------------------------------------
-__device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
+__device__ __forceinline__ float silu_f(float g) { return g * fast_sigmoid(g); }
 __device__ __forceinline__ float gelu_f(float f) {
   const float c = 0.7978845608028654f, a = 0.044715f;
   const float u = c * (f + a * f * f * f);
-  return 0.5f * f * (1.f + tanhf(u));
+  return 0.5f * f * (1.f + fast_tanh(u));
 }
 
 __global__ __launch_bounds__(256) void act_recompute_kernel(const uint16_t* __restrict__ g,
