@@ -182,17 +182,33 @@ def main():
     grads = tfb.make_grads(lcfg, M, ix0.M_kept, dev)
     lb.workspace(ix0.M_kept)
 
+    L = cfg.n_layers
+    if L > 1:
+        # a stack of L layers of the same shape (the saved set and weights of one layer serve every
+        # layer: the work does not depend on the values).  Gradients stay compact between layers;
+        # the bottom layer scatters dx to the full token layout.
+        gc = [tfb.make_grads(lcfg, M, ix0.M_kept, dev, dx_compact=True) for _ in range(2)]
+
     def step_filtered():
         ix = tfb.build_index(keep, B, S)
-        lb(weights, saved, dy, ix, grads)
+        if L == 1:
+            lb(weights, saved, dy, ix, grads)
+            return
+        lb(weights, saved, dy, ix, gc[0], dx_compact=True)
+        for layer in range(1, L - 1):
+            lb(weights, saved, gc[(layer - 1) % 2]["dx"], ix, gc[layer % 2], dy_compact=True,
+               dx_compact=True)
+        lb(weights, saved, gc[(L - 2) % 2]["dx"], ix, grads, dy_compact=True)
 
     ucfg = tfb.layer_cfg(cfg, unfiltered=True)
     ub = tfb.LayerBackward(ucfg, B, S, dev)
     uix = tfb.dense_index(B, S)
-    ugrads = tfb.make_grads(ucfg, M, M, dev)
+    ugrads = [tfb.make_grads(ucfg, M, M, dev) for _ in range(2 if L > 1 else 1)]
 
     def step_unfiltered():
-        ub(weights, saved, dy, uix, ugrads)
+        ub(weights, saved, dy, uix, ugrads[0])
+        for layer in range(1, L):
+            ub(weights, saved, ugrads[(layer - 1) % 2]["dx"], uix, ugrads[layer % 2])
 
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)  # > 256 MB MALL
     if args.copy_calibration_mb > 0:
@@ -262,6 +278,12 @@ def main():
     cu = ix.cu_seqlens.cpu().numpy()
     seq_counts = [int(cu[b + 1] - cu[b]) for b in range(B)]
     work = algorithmic_work(cfg, ix.M_kept, seq_counts)
+    if L > 1:  # every layer's GEMMs and attention; dY gathered by the top layer only
+        dy_bytes = 2.0 * ix.M_kept * 2 * cfg.H
+        work = dict(work, gemm_flops=L * work["gemm_flops"], attn_flops=L * work["attn_flops"],
+                    attn_dt_flops=L * work["attn_dt_flops"],
+                    gather_bytes=L * (work["gather_bytes"] - dy_bytes) + dy_bytes,
+                    gemm_bytes=L * work["gemm_bytes"], gemm_launches=L * work["gemm_launches"])
     gemm_tflops = work["gemm_flops"] / (gemm_ms * 1e-3) / 1e12
     attn_ms = sum(prof[k][0] for k in prof if k.startswith("attn_")) / n_prof
     attn_tflops = (work["attn_flops"] + work["attn_dt_flops"]) / (attn_ms * 1e-3) / 1e12 if attn_ms else None
@@ -281,7 +303,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}-shaped layer backward, B{B}xS{S}, {args.r}% filtered",
+        "config": {"workload": (f"{cfg.name}-shaped layer backward, B{B}xS{S}, {args.r}% filtered" if L == 1
+                                else f"{L} x {cfg.name}-shaped layers backward (compact chain), B{B}xS{S}, "
+                                     f"{args.r}% filtered"),
+                   "layers": L,
                    "B": B, "S": S, "hidden": cfg.H, "heads": f"{cfg.nq}/{cfg.nkv}x{cfg.d}",
                    "inter": cfg.I, "M": M, "M_kept": ix.M_kept, "parallelism": "single GPU"},
         "ms_filtered_cold": round(ms_f_cold, 4),
@@ -308,7 +333,10 @@ def main():
             "avg_launch_ms": round(gemm_ms / max(gemm_launches, 1), 5),
         },
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and L > 1:
+        log("[bench] no CPU oracle timing for a layer stack (one float64 layer at this size alone "
+            "takes minutes)")
+    elif not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(cfg, inp)
         log(f"[bench] cpu oracle: {out['cpu_baseline']['value']} ms per layer")

@@ -246,6 +246,16 @@ collider_status collider_profile_enable(int32_t on);
  * Process-wide.  Workspace sizes depend on it: query *_workspace_bytes after setting it.  Returns
  * COLLIDER_ERR_SHAPE for any other value. */
 collider_status collider_gemm_set_policy(int32_t policy);
+
+/* The work decomposition the current policy picks for one bf16 GEMM C[M, N] = A B with reduction
+ * length K, on the current device (host only, launches nothing).  layout 0: dX = dY w (A [M, K]
+ * K-contiguous, B [K, N] N-contiguous, bf16 C); layout 1: dW = dY^T X (A and B token-major, fp32 C).
+ * concurrent != 0: the plan for GEMMs that run beside another stream (the layer's).  out[7] receives
+ * tile rows, tile columns, K-splits, whole tiles, stream-K tiles, workgroups, and 1 when the
+ * direct-to-LDS kernel runs (0: register-staged).  COLLIDER_ERR_SHAPE for M or N <= 0, K < 0 or
+ * N % 8 != 0; COLLIDER_ERR_NULL for out == NULL. */
+collider_status collider_gemm_describe_plan(int32_t M, int32_t N, int32_t K, int32_t layout,
+                                           int32_t concurrent, int32_t* out);
 int32_t collider_profile_collect(char* names, int32_t name_cap, double* total_ms, int32_t* launches,
                                  int32_t max_kernels);
 const char* collider_status_string(collider_status s);

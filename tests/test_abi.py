@@ -110,3 +110,26 @@ def test_gemm_policy_values():
     assert L.collider_gemm_set_policy(7) == 2 and L.collider_gemm_set_policy(-1) == 2
     for p in (1, 2, 3, 0):
         assert L.collider_gemm_set_policy(p) == 0
+
+
+def test_gemm_plans_fill_the_cus_on_ragged_token_counts():
+    """Host-side planner: whole-tile plans for the layer's concurrent GEMMs pick a tile height that
+    fills 256 CUs for the ragged kept-token count, and the dense counts keep 256-row tiles."""
+    plan = tfb.collider_gemm_describe_plan
+    assert plan(4916, 2048, 11264, 0, concurrent=True)["bm"] == 160   # 248 tiles
+    assert plan(4916, 5632, 2048, 0, concurrent=True)["bm"] == 224    # 484 tiles, 2 waves
+    assert plan(5500, 2048, 2048, 0, concurrent=True)["bm"] == 192    # 232 tiles
+    assert plan(8192, 2048, 11264, 0, concurrent=True)["bm"] == 256   # 256 tiles
+    for shape in ((4916, 2048, 11264, 0), (11264, 2048, 4916, 1), (2048, 2048, 4916, 1), (77, 136, 64, 0)):
+        p = plan(*shape, concurrent=True)
+        assert p["splits"] == 1 and p["sk_tiles"] == 0
+        bm, bn = p["bm"], p["bn"]
+        assert p["dp_tiles"] == -(-shape[0] // bm) * -(-shape[1] // bn)
+    # token-major operands only take 128 / 256-row tiles
+    for M in (2048, 2560, 5632, 11264):
+        assert plan(M, 2048, 4916, 1)["bm"] in (128, 256)
+    L = tfb.lib()
+    out = (ctypes.c_int32 * 7)()
+    assert L.collider_gemm_describe_plan(0, 8, 8, 0, 0, out) == 2
+    assert L.collider_gemm_describe_plan(8, 12, 8, 0, 0, out) == 2
+    assert L.collider_gemm_describe_plan(8, 8, 8, 2, 0, out) == 2

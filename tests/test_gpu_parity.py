@@ -337,6 +337,40 @@ def test_layer_compact_chain_matches_full_layout():
         assert torch.equal(g1[k], g2[k]), k
 
 
+@pytest.mark.parametrize("name", ["small_llama", "small_phi"])
+def test_stack_of_layers(name):
+    """Three layers from one consistent forward, chained top to bottom with compact gradients
+    between layers (the same mask in every layer), against the oracle's stack backward."""
+    cfg = synth.get_config(name)
+    model = synth.make_model_inputs(cfg, seed=3, r_pct=40, n_layers=3)
+    keep = model["keep"]
+    ix = tfb.build_index(_dev_keep(keep), cfg.B, cfg.S)
+    lcfg = tfb.layer_cfg(cfg)
+    lb = tfb.LayerBackward(lcfg, cfg.B, cfg.S, "cuda")
+    g = bf16_dev(model["dy"])
+    outs = []
+    for li in reversed(range(3)):
+        inp = dict(cfg=cfg, weights=model["layers"][li]["weights"], saved=model["layers"][li]["saved"],
+                   dy=model["dy"])
+        weights, saved, _ = _upload_layer(inp)
+        grads = tfb.make_grads(lcfg, cfg.M, ix.M_kept, "cuda", dx_compact=li > 0)
+        lb(weights, saved, g, ix, grads, dy_compact=li < 2, dx_compact=li > 0)
+        outs.append(grads)
+        g = grads["dx"]
+    torch.cuda.synchronize()
+    ref = oracle.model_bwd(cfg, [{"weights": upcast(l["weights"]), "saved": upcast(l["saved"])}
+                                 for l in model["layers"]], synth.bf16_bits_to_f32(model["dy"]), keep)
+    idx = ix.idx[:ix.M_kept].cpu().numpy()
+    for li, grads in zip(reversed(range(3)), outs):
+        for gname, oname in GRAD_NAMES[cfg.kind].items():
+            r = ref[li][oname]
+            if gname == "dx" and li > 0:
+                r = r[idx]  # compact rows
+            e = rel_err(to64(grads[gname]), r)
+            assert e <= BF16_TOL, (li, gname, e)
+    assert np.all(to64(outs[-1]["dx"])[keep == 0] == 0.0)
+
+
 def test_layer_repeat_is_deterministic():
     cfg = synth.get_config("small_llama")
     inp = synth.make_layer_inputs(cfg)

@@ -95,6 +95,7 @@ def lib():
                                     P(CollIndex), P(LayerGrads), _i32, _c_p, sz, _c_p]),
         "collider_profile_enable": (st, [_i32]),
         "collider_gemm_set_policy": (st, [_i32]),
+        "collider_gemm_describe_plan": (st, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_i32)]),
         "collider_profile_collect": (_i32, [ctypes.c_char_p, _i32, P(ctypes.c_double), P(_i32), _i32]),
     }
     for name, (res, args) in sig.items():
@@ -221,6 +222,14 @@ def collider_gemm_set_policy(policy: int):
     """Process-wide GEMM work decomposition (0 cost model, 1 tiles + K-splits, 2 stream-K,
     3 whole tiles only).  Query workspace sizes after changing it."""
     _check(lib().collider_gemm_set_policy(int(policy)), "collider_gemm_set_policy")
+
+
+def collider_gemm_describe_plan(M, N, K, layout, concurrent=False):
+    """{bm, bn, splits, dp_tiles, sk_tiles, grid, lds} of the bf16 GEMM plan (host only)."""
+    out = (_i32 * 7)()
+    _check(lib().collider_gemm_describe_plan(int(M), int(N), int(K), int(layout), int(concurrent), out),
+           "collider_gemm_describe_plan")
+    return dict(zip(("bm", "bn", "splits", "dp_tiles", "sk_tiles", "grid", "lds"), list(out)))
 
 
 def collider_profile_enable(on: bool):

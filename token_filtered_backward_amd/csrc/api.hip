@@ -324,6 +324,31 @@ collider_status collider_gemm_set_policy(int32_t policy) {
   return COLLIDER_OK;
 }
 
+collider_status collider_gemm_describe_plan(int32_t M, int32_t N, int32_t K, int32_t layout,
+                                           int32_t concurrent, int32_t* out) {
+  if (!out) return COLLIDER_ERR_NULL;
+  if (M <= 0 || N <= 0 || K < 0 || N % 8 || (layout != 0 && layout != 1)) return COLLIDER_ERR_SHAPE;
+  GemmProblem g{};
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.concurrent = concurrent != 0;
+  if (layout == 0) {  // dX = dY w: A [M, K] K-contiguous, B [K, N] N-contiguous, bf16 out
+    g.a_kmajor = true;
+    g.lda = K;
+    g.ldb = N;
+    g.epi = EPI_BF16;
+  } else {  // dW = dY^T X: both operands token-major [K, M] and [K, N], fp32 out
+    g.lda = M;
+    g.ldb = N;
+    g.epi = EPI_F32;
+  }
+  int v[7];
+  gemm_describe_plan(g, v);
+  for (int i = 0; i < 7; ++i) out[i] = v[i];
+  return COLLIDER_OK;
+}
+
 collider_status collider_profile_enable(int32_t on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = on != 0;

@@ -547,11 +547,16 @@ __device__ __forceinline__ void issue_stage(const TileDMA<BM, AK, KT>& da, const
 
 // MFMAs of one k-tile (KT / 16 steps of k = 16) from one LDS stage; fragments of step kk+1 are read
 // while the MFMAs of step kk run (two register sets).
+// Wavefront layout of a BM x BN tile: 2 x 2 wavefronts when BM / 2 is a multiple of 32, else
+// 1 x 4 (BM = 160, 224: each wavefront covers all rows and a quarter of the columns).
+constexpr int wave_rows(int bm) { return (bm % 64 == 0) ? 2 : 1; }
+
 template <int BM, int BN, bool AK, bool BKM, int KT>
-__device__ __forceinline__ void mma_ktile(const char* As, const char* Bs,
-                                          f32x16 (&acc)[BM / 64][BN / 64], int wm, int wn,
-                                          int lane) {
-  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32, KS = KT / 16;
+__device__ __forceinline__ void mma_ktile(
+    const char* As, const char* Bs,
+    f32x16 (&acc)[BM / wave_rows(BM) / 32][BN / (4 / wave_rows(BM)) / 32], int wm, int wn, int lane) {
+  constexpr int WGM = wave_rows(BM), WGN = 4 / WGM;
+  constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32, KS = KT / 16;
   bf16x8 af[2][TM], bfv[2][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i) af[0][i] = read_frag<BM, AK, KT>(As, wm * WM + i * 32, 0, lane);
@@ -591,15 +596,17 @@ __device__ __forceinline__ void mma_ktile(const char* As, const char* Bs,
 template <int BM, int BN, int KT, bool AK, bool BKM, int EPI, int NS>
 __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
   constexpr int BK = KT;
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int WGM = wave_rows(BM), WGN = 4 / WGM;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wavefront blocks of whole 32 x 32 MFMA tiles");
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
   constexpr int LPW = (A_BYTES + B_BYTES) / 1024 / 4;  // load instructions per wave per k-tile
   extern __shared__ __align__(16) char lds[];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   // LDS byte address of the dynamic LDS block (the low half of its flat address)
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
   // operand buffers: rows of A are tokens (K-major A: M rows; MN-major A: K rows)
@@ -686,10 +693,12 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
     // epilogue through LDS: the fp32 tile is staged row-major in passes of EROWS rows, then every
     // thread finishes 8 consecutive columns of GPT rows with 16-byte loads / stores
     constexpr int LDE = BN + 8;  // +8 floats: the two lane halves' rows land 32 banks apart
-    constexpr int EROWS_FIT = (BM * LDE * 4 <= NS * STAGE) ? BM : ((64 * LDE * 4 <= NS * STAGE) ? 64 : 32);
-    // epilogues with two 16-byte side inputs per 8 outputs take shorter passes (registers)
+    // rows per pass: a divisor of BM that fits the stage buffers; epilogues with two 16-byte side
+    // inputs per 8 outputs take shorter passes (registers)
     constexpr int EROWS_REG = (EPI == EPI_SWIGLU || EPI == EPI_F32) ? 32 : 64;
-    constexpr int EROWS = EROWS_FIT < EROWS_REG ? EROWS_FIT : EROWS_REG;
+    constexpr int EROWS = (BM <= EROWS_REG && BM * LDE * 4 <= NS * STAGE) ? BM
+                          : (BM % 64 == 0 && 64 <= EROWS_REG && 64 * LDE * 4 <= NS * STAGE) ? 64 : 32;
+    static_assert(BM % EROWS == 0 && EROWS % 32 == 0, "epilogue passes cover whole accumulator blocks");
     static_assert(EROWS * LDE * 4 <= NS * STAGE, "epilogue pass must fit in the stage buffers");
     constexpr int CPR = BN / 8, RSTEP = 256 / CPR, GPT = EROWS / RSTEP;
     static_assert(EROWS % RSTEP == 0, "epilogue rows per pass");
@@ -829,13 +838,19 @@ struct TileCfg {
   int bm, bn;
   double t_iter;
 };
-constexpr TileCfg kCfgs[] = {{256, 256, 1.35}, {256, 128, 0.80}, {128, 256, 0.80}, {128, 128, 0.62}};
+// 160 / 192 / 224-row tiles (K-major A only) let a ragged token count fill the CUs: with N = 2048,
+// M' = 4916 makes 160 tiles of 256 rows but 248 of 160.
+constexpr TileCfg kCfgs[] = {{256, 256, 1.35}, {256, 128, 0.80}, {128, 256, 0.80}, {128, 128, 0.62},
+                             {160, 256, 0.94}, {192, 256, 1.07}, {224, 256, 1.31}};
+constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
 // Direct-to-LDS pipeline of each tile shape: k-tile depth KT and stage count NS, within the
 // 160 KB of LDS a workgroup may hold (NS * (BM + BN) * KT * 2 bytes).  Deeper pipelines hide more
 // memory latency; 32-deep k-tiles buy the extra stages for the large tiles.
 constexpr int lds_kt(int, int) { return 64; }
-constexpr int lds_ns(int bm, int bn) { return (bm == 256 && bn == 256) ? 2 : 3; }
+constexpr int lds_ns(int bm, int bn) {
+  return (bn == 256 && (bm == 256 || bm == 224 || bm == 192)) ? 2 : 3;
+}
 
 struct Plan {
   int cfg, bm, bn;
@@ -883,7 +898,8 @@ Plan make_plan(const GemmProblem& p) {
     return Plan{3, 128, 128, lds, 1, kBK, T, 0, 0, T, 0.0};
   }
   // 256 x 256 only in the direct-to-LDS kernel (staged through registers it would spill)
-  for (int c = lds ? 0 : 1; c < 4; ++c) {
+  for (int c = lds ? 0 : 1; c < kNumCfgs; ++c) {
+    if (c >= 4 && !(lds && p.a_kmajor)) continue;  // row counts other than 128 / 256: K-major A
     const TileCfg tc = kCfgs[c];
     const int kt = lds ? lds_kt(tc.bm, tc.bn) : kBK;
     const int ipt = (p.K + kt - 1) / kt;  // k-tiles per output tile, in the kernel's k-tile depth
@@ -954,11 +970,14 @@ collider_status launch_one(const GemmParams& gp, const char* name, hipStream_t s
 }
 
 // Layout / epilogue combinations the linear backward uses: dX GEMMs (A K-major, B N-major) with a
-// bf16 / SwiGLU / GELU epilogue; dW GEMMs (both operands token-major) with an fp32 epilogue.
+// bf16 / SwiGLU / GELU epilogue; dW GEMMs (both operands token-major) with an fp32 epilogue.  Tile
+// shapes exist where their operand layouts do: MN-major tiles of 128 or 256 rows, register-staged
+// kernels for 128 / 256 shapes below 256 x 256.
 template <int BM, int BN>
 collider_status launch_cfg(const GemmParams& gp, const GemmProblem& pr, const Plan& pl,
                            const char* name, hipStream_t s) {
-  constexpr bool kStaged = !(BM == 256 && BN == 256);  // 256 x 256 would spill staged
+  constexpr bool kStaged = (BM == 128 || BM == 256) && !(BM == 256 && BN == 256);
+  constexpr bool kMnA = BM % 128 == 0;
   if (pr.a_kmajor && !pr.b_kmajor) {
     switch (pr.epi) {
       case EPI_BF16:
@@ -975,8 +994,10 @@ collider_status launch_cfg(const GemmParams& gp, const GemmProblem& pr, const Pl
         break;
     }
   } else if (!pr.a_kmajor && !pr.b_kmajor && pr.epi == EPI_F32) {
-    if (pl.lds) return launch_lds<BM, BN, EPI_F32, false, false>(gp, pl.grid, name, s);
-    if constexpr (kStaged) return launch_one<BM, BN, EPI_F32, false, false>(gp, name, s);
+    if constexpr (kMnA) {
+      if (pl.lds) return launch_lds<BM, BN, EPI_F32, false, false>(gp, pl.grid, name, s);
+      if constexpr (kStaged) return launch_one<BM, BN, EPI_F32, false, false>(gp, name, s);
+    }
   }
   return COLLIDER_ERR_UNSUPPORTED;
 }
@@ -996,6 +1017,12 @@ collider_status launch_reduce(const GemmParams& gp, const GemmProblem& prob, int
 }  // namespace
 
 void gemm_set_policy(int policy) { g_policy.store(policy, std::memory_order_relaxed); }
+
+void gemm_describe_plan(const GemmProblem& p, int* out) {
+  const Plan pl = make_plan(p);
+  const int v[7] = {pl.bm, pl.bn, pl.splits, pl.dp_tiles, pl.sk_tiles, pl.grid, pl.lds ? 1 : 0};
+  for (int i = 0; i < 7; ++i) out[i] = v[i];
+}
 
 size_t gemm_bf16_workspace_bytes(const GemmProblem& p) {
   if (p.M <= 0 || p.N <= 0 || p.K <= 0) return 0;
@@ -1060,6 +1087,9 @@ collider_status gemm_bf16(const GemmProblem& prob, void* ws, size_t ws_bytes, hi
       break;
     case 1: st = launch_cfg<256, 128>(gp, prob, pl, name, s); break;
     case 2: st = launch_cfg<128, 256>(gp, prob, pl, name, s); break;
+    case 4: st = launch_cfg<160, 256>(gp, prob, pl, name, s); break;
+    case 5: st = launch_cfg<192, 256>(gp, prob, pl, name, s); break;
+    case 6: st = launch_cfg<224, 256>(gp, prob, pl, name, s); break;
     default: st = launch_cfg<128, 128>(gp, prob, pl, name, s); break;
   }
   if (st != COLLIDER_OK || pl.splits == 1) return st;

@@ -42,6 +42,55 @@ __device__ __forceinline__ int block_excl_scan(int v, int* total, int* s_wave) {
   return r;
 }
 
+// 8 mask bytes of tokens t0 .. t0+7 as a bit mask (bit e: token t0 + e kept); tokens >= M count
+// as filtered.  One 8-byte load when the whole group exists and the address allows it.
+__device__ __forceinline__ unsigned load_bits(const uint8_t* __restrict__ keep, int t0, int M) {
+  unsigned bits = 0;
+  if (t0 + 8 <= M && ((uintptr_t)(keep + t0) & 7) == 0) {
+    const uint2 w = *(const uint2*)(keep + t0);
+    const uint32_t lo = w.x, hi = w.y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bits |= (unsigned)(((lo >> (8 * e)) & 0xffu) != 0) << e;
+      bits |= (unsigned)(((hi >> (8 * e)) & 0xffu) != 0) << (e + 4);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e)
+      if (t0 + e < M) bits |= (unsigned)(keep[t0 + e] != 0) << e;
+  }
+  return bits;
+}
+
+// Writes idx / inv / cu for tokens t0 .. t0+7, whose first kept token gets compacted position pre.
+__device__ __forceinline__ void scatter_group(unsigned bits, int t0, int pre, int n_kept, int M, int S,
+                                              int32_t* __restrict__ idx, int32_t* __restrict__ inv,
+                                              int32_t* __restrict__ cu) {
+  int iv[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int t = t0 + e;
+    const bool k = (bits >> e) & 1u;
+    iv[e] = k ? pre : -1;
+    if (t < M) {
+      if (t % S == 0) cu[t / S] = pre;
+      if (k)
+        idx[pre] = t;
+      else
+        idx[n_kept + (t - pre)] = t;
+    }
+    pre += k;
+  }
+  if (t0 + 8 <= M && ((uintptr_t)(inv + t0) & 15) == 0) {
+    ((int4*)(inv + t0))[0] = make_int4(iv[0], iv[1], iv[2], iv[3]);
+    ((int4*)(inv + t0))[1] = make_int4(iv[4], iv[5], iv[6], iv[7]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e)
+      if (t0 + e < M) inv[t0 + e] = iv[e];
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void build_index_kernel(const uint8_t* __restrict__ keep,
                                                                int B, int S,
                                                                int32_t* __restrict__ idx,
@@ -50,42 +99,33 @@ __global__ __launch_bounds__(kThreads) void build_index_kernel(const uint8_t* __
                                                                int32_t* __restrict__ count) {
   __shared__ int s_wave[kWaves + 1];
   const int M = B * S;
-  // pass 1: number of kept tokens (needed to place the filtered positions after the kept ones)
-  int local = 0;
-  for (int t = threadIdx.x; t < M; t += kThreads) local += keep[t] != 0;
-  int total = 0;
-  (void)block_excl_scan(local, &total, s_wave);
-  const int n_kept = total;
-  // pass 2: chunked exclusive scan and scatter
-  int before = 0;  // kept tokens before the current chunk
-  for (int base = 0; base < M; base += kThreads * kPer) {
-    const int t0 = base + threadIdx.x * kPer;
-    unsigned bits = 0;
-    int cnt = 0;
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int t = t0 + e;
-      const bool k = (t < M) && keep[t] != 0;
-      bits |= (unsigned)k << e;
-      cnt += k;
+  constexpr int CHUNK = kThreads * kPer;
+  int n_kept;
+  if (M <= CHUNK) {
+    // one chunk: the scan of the only chunk also gives the total
+    const int t0 = threadIdx.x * kPer;
+    const unsigned bits = load_bits(keep, t0, M);
+    int total = 0;
+    const int pre = block_excl_scan(__popc(bits), &total, s_wave);
+    n_kept = total;
+    scatter_group(bits, t0, pre, n_kept, M, S, idx, inv, cu);
+  } else {
+    // pass 1: number of kept tokens (the filtered positions are placed after the kept ones)
+    int local = 0;
+    for (int t0 = threadIdx.x * kPer; t0 < M; t0 += CHUNK) local += __popc(load_bits(keep, t0, M));
+    int total = 0;
+    (void)block_excl_scan(local, &total, s_wave);
+    n_kept = total;
+    // pass 2: chunked exclusive scan and scatter
+    int before = 0;  // kept tokens before the current chunk
+    for (int base = 0; base < M; base += CHUNK) {
+      const int t0 = base + threadIdx.x * kPer;
+      const unsigned bits = load_bits(keep, t0, M);
+      int chunk_total = 0;
+      const int pre = before + block_excl_scan(__popc(bits), &chunk_total, s_wave);
+      scatter_group(bits, t0, pre, n_kept, M, S, idx, inv, cu);
+      before += chunk_total;
     }
-    int chunk_total = 0;
-    int pre = before + block_excl_scan(cnt, &chunk_total, s_wave);
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int t = t0 + e;
-      if (t >= M) break;
-      if (t % S == 0) cu[t / S] = pre;
-      if ((bits >> e) & 1u) {
-        idx[pre] = t;
-        inv[t] = pre;
-        ++pre;
-      } else {
-        idx[n_kept + (t - pre)] = t;
-        inv[t] = -1;
-      }
-    }
-    before += chunk_total;
   }
   if (threadIdx.x == 0) {
     cu[B] = n_kept;

@@ -159,6 +159,8 @@ struct GemmProblem {
 // Work decomposition of the bf16 GEMMs: 0 = cost model, 1 = whole tiles and K-splits only,
 // 2 = stream-K wherever the direct-to-LDS kernel applies, 3 = whole tiles only.
 void gemm_set_policy(int policy);
+// out[7] = tile rows, tile cols, K-splits, whole tiles, stream-K tiles, grid, direct-to-LDS kernel
+void gemm_describe_plan(const GemmProblem& p, int* out);
 size_t gemm_bf16_workspace_bytes(const GemmProblem& p);
 collider_status gemm_bf16(const GemmProblem& p, void* ws, size_t ws_bytes, hipStream_t s);
 collider_status gemm_f32(const GemmProblem& p, hipStream_t s);

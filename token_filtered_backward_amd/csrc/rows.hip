@@ -331,7 +331,8 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(
   }
 }
 
-static constexpr int kNormParts = 256;
+// partial-sum rows of the norm backward (one per workgroup): enough workgroups to fill the CUs
+static constexpr int kNormParts = 1024;
 int norm_bwd_parts(int rows) { return rows <= 0 ? 1 : (rows < kNormParts ? rows : kNormParts); }
 
 collider_status launch_norm_bwd(const uint16_t* dxn, const uint16_t* dres, const uint16_t* x,
@@ -357,31 +358,60 @@ collider_status launch_norm_bwd(const uint16_t* dxn, const uint16_t* dres, const
   return last_hip_status();
 }
 
-// out[col] (+)= sum_p parts[p, col]: 64 columns per workgroup, 4 interleaved part streams per
-// column summed in a fixed order (deterministic), so the dependent-load chain is n_part / 4 long.
+// out[col] (+)= sum_p parts[p, col], in a fixed order (deterministic): 16 columns per workgroup.
+// Thread (l, q) adds parts l, l + 64, l + 128, ... of column quad q (independent loads, one memory
+// latency), then the 64 lane sums of each column are combined by a fixed binary tree in LDS.
+template <bool VEC>
 __global__ __launch_bounds__(256) void colsum_parts_kernel(const float* __restrict__ parts,
                                                            int n_part, int H,
                                                            float* __restrict__ out,
                                                            int accumulate) {
-  __shared__ float red[4][64];
-  const int cl = threadIdx.x & 63, ps = threadIdx.x >> 6;
-  const int col = blockIdx.x * 64 + cl;
-  float s = 0.f;
-  if (col < H)
-    for (int p = ps; p < n_part; p += 4) s += parts[(int64_t)p * H + col];
-  red[ps][cl] = s;
+  __shared__ float4 red[64][4];
+  const int q = threadIdx.x & 3, l = threadIdx.x >> 2;
+  const int col = blockIdx.x * 16 + q * 4;
+  float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (col < H) {
+    for (int p = l; p < n_part; p += 64) {
+      const float* src = parts + (int64_t)p * H + col;
+      float4 v;
+      if constexpr (VEC) {
+        v = *(const float4*)src;
+      } else {
+        v.x = src[0];
+        v.y = col + 1 < H ? src[1] : 0.f;
+        v.z = col + 2 < H ? src[2] : 0.f;
+        v.w = col + 3 < H ? src[3] : 0.f;
+      }
+      sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+    }
+  }
+  red[l][q] = sum;
   __syncthreads();
-  if (ps == 0 && col < H) {
-    const float t = ((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl];
-    out[col] = accumulate ? out[col] + t : t;
+#pragma unroll
+  for (int w = 32; w > 0; w >>= 1) {
+    if (l < w) {
+      const float4 a = red[l][q], b = red[l + w][q];
+      red[l][q] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+    }
+    __syncthreads();
+  }
+  if (l == 0 && col < H) {
+    const float4 t = red[0][q];
+    const float tv[4] = {t.x, t.y, t.z, t.w};
+    for (int e = 0; e < 4 && col + e < H; ++e) out[col + e] = accumulate ? out[col + e] + tv[e] : tv[e];
   }
 }
 
 collider_status launch_colsum_parts(const float* parts, int n_part, int H, float* out,
                                     int accumulate, hipStream_t s) {
-  COLLIDER_LAUNCH("colsum_parts", s,
-                  hipLaunchKernelGGL(colsum_parts_kernel, dim3((H + 63) / 64), dim3(256), 0, s,
-                                     parts, n_part, H, out, accumulate));
+  if (H % 4 == 0)
+    COLLIDER_LAUNCH("colsum_parts", s,
+                    hipLaunchKernelGGL(colsum_parts_kernel<true>, dim3((H + 15) / 16), dim3(256), 0,
+                                       s, parts, n_part, H, out, accumulate));
+  else
+    COLLIDER_LAUNCH("colsum_parts", s,
+                    hipLaunchKernelGGL(colsum_parts_kernel<false>, dim3((H + 15) / 16), dim3(256), 0,
+                                       s, parts, n_part, H, out, accumulate));
   return last_hip_status();
 }
 
