@@ -507,6 +507,40 @@ struct TileDMA {
         dma16(rs, lq, off[i] + (uint32_t)((int64_t)k0 * ld * 2), 0u);
     }
   }
+  // load i (< PW) of this wave alone
+  __device__ __forceinline__ void issue_one(int i, rsrc_t rs, int64_t ld, int k0, uint32_t m0,
+                                            int wave) const {
+    const uint32_t lq = m0 + (uint32_t)(wave + 4 * i) * 1024u;
+    if constexpr (KMAJ)
+      dma16(rs, lq, off[i], (uint32_t)k0 * 2u);
+    else
+      dma16(rs, lq, off[i] + (uint32_t)((int64_t)k0 * ld * 2), 0u);
+  }
+};
+
+// The loads of one k-tile (A then B) into the LDS stage at byte m0, one instruction at a time, so
+// that they can be spread between MFMAs: a burst of 1 KB loads from every wavefront would queue at
+// the CU's vector memory unit and stall the wavefronts' MFMA issue behind it.
+template <int BM, int BN, bool AK, bool BKM, int KT>
+struct StageLoader {
+  using TA = TileDMA<BM, AK, KT>;
+  using TB = TileDMA<BN, BKM, KT>;
+  static constexpr int N = TA::PW + TB::PW;
+  const TA& da;
+  const TB& db;
+  rsrc_t ra, rb;
+  int64_t lda, ldb;
+  int ka, kb;  // first reduction index of the k-tile in A's and in the selected B segment's rows
+  uint32_t m0;
+  int wave;
+  bool on;     // false: no k-tile to load
+  __device__ __forceinline__ void issue(int q) const {  // q: a constant after unrolling
+    if (!on) return;
+    if (q < TA::PW)
+      da.issue_one(q, ra, lda, ka, m0, wave);
+    else
+      db.issue_one(q - TA::PW, rb, ldb, kb, m0 + BM * KT * 2, wave);
+  }
 };
 
 // 32x32x16 operand fragment: rows rbase .. rbase+31 (M or N index), k = kk*16 .. +15
@@ -545,18 +579,22 @@ __device__ __forceinline__ void issue_stage(const TileDMA<BM, AK, KT>& da, const
 #define VMCNT_WAIT(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 0xf) | (((n) >> 4) << 14) | (0x7 << 4) | (0xf << 8))
 
-// MFMAs of one k-tile (KT / 16 steps of k = 16) from one LDS stage; fragments of step kk+1 are read
-// while the MFMAs of step kk run (two register sets).
 // Wavefront layout of a BM x BN tile: 2 x 2 wavefronts when BM / 2 is a multiple of 32, else
 // 1 x 4 (BM = 160, 224: each wavefront covers all rows and a quarter of the columns).
 constexpr int wave_rows(int bm) { return (bm % 64 == 0) ? 2 : 1; }
 
-template <int BM, int BN, bool AK, bool BKM, int KT>
+// MFMAs of one k-tile (KT / 16 steps of k = 16) from one LDS stage; fragments of step kk+1 are read
+// while the MFMAs of step kk run (two register sets).  The loads of a later k-tile (`ld`) go out
+// one instruction at a time between the MFMAs, within the first SPN / SPD of them.
+template <int BM, int BN, bool AK, bool BKM, int KT, int SPN, int SPD>
 __device__ __forceinline__ void mma_ktile(
     const char* As, const char* Bs,
-    f32x16 (&acc)[BM / wave_rows(BM) / 32][BN / (4 / wave_rows(BM)) / 32], int wm, int wn, int lane) {
+    f32x16 (&acc)[BM / wave_rows(BM) / 32][BN / (4 / wave_rows(BM)) / 32], int wm, int wn, int lane,
+    const StageLoader<BM, BN, AK, BKM, KT>& ld) {
   constexpr int WGM = wave_rows(BM), WGN = 4 / WGM;
   constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32, KS = KT / 16;
+  constexpr int NQ = StageLoader<BM, BN, AK, BKM, KT>::N, MT = KS * TM * TN;
+  static_assert(MT * SPN >= NQ * SPD && SPN <= SPD, "every load gets an MFMA slot");
   bf16x8 af[2][TM], bfv[2][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i) af[0][i] = read_frag<BM, AK, KT>(As, wm * WM + i * 32, 0, lane);
@@ -577,9 +615,18 @@ __device__ __forceinline__ void mma_ktile(
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < TN; ++j) {
         acc[i][j] =
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfv[cur][j], acc[i][j], 0, 0, 0);
+        const int n = (kk * TM + i) * TN + j;  // MFMA number within the k-tile
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+          if (((q + 1) * MT * SPN) / (NQ * SPD) - 1 == n) {
+            __builtin_amdgcn_sched_barrier(0);
+            ld.issue(q);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -602,6 +649,7 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wavefront blocks of whole 32 x 32 MFMA tiles");
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
   constexpr int LPW = (A_BYTES + B_BYTES) / 1024 / 4;  // load instructions per wave per k-tile
+  static_assert(NS <= 3 && LPW * (NS - 2) < 64, "vmcnt range");
   extern __shared__ __align__(16) char lds[];
 
   const int lane = threadIdx.x & 63;
@@ -682,12 +730,17 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
         VMCNT_WAIT(0);
       }
       __syncthreads();
-      if (kt + NS - 1 < nk)  // refills the stage read in iteration kt-1
-        issue_stage<BM, BN, AK, BKM, KT>(da, db, ra, rb0, rb1, p.lda, p.ldb, kseg, two_seg,
-                                         kbeg + (kt + NS - 1) * BK,
-                                         lds0 + ((kt + NS - 1) % NS) * STAGE, wave);
+      // k-tile kt + NS - 1 refills the stage read in iteration kt - 1; its loads go out between
+      // this k-tile's MFMAs (within the first half with two stages, the first 3/4 with three)
+      const int kn = kbeg + (kt + NS - 1) * BK;
+      const bool seg1 = two_seg && kn >= kseg;
+      const StageLoader<BM, BN, AK, BKM, KT> sl{da, db, ra, seg1 ? rb1 : rb0, p.lda, p.ldb, kn,
+                                                seg1 ? kn - kseg : kn,
+                                                lds0 + ((kt + NS - 1) % NS) * STAGE, wave,
+                                                kt + NS - 1 < nk};
       const char* As = lds + (kt % NS) * STAGE;
-      mma_ktile<BM, BN, AK, BKM, KT>(As, As + A_BYTES, acc, wm, wn, lane);
+      mma_ktile<BM, BN, AK, BKM, KT, (NS == 2 ? 1 : 3), (NS == 2 ? 2 : 4)>(As, As + A_BYTES, acc, wm,
+                                                                        wn, lane, sl);
     }
 
     // epilogue through LDS: the fp32 tile is staged row-major in passes of EROWS rows, then every
