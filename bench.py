@@ -66,8 +66,10 @@ def algorithmic_work(cfg, M_kept, seq_counts):
                       2 * (Mk * (nqkv + I) + (nqkv + I) * H + Mk * H),     # dX (qkv and fc1)
                       2 * Mk * nqkv + 2 * Mk * H + 4 * nqkv * H,           # dW qkv
                       2 * Mk * I + 2 * Mk * H + 4 * I * H]                 # dW fc1
+    scatter_bytes = 2.0 * M_kept * H + 2.0 * cfg.M * H  # kept rows read, every row written
     return {"gemm_flops": gemm_flops, "attn_flops": attn_flops, "attn_dt_flops": attn_dt_flops,
-            "pairs": pairs, "gather_bytes": gather_bytes, "gemm_bytes": float(sum(gemm_bytes)),
+            "pairs": pairs, "gather_bytes": gather_bytes, "scatter_bytes": scatter_bytes,
+            "gemm_bytes": float(sum(gemm_bytes)),
             "gemm_launches": len(gemm_bytes)}
 
 
@@ -274,6 +276,22 @@ def main():
     gemm_ms = sum(prof[k][0] for k in gemm_names) / n_prof
     gemm_launches = sum(prof[k][1] for k in gemm_names) / n_prof
 
+    # context for the gather / scatter rates: a plain device-to-device copy (torch) of the same
+    # byte count on the same GPU, timed the same way
+    def copy_rate(nbytes):
+        n = max(int(nbytes) // 2 // 16 * 16, 16)  # read + write: half the bytes each way
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b_ = torch.empty_like(a)
+        for _ in range(3):
+            b_.copy_(a)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(10):
+            b_.copy_(a)
+        c1.record()
+        c1.synchronize()
+        return 2.0 * n / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
+
     ix = tfb.build_index(keep, B, S)
     cu = ix.cu_seqlens.cpu().numpy()
     seq_counts = [int(cu[b + 1] - cu[b]) for b in range(B)]
@@ -289,6 +307,8 @@ def main():
     attn_tflops = (work["attn_flops"] + work["attn_dt_flops"]) / (attn_ms * 1e-3) / 1e12 if attn_ms else None
     gather_ms = prof.get("gather_rows", (0.0, 1))[0] / n_prof
     gather_gbs = work["gather_bytes"] / (gather_ms * 1e-3) / 1e9 if gather_ms else None
+    scatter_ms = prof.get("scatter_rows", (0.0, 1))[0] / n_prof
+    scatter_gbs = work["scatter_bytes"] / (scatter_ms * 1e-3) / 1e9 if scatter_ms else None
 
     out = {
         "metric": METRIC,
@@ -318,6 +338,10 @@ def main():
         "gemm_tflops": round(gemm_tflops, 1),
         "attn_tflops": None if attn_tflops is None else round(attn_tflops, 1),
         "gather_gbs": None if gather_gbs is None else round(gather_gbs, 1),
+        "scatter_gbs": None if scatter_gbs is None else round(scatter_gbs, 1),
+        "hbm_frac_gather": None if gather_gbs is None else round(gather_gbs / PEAK_HBM_GBS, 4),
+        "hbm_frac_scatter": None if scatter_gbs is None else round(scatter_gbs / PEAK_HBM_GBS, 4),
+        "copy_gbs_same_bytes_as_gather": round(copy_rate(work["gather_bytes"] / max(L, 1)), 1),
         "kernel_ms_per_step": kernels,
         "kernel_ms_per_step_unfiltered": kernels_unf,
         "roofline": {

@@ -884,17 +884,19 @@ int cu_count() {
   return n;
 }
 
-// Tile shapes and the time one workgroup (alone on its CU) spends per 64-deep k-tile on MI355X,
-// in microseconds: 256 x 256 measured at 1.35 us, the others scaled by their flops and their
-// lower MFMA-per-LDS-byte efficiency.
+// Tile shapes and the time one workgroup spends per 64-deep k-tile on MI355X with the whole chip
+// busy, in microseconds, measured on the linear backward's GEMMs: t_k with A K-major (dX: B read
+// through the transposing LDS read), t_mn with both operands token-major (dW: both transposed, so
+// the narrow tiles are bound by LDS bandwidth).  160 / 192 / 224-row tiles (K-major A only) let a
+// ragged token count fill the CUs: with N = 2048, M' = 4916 makes 160 tiles of 256 rows but 248
+// of 160.
 struct TileCfg {
   int bm, bn;
-  double t_iter;
+  double t_k, t_mn;
 };
-// 160 / 192 / 224-row tiles (K-major A only) let a ragged token count fill the CUs: with N = 2048,
-// M' = 4916 makes 160 tiles of 256 rows but 248 of 160.
-constexpr TileCfg kCfgs[] = {{256, 256, 1.35}, {256, 128, 0.80}, {128, 256, 0.80}, {128, 128, 0.62},
-                             {160, 256, 0.94}, {192, 256, 1.07}, {224, 256, 1.31}};
+constexpr TileCfg kCfgs[] = {{256, 256, 1.62, 1.80}, {256, 128, 1.01, 1.45}, {128, 256, 1.14, 1.37},
+                             {128, 128, 0.69, 0.91}, {160, 256, 1.43, 0.0},  {192, 256, 1.44, 0.0},
+                             {224, 256, 1.54, 0.0}};
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
 // Direct-to-LDS pipeline of each tile shape: k-tile depth KT and stage count NS, within the
@@ -950,13 +952,22 @@ Plan make_plan(const GemmProblem& p) {
     const int T = ((p.M + 127) / 128) * ((p.N + 127) / 128);
     return Plan{3, 128, 128, lds, 1, kBK, T, 0, 0, T, 0.0};
   }
+  // tuning override: COLLIDER_GEMM_TILE=<rows>x<cols> restricts the plan to that tile shape
+  // wherever it applies
+  static const int force_tile = [] {
+    const char* e = getenv("COLLIDER_GEMM_TILE");
+    int r = 0, c = 0;
+    return (e && sscanf(e, "%dx%d", &r, &c) == 2) ? r * 1000 + c : 0;
+  }();
   // 256 x 256 only in the direct-to-LDS kernel (staged through registers it would spill)
+  for (int pass = 0; pass < 2 && best.cost >= 1e300; ++pass)  // pass 1: the override does not apply
   for (int c = lds ? 0 : 1; c < kNumCfgs; ++c) {
     if (c >= 4 && !(lds && p.a_kmajor)) continue;  // row counts other than 128 / 256: K-major A
+    if (pass == 0 && force_tile && force_tile != kCfgs[c].bm * 1000 + kCfgs[c].bn) continue;
     const TileCfg tc = kCfgs[c];
     const int kt = lds ? lds_kt(tc.bm, tc.bn) : kBK;
     const int ipt = (p.K + kt - 1) / kt;  // k-tiles per output tile, in the kernel's k-tile depth
-    const double t_it = tc.t_iter * (lds ? 1.0 : 1.5);
+    const double t_it = (p.a_kmajor ? tc.t_k : tc.t_mn) * (lds ? 1.0 : 1.5);
     const int per_cu = (!lds && c == 3) ? 2 : 1;  // LDS-limited residency
     const long tiles = (long)((p.M + tc.bm - 1) / tc.bm) * ((p.N + tc.bn - 1) / tc.bn);
     const double epi_tile = tc.bm * tc.bn * eb / bw_cu, part_tile = tc.bm * tc.bn * 4.0 / bw_cu;
@@ -983,7 +994,7 @@ Plan make_plan(const GemmProblem& p) {
       const double cost = (double)dp / grid * ((double)ipt * kt / kBK * t_it + epi_tile) + per_wg * t_it +
                           (double)sk / grid * epi_tile + 2.0 * part_tile +
                           2.0 * grid * tc.bm * tc.bn * 4.0 / bw + 4.0;
-      if (cost < best.cost * 0.98 || policy == 2)
+      if (cost < best.cost * 0.98)
         best = Plan{c, tc.bm, tc.bn, lds, 1, ipt * kt, (int)dp, (int)sk, ipt, (int)grid, cost};
     }
   }

@@ -11,37 +11,72 @@ namespace collider {
 // ------------------------------------------------------------------------------------------
 // gather: dst[c] = src[idx[c]], several tensors per launch (blockIdx.y = descriptor)
 // ------------------------------------------------------------------------------------------
+// Each workgroup moves up to kChunks 16-byte chunks (64 KB): the row indices of its rows are
+// staged in LDS first, then every thread issues all of its loads before any store, so that many
+// loads are in flight per thread.  One launch covers up to 8 tensors; their workgroups are laid
+// out one tensor after another (blk0[i] = first workgroup of tensor i).
+static constexpr int kPerThread = 16;
+static constexpr int kChunks = 256 * kPerThread;
+
 struct GatherBatch {
   GatherDesc d[8];
+  int blk0[9];
 };
 
-static constexpr int kRowsPerBlock = 16;
+__device__ __forceinline__ int rows_per_block(int per_row) {
+  return per_row >= kChunks ? 1 : kChunks / per_row;
+}
 
 __global__ __launch_bounds__(256) void gather_rows_kernel(GatherBatch batch,
                                                           const int32_t* __restrict__ idx,
                                                           int n_rows) {
-  const GatherDesc& d = batch.d[blockIdx.y];
-  const int r0 = blockIdx.x * kRowsPerBlock;
-  const int nr = min(kRowsPerBlock, n_rows - r0);
-  if (nr <= 0) return;
+  __shared__ int s_row[kChunks];
+  // this workgroup's tensor (constant indices only: a runtime index into the by-value batch
+  // would copy it to scratch memory)
+  GatherDesc d = batch.d[0];
+  int blk0 = 0;
+#pragma unroll
+  for (int k = 1; k < 8; ++k)
+    if ((int)blockIdx.x >= batch.blk0[k]) {
+      d = batch.d[k];
+      blk0 = batch.blk0[k];
+    }
   const int per_row = d.row_vec16;
-  const int items = nr * per_row;
+  const int rpb = rows_per_block(per_row > 0 ? per_row : 1);  // same count as the host's
+  const int r0 = ((int)blockIdx.x - blk0) * rpb;
+  const int nr = min(rpb, n_rows - r0);
+  if (nr <= 0) return;
+  for (int i = threadIdx.x; i < nr; i += 256) s_row[i] = idx[r0 + i];
+  __syncthreads();
   const uint4* __restrict__ src = (const uint4*)d.src;
   uint4* __restrict__ dst = (uint4*)d.dst;
-  for (int i = threadIdx.x; i < items; i += 256) {
-    const int rr = i / per_row, v = i - rr * per_row;
-    const int c = r0 + rr;
-    const int64_t t = idx[c];
-    dst[(int64_t)c * d.ld_dst + v] = src[t * d.ld_src + v];
+  const int items = nr * per_row;
+  for (int base = 0; base < items; base += kChunks) {
+    uint4 v[kPerThread];
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+      const int i = base + threadIdx.x + 256 * u;
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (i < items) {
+        const int rr = i / per_row, c = i - rr * per_row;
+        v[u] = src[(int64_t)s_row[rr] * d.ld_src + c];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+      const int i = base + threadIdx.x + 256 * u;
+      if (i < items) {
+        const int rr = i / per_row, c = i - rr * per_row;
+        dst[(int64_t)(r0 + rr) * d.ld_dst + c] = v[u];
+      }
+    }
   }
   if (d.tail_bytes) {  // 4-byte tail words (row bytes not a multiple of 16)
     const int tw = d.tail_bytes >> 2;
     for (int i = threadIdx.x; i < nr * tw; i += 256) {
       const int rr = i / tw, w = i - rr * tw;
-      const int c = r0 + rr;
-      const int64_t t = idx[c];
-      const uint32_t* s32 = (const uint32_t*)(src + t * d.ld_src + per_row);
-      uint32_t* d32 = (uint32_t*)(dst + (int64_t)c * d.ld_dst + per_row);
+      const uint32_t* s32 = (const uint32_t*)(src + (int64_t)s_row[rr] * d.ld_src + per_row);
+      uint32_t* d32 = (uint32_t*)(dst + (int64_t)(r0 + rr) * d.ld_dst + per_row);
       d32[w] = s32[w];
     }
   }
@@ -51,12 +86,21 @@ collider_status launch_gather_rows(const GatherDesc* d, int n_desc, const int32_
                                    hipStream_t s) {
   if (n_rows <= 0 || n_desc <= 0) return COLLIDER_OK;
   for (int base = 0; base < n_desc; base += 8) {
-    GatherBatch b;
+    GatherBatch b{};
     const int n = n_desc - base < 8 ? n_desc - base : 8;
-    for (int i = 0; i < n; ++i) b.d[i] = d[base + i];
-    dim3 grid((n_rows + kRowsPerBlock - 1) / kRowsPerBlock, n);
+    int blocks = 0;
+    for (int i = 0; i < 9; ++i) b.blk0[i] = 0x7fffffff;
+    for (int i = 0; i < n; ++i) {
+      b.d[i] = d[base + i];
+      const int pr = d[base + i].row_vec16 > 0 ? d[base + i].row_vec16 : 1;
+      const int rpb = pr >= kChunks ? 1 : kChunks / pr;
+      b.blk0[i] = blocks;
+      blocks += (n_rows + rpb - 1) / rpb;
+    }
+    b.blk0[n] = blocks;
     COLLIDER_LAUNCH("gather_rows", s,
-                    hipLaunchKernelGGL(gather_rows_kernel, grid, dim3(256), 0, s, b, idx, n_rows));
+                    hipLaunchKernelGGL(gather_rows_kernel, dim3(blocks), dim3(256), 0, s, b, idx,
+                                       n_rows));
   }
   return last_hip_status();
 }
@@ -94,18 +138,33 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4* __restri
                                                            int64_t ld_dst,
                                                            const int32_t* __restrict__ inv, int M,
                                                            int per_row, int zero_fill) {
-  const int r0 = blockIdx.x * kRowsPerBlock;
-  const int nr = min(kRowsPerBlock, M - r0);
+  __shared__ int s_inv[kChunks];
+  const int rpb = rows_per_block(per_row);
+  const int r0 = blockIdx.x * rpb;
+  const int nr = min(rpb, M - r0);
   if (nr <= 0) return;
+  for (int i = threadIdx.x; i < nr; i += 256) s_inv[i] = inv[r0 + i];
+  __syncthreads();
   const int items = nr * per_row;
-  for (int i = threadIdx.x; i < items; i += 256) {
-    const int rr = i / per_row, v = i - rr * per_row;
-    const int t = r0 + rr;
-    const int c = inv[t];
-    if (c >= 0) {
-      dst[(int64_t)t * ld_dst + v] = src[(int64_t)c * ld_src + v];
-    } else if (zero_fill) {
-      dst[(int64_t)t * ld_dst + v] = make_uint4(0, 0, 0, 0);
+  for (int base = 0; base < items; base += kChunks) {
+    uint4 v[kPerThread];
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+      const int i = base + threadIdx.x + 256 * u;
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (i < items) {
+        const int rr = i / per_row, c = i - rr * per_row;
+        const int ci = s_inv[rr];
+        if (ci >= 0) v[u] = src[(int64_t)ci * ld_src + c];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+      const int i = base + threadIdx.x + 256 * u;
+      if (i < items) {
+        const int rr = i / per_row, c = i - rr * per_row;
+        if (zero_fill || s_inv[rr] >= 0) dst[(int64_t)(r0 + rr) * ld_dst + c] = v[u];
+      }
     }
   }
 }
@@ -128,7 +187,9 @@ collider_status launch_scatter_bytes(const void* src, int64_t ld_src_b, void* ds
   if (M <= 0) return COLLIDER_OK;
   if (row_bytes % 16 == 0 && ld_src_b % 16 == 0 && ld_dst_b % 16 == 0 && aligned16(src) &&
       aligned16(dst)) {
-    dim3 grid((M + kRowsPerBlock - 1) / kRowsPerBlock);
+    const int pr = row_bytes / 16;
+    const int rpb = pr >= kChunks ? 1 : kChunks / pr;
+    dim3 grid((M + rpb - 1) / rpb);
     COLLIDER_LAUNCH("scatter_rows", s,
                     hipLaunchKernelGGL(scatter_rows_kernel, grid, dim3(256), 0, s,
                                        (const uint4*)src, ld_src_b / 16, (uint4*)dst,
@@ -145,6 +206,9 @@ collider_status launch_scatter_bytes(const void* src, int64_t ld_src_b, void* ds
 // ------------------------------------------------------------------------------------------
 // norm recompute: xn[c] = bf16(norm(x[rowmap[c]])), RMSNorm (mean == nullptr) or LayerNorm
 // ------------------------------------------------------------------------------------------
+// One wavefront per row; all of the row's loads are issued before any arithmetic (NV 16-byte
+// vectors per lane, H <= 512 * NV).
+template <int NV>
 __global__ __launch_bounds__(256) void norm_recompute_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ mean, const float* __restrict__ rstd,
     const float* __restrict__ gamma, const float* __restrict__ beta,
@@ -157,8 +221,15 @@ __global__ __launch_bounds__(256) void norm_recompute_kernel(
   const float rs = rstd[r];
   const uint4* xr = (const uint4*)(x + r * H);
   uint4* out = (uint4*)(xn + (int64_t)c * H);
-  for (int v = lane; v < H / 8; v += 64) {
-    const uint4 xv = xr[v];
+  const int nvec = H / 8;
+  uint4 xv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (lane + 64 * i < nvec) xv[i] = xr[lane + 64 * i];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = lane + 64 * i;
+    if (v >= nvec) continue;
     const float4 g0 = ((const float4*)gamma)[2 * v], g1 = ((const float4*)gamma)[2 * v + 1];
     float4 b0 = make_float4(0, 0, 0, 0), b1 = b0;
     if (beta) {
@@ -166,10 +237,10 @@ __global__ __launch_bounds__(256) void norm_recompute_kernel(
       b1 = ((const float4*)beta)[2 * v + 1];
     }
     uint4 o;
-    o.x = pack2bf((bflo(xv.x) - mu) * rs * g0.x + b0.x, (bfhi(xv.x) - mu) * rs * g0.y + b0.y);
-    o.y = pack2bf((bflo(xv.y) - mu) * rs * g0.z + b0.z, (bfhi(xv.y) - mu) * rs * g0.w + b0.w);
-    o.z = pack2bf((bflo(xv.z) - mu) * rs * g1.x + b1.x, (bfhi(xv.z) - mu) * rs * g1.y + b1.y);
-    o.w = pack2bf((bflo(xv.w) - mu) * rs * g1.z + b1.z, (bfhi(xv.w) - mu) * rs * g1.w + b1.w);
+    o.x = pack2bf((bflo(xv[i].x) - mu) * rs * g0.x + b0.x, (bfhi(xv[i].x) - mu) * rs * g0.y + b0.y);
+    o.y = pack2bf((bflo(xv[i].y) - mu) * rs * g0.z + b0.z, (bfhi(xv[i].y) - mu) * rs * g0.w + b0.w);
+    o.z = pack2bf((bflo(xv[i].z) - mu) * rs * g1.x + b1.x, (bfhi(xv[i].z) - mu) * rs * g1.y + b1.y);
+    o.w = pack2bf((bflo(xv[i].w) - mu) * rs * g1.z + b1.z, (bfhi(xv[i].w) - mu) * rs * g1.w + b1.w);
     out[v] = o;
   }
 }
@@ -178,9 +249,20 @@ collider_status launch_norm_recompute(const uint16_t* x, const float* mean, cons
                                       const float* gamma, const float* beta, const int32_t* rowmap,
                                       int rows, int H, uint16_t* xn, hipStream_t s) {
   if (rows <= 0) return COLLIDER_OK;
-  COLLIDER_LAUNCH("norm_recompute", s,
-                  hipLaunchKernelGGL(norm_recompute_kernel, dim3((rows + 3) / 4), dim3(256), 0, s,
-                                     x, mean, rstd, gamma, beta, rowmap, rows, H, xn));
+  const int nv = (H / 8 + 63) / 64;
+  dim3 grid((rows + 3) / 4), block(256);
+#define NR_CASE(N)                                                                             \
+  case N:                                                                                      \
+    COLLIDER_LAUNCH("norm_recompute", s,                                                       \
+                    hipLaunchKernelGGL(norm_recompute_kernel<N>, grid, block, 0, s, x, mean, rstd, \
+                                       gamma, beta, rowmap, rows, H, xn));                     \
+    break;
+  switch (nv) {
+    NR_CASE(1) NR_CASE(2) NR_CASE(3) NR_CASE(4) NR_CASE(5) NR_CASE(6) NR_CASE(7) NR_CASE(8)
+    default:
+      return COLLIDER_ERR_UNSUPPORTED;
+  }
+#undef NR_CASE
   return last_hip_status();
 }
 
@@ -194,11 +276,13 @@ __device__ __forceinline__ float gelu_f(float f) {
   return 0.5f * f * (1.f + fast_tanh(u));
 }
 
+// One wavefront per row, the row's loads issued first in batches of up to 8 vectors per lane.
 __global__ __launch_bounds__(256) void act_recompute_kernel(const uint16_t* __restrict__ g,
                                                             const uint16_t* __restrict__ up,
                                                             const int32_t* __restrict__ rowmap,
                                                             int rows, int I,
                                                             uint16_t* __restrict__ a) {
+  constexpr int NB = 8;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = blockIdx.x * 4 + wave;
   if (c >= rows) return;
@@ -206,21 +290,34 @@ __global__ __launch_bounds__(256) void act_recompute_kernel(const uint16_t* __re
   const uint4* gr = (const uint4*)(g + r * I);
   const uint4* ur = up ? (const uint4*)(up + r * I) : nullptr;
   uint4* out = (uint4*)(a + (int64_t)c * I);
-  for (int v = lane; v < I / 8; v += 64) {
-    const uint4 gv = gr[v];
-    uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-    uint32_t ow[4];
-    if (ur) {
-      const uint4 uv = ur[v];
-      uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
+  const int nvec = I / 8;
+  for (int v0 = lane; v0 < nvec; v0 += 64 * NB) {
+    uint4 gv[NB], uv[NB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        ow[i] = pack2bf(silu_f(bflo(gw[i])) * bflo(uw[i]), silu_f(bfhi(gw[i])) * bfhi(uw[i]));
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ow[i] = pack2bf(gelu_f(bflo(gw[i])), gelu_f(bfhi(gw[i])));
+    for (int b = 0; b < NB; ++b) {
+      const int v = v0 + 64 * b;
+      if (v < nvec) {
+        gv[b] = gr[v];
+        if (ur) uv[b] = ur[v];
+      }
     }
-    out[v] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int v = v0 + 64 * b;
+      if (v >= nvec) continue;
+      const uint32_t gw[4] = {gv[b].x, gv[b].y, gv[b].z, gv[b].w};
+      uint32_t ow[4];
+      if (ur) {
+        const uint32_t uw[4] = {uv[b].x, uv[b].y, uv[b].z, uv[b].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ow[i] = pack2bf(silu_f(bflo(gw[i])) * bflo(uw[i]), silu_f(bfhi(gw[i])) * bfhi(uw[i]));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ow[i] = pack2bf(gelu_f(bflo(gw[i])), gelu_f(bfhi(gw[i])));
+      }
+      out[v] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+    }
   }
 }
 
@@ -247,6 +344,36 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// One row's inputs for one lane: NV 8-element vectors of dxn, x, dres, and the row statistics.
+template <int NV>
+struct NormRow {
+  uint4 d[NV], x[NV], r[NV];
+  float mu, rs;
+};
+
+template <int NV>
+__device__ __forceinline__ void load_norm_row(NormRow<NV>& R, const uint16_t* __restrict__ dxn,
+                                              const uint16_t* __restrict__ dres,
+                                              const uint16_t* __restrict__ x,
+                                              const float* __restrict__ mean,
+                                              const float* __restrict__ rstd,
+                                              const int32_t* __restrict__ rowmap, int c, int H,
+                                              int lane) {
+  const int64_t r = rowmap ? rowmap[c] : c;
+  R.mu = mean ? mean[r] : 0.f;
+  R.rs = rstd[r];
+  const int nvec = H >> 3;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = lane + 64 * i;
+    if (v < nvec) {
+      R.d[i] = ((const uint4*)(dxn + (int64_t)c * H))[v];
+      R.x[i] = ((const uint4*)(x + r * H))[v];
+      R.r[i] = ((const uint4*)(dres + (int64_t)c * H))[v];
+    }
+  }
+}
+
 template <int NV>
 __global__ __launch_bounds__(256) void norm_bwd_kernel(
     const uint16_t* __restrict__ dxn, const uint16_t* __restrict__ dres,
@@ -256,34 +383,42 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(
     int rows_per_part) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nvec = H >> 3;
-  float acc_g[NV][8], acc_b[NV][8];
+  float acc_g[NV][8], acc_b[NV][8], gm[NV][8];
 #pragma unroll
-  for (int i = 0; i < NV; ++i)
+  for (int i = 0; i < NV; ++i) {
+    const int v = lane + 64 * i;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc_g[i][j] = acc_b[i][j] = 0.f;
+    for (int j = 0; j < 8; ++j) acc_g[i][j] = acc_b[i][j] = gm[i][j] = 0.f;
+    if (v < nvec) {
+      const float4 g0 = ((const float4*)gamma)[2 * v], g1 = ((const float4*)gamma)[2 * v + 1];
+      gm[i][0] = g0.x; gm[i][1] = g0.y; gm[i][2] = g0.z; gm[i][3] = g0.w;
+      gm[i][4] = g1.x; gm[i][5] = g1.y; gm[i][6] = g1.z; gm[i][7] = g1.w;
+    }
+  }
   const int c_begin = blockIdx.x * rows_per_part;
   const int c_end = min(rows, c_begin + rows_per_part);
-  for (int c = c_begin + wave; c < c_end; c += 4) {
-    const int64_t r = rowmap ? rowmap[c] : c;
-    const float mu = mean ? mean[r] : 0.f;
-    const float rs = rstd[r];
+  // rows c_begin + wave, + 4, ...: the next row's loads are issued before the current row is
+  // processed
+  NormRow<NV> cur, nxt;
+  int c = c_begin + wave;
+  if (c < c_end) load_norm_row(cur, dxn, dres, x, mean, rstd, rowmap, c, H, lane);
+  for (; c < c_end; c += 4) {
+    if (c + 4 < c_end) load_norm_row(nxt, dxn, dres, x, mean, rstd, rowmap, c + 4, H, lane);
+    const float mu = cur.mu, rs = cur.rs;
     float gv[NV][8], xh[NV][8];
     float s_g = 0.f, s_gx = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int v = lane + 64 * i;
       if (v < nvec) {
-        const uint4 dv = ((const uint4*)(dxn + (int64_t)c * H))[v];
-        const uint4 xv = ((const uint4*)(x + r * H))[v];
-        const float4 g0 = ((const float4*)gamma)[2 * v], g1 = ((const float4*)gamma)[2 * v + 1];
-        const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w}, xw[4] = {xv.x, xv.y, xv.z, xv.w};
-        const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        const uint32_t dw[4] = {cur.d[i].x, cur.d[i].y, cur.d[i].z, cur.d[i].w};
+        const uint32_t xw[4] = {cur.x[i].x, cur.x[i].y, cur.x[i].z, cur.x[i].w};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float d = (j & 1) ? bfhi(dw[j >> 1]) : bflo(dw[j >> 1]);
           const float xx = (j & 1) ? bfhi(xw[j >> 1]) : bflo(xw[j >> 1]);
           xh[i][j] = (xx - mu) * rs;
-          gv[i][j] = d * gm[j];
+          gv[i][j] = d * gm[i][j];
           s_g += gv[i][j];
           s_gx += gv[i][j] * xh[i][j];
           acc_g[i][j] += d * xh[i][j];
@@ -298,8 +433,7 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(
     for (int i = 0; i < NV; ++i) {
       const int v = lane + 64 * i;
       if (v < nvec) {
-        const uint4 rv = ((const uint4*)(dres + (int64_t)c * H))[v];
-        const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
+        const uint32_t rw[4] = {cur.r[i].x, cur.r[i].y, cur.r[i].z, cur.r[i].w};
         uint32_t ow[4];
 #pragma unroll
         for (int j2 = 0; j2 < 4; ++j2) {
@@ -310,6 +444,7 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(
         ((uint4*)(dx + (int64_t)c * H))[v] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
       }
     }
+    cur = nxt;
   }
   // combine the 4 wavefronts' column partials through LDS, in a fixed order
   __shared__ float red[4][512];
@@ -331,8 +466,8 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(
   }
 }
 
-// partial-sum rows of the norm backward (one per workgroup): enough workgroups to fill the CUs
-static constexpr int kNormParts = 1024;
+// partial-sum rows of the norm backward (one per workgroup)
+static constexpr int kNormParts = 256;
 int norm_bwd_parts(int rows) { return rows <= 0 ? 1 : (rows < kNormParts ? rows : kNormParts); }
 
 collider_status launch_norm_bwd(const uint16_t* dxn, const uint16_t* dres, const uint16_t* x,
