@@ -32,7 +32,7 @@ namespace {
 // kernel's events bracket it alone).
 struct Side {
   hipStream_t s = nullptr;
-  hipEvent_t ev[5] = {};
+  hipEvent_t ev[8] = {};
 };
 
 collider_status side_stream(Side** out) {
@@ -216,24 +216,11 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     if (st != COLLIDER_OK) return st;  \
   } while (0)
 
-  if (Mk > 0 && !unf) {
-    // 1. gathers of the saved tensors the dense GEMMs / attention read as compacted operands
-    GatherDesc gd[6];
-    int nd = 0;
-    auto add = [&](const void* src, void* dst, int row_bytes) {
-      gd[nd++] = GatherDesc{src, dst, row_bytes / 16, row_bytes / 16, row_bytes / 16, 0};
-    };
-    if (!dy_compact) add(dy, b.dy_c, H * 2);
-    add(sv->o, b.o_c, nqd * 2);
-    add(sv->q, b.q_c, nqd * 2);
-    add(sv->k, b.k_c, nkvd * 2);
-    add(sv->v, b.v_c, nkvd * 2);
-    add(sv->lse, b.lse_c, nq * 4);
-    CHECK(launch_gather_rows(gd, nd, idx, Mk, s));
-  }
-  // Weight-gradient GEMMs (and the normalised inputs only they read) run on a side stream,
-  // forked from and joined back to the caller's stream with events; the critical path
-  // dA -> dX -> norm bwd -> dO -> attention -> dX -> norm bwd -> scatter stays on `s`.
+  // Weight-gradient GEMMs, the inputs only they read (normalised / activated saved tensors) and
+  // the gathers attention needs later run on a side stream, forked from and joined back to the
+  // caller's stream with events: the memory-bound work there overlaps the dX chain's GEMMs, and
+  // the critical path dA -> dX -> norm bwd -> dO -> attention -> dX -> norm bwd -> scatter stays
+  // on `s`.
   Side* side = nullptr;
   CHECK(side_stream(&side));
   hipStream_t s1 = side ? side->s : s;
@@ -242,6 +229,25 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     if (hipEventRecord(side->ev[e], from) != hipSuccess) return COLLIDER_ERR_HIP;
     return hipStreamWaitEvent(to, side->ev[e], 0) == hipSuccess ? COLLIDER_OK : COLLIDER_ERR_HIP;
   };
+  if (Mk > 0 && !unf && !dy_compact) {  // 1. the upstream gradient's kept rows (dA GEMM operand)
+    GatherDesc gd{dy, b.dy_c, H * 2 / 16, H * 2 / 16, H * 2 / 16, 0};
+    CHECK(launch_gather_rows(&gd, 1, idx, Mk, s));
+  }
+  CHECK(handoff(5, s, s1));  // fork: dY' ready
+  if (Mk > 0 && !unf) {  // 2. saved tensors attention and dW_o read as compacted operands
+    GatherDesc gd[5];
+    int nd = 0;
+    auto add = [&](const void* src, void* dst, int row_bytes) {
+      gd[nd++] = GatherDesc{src, dst, row_bytes / 16, row_bytes / 16, row_bytes / 16, 0};
+    };
+    add(sv->o, b.o_c, nqd * 2);
+    add(sv->q, b.q_c, nqd * 2);
+    add(sv->k, b.k_c, nkvd * 2);
+    add(sv->v, b.v_c, nkvd * 2);
+    add(sv->lse, b.lse_c, nq * 4);
+    CHECK(launch_gather_rows(gd, nd, idx, Mk, s1));
+  }
+  if (side && hipEventRecord(side->ev[6], s1) != hipSuccess) return COLLIDER_ERR_HIP;
   collider_attn_io io{};
   io.q = b.q_c; io.ld_q = nqd;
   io.k = b.k_c; io.ld_k = nkvd;
@@ -254,8 +260,7 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
   io.dv = b.dqkv + nqd + nkvd; io.ld_dv = ldq;
   if (llama) {
     CHECK(launch_act_recompute((const uint16_t*)sv->gate, (const uint16_t*)sv->up, idx, Mk, I,
-                               b.act_c, s));
-    CHECK(handoff(0, s, s1));  // gathered dY', O' and a' ready
+                               b.act_c, s1));
     CHECK(launch_norm_recompute((const uint16_t*)sv->h, nullptr, sv->rstd2, w->gamma2, nullptr, idx,
                                 Mk, H, b.xn_c, s1));
     CHECK(gemm_bf16(g_dw2, b.gemm_ws2, b.gemm_ws2_bytes, s1));
@@ -269,6 +274,7 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     CHECK(handoff(2, s, s1));  // dh ready
     CHECK(gemm_bf16(g_dwo, b.gemm_ws2, b.gemm_ws2_bytes, s1));
     CHECK(gemm_bf16(g_dO, b.gemm_ws, b.gemm_ws_bytes, s));
+    if (side && hipStreamWaitEvent(s, side->ev[6], 0) != hipSuccess) return COLLIDER_ERR_HIP;
     CHECK(attn_bwd(ac, aix, io, b.attn_ws, b.attn_ws_bytes, s));
     CHECK(handoff(3, s, s1));  // [dq|dk|dv] ready
     CHECK(launch_norm_recompute((const uint16_t*)sv->x, nullptr, sv->rstd1, w->gamma1, nullptr, idx,
@@ -279,14 +285,14 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
                           H, b.dx_c, b.part_g, nullptr, parts, s));
     CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dgamma1, c.accumulate, s));
   } else {
-    CHECK(launch_act_recompute((const uint16_t*)sv->f, nullptr, idx, Mk, I, b.act_c, s));
-    CHECK(handoff(0, s, s1));  // gathered dY', O' and gelu(f') ready
+    CHECK(launch_act_recompute((const uint16_t*)sv->f, nullptr, idx, Mk, I, b.act_c, s1));
     CHECK(launch_norm_recompute((const uint16_t*)sv->x, sv->mean, sv->rstd1, w->ln_gamma, w->ln_beta,
                                 idx, Mk, H, b.xn_c, s1));
     CHECK(gemm_bf16(g_dw2, b.gemm_ws2, b.gemm_ws2_bytes, s1));
     CHECK(gemm_bf16(g_dwo, b.gemm_ws2, b.gemm_ws2_bytes, s1));
     CHECK(gemm_bf16(g_dA, b.gemm_ws, b.gemm_ws_bytes, s));
     CHECK(gemm_bf16(g_dO, b.gemm_ws, b.gemm_ws_bytes, s));
+    if (side && hipStreamWaitEvent(s, side->ev[6], 0) != hipSuccess) return COLLIDER_ERR_HIP;
     CHECK(attn_bwd(ac, aix, io, b.attn_ws, b.attn_ws_bytes, s));
     CHECK(handoff(1, s, s1));  // [dq|dk|dv|dF] ready
     CHECK(gemm_bf16(g_dwqkv, b.gemm_ws2, b.gemm_ws2_bytes, s1));

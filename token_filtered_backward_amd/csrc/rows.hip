@@ -51,6 +51,9 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(GatherBatch batch,
   const uint4* __restrict__ src = (const uint4*)d.src;
   uint4* __restrict__ dst = (uint4*)d.dst;
   const int items = nr * per_row;
+  // row / column of a chunk: shift and mask for power-of-two row widths (no integer division)
+  const bool pow2 = per_row > 0 && (per_row & (per_row - 1)) == 0;
+  const int sh = pow2 ? __ffs(per_row) - 1 : 0;
   for (int base = 0; base < items; base += kChunks) {
     uint4 v[kPerThread];
 #pragma unroll
@@ -58,7 +61,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(GatherBatch batch,
       const int i = base + threadIdx.x + 256 * u;
       v[u] = make_uint4(0, 0, 0, 0);
       if (i < items) {
-        const int rr = i / per_row, c = i - rr * per_row;
+        const int rr = pow2 ? i >> sh : i / per_row, c = pow2 ? i & (per_row - 1) : i - rr * per_row;
         v[u] = src[(int64_t)s_row[rr] * d.ld_src + c];
       }
     }
@@ -66,7 +69,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(GatherBatch batch,
     for (int u = 0; u < kPerThread; ++u) {
       const int i = base + threadIdx.x + 256 * u;
       if (i < items) {
-        const int rr = i / per_row, c = i - rr * per_row;
+        const int rr = pow2 ? i >> sh : i / per_row, c = pow2 ? i & (per_row - 1) : i - rr * per_row;
         dst[(int64_t)(r0 + rr) * d.ld_dst + c] = v[u];
       }
     }
@@ -146,6 +149,8 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4* __restri
   for (int i = threadIdx.x; i < nr; i += 256) s_inv[i] = inv[r0 + i];
   __syncthreads();
   const int items = nr * per_row;
+  const bool pow2 = (per_row & (per_row - 1)) == 0;
+  const int sh = pow2 ? __ffs(per_row) - 1 : 0;
   for (int base = 0; base < items; base += kChunks) {
     uint4 v[kPerThread];
 #pragma unroll
@@ -153,7 +158,7 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4* __restri
       const int i = base + threadIdx.x + 256 * u;
       v[u] = make_uint4(0, 0, 0, 0);
       if (i < items) {
-        const int rr = i / per_row, c = i - rr * per_row;
+        const int rr = pow2 ? i >> sh : i / per_row, c = pow2 ? i & (per_row - 1) : i - rr * per_row;
         const int ci = s_inv[rr];
         if (ci >= 0) v[u] = src[(int64_t)ci * ld_src + c];
       }
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4* __restri
     for (int u = 0; u < kPerThread; ++u) {
       const int i = base + threadIdx.x + 256 * u;
       if (i < items) {
-        const int rr = i / per_row, c = i - rr * per_row;
+        const int rr = pow2 ? i >> sh : i / per_row, c = pow2 ? i & (per_row - 1) : i - rr * per_row;
         if (zero_fill || s_inv[rr] >= 0) dst[(int64_t)(r0 + rr) * ld_dst + c] = v[u];
       }
     }
