@@ -136,6 +136,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfiltered", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch every kernel eagerly each step")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a plain copy of "
                          "known size, to calibrate HBM byte counters in a profiler run)")
@@ -191,10 +192,12 @@ def main():
         # the bottom layer scatters dx to the full token layout.
         gc = [tfb.make_grads(lcfg, M, ix0.M_kept, dev, dx_compact=True) for _ in range(2)]
 
-    def step_filtered():
-        ix = tfb.build_index(keep, B, S)
+    ixp = tfb.build_index(keep, B, S)  # index buffers reused every step
+
+    def step_filtered(graph=False):
+        ix = tfb.build_index(keep, B, S, out=ixp)
         if L == 1:
-            lb(weights, saved, dy, ix, grads)
+            lb(weights, saved, dy, ix, grads, graph=graph)
             return
         lb(weights, saved, dy, ix, gc[0], dx_compact=True)
         for layer in range(1, L - 1):
@@ -207,7 +210,10 @@ def main():
     uix = tfb.dense_index(B, S)
     ugrads = [tfb.make_grads(ucfg, M, M, dev) for _ in range(2 if L > 1 else 1)]
 
-    def step_unfiltered():
+    def step_unfiltered(graph=False):
+        if L == 1:
+            ub(weights, saved, dy, uix, ugrads[0], graph=graph)
+            return
         ub(weights, saved, dy, uix, ugrads[0])
         for layer in range(1, L):
             ub(weights, saved, ugrads[(layer - 1) % 2]["dx"], uix, ugrads[layer % 2])
@@ -243,13 +249,27 @@ def main():
             cold.append(e0.elapsed_time(e1))
         return warm, float(np.median(cold))
 
-    log(f"[bench] timing filtered step: warmup {args.warmup}, steps {args.steps}")
-    ms_f, ms_f_cold = timed(step_filtered, args.steps, args.warmup)
-    log(f"[bench] filtered: {ms_f:.3f} ms/step (cold median {ms_f_cold:.3f})")
-    ms_u = ms_u_cold = None
+    # Each path is timed with eager launches and as a replayed HIP graph of the layer (one launch;
+    # the index is rebuilt in place and waited for every step, and top-k keeps the kept count
+    # fixed).  Each path is reported in its faster mode, so the speedup never rests on a slower
+    # baseline.
+    graph = L == 1 and not args.no_graph
+
+    def best_of(step, label):
+        warm_e, cold_e = timed(step, args.steps, args.warmup)
+        res = {"eager": (warm_e, cold_e)}
+        if graph:
+            res["graph"] = timed(lambda: step(True), args.steps, args.warmup)
+        for mode, (w_, c_) in res.items():
+            log(f"[bench] {label}, {mode}: {w_:.3f} ms/step (cold median {c_:.3f})")
+        mode = min(res, key=lambda m: res[m][0])
+        return res[mode][0], res[mode][1], mode, {m: round(v[0], 4) for m, v in res.items()}
+
+    log(f"[bench] timing: warmup {args.warmup}, steps {args.steps}")
+    ms_f, ms_f_cold, mode_f, modes_f = best_of(step_filtered, "filtered")
+    ms_u = ms_u_cold = mode_u = modes_u = None
     if not args.no_unfiltered:
-        ms_u, ms_u_cold = timed(step_unfiltered, args.steps, args.warmup)
-        log(f"[bench] unfiltered: {ms_u:.3f} ms/step (cold median {ms_u_cold:.3f})")
+        ms_u, ms_u_cold, mode_u, modes_u = best_of(step_unfiltered, "unfiltered")
 
     # per-kernel durations from HIP events recorded by the library on its launch stream
     n_prof = max(3, min(args.steps, 10))
@@ -329,6 +349,8 @@ def main():
                    "layers": L,
                    "B": B, "S": S, "hidden": cfg.H, "heads": f"{cfg.nq}/{cfg.nkv}x{cfg.d}",
                    "inter": cfg.I, "M": M, "M_kept": ix.M_kept, "parallelism": "single GPU"},
+        "launch_mode": {"filtered": mode_f, "unfiltered": mode_u},
+        "ms_by_launch_mode": {"filtered": modes_f, "unfiltered": modes_u},
         "ms_filtered_cold": round(ms_f_cold, 4),
         "ms_unfiltered": None if ms_u is None else round(ms_u, 4),
         "ms_unfiltered_cold": None if ms_u_cold is None else round(ms_u_cold, 4),

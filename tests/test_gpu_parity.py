@@ -371,6 +371,45 @@ def test_stack_of_layers(name):
     assert np.all(to64(outs[-1]["dx"])[keep == 0] == 0.0)
 
 
+@pytest.mark.parametrize("name", ["small_llama", "small_phi"])
+def test_layer_graph_replay_matches_eager(name):
+    """The layer recorded into a HIP graph and replayed gives the eager result bit for bit, on every
+    replay, with eager work and synchronisation between replays and with a new mask of the same
+    kept count rebuilt in place."""
+    cfg = synth.get_config(name)
+    inp = synth.make_layer_inputs(cfg, r_pct=40)
+    weights, saved, dy = _upload_layer(inp)
+    lcfg = tfb.layer_cfg(cfg)
+    keep1 = inp["keep"]
+    keep2 = synth.make_keep(cfg.M, 40, 77)  # another mask, same kept count
+    assert keep1.sum() == keep2.sum()
+
+    def eager(keep):
+        ix = tfb.build_index(_dev_keep(keep), cfg.B, cfg.S)
+        g = tfb.make_grads(lcfg, cfg.M, ix.M_kept, "cuda")
+        tfb.LayerBackward(lcfg, cfg.B, cfg.S, "cuda")(weights, saved, dy, ix, g)
+        torch.cuda.synchronize()
+        return {k: v.clone() for k, v in g.items()}
+
+    ref1, ref2 = eager(keep1), eager(keep2)
+    lb = tfb.LayerBackward(lcfg, cfg.B, cfg.S, "cuda")
+    ix = tfb.build_index(_dev_keep(keep1), cfg.B, cfg.S)
+    grads = tfb.make_grads(lcfg, cfg.M, ix.M_kept, "cuda")
+    junk = torch.zeros(1 << 20, device="cuda")
+    for rep, (keep, ref) in enumerate([(keep1, ref1), (keep1, ref1), (keep2, ref2), (keep1, ref1)]):
+        ix = tfb.build_index(_dev_keep(keep), cfg.B, cfg.S, out=ix)
+        for gt in grads.values():
+            gt.fill_(float("nan"))
+        lb(weights, saved, dy, ix, grads, graph=True)
+        junk.add_(1.0)  # eager work between replays
+        torch.cuda.synchronize()
+        for k in ref:
+            a, b = grads[k], ref[k]
+            same = torch.equal(a.view(torch.int16), b.view(torch.int16)) if a.dtype == torch.bfloat16 \
+                else torch.equal(a, b)
+            assert same, (rep, k)
+
+
 def test_layer_repeat_is_deterministic():
     cfg = synth.get_config("small_llama")
     inp = synth.make_layer_inputs(cfg)

@@ -271,16 +271,23 @@ class Index:
                          self.count.data_ptr(), self.B, self.S, self.M_kept)
 
 
-def build_index(keep: torch.Tensor, B: int, S: int, stream=None) -> Index:
-    """Compact a [B*S] uint8 keep mask on the device; waits once for the kept count."""
+def build_index(keep: torch.Tensor, B: int, S: int, stream=None, out: "Index" = None) -> Index:
+    """Compact a [B*S] uint8 keep mask on the device; waits once for the kept count.  With `out`
+    the index is rebuilt in that index's buffers (same addresses every step)."""
     dev = keep.device
     M = B * S
-    idx = torch.empty(M, dtype=torch.int32, device=dev)
-    inv = torch.empty(M, dtype=torch.int32, device=dev)
-    cu = torch.empty(B + 1, dtype=torch.int32, device=dev)
-    count = torch.empty(1, dtype=torch.int32, device=dev)
+    if out is not None and out.B == B and out.S == S and out.idx.numel() == M:
+        idx, inv, cu, count = out.idx, out.inv, out.cu_seqlens, out.count
+    else:
+        idx = torch.empty(M, dtype=torch.int32, device=dev)
+        inv = torch.empty(M, dtype=torch.int32, device=dev)
+        cu = torch.empty(B + 1, dtype=torch.int32, device=dev)
+        count = torch.empty(1, dtype=torch.int32, device=dev)
     collider_build_index(keep, B, S, idx, inv, cu, count, stream)
     mk = collider_index_count_host(count, stream)
+    if out is not None and out.idx is idx:
+        out.M_kept = mk
+        return out
     return Index(idx, inv, cu, count, B, S, mk)
 
 
@@ -332,11 +339,43 @@ class LayerBackward:
             self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self.ws
 
+    def _args(self, weights, saved, dy, index, grads, dy_compact, dx_compact):
+        """ctypes arguments of one call, reused while every pointer stays the same (building the
+        structures costs more host time than the library's launches)."""
+        key = (tuple(t.data_ptr() for t in weights.values()), tuple(saved.keys()),
+               tuple(t.data_ptr() for t in saved.values()), tuple(grads.keys()),
+               tuple(t.data_ptr() for t in grads.values()), dy.data_ptr(), index.idx.data_ptr(),
+               index.M_kept, bool(dy_compact), bool(dx_compact), tuple(weights.keys()))
+        if getattr(self, "_key", None) != key:
+            ws = self.workspace(index.M_kept)
+            self._key = key
+            self._cargs = (ctypes.byref(self.cfg), ctypes.byref(_struct(LayerWeights, weights)),
+                           ctypes.byref(_struct(LayerSaved, saved)), ctypes.c_void_p(dy.data_ptr()),
+                           int(dy_compact), ctypes.byref(index.c()),
+                           ctypes.byref(_struct(LayerGrads, grads)), int(dx_compact),
+                           ctypes.c_void_p(ws.data_ptr()), ws.numel())
+        return self._cargs
+
     def __call__(self, weights: dict, saved: dict, dy, index: Index, grads: dict, dy_compact=False,
-                 dx_compact=False, stream=None):
-        ws = self.workspace(index.M_kept)
-        collider_layer_bwd(self.cfg, _struct(LayerWeights, weights), _struct(LayerSaved, saved), dy,
-                           dy_compact, index.c(), _struct(LayerGrads, grads), dx_compact, ws, stream)
+                 dx_compact=False, stream=None, graph=False):
+        """graph=True records the call into a HIP graph on first use and replays it while every
+        pointer and the kept count stay the same (one launch instead of the layer's ~30; with
+        top-k selection the kept count is the same every step).  The index buffers must then be
+        reused across steps (build_index(..., out=index))."""
+        args = self._args(weights, saved, dy, index, grads, dy_compact, dx_compact)
+        if not graph:
+            _check(lib().collider_layer_bwd(*args, _stream(stream)), "collider_layer_bwd")
+            return grads
+        if getattr(self, "_graph_key", None) != self._key:
+            # one eager call first: the library's one-time set-up (side stream, kernel attributes)
+            # must not happen inside the capture
+            _check(lib().collider_layer_bwd(*args, _stream(stream)), "collider_layer_bwd")
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                _check(lib().collider_layer_bwd(*args, _stream()), "collider_layer_bwd")
+            self._graph, self._graph_key = g, self._key
+        self._graph.replay()
         return grads
 
 

@@ -22,6 +22,8 @@
 // transpose reads per fragment follows the 32x32 accumulator layout (rows 8*(r/4) + 4*(lane/32) +
 // r%4), so the P / dS registers feed the MFMA without any data movement.  The next tile is fetched
 // into registers while the MFMAs of the current one run (two LDS buffers, one barrier per tile).
+#include <cstdlib>
+
 #include "internal.h"
 
 namespace collider {
@@ -525,12 +527,20 @@ __global__ __launch_bounds__(256) void attn_dkv_finalize_kernel(AttnParams p) {
 // ------------------------------------------------------------------------------------------
 // host side
 // ------------------------------------------------------------------------------------------
+// Head slices of the dK / dV kernel: the fewest that give `target` workgroups (each slice adds a
+// partial dK / dV buffer the finalize kernel reads back).  COLLIDER_ATTN_MIN_WG overrides the
+// target (tuning).
 static int choose_hs(const collider_attn_cfg& c, int B, int M_kept) {
+  static const long target = [] {
+    const char* e = getenv("COLLIDER_ATTN_MIN_WG");
+    const long v = e ? atol(e) : 0;
+    return v > 0 ? v : 1024L;
+  }();
   const int G = c.n_q_heads / c.n_kv_heads;
   const long kblocks = (long)(M_kept + 127) / 128 + B;
   for (int hs = 1; hs <= G; ++hs) {
     if (G % hs) continue;
-    if (kblocks * c.n_kv_heads * hs >= 1024) return hs;
+    if (kblocks * c.n_kv_heads * hs >= target) return hs;
   }
   return G;
 }

@@ -870,6 +870,20 @@ constexpr int kMaxDevices = 64;
 
 std::atomic<int> g_policy{0};
 
+// Raises a kernel's dynamic-LDS limit once per device (the call costs microseconds of host time,
+// and every launch would otherwise repeat it).
+void set_lds_limit_once(const void* kern, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    return;
+  }
+  const uint64_t bit = 1ull << dev;
+  if (done.load(std::memory_order_acquire) & bit) return;
+  if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess)
+    done.fetch_or(bit, std::memory_order_acq_rel);
+}
+
 // Compute units of the current device, read once per device.
 int cu_count() {
   static std::atomic<int> cache[kMaxDevices];
@@ -1013,7 +1027,8 @@ collider_status launch_lds(const GemmParams& gp, int grid, const char* name, hip
   const size_t lds = (size_t)NS * (BM + BN) * KT * sizeof(uint16_t);
   static_assert(NS * (BM + BN) * KT * 2 <= 160 * 1024, "LDS budget");
   auto kern = gemm_lds_kernel<BM, BN, KT, AK, BKM, EPI, NS>;
-  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static std::atomic<uint64_t> attr_set{0};  // devices whose LDS limit is raised for this kernel
+  set_lds_limit_once((const void*)kern, (int)lds, attr_set);
   COLLIDER_LAUNCH(name, s, hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, gp));
   collider_status st = last_hip_status();
   if (st != COLLIDER_OK || gp.sk_tiles == 0) return st;
@@ -1028,7 +1043,8 @@ collider_status launch_one(const GemmParams& gp, const char* name, hipStream_t s
   const int total = gp.tiles_m * gp.tiles_n * gp.splits;
   const size_t lds = 2 * (size_t)(BM + BN) * (kBK + 8) * sizeof(uint16_t);
   auto kern = gemm_bf16_kernel<BM, BN, kBK, AK, BKM, EPI>;
-  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static std::atomic<uint64_t> attr_set{0};
+  set_lds_limit_once((const void*)kern, (int)lds, attr_set);
   COLLIDER_LAUNCH(name, s, hipLaunchKernelGGL(kern, dim3(total), dim3(256), lds, s, gp));
   return last_hip_status();
 }

@@ -349,37 +349,7 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// One row's inputs for one lane: NV 8-element vectors of dxn, x, dres, and the row statistics.
-template <int NV>
-struct NormRow {
-  uint4 d[NV], x[NV], r[NV];
-  float mu, rs;
-};
-
-template <int NV>
-__device__ __forceinline__ void load_norm_row(NormRow<NV>& R, const uint16_t* __restrict__ dxn,
-                                              const uint16_t* __restrict__ dres,
-                                              const uint16_t* __restrict__ x,
-                                              const float* __restrict__ mean,
-                                              const float* __restrict__ rstd,
-                                              const int32_t* __restrict__ rowmap, int c, int H,
-                                              int lane) {
-  const int64_t r = rowmap ? rowmap[c] : c;
-  R.mu = mean ? mean[r] : 0.f;
-  R.rs = rstd[r];
-  const int nvec = H >> 3;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int v = lane + 64 * i;
-    if (v < nvec) {
-      R.d[i] = ((const uint4*)(dxn + (int64_t)c * H))[v];
-      R.x[i] = ((const uint4*)(x + r * H))[v];
-      R.r[i] = ((const uint4*)(dres + (int64_t)c * H))[v];
-    }
-  }
-}
-
-template <int NV>
+template <int NV, bool LN>
 __global__ __launch_bounds__(256) void norm_bwd_kernel(
     const uint16_t* __restrict__ dxn, const uint16_t* __restrict__ dres,
     const uint16_t* __restrict__ x, const float* __restrict__ mean, const float* __restrict__ rstd,
@@ -388,46 +358,49 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(
     int rows_per_part) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nvec = H >> 3;
-  float acc_g[NV][8], acc_b[NV][8], gm[NV][8];
+  float acc_g[NV][8], acc_b[NV][8];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int v = lane + 64 * i;
+  for (int i = 0; i < NV; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc_g[i][j] = acc_b[i][j] = gm[i][j] = 0.f;
-    if (v < nvec) {
-      const float4 g0 = ((const float4*)gamma)[2 * v], g1 = ((const float4*)gamma)[2 * v + 1];
-      gm[i][0] = g0.x; gm[i][1] = g0.y; gm[i][2] = g0.z; gm[i][3] = g0.w;
-      gm[i][4] = g1.x; gm[i][5] = g1.y; gm[i][6] = g1.z; gm[i][7] = g1.w;
-    }
-  }
+    for (int j = 0; j < 8; ++j) acc_g[i][j] = acc_b[i][j] = 0.f;
   const int c_begin = blockIdx.x * rows_per_part;
   const int c_end = min(rows, c_begin + rows_per_part);
-  // rows c_begin + wave, + 4, ...: the next row's loads are issued before the current row is
-  // processed
-  NormRow<NV> cur, nxt;
-  int c = c_begin + wave;
-  if (c < c_end) load_norm_row(cur, dxn, dres, x, mean, rstd, rowmap, c, H, lane);
-  for (; c < c_end; c += 4) {
-    if (c + 4 < c_end) load_norm_row(nxt, dxn, dres, x, mean, rstd, rowmap, c + 4, H, lane);
-    const float mu = cur.mu, rs = cur.rs;
-    float gv[NV][8], xh[NV][8];
+  // few registers (the row's three inputs stay packed; gamma and x-hat are re-derived in the
+  // second sweep) so that many wavefronts per SIMD hide the loads' latency; all of a row's loads
+  // are issued together
+#pragma unroll 1
+  for (int c = c_begin + wave; c < c_end; c += 4) {
+    const int64_t r = rowmap ? rowmap[c] : c;
+    const float mu = mean ? mean[r] : 0.f;
+    const float rs = rstd[r];
+    uint4 dv[NV], xv[NV], rv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int v = lane + 64 * i;
+      if (v < nvec) {
+        dv[i] = ((const uint4*)(dxn + (int64_t)c * H))[v];
+        xv[i] = ((const uint4*)(x + r * H))[v];
+        rv[i] = ((const uint4*)(dres + (int64_t)c * H))[v];
+      }
+    }
     float s_g = 0.f, s_gx = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int v = lane + 64 * i;
       if (v < nvec) {
-        const uint32_t dw[4] = {cur.d[i].x, cur.d[i].y, cur.d[i].z, cur.d[i].w};
-        const uint32_t xw[4] = {cur.x[i].x, cur.x[i].y, cur.x[i].z, cur.x[i].w};
+        const float4 g0 = ((const float4*)gamma)[2 * v], g1 = ((const float4*)gamma)[2 * v + 1];
+        const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        const uint32_t dw[4] = {dv[i].x, dv[i].y, dv[i].z, dv[i].w};
+        const uint32_t xw[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float d = (j & 1) ? bfhi(dw[j >> 1]) : bflo(dw[j >> 1]);
-          const float xx = (j & 1) ? bfhi(xw[j >> 1]) : bflo(xw[j >> 1]);
-          xh[i][j] = (xx - mu) * rs;
-          gv[i][j] = d * gm[i][j];
-          s_g += gv[i][j];
-          s_gx += gv[i][j] * xh[i][j];
-          acc_g[i][j] += d * xh[i][j];
-          acc_b[i][j] += d;
+          const float xh = (((j & 1) ? bfhi(xw[j >> 1]) : bflo(xw[j >> 1])) - mu) * rs;
+          const float gv = d * gm[j];
+          s_g += gv;
+          s_gx += gv * xh;
+          acc_g[i][j] += d * xh;
+          if constexpr (LN) acc_b[i][j] += d;
         }
       }
     }
@@ -438,23 +411,30 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(
     for (int i = 0; i < NV; ++i) {
       const int v = lane + 64 * i;
       if (v < nvec) {
-        const uint32_t rw[4] = {cur.r[i].x, cur.r[i].y, cur.r[i].z, cur.r[i].w};
+        const float4 g0 = ((const float4*)gamma)[2 * v], g1 = ((const float4*)gamma)[2 * v + 1];
+        const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        const uint32_t dw[4] = {dv[i].x, dv[i].y, dv[i].z, dv[i].w};
+        const uint32_t xw[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+        const uint32_t rw[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
         uint32_t ow[4];
 #pragma unroll
         for (int j2 = 0; j2 < 4; ++j2) {
-          const float a0 = bflo(rw[j2]) + rs * (gv[i][2 * j2] - s_g - xh[i][2 * j2] * s_gx);
-          const float a1 = bfhi(rw[j2]) + rs * (gv[i][2 * j2 + 1] - s_g - xh[i][2 * j2 + 1] * s_gx);
+          const float g_a = bflo(dw[j2]) * gm[2 * j2], g_b = bfhi(dw[j2]) * gm[2 * j2 + 1];
+          const float x_a = (bflo(xw[j2]) - mu) * rs, x_b = (bfhi(xw[j2]) - mu) * rs;
+          const float a0 = bflo(rw[j2]) + rs * (g_a - s_g - x_a * s_gx);
+          const float a1 = bfhi(rw[j2]) + rs * (g_b - s_g - x_b * s_gx);
           ow[j2] = pack2bf(a0, a1);
         }
         ((uint4*)(dx + (int64_t)c * H))[v] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
       }
     }
-    cur = nxt;
   }
   // combine the 4 wavefronts' column partials through LDS, in a fixed order
   __shared__ float red[4][512];
+#pragma unroll
   for (int i = 0; i < NV; ++i) {
-    for (int which = 0; which < (part_dbeta ? 2 : 1); ++which) {
+#pragma unroll
+    for (int which = 0; which < (LN ? 2 : 1); ++which) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) red[wave][lane * 8 + j] = which ? acc_b[i][j] : acc_g[i][j];
       __syncthreads();
@@ -471,8 +451,8 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(
   }
 }
 
-// partial-sum rows of the norm backward (one per workgroup)
-static constexpr int kNormParts = 256;
+// partial-sum rows of the norm backward (one per workgroup): enough workgroups to fill the CUs
+static constexpr int kNormParts = 1024;
 int norm_bwd_parts(int rows) { return rows <= 0 ? 1 : (rows < kNormParts ? rows : kNormParts); }
 
 collider_status launch_norm_bwd(const uint16_t* dxn, const uint16_t* dres, const uint16_t* x,
@@ -484,10 +464,16 @@ collider_status launch_norm_bwd(const uint16_t* dxn, const uint16_t* dres, const
   dim3 grid(n_part), block(256);
 #define NB_CASE(N)                                                                              \
   case N:                                                                                       \
-    COLLIDER_LAUNCH("norm_bwd", s,                                                              \
-                    hipLaunchKernelGGL(norm_bwd_kernel<N>, grid, block, 0, s, dxn, dres, x, mean, \
-                                       rstd, gamma, rowmap, rows, H, dx, part_dgamma,           \
-                                       part_dbeta, rpp));                                       \
+    if (part_dbeta)                                                                             \
+      COLLIDER_LAUNCH("norm_bwd", s,                                                            \
+                      hipLaunchKernelGGL((norm_bwd_kernel<N, true>), grid, block, 0, s, dxn, dres, \
+                                         x, mean, rstd, gamma, rowmap, rows, H, dx, part_dgamma, \
+                                         part_dbeta, rpp));                                     \
+    else                                                                                        \
+      COLLIDER_LAUNCH("norm_bwd", s,                                                            \
+                      hipLaunchKernelGGL((norm_bwd_kernel<N, false>), grid, block, 0, s, dxn,   \
+                                         dres, x, mean, rstd, gamma, rowmap, rows, H, dx,       \
+                                         part_dgamma, part_dbeta, rpp));                        \
     break;
   switch (nv) {
     NB_CASE(1) NB_CASE(2) NB_CASE(3) NB_CASE(4) NB_CASE(5) NB_CASE(6) NB_CASE(7) NB_CASE(8)
