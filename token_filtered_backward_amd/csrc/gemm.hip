@@ -457,13 +457,34 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 }
 
 
-// 16-byte buffer load of each lane straight into LDS (M0 = LDS base of the wave, lane i lands at
-// M0 + 16*i; address = base + voff + soff).  Issued as inline assembly: the compiler then inserts no
-// waits for it of its own (it cannot tell which LDS bytes the copy writes and would wait for every
-// outstanding load at each LDS read); completion is tracked explicitly with s_waitcnt vmcnt in the
-// k-loop.
+// Where one operand's k-tile comes from: a buffer resource and a scalar byte offset.  K-major
+// operands keep the whole buffer and take the k offset as the scalar offset; their rows, which the
+// range check must see, are in the per-lane vector offsets.  MN-major operands (whose rows are k)
+// instead advance the resource's base to the k-tile's first row and shorten its range by as much,
+// so the per-lane offsets stay fixed and rows past the end still read as zeros.  Both cost a few
+// scalar instructions per k-tile and none per load.
+struct KSrc {
+  rsrc_t rs;
+  uint32_t soff;
+};
+template <bool KMAJ>
+__device__ __forceinline__ KSrc ktile_src(const void* base, uint32_t bytes, int64_t ld, int k0) {
+  if constexpr (KMAJ) {
+    return KSrc{make_rsrc(base, bytes), (uint32_t)k0 * 2u};
+  } else {
+    const uint64_t adv = (uint64_t)k0 * (uint64_t)ld * 2u;
+    return KSrc{make_rsrc((const char*)base + adv, adv < bytes ? bytes - (uint32_t)adv : 0u), 0u};
+  }
+}
+
+// 16-byte buffer load of each lane straight into LDS (M0 = LDS byte address of the wavefront's
+// 1 KB slot, lane i lands at M0 + 16 i; global address = base + voff + soff).  Issued as inline
+// assembly: the compiler then inserts no waits of its own (it cannot tell which LDS bytes the copy
+// writes and would wait for every outstanding load at each LDS read); completion is tracked
+// explicitly with s_waitcnt vmcnt in the k-loop.  An LDS-DMA load reads M0 one wait state after a
+// scalar write of M0 at the earliest on this GPU family, hence the s_nop between the two.
 __device__ __forceinline__ void dma16(rsrc_t rs, uint32_t m0, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "s"(m0), "v"(voff), "s"(rs), "s"(soff)
                : "memory", "m0");
@@ -471,10 +492,8 @@ __device__ __forceinline__ void dma16(rsrc_t rs, uint32_t m0, uint32_t voff, uin
 
 // Direct loads of one operand tile, [R x KT] (K-major) or [KT x R] (MN-major) in LDS.  Wave w
 // issues loads q = w, w + 4, ...; load q fills LDS bytes [1024 q, 1024 q + 1024) of the tile.  The
-// per-lane byte offsets are computed once per output tile.  K-major: the k offset of a k-tile goes
-// into the scalar offset, and the vector offset holds the row part, which alone decides whether the
-// range check zero-fills a row past the end of the operand.  MN-major: rows are k, so the k offset
-// goes into the vector offset.
+// per-lane byte offsets (relative to the k-tile's source, see ktile_src) are computed once per
+// output tile.
 template <int R, bool KMAJ, int KT>
 struct TileDMA {
   static constexpr int NI = R * KT * 2 / 1024, PW = NI / 4;
@@ -496,31 +515,16 @@ struct TileDMA {
       }
     }
   }
-  // the k-tile starting at reduction index k0 of this buffer, into the LDS tile at byte m0
-  __device__ __forceinline__ void issue(rsrc_t rs, int64_t ld, int k0, uint32_t m0, int wave) const {
-#pragma unroll
-    for (int i = 0; i < PW; ++i) {
-      const uint32_t lq = m0 + (uint32_t)(wave + 4 * i) * 1024u;
-      if constexpr (KMAJ)
-        dma16(rs, lq, off[i], (uint32_t)k0 * 2u);
-      else
-        dma16(rs, lq, off[i] + (uint32_t)((int64_t)k0 * ld * 2), 0u);
-    }
-  }
-  // load i (< PW) of this wave alone
-  __device__ __forceinline__ void issue_one(int i, rsrc_t rs, int64_t ld, int k0, uint32_t m0,
-                                            int wave) const {
-    const uint32_t lq = m0 + (uint32_t)(wave + 4 * i) * 1024u;
-    if constexpr (KMAJ)
-      dma16(rs, lq, off[i], (uint32_t)k0 * 2u);
-    else
-      dma16(rs, lq, off[i] + (uint32_t)((int64_t)k0 * ld * 2), 0u);
+  // load I (< PW) of this wave; mw = LDS byte address of the wave's first slot in the tile
+  template <int I>
+  __device__ __forceinline__ void issue_one(const KSrc& s, uint32_t mw) const {
+    dma16(s.rs, mw + (uint32_t)I * 4096u, off[I], s.soff);
   }
 };
 
-// The loads of one k-tile (A then B) into the LDS stage at byte m0, one instruction at a time, so
-// that they can be spread between MFMAs: a burst of 1 KB loads from every wavefront would queue at
-// the CU's vector memory unit and stall the wavefronts' MFMA issue behind it.
+// The loads of one k-tile (A then B) into an LDS stage, one instruction at a time, so that they can
+// be spread between MFMAs: a burst of 1 KB loads from every wavefront would queue at the CU's vector
+// memory unit and stall the wavefronts' MFMA issue behind it.
 template <int BM, int BN, bool AK, bool BKM, int KT>
 struct StageLoader {
   using TA = TileDMA<BM, AK, KT>;
@@ -528,52 +532,78 @@ struct StageLoader {
   static constexpr int N = TA::PW + TB::PW;
   const TA& da;
   const TB& db;
-  rsrc_t ra, rb;
-  int64_t lda, ldb;
-  int ka, kb;  // first reduction index of the k-tile in A's and in the selected B segment's rows
-  uint32_t m0;
-  int wave;
-  bool on;     // false: no k-tile to load
-  __device__ __forceinline__ void issue(int q) const {  // q: a constant after unrolling
-    if (!on) return;
-    if (q < TA::PW)
-      da.issue_one(q, ra, lda, ka, m0, wave);
-    else
-      db.issue_one(q - TA::PW, rb, ldb, kb, m0 + BM * KT * 2, wave);
+  KSrc a, b;
+  uint32_t ma, mb;  // LDS byte address of this wavefront's first slot in the A / B tile
+  // load q of the k-tile; q is a constant once the caller's loops are unrolled, and the chain of
+  // comparisons folds to the one load
+  template <int Q = 0>
+  __device__ __forceinline__ void issue(int q) const {
+    if (q == Q) {
+      if constexpr (Q < TA::PW)
+        da.template issue_one<Q>(a, ma);
+      else
+        db.template issue_one<Q - TA::PW>(b, mb);
+    } else if constexpr (Q + 1 < N) {
+      issue<Q + 1>(q);
+    }
   }
 };
 
-// 32x32x16 operand fragment: rows rbase .. rbase+31 (M or N index), k = kk*16 .. +15
-template <int R, bool KMAJ, int KT>
-__device__ __forceinline__ bf16x8 read_frag(const char* lds_tile, int rbase, int kk, int lane) {
-  if constexpr (KMAJ) {
-    const int r = rbase + (lane & 31), c = kk * 2 + (lane >> 5);
-    return *(const bf16x8*)(lds_tile + kmaj_off<KT>(r, c));
-  } else {
-    const int g = lane >> 4, j = lane & 15;
-    const int col = rbase + 16 * (g & 1) + 4 * (j & 3);
-    const int kb = kk * 16 + 8 * (g >> 1) + (j >> 2);
-    const int c = col >> 3, within = (col & 7) * 2;
-    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (v4s __attribute__((address_space(3)))*)(lds_tile + mnmaj_off<R>(kb, c) + within));
-    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (v4s __attribute__((address_space(3)))*)(lds_tile + mnmaj_off<R>(kb + 4, c) + within));
-    typedef short v8s __attribute__((ext_vector_type(8)));
-    const v8s both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8, both);
+// Per-lane LDS byte offsets of a wavefront's MFMA fragments (32 rows x 16 k) inside an operand tile,
+// computed once per kernel.  K-major tile: the offset depends on the k-step (the swizzle mixes the
+// chunk with row bits) but not on the fragment (fragments lie 32 rows apart, a whole number of
+// swizzle periods): one offset per k-step, fragment f at + 64 KT f bytes.  MN-major tile: the offset
+// depends on the fragment (its columns enter the swizzle) but not on the k-step (16 rows, a whole
+// number of periods of the 4-row swizzle): one offset per fragment, k-step kk at + 32 R kk bytes and
+// the second four-row read at + 8 R.  Reads then take one address register per offset and a
+// constant in the instruction.
+//   ds_read_b64_tr_b16 (MN-major): within a group of 16 lanes, lane j addresses row k0 + j/4, columns
+//   n + 4*(j%4) .. +3, and lane i receives rows k0 .. k0+3 of column n + i - exactly the
+//   k-contiguous operand layout the MFMA expects.
+template <int R, bool KMAJ, int KT, int NF>
+struct FragOffsets {
+  static constexpr int KS = KT / 16, N = KMAJ ? KS : NF;
+  uint32_t o[N];
+  // rbase: the wavefront's first row (K-major) / column (MN-major) within the tile
+  __device__ __forceinline__ void init(int rbase, int lane) {
+#pragma unroll
+    for (int x = 0; x < N; ++x) {
+      if constexpr (KMAJ) {
+        o[x] = (uint32_t)kmaj_off<KT>(rbase + (lane & 31), x * 2 + (lane >> 5));
+      } else {
+        const int g = lane >> 4, j = lane & 15;
+        const int col = rbase + x * 32 + 16 * (g & 1) + 4 * (j & 3);
+        const int kb = 8 * (g >> 1) + (j >> 2);
+        o[x] = (uint32_t)(mnmaj_off<R>(kb, col >> 3) + (col & 7) * 2);
+      }
+    }
   }
-}
-
-// Loads of one k-tile (A then B) into the LDS stage at byte m0.  B may come in two row segments
-// (B0 for k < kseg, B1 after); kseg is a multiple of 64, so a k-tile never straddles them.
-template <int BM, int BN, bool AK, bool BKM, int KT>
-__device__ __forceinline__ void issue_stage(const TileDMA<BM, AK, KT>& da, const TileDMA<BN, BKM, KT>& db,
-                                            rsrc_t ra, rsrc_t rb0, rsrc_t rb1, int64_t lda, int64_t ldb,
-                                            int kseg, bool two_seg, int k0, uint32_t m0, int wave) {
-  da.issue(ra, lda, k0, m0, wave);
-  const bool seg1 = two_seg && k0 >= kseg;
-  db.issue(seg1 ? rb1 : rb0, ldb, seg1 ? k0 - kseg : k0, m0 + BM * KT * 2, wave);
-}
+  // the wavefront's address registers for a tile at LDS byte address `tile`: one add each, kept
+  // opaque so that the compiler folds every fragment's constant into the instruction's offset field
+  // instead of holding one precomputed address per read
+  __device__ __forceinline__ void bind(uint32_t tile, uint32_t (&a)[N]) const {
+#pragma unroll
+    for (int x = 0; x < N; ++x) {
+      a[x] = tile + o[x];
+      asm volatile("" : "+v"(a[x]));
+    }
+  }
+  __device__ __forceinline__ static bf16x8 read(const uint32_t (&a)[N], int f, int kk) {
+    typedef __attribute__((address_space(3))) const char* lds_cptr;
+    if constexpr (KMAJ) {
+      return *(const __attribute__((address_space(3))) bf16x8*)(lds_cptr)(uintptr_t)(a[kk] + f * 64 * KT);
+    } else {
+      const uint32_t b = a[f] + kk * 32 * R;
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(lds_cptr)(uintptr_t)b);
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(lds_cptr)(uintptr_t)(b + 8 * R));
+      typedef short v8s __attribute__((ext_vector_type(8)));
+      const v8s both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_bit_cast(bf16x8, both);
+    }
+  }
+};
 
 // s_waitcnt vmcnt(n), other counters unconstrained (gfx9 encoding)
 #define VMCNT_WAIT(n) \
@@ -584,32 +614,37 @@ __device__ __forceinline__ void issue_stage(const TileDMA<BM, AK, KT>& da, const
 constexpr int wave_rows(int bm) { return (bm % 64 == 0) ? 2 : 1; }
 
 // MFMAs of one k-tile (KT / 16 steps of k = 16) from one LDS stage; fragments of step kk+1 are read
-// while the MFMAs of step kk run (two register sets).  The loads of a later k-tile (`ld`) go out
-// one instruction at a time between the MFMAs, within the first SPN / SPD of them.
-template <int BM, int BN, bool AK, bool BKM, int KT, int SPN, int SPD>
+// while the MFMAs of step kk run (two register sets).  With LOAD, the loads of a later k-tile (`ld`)
+// go out one instruction at a time between the MFMAs, within the first SPN / SPD of them.
+template <int BM, int BN, bool AK, bool BKM, int KT, int SPN, int SPD, bool LOAD>
 __device__ __forceinline__ void mma_ktile(
-    const char* As, const char* Bs,
-    f32x16 (&acc)[BM / wave_rows(BM) / 32][BN / (4 / wave_rows(BM)) / 32], int wm, int wn, int lane,
+    uint32_t As, uint32_t Bs,
+    f32x16 (&acc)[BM / wave_rows(BM) / 32][BN / (4 / wave_rows(BM)) / 32],
+    const FragOffsets<BM, AK, KT, BM / wave_rows(BM) / 32>& fa,
+    const FragOffsets<BN, BKM, KT, BN / (4 / wave_rows(BM)) / 32>& fb,
     const StageLoader<BM, BN, AK, BKM, KT>& ld) {
   constexpr int WGM = wave_rows(BM), WGN = 4 / WGM;
   constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32, KS = KT / 16;
   constexpr int NQ = StageLoader<BM, BN, AK, BKM, KT>::N, MT = KS * TM * TN;
   static_assert(MT * SPN >= NQ * SPD && SPN <= SPD, "every load gets an MFMA slot");
+  using FA = FragOffsets<BM, AK, KT, TM>;
+  using FB = FragOffsets<BN, BKM, KT, TN>;
+  uint32_t aa[FA::N], ba[FB::N];
+  fa.bind(As, aa);
+  fb.bind(Bs, ba);
   bf16x8 af[2][TM], bfv[2][TN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) af[0][i] = read_frag<BM, AK, KT>(As, wm * WM + i * 32, 0, lane);
+  for (int i = 0; i < TM; ++i) af[0][i] = FA::read(aa, i, 0);
 #pragma unroll
-  for (int j = 0; j < TN; ++j) bfv[0][j] = read_frag<BN, BKM, KT>(Bs, wn * WN + j * 32, 0, lane);
+  for (int j = 0; j < TN; ++j) bfv[0][j] = FB::read(ba, j, 0);
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) {
     const int cur = kk & 1;
     if (kk + 1 < KS) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[cur ^ 1][i] = read_frag<BM, AK, KT>(As, wm * WM + i * 32, kk + 1, lane);
+      for (int i = 0; i < TM; ++i) af[cur ^ 1][i] = FA::read(aa, i, kk + 1);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfv[cur ^ 1][j] = read_frag<BN, BKM, KT>(Bs, wn * WN + j * 32, kk + 1, lane);
+      for (int j = 0; j < TN; ++j) bfv[cur ^ 1][j] = FB::read(ba, j, kk + 1);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -618,14 +653,16 @@ __device__ __forceinline__ void mma_ktile(
       for (int j = 0; j < TN; ++j) {
         acc[i][j] =
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfv[cur][j], acc[i][j], 0, 0, 0);
-        const int n = (kk * TM + i) * TN + j;  // MFMA number within the k-tile
+        if constexpr (LOAD) {
+          const int n = (kk * TM + i) * TN + j;  // MFMA number within the k-tile
 #pragma unroll
-        for (int q = 0; q < NQ; ++q)
-          if (((q + 1) * MT * SPN) / (NQ * SPD) - 1 == n) {
-            __builtin_amdgcn_sched_barrier(0);
-            ld.issue(q);
-            __builtin_amdgcn_sched_barrier(0);
-          }
+          for (int q = 0; q < NQ; ++q)
+            if (((q + 1) * MT * SPN) / (NQ * SPD) - 1 == n) {
+              __builtin_amdgcn_sched_barrier(0);
+              ld.issue(q);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+        }
       }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -657,13 +694,28 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
   const int wm = wave / WGN, wn = wave % WGN;
   // LDS byte address of the dynamic LDS block (the low half of its flat address)
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-  // operand buffers: rows of A are tokens (K-major A: M rows; MN-major A: K rows)
-  const rsrc_t ra = make_rsrc(p.A, (uint32_t)((int64_t)(AK ? p.M : p.K) * p.lda * 2));
+  // operand buffer sizes in bytes: A has M rows when K-major, K rows when MN-major; B's two
+  // segments hold reduction indices [0, kseg) and [kseg, K)
+  const uint32_t a_bytes = (uint32_t)((int64_t)(AK ? p.M : p.K) * p.lda * 2);
   const int kseg = p.B1 ? p.kseg : p.K;
   const bool two_seg = p.B1 != nullptr;
-  const rsrc_t rb0 = make_rsrc(p.B0, (uint32_t)((int64_t)kseg * p.ldb * 2));
-  const rsrc_t rb1 =
-      make_rsrc(p.B1 ? p.B1 : p.B0, (uint32_t)((int64_t)(p.B1 ? p.K - kseg : 0) * p.ldb * 2));
+  const uint32_t b0_bytes = (uint32_t)((int64_t)(BKM ? p.N : kseg) * p.ldb * 2);
+  const uint32_t b1_bytes = (uint32_t)((int64_t)(BKM ? p.N : p.K - kseg) * p.ldb * 2);
+  // the loads of the k-tile starting at reduction index k into the LDS stage at byte address st
+  auto loader = [&](const TileDMA<BM, AK, KT>& da, const TileDMA<BN, BKM, KT>& db, int k,
+                    uint32_t st, bool on) {
+    const bool seg1 = two_seg && k >= kseg;
+    const uint32_t mw = st + (uint32_t)wave * 1024u;
+    return StageLoader<BM, BN, AK, BKM, KT>{
+        da, db, ktile_src<AK>(p.A, on ? a_bytes : 0u, p.lda, k),
+        seg1 ? ktile_src<BKM>(p.B1, on ? b1_bytes : 0u, p.ldb, k - kseg)
+             : ktile_src<BKM>(p.B0, on ? b0_bytes : 0u, p.ldb, k),
+        mw, mw + (uint32_t)A_BYTES};
+  };
+  FragOffsets<BM, AK, KT, TM> fa;
+  FragOffsets<BN, BKM, KT, TN> fb;
+  fa.init(wm * WM, lane);
+  fb.init(wn * WN, lane);
 
   const int dp_items = p.dp_tiles * p.splits;
   const int kts = p.k_split / BK;  // k-tiles per K-split
@@ -719,29 +771,25 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
     __syncthreads();  // previous item's readers are done with every stage
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
-      if (s < nk)
-        issue_stage<BM, BN, AK, BKM, KT>(da, db, ra, rb0, rb1, p.lda, p.ldb, kseg, two_seg,
-                                         kbeg + s * BK, lds0 + s * STAGE, wave);
-    for (int kt = 0; kt < nk; ++kt) {
-      // tile kt complete (for this wave), then visible to all waves
-      if (kt + NS - 2 < nk) {
-        VMCNT_WAIT(LPW * (NS - 2));
-      } else {
-        VMCNT_WAIT(0);
+      {
+        const auto sl = loader(da, db, kbeg + s * BK, lds0 + s * STAGE, s < nk);
+#pragma unroll
+        for (int q = 0; q < StageLoader<BM, BN, AK, BKM, KT>::N; ++q) sl.issue(q);
       }
+    // k-tile kt + NS - 1 refills the stage read in iteration kt - 1; its loads go out between
+    // k-tile kt's MFMAs (within the first half with two stages, the first 3/4 with three).  Past the
+    // last k-tile the loads still go out, from a source of range 0: they read nothing and write
+    // zeros into a stage no k-tile reads any more, and the k-loop keeps a single MFMA sequence.
+    for (int kt = 0; kt < nk; ++kt) {
+      VMCNT_WAIT(LPW * (NS - 2));  // tile kt complete (for this wave), then visible to all waves
       __syncthreads();
-      // k-tile kt + NS - 1 refills the stage read in iteration kt - 1; its loads go out between
-      // this k-tile's MFMAs (within the first half with two stages, the first 3/4 with three)
-      const int kn = kbeg + (kt + NS - 1) * BK;
-      const bool seg1 = two_seg && kn >= kseg;
-      const StageLoader<BM, BN, AK, BKM, KT> sl{da, db, ra, seg1 ? rb1 : rb0, p.lda, p.ldb, kn,
-                                                seg1 ? kn - kseg : kn,
-                                                lds0 + ((kt + NS - 1) % NS) * STAGE, wave,
-                                                kt + NS - 1 < nk};
-      const char* As = lds + (kt % NS) * STAGE;
-      mma_ktile<BM, BN, AK, BKM, KT, (NS == 2 ? 1 : 3), (NS == 2 ? 2 : 4)>(As, As + A_BYTES, acc, wm,
-                                                                        wn, lane, sl);
+      const uint32_t As = lds0 + (uint32_t)((kt % NS) * STAGE);
+      const auto sl = loader(da, db, kbeg + (kt + NS - 1) * BK, lds0 + ((kt + NS - 1) % NS) * STAGE,
+                             kt + NS - 1 < nk);
+      mma_ktile<BM, BN, AK, BKM, KT, (NS == 2 ? 1 : 3), (NS == 2 ? 2 : 4), true>(
+          As, As + A_BYTES, acc, fa, fb, sl);
     }
+    VMCNT_WAIT(0);  // the zero-range loads have landed before the epilogue reuses the stages
 
     // epilogue through LDS: the fp32 tile is staged row-major in passes of EROWS rows, then every
     // thread finishes 8 consecutive columns of GPT rows with 16-byte loads / stores
