@@ -76,6 +76,20 @@ collider_status collider_build_index(const uint8_t* keep, int32_t B, int32_t S, 
                                      int32_t* inv, int32_t* cu_seqlens, int32_t* count,
                                      hipStream_t stream);
 
+/* Mask -> index when the caller already knows how many tokens the mask keeps (a filter that keeps
+ * a fixed number of tokens per batch, such as a top-k on per-token scores): the same outputs as
+ * collider_build_index, without the host wait for the count.  expected_count becomes M_kept of the
+ * index; on the device, compacted positions >= expected_count are left out of inv (-1) and
+ * cu_seqlens (clamped), so that every consumer sized for expected_count rows stays in bounds
+ * whatever the mask holds.  *mismatch (device int32, written by every call) = 1 if the mask keeps
+ * another number of tokens - the gradients computed from such an index are then not the filtered
+ * gradient and must be discarded - else 0; *count holds the true count either way.
+ * COLLIDER_ERR_SHAPE if expected_count < 0 or > B*S; COLLIDER_ERR_NULL for a null pointer. */
+collider_status collider_build_index_expect(const uint8_t* keep, int32_t B, int32_t S,
+                                            int32_t expected_count, int32_t* idx, int32_t* inv,
+                                            int32_t* cu_seqlens, int32_t* count, int32_t* mismatch,
+                                            hipStream_t stream);
+
 /* Copies *count_dev to *count_host (host pointer) and waits for it: the one host sync of a step. */
 collider_status collider_index_count_host(const int32_t* count_dev, int32_t* count_host,
                                           hipStream_t stream);

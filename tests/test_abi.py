@@ -47,6 +47,9 @@ def test_host_validation_errors():
     p = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
     assert L.collider_build_index(None, 1, 1, p, p, p, p, None) == 1
     assert L.collider_build_index(p, 0, 1, p, p, p, p, None) == 2
+    assert L.collider_build_index_expect(p, 2, 4, -1, p, p, p, p, p, None) == 2   # count < 0
+    assert L.collider_build_index_expect(p, 2, 4, 9, p, p, p, p, p, None) == 2    # count > B*S
+    assert L.collider_build_index_expect(p, 2, 4, 3, p, p, p, p, None, None) == 1  # no flag
     assert L.collider_gather_rows(p, 8, p, 8, p, 1, 8, 7, None) == 4          # bad dtype
     assert L.collider_gather_rows(p, 4, p, 8, p, 1, 8, 1, None) == 2          # ld < row
     assert L.collider_gather_rows(None, 8, p, 8, p, 1, 8, 1, None) == 1

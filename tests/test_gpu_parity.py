@@ -49,6 +49,33 @@ def test_build_index_bit_exact(B, S, pattern):
     assert int(ix.count.cpu()[0]) == ref["count"]
 
 
+@pytest.mark.parametrize("B,S,pattern", [(4, 2048, "topk"), (5, 3001, "rand"), (1, 70000, "rand"),
+                                         (1, 7, "none"), (2, 5, "all")])
+@pytest.mark.parametrize("delta", [0, -5, 3])
+def test_build_index_with_announced_count(B, S, pattern, delta):
+    """The index build that takes the kept count from the caller: with the true count it equals the
+    ordinary build bit for bit; with a wrong one it flags the mismatch and keeps inv / cu_seqlens
+    inside the announced count (idx stays the full partition, count the true count)."""
+    keep = _keep(B * S, pattern, seed=B * S + 1)
+    ref = oracle.build_index(keep, B, S)
+    n = ref["count"]
+    expect = min(max(n + delta, 0), B * S)
+    ix = tfb.build_index(_dev_keep(keep), B, S, expect=expect)
+    assert ix.M_kept == expect
+    idx, inv = ix.idx.cpu().numpy(), ix.inv.cpu().numpy()
+    cu, count, mm = ix.cu_seqlens.cpu().numpy(), int(ix.count.cpu()[0]), int(ix.mismatch.cpu()[0])
+    assert count == n and np.array_equal(idx, ref["partition"])
+    assert mm == int(expect != n)
+    exp_inv = np.where(ref["inv"] < expect, ref["inv"], -1)
+    assert np.array_equal(inv, exp_inv)
+    assert np.array_equal(cu, np.minimum(ref["cu_seqlens"], expect))
+    if expect == n:
+        ix.check()
+    else:
+        with pytest.raises(tfb.ColliderError):
+            ix.check()
+
+
 @pytest.mark.parametrize("cols,dtype", [(2048, torch.bfloat16), (256, torch.bfloat16), (32, torch.float32),
                                         (12, torch.bfloat16), (5, torch.float32), (4096, torch.float32)])
 def test_gather_scatter_bit_exact(cols, dtype):
@@ -375,7 +402,7 @@ def test_stack_of_layers(name):
 def test_layer_graph_replay_matches_eager(name):
     """The layer recorded into a HIP graph and replayed gives the eager result bit for bit, on every
     replay, with eager work and synchronisation between replays and with a new mask of the same
-    kept count rebuilt in place."""
+    kept count rebuilt in place, the count taken from the device or announced by the host."""
     cfg = synth.get_config(name)
     inp = synth.make_layer_inputs(cfg, r_pct=40)
     weights, saved, dy = _upload_layer(inp)
@@ -397,7 +424,9 @@ def test_layer_graph_replay_matches_eager(name):
     grads = tfb.make_grads(lcfg, cfg.M, ix.M_kept, "cuda")
     junk = torch.zeros(1 << 20, device="cuda")
     for rep, (keep, ref) in enumerate([(keep1, ref1), (keep1, ref1), (keep2, ref2), (keep1, ref1)]):
-        ix = tfb.build_index(_dev_keep(keep), cfg.B, cfg.S, out=ix)
+        # odd replays take the kept count from the host (no wait for the index build)
+        ix = tfb.build_index(_dev_keep(keep), cfg.B, cfg.S, out=ix,
+                             expect=int(keep.sum()) if rep % 2 else None)
         for gt in grads.values():
             gt.fill_(float("nan"))
         lb(weights, saved, dy, ix, grads, graph=True)
@@ -408,6 +437,7 @@ def test_layer_graph_replay_matches_eager(name):
             same = torch.equal(a.view(torch.int16), b.view(torch.int16)) if a.dtype == torch.bfloat16 \
                 else torch.equal(a, b)
             assert same, (rep, k)
+        ix.check()
 
 
 def test_layer_repeat_is_deterministic():

@@ -82,6 +82,7 @@ def lib():
     sig = {
         "collider_status_string": (ctypes.c_char_p, [_i32]),
         "collider_build_index": (st, [_c_p, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _c_p]),
+        "collider_build_index_expect": (st, [_c_p, _i32, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
         "collider_index_count_host": (st, [_c_p, P(_i32), _c_p]),
         "collider_gather_rows": (st, [_c_p, _i64, _c_p, _i64, _c_p, _i32, _i32, _i32, _c_p]),
         "collider_scatter_rows": (st, [_c_p, _i64, _c_p, _i64, _c_p, _i32, _i32, _i32, _i32, _c_p]),
@@ -153,6 +154,13 @@ def _dt(t):
 def collider_build_index(keep, B, S, idx, inv, cu_seqlens, count, stream=None):
     _check(lib().collider_build_index(_ptr(keep), B, S, _ptr(idx), _ptr(inv), _ptr(cu_seqlens),
                                       _ptr(count), _stream(stream)), "collider_build_index")
+
+
+def collider_build_index_expect(keep, B, S, expected_count, idx, inv, cu_seqlens, count, mismatch,
+                                stream=None):
+    _check(lib().collider_build_index_expect(_ptr(keep), B, S, int(expected_count), _ptr(idx), _ptr(inv),
+                                             _ptr(cu_seqlens), _ptr(count), _ptr(mismatch),
+                                             _stream(stream)), "collider_build_index_expect")
 
 
 def collider_index_count_host(count, stream=None) -> int:
@@ -265,30 +273,49 @@ class Index:
     B: int
     S: int
     M_kept: int
+    mismatch: torch.Tensor = None  # set by build_index(..., expect=n): device flag, 1 = count != n
 
     def c(self) -> CollIndex:
         return CollIndex(self.idx.data_ptr(), self.inv.data_ptr(), self.cu_seqlens.data_ptr(),
                          self.count.data_ptr(), self.B, self.S, self.M_kept)
 
+    def check(self):
+        """For an index built with an announced count: raise if the mask kept another number of
+        tokens (waits for the index build)."""
+        if self.mismatch is not None and int(self.mismatch.item()) != 0:
+            raise ColliderError(f"keep mask holds {int(self.count.item())} kept tokens, "
+                                f"{self.M_kept} were announced")
 
-def build_index(keep: torch.Tensor, B: int, S: int, stream=None, out: "Index" = None) -> Index:
-    """Compact a [B*S] uint8 keep mask on the device; waits once for the kept count.  With `out`
+
+def build_index(keep: torch.Tensor, B: int, S: int, stream=None, out: "Index" = None,
+                expect: int = None) -> Index:
+    """Compact a [B*S] uint8 keep mask on the device.  Without `expect` this waits once for the
+    kept count.  With `expect` (the number of tokens the mask is known to keep, e.g. a top-k) it
+    does not wait: the device checks the count, and Index.check() reports a mismatch.  With `out`
     the index is rebuilt in that index's buffers (same addresses every step)."""
     dev = keep.device
     M = B * S
     if out is not None and out.B == B and out.S == S and out.idx.numel() == M:
-        idx, inv, cu, count = out.idx, out.inv, out.cu_seqlens, out.count
+        idx, inv, cu, count, mm = out.idx, out.inv, out.cu_seqlens, out.count, out.mismatch
     else:
         idx = torch.empty(M, dtype=torch.int32, device=dev)
         inv = torch.empty(M, dtype=torch.int32, device=dev)
         cu = torch.empty(B + 1, dtype=torch.int32, device=dev)
         count = torch.empty(1, dtype=torch.int32, device=dev)
-    collider_build_index(keep, B, S, idx, inv, cu, count, stream)
-    mk = collider_index_count_host(count, stream)
+        mm = None
+    if expect is None:
+        collider_build_index(keep, B, S, idx, inv, cu, count, stream)
+        mk = collider_index_count_host(count, stream)
+        mm = None
+    else:
+        if mm is None:
+            mm = torch.zeros(1, dtype=torch.int32, device=dev)
+        collider_build_index_expect(keep, B, S, expect, idx, inv, cu, count, mm, stream)
+        mk = int(expect)
     if out is not None and out.idx is idx:
-        out.M_kept = mk
+        out.M_kept, out.mismatch = mk, mm
         return out
-    return Index(idx, inv, cu, count, B, S, mk)
+    return Index(idx, inv, cu, count, B, S, mk, mm)
 
 
 def layer_cfg(shape, dmode=ATTN_D_FILTERED, accumulate=False, unfiltered=False) -> LayerCfg:

@@ -110,7 +110,18 @@ collider_status collider_build_index(const uint8_t* keep, int32_t B, int32_t S, 
                                      hipStream_t stream) {
   if (!keep || !idx || !inv || !cu_seqlens || !count) return COLLIDER_ERR_NULL;
   if (B < 1 || S < 1 || (int64_t)B * S > (1 << 30)) return COLLIDER_ERR_SHAPE;
-  return launch_build_index(keep, B, S, idx, inv, cu_seqlens, count, stream);
+  return launch_build_index(keep, B, S, idx, inv, cu_seqlens, count, -1, nullptr, stream);
+}
+
+collider_status collider_build_index_expect(const uint8_t* keep, int32_t B, int32_t S,
+                                            int32_t expected_count, int32_t* idx, int32_t* inv,
+                                            int32_t* cu_seqlens, int32_t* count, int32_t* mismatch,
+                                            hipStream_t stream) {
+  if (!keep || !idx || !inv || !cu_seqlens || !count || !mismatch) return COLLIDER_ERR_NULL;
+  if (B < 1 || S < 1 || (int64_t)B * S > (1 << 30)) return COLLIDER_ERR_SHAPE;
+  if (expected_count < 0 || (int64_t)expected_count > (int64_t)B * S) return COLLIDER_ERR_SHAPE;
+  return launch_build_index(keep, B, S, idx, inv, cu_seqlens, count, expected_count, mismatch,
+                            stream);
 }
 
 collider_status collider_index_count_host(const int32_t* count_dev, int32_t* count_host,

@@ -63,17 +63,20 @@ __device__ __forceinline__ unsigned load_bits(const uint8_t* __restrict__ keep, 
 }
 
 // Writes idx / inv / cu for tokens t0 .. t0+7, whose first kept token gets compacted position pre.
+// Compacted positions at or past lim are left out of inv and cu (lim = the count the caller
+// announced; INT_MAX when it announced none), so that no consumer sized for lim rows ever indexes
+// past them.
 __device__ __forceinline__ void scatter_group(unsigned bits, int t0, int pre, int n_kept, int M, int S,
-                                              int32_t* __restrict__ idx, int32_t* __restrict__ inv,
-                                              int32_t* __restrict__ cu) {
+                                              int lim, int32_t* __restrict__ idx,
+                                              int32_t* __restrict__ inv, int32_t* __restrict__ cu) {
   int iv[kPer];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
     const int t = t0 + e;
     const bool k = (bits >> e) & 1u;
-    iv[e] = k ? pre : -1;
+    iv[e] = (k && pre < lim) ? pre : -1;
     if (t < M) {
-      if (t % S == 0) cu[t / S] = pre;
+      if (t % S == 0) cu[t / S] = min(pre, lim);
       if (k)
         idx[pre] = t;
       else
@@ -96,9 +99,12 @@ __global__ __launch_bounds__(kThreads) void build_index_kernel(const uint8_t* __
                                                                int32_t* __restrict__ idx,
                                                                int32_t* __restrict__ inv,
                                                                int32_t* __restrict__ cu,
-                                                               int32_t* __restrict__ count) {
+                                                               int32_t* __restrict__ count,
+                                                               int expect,
+                                                               int32_t* __restrict__ mismatch) {
   __shared__ int s_wave[kWaves + 1];
   const int M = B * S;
+  const int lim = expect >= 0 ? expect : 0x7fffffff;
   constexpr int CHUNK = kThreads * kPer;
   int n_kept;
   if (M <= CHUNK) {
@@ -108,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void build_index_kernel(const uint8_t* __
     int total = 0;
     const int pre = block_excl_scan(__popc(bits), &total, s_wave);
     n_kept = total;
-    scatter_group(bits, t0, pre, n_kept, M, S, idx, inv, cu);
+    scatter_group(bits, t0, pre, n_kept, M, S, lim, idx, inv, cu);
   } else {
     // pass 1: number of kept tokens (the filtered positions are placed after the kept ones)
     int local = 0;
@@ -123,21 +129,23 @@ __global__ __launch_bounds__(kThreads) void build_index_kernel(const uint8_t* __
       const unsigned bits = load_bits(keep, t0, M);
       int chunk_total = 0;
       const int pre = before + block_excl_scan(__popc(bits), &chunk_total, s_wave);
-      scatter_group(bits, t0, pre, n_kept, M, S, idx, inv, cu);
+      scatter_group(bits, t0, pre, n_kept, M, S, lim, idx, inv, cu);
       before += chunk_total;
     }
   }
   if (threadIdx.x == 0) {
-    cu[B] = n_kept;
+    cu[B] = min(n_kept, lim);
     count[0] = n_kept;
+    if (mismatch) mismatch[0] = (expect >= 0 && n_kept != expect) ? 1 : 0;
   }
 }
 
 collider_status launch_build_index(const uint8_t* keep, int B, int S, int32_t* idx, int32_t* inv,
-                                   int32_t* cu, int32_t* count, hipStream_t s) {
+                                   int32_t* cu, int32_t* count, int expect, int32_t* mismatch,
+                                   hipStream_t s) {
   COLLIDER_LAUNCH("build_index", s,
                   hipLaunchKernelGGL(build_index_kernel, dim3(1), dim3(kThreads), 0, s, keep, B, S,
-                                     idx, inv, cu, count));
+                                     idx, inv, cu, count, expect, mismatch));
   return last_hip_status();
 }
 

@@ -85,8 +85,11 @@ struct Carver {
 // ------------------------------------------------------------------------------------------
 
 // mask -> index (index.hip)
+// expect >= 0: the count the caller announced (inv / cu never reach past it; *mismatch, when
+// given, is set to 1 if the mask keeps another number of tokens, else 0); expect < 0: none
 collider_status launch_build_index(const uint8_t* keep, int B, int S, int32_t* idx, int32_t* inv,
-                                   int32_t* cu, int32_t* count, hipStream_t s);
+                                   int32_t* cu, int32_t* count, int expect, int32_t* mismatch,
+                                   hipStream_t s);
 
 // rows.hip
 struct GatherDesc {
