@@ -759,6 +759,26 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
     da.init(p.lda, m0, wave, lane);
     db.init(p.ldb, n0, wave, lane);
 
+    // epilogue layout: the fp32 tile is staged row-major in passes of EROWS rows, then every
+    // thread finishes 8 consecutive columns of GPT rows with 16-byte loads / stores
+    constexpr int LDE = BN + 8;  // +8 floats: the two lane halves' rows land 32 banks apart
+    // rows per pass: a divisor of BM that fits the stage buffers; epilogues with two 16-byte side
+    // inputs per 8 outputs take shorter passes (registers)
+    constexpr int EROWS_REG = (EPI == EPI_SWIGLU || EPI == EPI_F32) ? 32 : 64;
+    constexpr int EROWS = (BM <= EROWS_REG && BM * LDE * 4 <= NS * STAGE) ? BM
+                          : (BM % 64 == 0 && 64 <= EROWS_REG && 64 * LDE * 4 <= NS * STAGE) ? 64 : 32;
+    static_assert(BM % EROWS == 0 && EROWS % 32 == 0, "epilogue passes cover whole accumulator blocks");
+    static_assert(EROWS * LDE * 4 <= NS * STAGE, "epilogue pass must fit in the stage buffers");
+    constexpr int CPR = BN / 8, RSTEP = 256 / CPR, GPT = EROWS / RSTEP;
+    static_assert(EROWS % RSTEP == 0, "epilogue rows per pass");
+    const int cg = threadIdx.x % CPR, rsub = threadIdx.x / CPR;
+    const int n = n0 + cg * 8;
+    // side inputs of the first epilogue pass (SwiGLU / GELU rows, or C when accumulating): loaded
+    // now, so that their latency overlaps the k-loop (loads return in order, so the k-loop's own
+    // waits never stop short of them)
+    uint4 sa[GPT], sb[GPT];
+    if (mode == 0) prefetch_side<EPI, GPT>(p, m0 + rsub, RSTEP, n, sa, sb);
+
     f32x16 acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -791,25 +811,15 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
     }
     VMCNT_WAIT(0);  // the zero-range loads have landed before the epilogue reuses the stages
 
-    // epilogue through LDS: the fp32 tile is staged row-major in passes of EROWS rows, then every
-    // thread finishes 8 consecutive columns of GPT rows with 16-byte loads / stores
-    constexpr int LDE = BN + 8;  // +8 floats: the two lane halves' rows land 32 banks apart
-    // rows per pass: a divisor of BM that fits the stage buffers; epilogues with two 16-byte side
-    // inputs per 8 outputs take shorter passes (registers)
-    constexpr int EROWS_REG = (EPI == EPI_SWIGLU || EPI == EPI_F32) ? 32 : 64;
-    constexpr int EROWS = (BM <= EROWS_REG && BM * LDE * 4 <= NS * STAGE) ? BM
-                          : (BM % 64 == 0 && 64 <= EROWS_REG && 64 * LDE * 4 <= NS * STAGE) ? 64 : 32;
-    static_assert(BM % EROWS == 0 && EROWS % 32 == 0, "epilogue passes cover whole accumulator blocks");
-    static_assert(EROWS * LDE * 4 <= NS * STAGE, "epilogue pass must fit in the stage buffers");
-    constexpr int CPR = BN / 8, RSTEP = 256 / CPR, GPT = EROWS / RSTEP;
-    static_assert(EROWS % RSTEP == 0, "epilogue rows per pass");
-    const int cg = threadIdx.x % CPR, rsub = threadIdx.x / CPR;
-    const int n = n0 + cg * 8;
+    // epilogue through LDS (constants and the first pass's side inputs set up before the k-loop)
     float* E = (float*)lds;
 #pragma unroll
     for (int pass = 0; pass < BM / EROWS; ++pass) {
-      uint4 sa[GPT], sb[GPT];
-      if (mode == 0) prefetch_side<EPI, GPT>(p, m0 + pass * EROWS + rsub, RSTEP, n, sa, sb);
+      // side inputs of the next pass go out now; their latency (an index load, then the rows)
+      // overlaps this pass
+      uint4 na[GPT], nb[GPT];
+      if (pass + 1 < BM / EROWS && mode == 0)
+        prefetch_side<EPI, GPT>(p, m0 + (pass + 1) * EROWS + rsub, RSTEP, n, na, nb);
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
@@ -840,6 +850,11 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
           else
             epi_finish8<EPI>(p, m, n, vv, sa[i], sb[i]);
         }
+      }
+#pragma unroll
+      for (int i = 0; i < GPT; ++i) {
+        sa[i] = na[i];
+        sb[i] = nb[i];
       }
     }
   }
