@@ -138,6 +138,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfiltered", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch every kernel eagerly each step")
+    ap.add_argument("--weight-layout", choices=("in_out", "out_in"), default="in_out",
+                    help="projection weights stored [in, out] (y = x W, the pages' notation) or "
+                         "[out, in] (torch nn.Linear); LLAMA-kind layers only take in_out")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a plain copy of "
                          "known size, to calibrate HBM byte counters in a profiler run)")
@@ -179,8 +182,12 @@ def main():
     dy = up(inp["dy"])
     keep = torch.from_numpy(inp["keep"]).to(dev)
     B, S, M = cfg.B, cfg.S, cfg.M
+    # weight storage layout (set up once, before timing; the weight gradients come out in it)
+    layout = tfb.WEIGHTS_IN_OUT if (args.weight_layout == "in_out" and cfg.kind == "llama") else tfb.WEIGHTS_OUT_IN
+    if layout == tfb.WEIGHTS_IN_OUT:
+        weights = tfb.to_in_out(weights)
 
-    lcfg = tfb.layer_cfg(cfg)
+    lcfg = tfb.layer_cfg(cfg, weight_layout=layout)
     lb = tfb.LayerBackward(lcfg, B, S, dev)
     ix0 = tfb.build_index(keep, B, S)
     grads = tfb.make_grads(lcfg, M, ix0.M_kept, dev)
@@ -210,7 +217,7 @@ def main():
                dx_compact=True)
         lb(weights, saved, gc[(L - 2) % 2]["dx"], ix, grads, dy_compact=True)
 
-    ucfg = tfb.layer_cfg(cfg, unfiltered=True)
+    ucfg = tfb.layer_cfg(cfg, unfiltered=True, weight_layout=layout)
     ub = tfb.LayerBackward(ucfg, B, S, dev)
     uix = tfb.dense_index(B, S)
     ugrads = [tfb.make_grads(ucfg, M, M, dev) for _ in range(2 if L > 1 else 1)]
@@ -360,7 +367,8 @@ def main():
                                      f"{args.r}% filtered"),
                    "layers": L,
                    "B": B, "S": S, "hidden": cfg.H, "heads": f"{cfg.nq}/{cfg.nkv}x{cfg.d}",
-                   "inter": cfg.I, "M": M, "M_kept": ix.M_kept, "parallelism": "single GPU"},
+                   "inter": cfg.I, "M": M, "M_kept": ix.M_kept, "parallelism": "single GPU",
+                   "weight_layout": "in_out" if layout == tfb.WEIGHTS_IN_OUT else "out_in"},
         "launch_mode": {"filtered": mode_f, "unfiltered": mode_u},
         "ms_by_launch_mode": {"filtered": modes_f, "unfiltered": modes_u},
         "ms_filtered_cold": round(ms_f_cold, 4),

@@ -186,9 +186,21 @@ typedef struct {
                                    the method is measured against: the index arrays are not read
                                    (only B, S), nothing is gathered or scattered, every GEMM and
                                    the attention run on the full layout, dmode is taken as FULL */
+  int32_t weight_layout;        /* collider_weight_layout: how the projection weights and their
+                                   gradients are stored (LLAMA only may take IN_OUT) */
 } collider_layer_cfg;
 
-typedef struct {                /* bf16 weights [out, in]; float32 norm parameters */
+/* COLLIDER_WEIGHTS_OUT_IN: w [out, in], y = x w^T (torch nn.Linear), the layouts listed below.
+ * COLLIDER_WEIGHTS_IN_OUT: W [in, out], y = x W (the notation of the Collider pages, dX = dY W^T):
+ * every projection weight and its gradient is the transpose of the OUT_IN one - W_qkv [H, nqkv]
+ * (q columns, then k, then v), W_o [nq*d, H], W_gateup [H, 2I] (gate columns then up), W_down
+ * [I, H].  With IN_OUT each weight row is contiguous along the reduction of the activation-gradient
+ * GEMM, so both of its operands are read with 16-byte LDS reads (OUT_IN needs the transposing
+ * 8-byte reads, a third of the LDS bandwidth). */
+typedef enum { COLLIDER_WEIGHTS_OUT_IN = 0, COLLIDER_WEIGHTS_IN_OUT = 1 } collider_weight_layout;
+
+typedef struct {                /* bf16 weights, shapes for COLLIDER_WEIGHTS_OUT_IN (IN_OUT: the
+                                   transposes); float32 norm parameters */
   const void* w_qkv;            /* [(nq+2nkv)*d, H]: q rows, then k, then v */
   const void* w_o;              /* [H, nq*d] */
   const void* w_gateup;         /* LLAMA [2I, H]: gate rows then up rows */
@@ -217,7 +229,7 @@ typedef struct {                /* forward activations, full token layout [M, ..
   const void* f;                /* PHI bf16 [M, I] fc1 pre-activation */
 } collider_layer_saved;
 
-typedef struct {                /* outputs */
+typedef struct {                /* outputs (weight gradients in the weights' layout) */
   void* dx;                     /* bf16 [M, H] (dx_compact = 0) or [M_kept, H] (dx_compact != 0) */
   float* dw_qkv;                /* [(nq+2nkv)*d, H] */
   float* dw_o;                  /* [H, nq*d] */

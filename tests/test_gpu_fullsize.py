@@ -27,20 +27,23 @@ def _inputs(name, r, n_layers=None):
     return synth.make_layer_inputs(cfg, seed=0, r_pct=r)
 
 
-def _run(inp, dmode, unfiltered=False):
+def _run(inp, dmode, unfiltered=False, weight_layout=0):
     cfg = inp["cfg"]
     weights, saved, dy = _upload_layer(inp)
+    if weight_layout == tfb.WEIGHTS_IN_OUT:
+        weights = tfb.to_in_out(weights)
     if unfiltered:
         ix = tfb.dense_index(cfg.B, cfg.S)
     else:
         ix = tfb.build_index(_dev_keep(inp["keep"]), cfg.B, cfg.S)
-    lcfg = tfb.layer_cfg(cfg, dmode=dmode, unfiltered=unfiltered)
+    lcfg = tfb.layer_cfg(cfg, dmode=dmode, unfiltered=unfiltered, weight_layout=weight_layout)
     grads = tfb.make_grads(lcfg, cfg.M, ix.M_kept, "cuda")
     for g in grads.values():
         g.fill_(float("nan"))
     tfb.LayerBackward(lcfg, cfg.B, cfg.S, "cuda")(weights, saved, dy, ix, grads)
     torch.cuda.synchronize()
-    return {k: to64(v) for k, v in grads.items()}
+    # weight gradients in the [out, in] layout the oracle returns
+    return {k: (to64(v).T if weight_layout and k.startswith("dw_") else to64(v)) for k, v in grads.items()}
 
 
 def _compare(cfg, got, ref, keep):
@@ -52,13 +55,15 @@ def _compare(cfg, got, ref, keep):
     assert not bad, errs
 
 
-@pytest.mark.parametrize("name,r,dmode", [("tinyllama", 40, 0), ("tinyllama", 40, 1), ("qwen25", 40, 0),
-                                          ("phi15", 0, 0), ("phi15", 20, 0), ("phi15", 40, 0),
-                                          ("phi15", 60, 0)])
-def test_layer_fullsize(name, r, dmode):
+@pytest.mark.parametrize("name,r,dmode,layout", [("tinyllama", 40, 0, 0), ("tinyllama", 40, 1, 0),
+                                                 ("tinyllama", 40, 0, 1), ("qwen25", 40, 0, 0),
+                                                 ("qwen25", 40, 0, 1), ("phi15", 0, 0, 0),
+                                                 ("phi15", 20, 0, 0), ("phi15", 40, 0, 0),
+                                                 ("phi15", 60, 0, 0)])
+def test_layer_fullsize(name, r, dmode, layout):
     cfg = synth.get_config(name)
     inp = synth.make_layer_inputs(cfg, seed=0, r_pct=r)
-    got = _run(inp, dmode)
+    got = _run(inp, dmode, weight_layout=layout)
     ref = oracle.layer_bwd(cfg, upcast(inp["weights"]), upcast(inp["saved"]),
                            synth.bf16_bits_to_f32(inp["dy"]), inp["keep"],
                            "filtered" if dmode == 0 else "full_d")

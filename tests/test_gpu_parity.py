@@ -316,6 +316,40 @@ def test_layer_parity_small(name, dmode, r):
     run_layer_and_compare(inp, dmode)
 
 
+@pytest.mark.parametrize("name", ["small_llama", "small_llama_d128"])
+@pytest.mark.parametrize("r", [0, 40])
+def test_layer_weight_layouts(name, r):
+    """Weights stored [in, out] give the same gradients as [out, in] - dx and the norm gains bit for
+    bit, every weight gradient as the exact transpose - and match the oracle."""
+    cfg = synth.get_config(name)
+    inp = synth.make_layer_inputs(cfg, r_pct=r)
+    weights, saved, dy = _upload_layer(inp)
+    ix = tfb.build_index(_dev_keep(inp["keep"]), cfg.B, cfg.S)
+    out = {}
+    for layout, w in ((tfb.WEIGHTS_OUT_IN, weights), (tfb.WEIGHTS_IN_OUT, tfb.to_in_out(weights))):
+        lcfg = tfb.layer_cfg(cfg, weight_layout=layout)
+        grads = tfb.make_grads(lcfg, cfg.M, ix.M_kept, "cuda")
+        for g in grads.values():
+            g.fill_(float("nan"))
+        tfb.layer_bwd(lcfg, w, saved, dy, ix, grads)
+        torch.cuda.synchronize()
+        out[layout] = grads
+    g0, g1 = out[tfb.WEIGHTS_OUT_IN], out[tfb.WEIGHTS_IN_OUT]
+    for k in g0:
+        a = g1[k].t() if k.startswith("dw_") else g1[k]
+        b = g0[k]
+        assert a.shape == b.shape, k
+        same = torch.equal(a.contiguous().view(torch.int16), b.view(torch.int16)) if b.dtype == torch.bfloat16 \
+            else torch.equal(a.contiguous(), b)
+        assert same, k
+    ref = oracle.layer_bwd(cfg, upcast(inp["weights"]), upcast(inp["saved"]),
+                           synth.bf16_bits_to_f32(inp["dy"]), inp["keep"], "filtered")
+    for gname, oname in GRAD_NAMES["llama"].items():
+        got = to64(g1[gname])
+        got = got.T if gname.startswith("dw_") else got
+        assert rel_err(got, ref[oname]) <= BF16_TOL, gname
+
+
 @pytest.mark.parametrize("policy", [tfb.GEMM_POLICY_SPLITK, tfb.GEMM_POLICY_STREAMK, tfb.GEMM_POLICY_TILES])
 @pytest.mark.parametrize("name", ["small_llama", "small_phi"])
 def test_layer_parity_gemm_policies(gemm_policy, policy, name):

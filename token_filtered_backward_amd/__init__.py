@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libcollider.so")
 F32, BF16 = 0, 1
 ATTN_D_FILTERED, ATTN_D_FULL = 0, 1
 LAYER_LLAMA, LAYER_PHI = 0, 1
+WEIGHTS_OUT_IN, WEIGHTS_IN_OUT = 0, 1
 
 _c_p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -47,7 +48,7 @@ class LayerCfg(ctypes.Structure):
     _fields_ = [("kind", _i32), ("hidden", _i32), ("n_q_heads", _i32), ("n_kv_heads", _i32),
                 ("head_dim", _i32), ("rot_dims", _i32), ("inter", _i32),
                 ("rope_base", ctypes.c_float), ("dmode", _i32), ("accumulate", _i32),
-                ("unfiltered", _i32)]
+                ("unfiltered", _i32), ("weight_layout", _i32)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -318,12 +319,22 @@ def build_index(keep: torch.Tensor, B: int, S: int, stream=None, out: "Index" = 
     return Index(idx, inv, cu, count, B, S, mk, mm)
 
 
-def layer_cfg(shape, dmode=ATTN_D_FILTERED, accumulate=False, unfiltered=False) -> LayerCfg:
+def layer_cfg(shape, dmode=ATTN_D_FILTERED, accumulate=False, unfiltered=False,
+              weight_layout=WEIGHTS_OUT_IN) -> LayerCfg:
     """LayerCfg from any object with kind/H/nq/nkv/d/rot/I/rope_base attributes.
-    unfiltered=True selects the ordinary dense backward over all tokens (the baseline)."""
+    unfiltered=True selects the ordinary dense backward over all tokens (the baseline);
+    weight_layout=WEIGHTS_IN_OUT takes every projection weight (and returns its gradient) as
+    W [in, out] instead of w [out, in]."""
     return LayerCfg(LAYER_LLAMA if shape.kind == "llama" else LAYER_PHI, shape.H, shape.nq, shape.nkv,
                     shape.d, shape.rot, shape.I, float(shape.rope_base), dmode, int(accumulate),
-                    int(unfiltered))
+                    int(unfiltered), int(weight_layout))
+
+
+def to_in_out(weights: dict) -> dict:
+    """The projection weights of a [out, in] weight dict as contiguous [in, out] matrices (the
+    norm parameters unchanged), for weight_layout=WEIGHTS_IN_OUT."""
+    proj = ("w_qkv", "w_o", "w_gateup", "w_down", "w_fc1", "w_fc2")
+    return {k: (v.t().contiguous() if k in proj and v is not None else v) for k, v in weights.items()}
 
 
 def dense_index(B: int, S: int) -> Index:
@@ -340,13 +351,18 @@ def make_grads(cfg: LayerCfg, M: int, M_kept: int, device, dx_compact=False) -> 
     H, I, d = cfg.hidden, cfg.inter, cfg.head_dim
     nqkv = (cfg.n_q_heads + 2 * cfg.n_kv_heads) * d
     f32 = dict(dtype=torch.float32, device=device)
+    io = cfg.weight_layout == WEIGHTS_IN_OUT
+
+    def w(rows, cols):  # a weight gradient in the weights' layout
+        return torch.empty((cols, rows) if io else (rows, cols), **f32)
+
     g = {"dx": torch.empty((M_kept if dx_compact else M, H), dtype=torch.bfloat16, device=device),
-         "dw_qkv": torch.empty((nqkv, H), **f32), "dw_o": torch.empty((H, cfg.n_q_heads * d), **f32)}
+         "dw_qkv": w(nqkv, H), "dw_o": w(H, cfg.n_q_heads * d)}
     if cfg.kind == LAYER_LLAMA:
-        g.update(dw_gateup=torch.empty((2 * I, H), **f32), dw_down=torch.empty((H, I), **f32),
+        g.update(dw_gateup=w(2 * I, H), dw_down=w(H, I),
                  dgamma1=torch.empty(H, **f32), dgamma2=torch.empty(H, **f32))
     else:
-        g.update(dw_fc1=torch.empty((I, H), **f32), dw_fc2=torch.empty((H, I), **f32),
+        g.update(dw_fc1=w(I, H), dw_fc2=w(H, I),
                  dln_gamma=torch.empty(H, **f32), dln_beta=torch.empty(H, **f32))
     return g
 

@@ -1136,6 +1136,19 @@ collider_status launch_cfg(const GemmParams& gp, const GemmProblem& pr, const Pl
         if constexpr (kStaged) return launch_one<BM, BN, EPI_GELU, true, false>(gp, name, s);
         break;
     }
+  } else if (pr.a_kmajor && pr.b_kmajor) {
+    // activation gradients with weights stored [in, out] (each weight row K-contiguous): both
+    // operands read with 16-byte LDS reads
+    switch (pr.epi) {
+      case EPI_BF16:
+        if (pl.lds) return launch_lds<BM, BN, EPI_BF16, true, true>(gp, pl.grid, name, s);
+        if constexpr (kStaged) return launch_one<BM, BN, EPI_BF16, true, true>(gp, name, s);
+        break;
+      case EPI_SWIGLU:
+        if (pl.lds) return launch_lds<BM, BN, EPI_SWIGLU, true, true>(gp, pl.grid, name, s);
+        if constexpr (kStaged) return launch_one<BM, BN, EPI_SWIGLU, true, true>(gp, name, s);
+        break;
+    }
   } else if (!pr.a_kmajor && !pr.b_kmajor && pr.epi == EPI_F32) {
     if constexpr (kMnA) {
       if (pl.lds) return launch_lds<BM, BN, EPI_F32, false, false>(gp, pl.grid, name, s);

@@ -116,15 +116,29 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
   // GEMM problems (pointers are only meaningful when not dry)
   const int32_t* idx = unf ? nullptr : ix.idx;  // row map of the saved tensors (null: identity)
   GemmProblem g_dA{}, g_dw2{}, g_dXmid{}, g_dwmid{}, g_dO{}, g_dwo{}, g_dXin{}, g_dwqkv{}, g_dwfc1{};
+  // Weight layouts.  [out, in] (w, y = x w^T): the activation gradient dX = dY w reads w with
+  // n = in contiguous (B(k, n) = w[k][n]), the weight gradient is dw = dY^T X [out, in].
+  // [in, out] (W = w^T): dX = dY W^T reads each row of W contiguous along the reduction
+  // (B(k, n) = W[n][k]), the weight gradient is dW = X^T dY [in, out] - the same GEMM with the
+  // operands swapped.  `wout` is the weight's output width (its leading dimension when [out, in]
+  // is w's row length `win`).
+  const bool w_io = c.weight_layout == COLLIDER_WEIGHTS_IN_OUT;
   auto dx_gemm = [&](GemmProblem& p, int n, int k, const void* A, int64_t lda, const void* Bm,
                      int64_t ldb, int epi, void* C, int64_t ldc) {
+    // n: in features, k: out features; ldb: the row length of w [out, in] (= n)
     p.M = Mk; p.N = n; p.K = k;
     p.A = A; p.lda = lda; p.a_kmajor = true;
-    p.B0 = Bm; p.ldb = ldb; p.b_kmajor = false;
+    p.B0 = Bm; p.ldb = w_io ? k : ldb; p.b_kmajor = w_io;
     p.epi = epi; p.C = C; p.ldc = ldc;
   };
   auto dw_gemm = [&](GemmProblem& p, int m, int n, const void* A, int64_t lda, const void* Bm,
                      int64_t ldb, float* C) {
+    // dw [m = out, n = in] = dY^T [m, M'] X [M', n]; with [in, out] weights the transpose
+    if (w_io) {
+      std::swap(m, n);
+      std::swap(A, Bm);
+      std::swap(lda, ldb);
+    }
     p.M = m; p.N = n; p.K = Mk;
     p.A = A; p.lda = lda; p.a_kmajor = false;
     p.B0 = Bm; p.ldb = ldb; p.b_kmajor = false;
