@@ -614,7 +614,7 @@ struct FragOffsets {
 constexpr int wave_rows(int bm) { return (bm % 64 == 0) ? 2 : 1; }
 
 // MFMAs of one k-tile (KT / 16 steps of k = 16) from one LDS stage; fragments of step kk+1 are read
-// while the MFMAs of step kk run (two register sets).  With LOAD, the loads of a later k-tile (`ld`)
+// while the MFMAs of step kk run (two register sets), interleaved with them.  With LOAD, the loads of a later k-tile (`ld`)
 // go out one instruction at a time between the MFMAs, within the first SPN / SPD of them.
 template <int BM, int BN, bool AK, bool BKM, int KT, int SPN, int SPD, bool LOAD>
 __device__ __forceinline__ void mma_ktile(
@@ -637,15 +637,12 @@ __device__ __forceinline__ void mma_ktile(
   for (int i = 0; i < TM; ++i) af[0][i] = FA::read(aa, i, 0);
 #pragma unroll
   for (int j = 0; j < TN; ++j) bfv[0][j] = FB::read(ba, j, 0);
+  // the next k-step's fragments (A then B, NR reads) go out one at a time between the first half
+  // of this k-step's MFMAs: a burst of LDS reads ahead of the MFMAs would hold up MFMA issue
+  constexpr int NR = TM + TN;
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) {
     const int cur = kk & 1;
-    if (kk + 1 < KS) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) af[cur ^ 1][i] = FA::read(aa, i, kk + 1);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bfv[cur ^ 1][j] = FB::read(ba, j, kk + 1);
-    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -653,6 +650,19 @@ __device__ __forceinline__ void mma_ktile(
       for (int j = 0; j < TN; ++j) {
         acc[i][j] =
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfv[cur][j], acc[i][j], 0, 0, 0);
+        if (kk + 1 < KS) {
+          const int l = i * TN + j;  // MFMA number within the k-step
+#pragma unroll
+          for (int r = 0; r < NR; ++r)
+            if ((r * TM * TN) / (2 * NR) == l) {
+              __builtin_amdgcn_sched_barrier(0);
+              if (r < TM)
+                af[cur ^ 1][r] = FA::read(aa, r, kk + 1);
+              else
+                bfv[cur ^ 1][r - TM] = FB::read(ba, r - TM, kk + 1);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+        }
         if constexpr (LOAD) {
           const int n = (kk * TM + i) * TN + j;  // MFMA number within the k-tile
 #pragma unroll
