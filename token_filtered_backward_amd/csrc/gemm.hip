@@ -32,6 +32,7 @@ struct GemmParams {
   int k_split;  // reduction length handled by one split (multiple of the k-tile)
   int splits;
   int tiles_m, tiles_n;
+  int group_m;   // tile rows per group of the direct-to-LDS kernel's tile numbering (tile_coords)
   // work decomposition of the direct-to-LDS kernel: tiles [0, dp_tiles) are whole work items
   // (times `splits` K-splits); tiles [dp_tiles, dp_tiles + sk_tiles) are shared out as one
   // stream-K range of k-tiles per workgroup
@@ -316,6 +317,20 @@ __device__ __forceinline__ int xcd_remap(int L, int T) {
   const int per = T / 8;
   if (L < per * 8) return (L % 8) * per + L / 8;
   return L;
+}
+
+// Output tile (row, column) of tile number t in the direct-to-LDS kernel's numbering: column by
+// column within groups of group_m tile rows, one group after another.  A run of consecutive numbers
+// - what the workgroups of one XCD receive (xcd_remap) - then covers a compact block of tile rows
+// and columns, so the XCD's L2 serves few distinct A row panels and B column panels at a time
+// (row-major numbering gives one XCD a band of whole tile rows, which needs every B column).
+__device__ __forceinline__ void tile_coords(const GemmParams& p, int t, int& tm, int& tn) {
+  const int per_group = p.group_m * p.tiles_n;
+  const int g = t / per_group, first = g * p.group_m;
+  const int gm = min(p.group_m, p.tiles_m - first);
+  const int w = t - g * per_group;
+  tm = first + w % gm;
+  tn = w / gm;
 }
 
 // One workgroup of 4 wavefronts (2 x 2) computes a BM x BN tile; each wavefront a
@@ -760,7 +775,8 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
     } else {
       break;
     }
-    const int tm = t / p.tiles_n, tn = t % p.tiles_n;
+    int tm, tn;
+    tile_coords(p, t, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int nk = kt1 - kt0;
     const int kbeg = kt0 * BK;
@@ -883,7 +899,9 @@ __global__ __launch_bounds__(256) void sk_fixup_kernel(GemmParams p, int G) {
   const int g1 = (int)((e * G + n_it - 1) / n_it - 1);
   if (g0 == g1) return;  // one workgroup covered the whole tile and finished it
   const int t = p.dp_tiles + st;
-  const int m0 = (t / p.tiles_n) * BM, n0 = (t % p.tiles_n) * BN;
+  int tm, tn;
+  tile_coords(p, t, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
   const int cg = threadIdx.x % CPR, rsub = threadIdx.x / CPR;
   const int n = n0 + cg * 8;
   const int rfirst = blockIdx.y * ROWS + rsub;
@@ -1180,6 +1198,30 @@ collider_status launch_reduce(const GemmParams& gp, const GemmProblem& prob, int
   return last_hip_status();
 }
 
+// Tile rows per group of the tile numbering (tile_coords): the power of two that makes the block
+// of tiles one XCD runs at a time (about 32, one per CU) read the fewest operand bytes per k-step,
+// gm row panels of A (bm rows each) plus ceil(c / gm) column panels of B (bn columns each).
+int tile_group_rows(int tiles_m, int tiles_n, int bm, int bn) {
+  const int total = tiles_m * tiles_n;
+  const int c = std::max(1, std::min(32, (total + 7) / 8));
+  int best = 1;
+  double best_cost = 1e30;
+  for (int gm = 1; gm <= tiles_m; gm *= 2) {
+    // c consecutive tiles: within one group, min(gm, c) rows x ceil(c / gm) columns; past a
+    // group's gm * tiles_n tiles, whole groups of every column
+    const int per_group = gm * tiles_n;
+    const int rows = c <= per_group ? std::min(gm, c)
+                                    : std::min(tiles_m, gm * ((c + per_group - 1) / per_group));
+    const int cols = c <= per_group ? (c + gm - 1) / gm : tiles_n;
+    const double cost = (double)rows * bm + (double)cols * bn;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = gm;
+    }
+  }
+  return best;
+}
+
 }  // namespace
 
 void gemm_set_policy(int policy) { g_policy.store(policy, std::memory_order_relaxed); }
@@ -1212,6 +1254,7 @@ collider_status gemm_bf16(const GemmProblem& prob, void* ws, size_t ws_bytes, hi
   gp.splits = pl.splits;
   gp.tiles_m = (prob.M + pl.bm - 1) / pl.bm;
   gp.tiles_n = (prob.N + pl.bn - 1) / pl.bn;
+  gp.group_m = tile_group_rows(gp.tiles_m, gp.tiles_n, pl.bm, pl.bn);
   gp.ipt = pl.ipt;
   gp.dp_tiles = pl.dp_tiles;
   gp.sk_tiles = pl.sk_tiles;
