@@ -184,7 +184,7 @@ size_t collider_linear_workspace_bytes(collider_dtype dt, int32_t M_kept, int32_
   GemmProblem a, b;
   linear_problems(dt, M_kept, K, N, nullptr, K, nullptr, N, nullptr, nullptr, nullptr, 0, &a, &b);
   Carver cv(nullptr);
-  cv.take<float>((size_t)norm_bwd_parts(M_kept) * N);  // bias column-sum partials
+  cv.take<float>((size_t)colsum_parts_count(M_kept) * N);  // bias column-sum partials
   if (dt == COLLIDER_BF16)
     cv.take<char>(std::max(gemm_bf16_workspace_bytes(a), gemm_bf16_workspace_bytes(b)));
   return cv.bytes();
@@ -208,7 +208,7 @@ collider_status collider_linear_bwd_reduced(collider_dtype dt, int32_t M_kept, i
   GemmProblem pdx, pdw;
   linear_problems(dt, M_kept, K, N, x, ld_x, dy, ld_dy, w, dx, dw, accumulate, &pdx, &pdw);
   Carver cv(ws);
-  float* parts = cv.take<float>((size_t)norm_bwd_parts(M_kept) * N);
+  float* parts = cv.take<float>((size_t)colsum_parts_count(M_kept) * N);
   char* gws = cv.take<char>(0);
   const size_t gws_bytes = ws_bytes > (size_t)(gws - (char*)ws) ? ws_bytes - (gws - (char*)ws) : 0;
   collider_status st = COLLIDER_OK;

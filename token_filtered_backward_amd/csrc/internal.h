@@ -114,12 +114,19 @@ collider_status launch_norm_recompute(const uint16_t* x, const float* mean, cons
 // a = act(gate/f [rowmap[c]]) as bf16: SwiGLU (up != nullptr) or GELU-tanh (up == nullptr)
 collider_status launch_act_recompute(const uint16_t* g, const uint16_t* up, const int32_t* rowmap,
                                      int rows, int I, uint16_t* a, hipStream_t s);
-// dx = dres + norm_bwd(dxn; x[rowmap], stats) ; per-block partial sums for dgamma (and dbeta)
+// dx = dres + norm_bwd(dxn; x[rowmap], stats)
 collider_status launch_norm_bwd(const uint16_t* dxn, const uint16_t* dres, const uint16_t* x,
                                 const float* mean, const float* rstd, const float* gamma,
-                                const int32_t* rowmap, int rows, int H, uint16_t* dx,
-                                float* part_dgamma, float* part_dbeta, int n_part, hipStream_t s);
-int norm_bwd_parts(int rows);
+                                const int32_t* rowmap, int rows, int H, uint16_t* dx, hipStream_t s);
+// partial column sums for dgamma = sum dxn * xhat (and dbeta = sum dxn when part_dbeta != null):
+// n_part rows of H floats each, summed by launch_colsum_parts
+collider_status launch_norm_grad_parts(const uint16_t* dxn, const uint16_t* x, const float* mean,
+                                       const float* rstd, const int32_t* rowmap, int rows, int H,
+                                       float* part_dgamma, float* part_dbeta, int n_part,
+                                       hipStream_t s);
+int norm_grad_parts(int rows, int H);
+// partial-sum rows launch_colsum uses for `rows` rows
+int colsum_parts_count(int rows);
 collider_status launch_colsum_parts(const float* parts, int n_part, int H, float* out,
                                     int accumulate, hipStream_t s);
 // column sums of a bf16 / f32 matrix (bias gradient)

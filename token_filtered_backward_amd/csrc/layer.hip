@@ -61,6 +61,7 @@ struct LayerBufs {
   float* lse_c;
   uint16_t *act_c, *xn_c, *dmid, *dqkv, *dxn, *dh, *do_c, *dx_c;
   float *part_g, *part_b;
+  uint16_t* dxn1;
   void* gemm_ws;   // split-K partials of the GEMMs on the caller's stream
   void* gemm_ws2;  // ... and of the weight-gradient GEMMs on the side stream
   void* attn_ws;
@@ -79,7 +80,7 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
   const int H = c.hidden, I = c.inter, d = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
   const int nqd = nq * d, nkvd = nkv * d, nqkv = nqd + 2 * nkvd;
   const int mid = llama ? 2 * I : nqkv + I;  // width of [dgate|dup] or [dq|dk|dv|dF]
-  const int parts = norm_bwd_parts(Mk);
+  const int parts = norm_grad_parts(Mk, H);
   const bool dry = need != nullptr;
 
   Carver cv(dry ? nullptr : ws);
@@ -107,6 +108,9 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
   b.dqkv = llama ? cv.take<uint16_t>((size_t)Mk * nqkv) : b.dmid;
   const int ldq = llama ? nqkv : mid;
   b.dxn = cv.take<uint16_t>((size_t)Mk * H);
+  // the second norm backward's input gets its own buffer: the side stream may still be reading
+  // the first one's (for the gain gradient) when the QKV activation-gradient GEMM writes it
+  b.dxn1 = llama ? cv.take<uint16_t>((size_t)Mk * H) : b.dxn;
   b.dh = llama ? cv.take<uint16_t>((size_t)Mk * H) : nullptr;
   b.do_c = cv.take<uint16_t>((size_t)Mk * nqd);
   b.dx_c = (dx_compact || unf) ? (uint16_t*)(gr ? gr->dx : nullptr) : cv.take<uint16_t>((size_t)Mk * H);
@@ -157,7 +161,7 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     dw_gemm(g_dwmid, 2 * I, H, b.dmid, mid, b.xn_c, H, gr ? gr->dw_gateup : nullptr);
     dx_gemm(g_dO, nqd, H, b.dh, H, w ? w->w_o : nullptr, nqd, EPI_BF16, b.do_c, nqd);
     dw_gemm(g_dwo, H, nqd, b.dh, H, b.o_c, nqd, gr ? gr->dw_o : nullptr);
-    dx_gemm(g_dXin, H, nqkv, b.dqkv, ldq, w ? w->w_qkv : nullptr, H, EPI_BF16, b.dxn, H);
+    dx_gemm(g_dXin, H, nqkv, b.dqkv, ldq, w ? w->w_qkv : nullptr, H, EPI_BF16, b.dxn1, H);
     dw_gemm(g_dwqkv, nqkv, H, b.dqkv, ldq, b.xn_c, H, gr ? gr->dw_qkv : nullptr);
   } else {
     uint16_t* dF = b.dmid ? b.dmid + nqkv : nullptr;
@@ -283,10 +287,12 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     CHECK(gemm_bf16(g_dwmid, b.gemm_ws2, b.gemm_ws2_bytes, s1));
     CHECK(gemm_bf16(g_dXmid, b.gemm_ws, b.gemm_ws_bytes, s));
     CHECK(launch_norm_bwd(b.dxn, b.dy_c, (const uint16_t*)sv->h, nullptr, sv->rstd2, w->gamma2, idx,
-                          Mk, H, b.dh, b.part_g, nullptr, parts, s));
-    CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dgamma2, c.accumulate, s));
-    CHECK(handoff(2, s, s1));  // dh ready
+                          Mk, H, b.dh, s));
+    CHECK(handoff(2, s, s1));  // dh ready (and dXn2, for the gain gradient)
     CHECK(gemm_bf16(g_dwo, b.gemm_ws2, b.gemm_ws2_bytes, s1));
+    CHECK(launch_norm_grad_parts(b.dxn, (const uint16_t*)sv->h, nullptr, sv->rstd2, idx, Mk, H,
+                                 b.part_g, nullptr, parts, s1));
+    CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dgamma2, c.accumulate, s1));
     CHECK(gemm_bf16(g_dO, b.gemm_ws, b.gemm_ws_bytes, s));
     if (side && hipStreamWaitEvent(s, side->ev[6], 0) != hipSuccess) return COLLIDER_ERR_HIP;
     CHECK(attn_bwd(ac, aix, io, b.attn_ws, b.attn_ws_bytes, s));
@@ -295,9 +301,12 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
                                 Mk, H, b.xn_c, s1));
     CHECK(gemm_bf16(g_dwqkv, b.gemm_ws2, b.gemm_ws2_bytes, s1));
     CHECK(gemm_bf16(g_dXin, b.gemm_ws, b.gemm_ws_bytes, s));
-    CHECK(launch_norm_bwd(b.dxn, b.dh, (const uint16_t*)sv->x, nullptr, sv->rstd1, w->gamma1, idx, Mk,
-                          H, b.dx_c, b.part_g, nullptr, parts, s));
-    CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dgamma1, c.accumulate, s));
+    CHECK(handoff(7, s, s1));  // dXn1 ready: the gain gradient on the side stream
+    CHECK(launch_norm_grad_parts(b.dxn1, (const uint16_t*)sv->x, nullptr, sv->rstd1, idx, Mk, H,
+                                 b.part_g, nullptr, parts, s1));
+    CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dgamma1, c.accumulate, s1));
+    CHECK(launch_norm_bwd(b.dxn1, b.dh, (const uint16_t*)sv->x, nullptr, sv->rstd1, w->gamma1, idx, Mk,
+                          H, b.dx_c, s));
   } else {
     CHECK(launch_act_recompute((const uint16_t*)sv->f, nullptr, idx, Mk, I, b.act_c, s1));
     CHECK(launch_norm_recompute((const uint16_t*)sv->x, sv->mean, sv->rstd1, w->ln_gamma, w->ln_beta,
@@ -312,10 +321,13 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     CHECK(gemm_bf16(g_dwqkv, b.gemm_ws2, b.gemm_ws2_bytes, s1));
     CHECK(gemm_bf16(g_dwfc1, b.gemm_ws2, b.gemm_ws2_bytes, s1));
     CHECK(gemm_bf16(g_dXin, b.gemm_ws, b.gemm_ws_bytes, s));
+    CHECK(handoff(7, s, s1));  // dXn ready: the gain and bias gradients on the side stream
+    CHECK(launch_norm_grad_parts(b.dxn, (const uint16_t*)sv->x, sv->mean, sv->rstd1, idx, Mk, H,
+                                 b.part_g, b.part_b, parts, s1));
+    CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dln_gamma, c.accumulate, s1));
+    CHECK(launch_colsum_parts(b.part_b, Mk > 0 ? parts : 0, H, gr->dln_beta, c.accumulate, s1));
     CHECK(launch_norm_bwd(b.dxn, b.dy_c, (const uint16_t*)sv->x, sv->mean, sv->rstd1, w->ln_gamma,
-                          idx, Mk, H, b.dx_c, b.part_g, b.part_b, parts, s));
-    CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dln_gamma, c.accumulate, s));
-    CHECK(launch_colsum_parts(b.part_b, Mk > 0 ? parts : 0, H, gr->dln_beta, c.accumulate, s));
+                          idx, Mk, H, b.dx_c, s));
   }
   if (!dx_compact && !unf) CHECK(launch_scatter_bytes(b.dx_c, (int64_t)H * 2, gr->dx, (int64_t)H * 2, ix.inv,
                                               M, H * 2, 1, s));

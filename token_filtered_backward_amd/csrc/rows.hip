@@ -6,6 +6,8 @@
 // [M_kept, C] operands; the scatter puts results back with filtered rows exactly zero.
 #include "internal.h"
 
+#include <algorithm>
+
 namespace collider {
 
 // ------------------------------------------------------------------------------------------
@@ -336,12 +338,13 @@ collider_status launch_act_recompute(const uint16_t* g, const uint16_t* up, cons
 }
 
 // ------------------------------------------------------------------------------------------
-// norm backward + residual:
+// norm backward + residual, in two kernels:
 //   xhat = (x - mean) * rstd (mean = 0 for RMSNorm), g = dxn * gamma,
 //   RMSNorm:   dx = rstd * (g - xhat * mean(g * xhat))
 //   LayerNorm: dx = rstd * (g - mean(g) - xhat * mean(g * xhat))
-//   out = dres + dx (bf16); per-block partial column sums of dxn * xhat (and dxn)
-// One wavefront per row, the row held in registers (NV 8-element vectors per lane, H <= 512*NV).
+//   out = dres + dx (bf16)                          norm_bwd_kernel, on the activation-gradient path
+//   dgamma = sum_rows dxn * xhat, dbeta = sum_rows dxn    norm_grad_parts_kernel + colsum_parts,
+//                                                    which nothing on that path waits for
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -349,131 +352,149 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-template <int NV, bool LN>
+// One wavefront per row (4 rows per workgroup), the row in registers (NV 8-element vectors per
+// lane, H <= 512 * NV); all of a row's loads are issued together and nothing is kept across rows,
+// so that many wavefronts per SIMD hide the loads' latency.
+template <int NV>
 __global__ __launch_bounds__(256) void norm_bwd_kernel(
     const uint16_t* __restrict__ dxn, const uint16_t* __restrict__ dres,
     const uint16_t* __restrict__ x, const float* __restrict__ mean, const float* __restrict__ rstd,
     const float* __restrict__ gamma, const int32_t* __restrict__ rowmap, int rows, int H,
-    uint16_t* __restrict__ dx, float* __restrict__ part_dgamma, float* __restrict__ part_dbeta,
-    int rows_per_part) {
+    uint16_t* __restrict__ dx) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 4 + wave;
+  if (c >= rows) return;
   const int nvec = H >> 3;
-  float acc_g[NV][8], acc_b[NV][8];
+  const int64_t r = rowmap ? rowmap[c] : c;
+  const float mu = mean ? mean[r] : 0.f;
+  const float rs = rstd[r];
+  uint4 dv[NV], xv[NV], rv[NV];
 #pragma unroll
-  for (int i = 0; i < NV; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc_g[i][j] = acc_b[i][j] = 0.f;
-  const int c_begin = blockIdx.x * rows_per_part;
-  const int c_end = min(rows, c_begin + rows_per_part);
-  // few registers (the row's three inputs stay packed; gamma and x-hat are re-derived in the
-  // second sweep) so that many wavefronts per SIMD hide the loads' latency; all of a row's loads
-  // are issued together
-#pragma unroll 1
-  for (int c = c_begin + wave; c < c_end; c += 4) {
-    const int64_t r = rowmap ? rowmap[c] : c;
-    const float mu = mean ? mean[r] : 0.f;
-    const float rs = rstd[r];
-    uint4 dv[NV], xv[NV], rv[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int v = lane + 64 * i;
-      if (v < nvec) {
-        dv[i] = ((const uint4*)(dxn + (int64_t)c * H))[v];
-        xv[i] = ((const uint4*)(x + r * H))[v];
-        rv[i] = ((const uint4*)(dres + (int64_t)c * H))[v];
-      }
+  for (int i = 0; i < NV; ++i) {
+    const int v = lane + 64 * i;
+    if (v < nvec) {
+      dv[i] = ((const uint4*)(dxn + (int64_t)c * H))[v];
+      xv[i] = ((const uint4*)(x + r * H))[v];
+      rv[i] = ((const uint4*)(dres + (int64_t)c * H))[v];
     }
-    float s_g = 0.f, s_gx = 0.f;
+  }
+  float s_g = 0.f, s_gx = 0.f;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int v = lane + 64 * i;
-      if (v < nvec) {
-        const float4 g0 = ((const float4*)gamma)[2 * v], g1 = ((const float4*)gamma)[2 * v + 1];
-        const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-        const uint32_t dw[4] = {dv[i].x, dv[i].y, dv[i].z, dv[i].w};
-        const uint32_t xw[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+  for (int i = 0; i < NV; ++i) {
+    const int v = lane + 64 * i;
+    if (v < nvec) {
+      const float4 g0 = ((const float4*)gamma)[2 * v], g1 = ((const float4*)gamma)[2 * v + 1];
+      const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      const uint32_t dw[4] = {dv[i].x, dv[i].y, dv[i].z, dv[i].w};
+      const uint32_t xw[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float d = (j & 1) ? bfhi(dw[j >> 1]) : bflo(dw[j >> 1]);
-          const float xh = (((j & 1) ? bfhi(xw[j >> 1]) : bflo(xw[j >> 1])) - mu) * rs;
-          const float gv = d * gm[j];
-          s_g += gv;
-          s_gx += gv * xh;
-          acc_g[i][j] += d * xh;
-          if constexpr (LN) acc_b[i][j] += d;
-        }
-      }
-    }
-    s_g = wave_sum(s_g) / (float)H;
-    s_gx = wave_sum(s_gx) / (float)H;
-    if (!mean) s_g = 0.f;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int v = lane + 64 * i;
-      if (v < nvec) {
-        const float4 g0 = ((const float4*)gamma)[2 * v], g1 = ((const float4*)gamma)[2 * v + 1];
-        const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-        const uint32_t dw[4] = {dv[i].x, dv[i].y, dv[i].z, dv[i].w};
-        const uint32_t xw[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-        const uint32_t rw[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
-        uint32_t ow[4];
-#pragma unroll
-        for (int j2 = 0; j2 < 4; ++j2) {
-          const float g_a = bflo(dw[j2]) * gm[2 * j2], g_b = bfhi(dw[j2]) * gm[2 * j2 + 1];
-          const float x_a = (bflo(xw[j2]) - mu) * rs, x_b = (bfhi(xw[j2]) - mu) * rs;
-          const float a0 = bflo(rw[j2]) + rs * (g_a - s_g - x_a * s_gx);
-          const float a1 = bfhi(rw[j2]) + rs * (g_b - s_g - x_b * s_gx);
-          ow[j2] = pack2bf(a0, a1);
-        }
-        ((uint4*)(dx + (int64_t)c * H))[v] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+      for (int j = 0; j < 8; ++j) {
+        const float d = (j & 1) ? bfhi(dw[j >> 1]) : bflo(dw[j >> 1]);
+        const float xh = (((j & 1) ? bfhi(xw[j >> 1]) : bflo(xw[j >> 1])) - mu) * rs;
+        const float gv = d * gm[j];
+        s_g += gv;
+        s_gx += gv * xh;
       }
     }
   }
-  // combine the 4 wavefronts' column partials through LDS, in a fixed order
-  __shared__ float red[4][512];
+  s_g = wave_sum(s_g) / (float)H;
+  s_gx = wave_sum(s_gx) / (float)H;
+  if (!mean) s_g = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
+    const int v = lane + 64 * i;
+    if (v < nvec) {
+      const float4 g0 = ((const float4*)gamma)[2 * v], g1 = ((const float4*)gamma)[2 * v + 1];
+      const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      const uint32_t dw[4] = {dv[i].x, dv[i].y, dv[i].z, dv[i].w};
+      const uint32_t xw[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+      const uint32_t rw[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
+      uint32_t ow[4];
 #pragma unroll
-    for (int which = 0; which < (LN ? 2 : 1); ++which) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) red[wave][lane * 8 + j] = which ? acc_b[i][j] : acc_g[i][j];
-      __syncthreads();
-      for (int e = threadIdx.x; e < 512; e += 256) {
-        const int col = i * 512 + e;
-        if (col < H) {
-          const float sum = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
-          float* dst = which ? part_dbeta : part_dgamma;
-          dst[(int64_t)blockIdx.x * H + col] = sum;
-        }
+      for (int j2 = 0; j2 < 4; ++j2) {
+        const float g_a = bflo(dw[j2]) * gm[2 * j2], g_b = bfhi(dw[j2]) * gm[2 * j2 + 1];
+        const float x_a = (bflo(xw[j2]) - mu) * rs, x_b = (bfhi(xw[j2]) - mu) * rs;
+        const float a0 = bflo(rw[j2]) + rs * (g_a - s_g - x_a * s_gx);
+        const float a1 = bfhi(rw[j2]) + rs * (g_b - s_g - x_b * s_gx);
+        ow[j2] = pack2bf(a0, a1);
       }
-      __syncthreads();
+      ((uint4*)(dx + (int64_t)c * H))[v] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
     }
   }
 }
 
-// partial-sum rows of the norm backward (one per workgroup): enough workgroups to fill the CUs
-static constexpr int kNormParts = 1024;
-int norm_bwd_parts(int rows) { return rows <= 0 ? 1 : (rows < kNormParts ? rows : kNormParts); }
+// Partial column sums of dxn * xhat (and of dxn, LN) over one chunk of rows: workgroup
+// (column block cb, part p) covers 512 columns (8 per lane) and rows [p * rpp, (p + 1) * rpp), the
+// 4 wavefronts taking every fourth row; their sums are combined in a fixed order, so the result
+// is deterministic.  part_*[p, col].
+template <bool LN>
+__global__ __launch_bounds__(256) void norm_grad_parts_kernel(
+    const uint16_t* __restrict__ dxn, const uint16_t* __restrict__ x, const float* __restrict__ mean,
+    const float* __restrict__ rstd, const int32_t* __restrict__ rowmap, int rows, int H, int rpp,
+    float* __restrict__ part_dgamma, float* __restrict__ part_dbeta) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = blockIdx.x * 512 + lane * 8;
+  const bool on = col < H;
+  const int r0 = blockIdx.y * rpp, r1 = min(rows, r0 + rpp);
+  float ag[8], ab[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ag[j] = ab[j] = 0.f;
+#pragma unroll 2
+  for (int c = r0 + wave; c < r1; c += 4) {
+    const int64_t r = rowmap ? rowmap[c] : c;
+    const float mu = mean ? mean[r] : 0.f;
+    const float rs = rstd[r];
+    if (!on) continue;
+    const uint4 dv = *(const uint4*)(dxn + (int64_t)c * H + col);
+    const uint4 xv = *(const uint4*)(x + r * H + col);
+    const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w}, xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float d = (j & 1) ? bfhi(dw[j >> 1]) : bflo(dw[j >> 1]);
+      const float xh = (((j & 1) ? bfhi(xw[j >> 1]) : bflo(xw[j >> 1])) - mu) * rs;
+      ag[j] += d * xh;
+      if constexpr (LN) ab[j] += d;
+    }
+  }
+  __shared__ float red[2][4][512];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    red[0][wave][lane * 8 + j] = ag[j];
+    if constexpr (LN) red[1][wave][lane * 8 + j] = ab[j];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 512; e += 256) {
+    const int cc = blockIdx.x * 512 + e;
+    if (cc >= H) continue;
+    part_dgamma[(int64_t)blockIdx.y * H + cc] = ((red[0][0][e] + red[0][1][e]) + red[0][2][e]) + red[0][3][e];
+    if constexpr (LN)
+      part_dbeta[(int64_t)blockIdx.y * H + cc] = ((red[1][0][e] + red[1][1][e]) + red[1][2][e]) + red[1][3][e];
+  }
+}
+
+// partial-sum rows of a column sum over `rows` rows (bias gradient): enough to fill the CUs
+int colsum_parts_count(int rows) { return rows <= 0 ? 1 : (rows < 1024 ? rows : 1024); }
+
+// partial-sum rows of the gain gradients: enough workgroups (parts x 512-column blocks) to fill
+// the CUs, at least 4 rows per part
+int norm_grad_parts(int rows, int H) {
+  const int blocks = (H + 511) / 512;
+  int p = 1024 / blocks;
+  p = std::min(p, std::max(1, rows / 4));
+  return std::max(1, p);
+}
 
 collider_status launch_norm_bwd(const uint16_t* dxn, const uint16_t* dres, const uint16_t* x,
                                 const float* mean, const float* rstd, const float* gamma,
-                                const int32_t* rowmap, int rows, int H, uint16_t* dx,
-                                float* part_dgamma, float* part_dbeta, int n_part, hipStream_t s) {
-  const int rpp = rows <= 0 ? 1 : (rows + n_part - 1) / n_part;
+                                const int32_t* rowmap, int rows, int H, uint16_t* dx, hipStream_t s) {
+  if (rows <= 0) return COLLIDER_OK;
   const int nv = (H / 8 + 63) / 64;
-  dim3 grid(n_part), block(256);
+  dim3 grid((rows + 3) / 4), block(256);
 #define NB_CASE(N)                                                                              \
   case N:                                                                                       \
-    if (part_dbeta)                                                                             \
-      COLLIDER_LAUNCH("norm_bwd", s,                                                            \
-                      hipLaunchKernelGGL((norm_bwd_kernel<N, true>), grid, block, 0, s, dxn, dres, \
-                                         x, mean, rstd, gamma, rowmap, rows, H, dx, part_dgamma, \
-                                         part_dbeta, rpp));                                     \
-    else                                                                                        \
-      COLLIDER_LAUNCH("norm_bwd", s,                                                            \
-                      hipLaunchKernelGGL((norm_bwd_kernel<N, false>), grid, block, 0, s, dxn,   \
-                                         dres, x, mean, rstd, gamma, rowmap, rows, H, dx,       \
-                                         part_dgamma, part_dbeta, rpp));                        \
+    COLLIDER_LAUNCH("norm_bwd", s,                                                              \
+                    hipLaunchKernelGGL((norm_bwd_kernel<N>), grid, block, 0, s, dxn, dres, x,   \
+                                       mean, rstd, gamma, rowmap, rows, H, dx));                \
     break;
   switch (nv) {
     NB_CASE(1) NB_CASE(2) NB_CASE(3) NB_CASE(4) NB_CASE(5) NB_CASE(6) NB_CASE(7) NB_CASE(8)
@@ -481,6 +502,24 @@ collider_status launch_norm_bwd(const uint16_t* dxn, const uint16_t* dres, const
       return COLLIDER_ERR_UNSUPPORTED;
   }
 #undef NB_CASE
+  return last_hip_status();
+}
+
+collider_status launch_norm_grad_parts(const uint16_t* dxn, const uint16_t* x, const float* mean,
+                                       const float* rstd, const int32_t* rowmap, int rows, int H,
+                                       float* part_dgamma, float* part_dbeta, int n_part,
+                                       hipStream_t s) {
+  if (rows <= 0) return COLLIDER_OK;
+  const int rpp = (rows + n_part - 1) / n_part;
+  dim3 grid((H + 511) / 512, n_part), block(256);
+  if (part_dbeta)
+    COLLIDER_LAUNCH("norm_grad_parts", s,
+                    hipLaunchKernelGGL((norm_grad_parts_kernel<true>), grid, block, 0, s, dxn, x,
+                                       mean, rstd, rowmap, rows, H, rpp, part_dgamma, part_dbeta));
+  else
+    COLLIDER_LAUNCH("norm_grad_parts", s,
+                    hipLaunchKernelGGL((norm_grad_parts_kernel<false>), grid, block, 0, s, dxn, x,
+                                       mean, rstd, rowmap, rows, H, rpp, part_dgamma, part_dbeta));
   return last_hip_status();
 }
 
@@ -556,7 +595,7 @@ __global__ void colsum_partial_kernel(const void* __restrict__ x, int64_t ld, in
 
 collider_status launch_colsum(const void* x, int64_t ld, int rows, int cols, bool bf16, float* out,
                               int accumulate, float* ws, hipStream_t s) {
-  const int n_part = norm_bwd_parts(rows);
+  const int n_part = colsum_parts_count(rows);
   const int rpp = rows <= 0 ? 1 : (rows + n_part - 1) / n_part;
   COLLIDER_LAUNCH("colsum_partial", s,
                   hipLaunchKernelGGL(colsum_partial_kernel, dim3(n_part, (cols + 255) / 256),
