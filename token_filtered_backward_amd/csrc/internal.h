@@ -103,6 +103,8 @@ collider_status launch_gather_rows(const GatherDesc* d, int n_desc, const int32_
                                    hipStream_t s);
 collider_status launch_gather_bytes(const void* src, int64_t ld_src_b, void* dst, int64_t ld_dst_b,
                                     const int32_t* idx, int n_rows, int row_bytes, hipStream_t s);
+// dst[t] = src[inv[t]] for kept t; filtered t: zeros (zero_fill 1) or untouched (0); zero_fill 2:
+// only the filtered rows, as zeros (src unused)
 collider_status launch_scatter_bytes(const void* src, int64_t ld_src_b, void* dst, int64_t ld_dst_b,
                                      const int32_t* inv, int M, int row_bytes, int zero_fill,
                                      hipStream_t s);
@@ -114,10 +116,12 @@ collider_status launch_norm_recompute(const uint16_t* x, const float* mean, cons
 // a = act(gate/f [rowmap[c]]) as bf16: SwiGLU (up != nullptr) or GELU-tanh (up == nullptr)
 collider_status launch_act_recompute(const uint16_t* g, const uint16_t* up, const int32_t* rowmap,
                                      int rows, int I, uint16_t* a, hipStream_t s);
-// dx = dres + norm_bwd(dxn; x[rowmap], stats)
+// dx = dres + norm_bwd(dxn; x[rowmap], stats): row c of dx, or row rowmap[c] when dx_full != 0
+// (the full token layout)
 collider_status launch_norm_bwd(const uint16_t* dxn, const uint16_t* dres, const uint16_t* x,
                                 const float* mean, const float* rstd, const float* gamma,
-                                const int32_t* rowmap, int rows, int H, uint16_t* dx, hipStream_t s);
+                                const int32_t* rowmap, int rows, int H, uint16_t* dx, int dx_full,
+                                hipStream_t s);
 // partial column sums for dgamma = sum dxn * xhat (and dbeta = sum dxn when part_dbeta != null):
 // n_part rows of H floats each, summed by launch_colsum_parts
 collider_status launch_norm_grad_parts(const uint16_t* dxn, const uint16_t* x, const float* mean,

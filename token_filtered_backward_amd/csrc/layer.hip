@@ -113,7 +113,10 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
   b.dxn1 = llama ? cv.take<uint16_t>((size_t)Mk * H) : b.dxn;
   b.dh = llama ? cv.take<uint16_t>((size_t)Mk * H) : nullptr;
   b.do_c = cv.take<uint16_t>((size_t)Mk * nqd);
-  b.dx_c = (dx_compact || unf) ? (uint16_t*)(gr ? gr->dx : nullptr) : cv.take<uint16_t>((size_t)Mk * H);
+  // the last norm backward writes dx itself: compact rows, the full layout when unfiltered, or the
+  // kept rows of the full layout (their filtered rows zeroed on the side stream)
+  b.dx_c = (uint16_t*)(gr ? gr->dx : nullptr);
+  const int dx_full = (!dx_compact && !unf) ? 1 : 0;
   b.part_g = cv.take<float>((size_t)parts * H);
   b.part_b = cv.take<float>((size_t)parts * H);
 
@@ -252,6 +255,8 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     CHECK(launch_gather_rows(&gd, 1, idx, Mk, s));
   }
   CHECK(handoff(5, s, s1));  // fork: dY' ready
+  if (dx_full)  // the filtered rows of dx: +0.0 (the kept rows come from the last norm backward)
+    CHECK(launch_scatter_bytes(nullptr, 0, gr->dx, (int64_t)H * 2, ix.inv, M, H * 2, 2, s1));
   if (Mk > 0 && !unf) {  // 2. saved tensors attention and dW_o read as compacted operands
     GatherDesc gd[5];
     int nd = 0;
@@ -287,7 +292,7 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     CHECK(gemm_bf16(g_dwmid, b.gemm_ws2, b.gemm_ws2_bytes, s1));
     CHECK(gemm_bf16(g_dXmid, b.gemm_ws, b.gemm_ws_bytes, s));
     CHECK(launch_norm_bwd(b.dxn, b.dy_c, (const uint16_t*)sv->h, nullptr, sv->rstd2, w->gamma2, idx,
-                          Mk, H, b.dh, s));
+                          Mk, H, b.dh, 0, s));
     CHECK(handoff(2, s, s1));  // dh ready (and dXn2, for the gain gradient)
     CHECK(gemm_bf16(g_dwo, b.gemm_ws2, b.gemm_ws2_bytes, s1));
     CHECK(launch_norm_grad_parts(b.dxn, (const uint16_t*)sv->h, nullptr, sv->rstd2, idx, Mk, H,
@@ -306,7 +311,7 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
                                  b.part_g, nullptr, parts, s1));
     CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dgamma1, c.accumulate, s1));
     CHECK(launch_norm_bwd(b.dxn1, b.dh, (const uint16_t*)sv->x, nullptr, sv->rstd1, w->gamma1, idx, Mk,
-                          H, b.dx_c, s));
+                          H, b.dx_c, dx_full, s));
   } else {
     CHECK(launch_act_recompute((const uint16_t*)sv->f, nullptr, idx, Mk, I, b.act_c, s1));
     CHECK(launch_norm_recompute((const uint16_t*)sv->x, sv->mean, sv->rstd1, w->ln_gamma, w->ln_beta,
@@ -327,10 +332,8 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dln_gamma, c.accumulate, s1));
     CHECK(launch_colsum_parts(b.part_b, Mk > 0 ? parts : 0, H, gr->dln_beta, c.accumulate, s1));
     CHECK(launch_norm_bwd(b.dxn, b.dy_c, (const uint16_t*)sv->x, sv->mean, sv->rstd1, w->ln_gamma,
-                          idx, Mk, H, b.dx_c, s));
+                          idx, Mk, H, b.dx_c, dx_full, s));
   }
-  if (!dx_compact && !unf) CHECK(launch_scatter_bytes(b.dx_c, (int64_t)H * 2, gr->dx, (int64_t)H * 2, ix.inv,
-                                              M, H * 2, 1, s));
   CHECK(handoff(4, s1, s));  // join: every weight gradient is complete on the caller's stream
 #undef CHECK
   return COLLIDER_OK;

@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4* __restri
       if (i < items) {
         const int rr = pow2 ? i >> sh : i / per_row, c = pow2 ? i & (per_row - 1) : i - rr * per_row;
         const int ci = s_inv[rr];
-        if (ci >= 0) v[u] = src[(int64_t)ci * ld_src + c];
+        if (ci >= 0 && zero_fill != 2) v[u] = src[(int64_t)ci * ld_src + c];
       }
     }
 #pragma unroll
@@ -170,7 +170,8 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4* __restri
       const int i = base + threadIdx.x + 256 * u;
       if (i < items) {
         const int rr = pow2 ? i >> sh : i / per_row, c = pow2 ? i & (per_row - 1) : i - rr * per_row;
-        if (zero_fill || s_inv[rr] >= 0) dst[(int64_t)(r0 + rr) * ld_dst + c] = v[u];
+        const bool kept = s_inv[rr] >= 0;
+        if (zero_fill == 2 ? !kept : (zero_fill || kept)) dst[(int64_t)(r0 + rr) * ld_dst + c] = v[u];
       }
     }
   }
@@ -184,6 +185,7 @@ __global__ void scatter_u16_kernel(const uint16_t* __restrict__ src, int64_t ld_
   if (t >= M) return;
   const int c = inv[t];
   if (c < 0 && !zero_fill) return;
+  if (c >= 0 && zero_fill == 2) return;
   for (int j = threadIdx.x; j < row_u16; j += blockDim.x)
     dst[(int64_t)t * ld_dst + j] = c >= 0 ? src[(int64_t)c * ld_src + j] : (uint16_t)0;
 }
@@ -360,7 +362,7 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(
     const uint16_t* __restrict__ dxn, const uint16_t* __restrict__ dres,
     const uint16_t* __restrict__ x, const float* __restrict__ mean, const float* __restrict__ rstd,
     const float* __restrict__ gamma, const int32_t* __restrict__ rowmap, int rows, int H,
-    uint16_t* __restrict__ dx) {
+    uint16_t* __restrict__ dx, int dx_full) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = blockIdx.x * 4 + wave;
   if (c >= rows) return;
@@ -418,7 +420,7 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(
         const float a1 = bfhi(rw[j2]) + rs * (g_b - s_g - x_b * s_gx);
         ow[j2] = pack2bf(a0, a1);
       }
-      ((uint4*)(dx + (int64_t)c * H))[v] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+      ((uint4*)(dx + (dx_full ? r : (int64_t)c) * H))[v] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
     }
   }
 }
@@ -486,7 +488,8 @@ int norm_grad_parts(int rows, int H) {
 
 collider_status launch_norm_bwd(const uint16_t* dxn, const uint16_t* dres, const uint16_t* x,
                                 const float* mean, const float* rstd, const float* gamma,
-                                const int32_t* rowmap, int rows, int H, uint16_t* dx, hipStream_t s) {
+                                const int32_t* rowmap, int rows, int H, uint16_t* dx, int dx_full,
+                                hipStream_t s) {
   if (rows <= 0) return COLLIDER_OK;
   const int nv = (H / 8 + 63) / 64;
   dim3 grid((rows + 3) / 4), block(256);
@@ -494,7 +497,7 @@ collider_status launch_norm_bwd(const uint16_t* dxn, const uint16_t* dres, const
   case N:                                                                                       \
     COLLIDER_LAUNCH("norm_bwd", s,                                                              \
                     hipLaunchKernelGGL((norm_bwd_kernel<N>), grid, block, 0, s, dxn, dres, x,   \
-                                       mean, rstd, gamma, rowmap, rows, H, dx));                \
+                                       mean, rstd, gamma, rowmap, rows, H, dx, dx_full));       \
     break;
   switch (nv) {
     NB_CASE(1) NB_CASE(2) NB_CASE(3) NB_CASE(4) NB_CASE(5) NB_CASE(6) NB_CASE(7) NB_CASE(8)
