@@ -486,20 +486,27 @@ def test_layer_repeat_is_deterministic():
         assert torch.equal(a[k], b[k]), k
 
 
-@pytest.mark.parametrize("name", ["small_llama", "small_llama_d128", "small_phi"])
-def test_unfiltered_baseline(name):
+@pytest.mark.parametrize("name,layout", [("small_llama", 0), ("small_llama_d128", 0), ("small_phi", 0),
+                                         ("small_llama", 1)])
+def test_unfiltered_baseline(name, layout):
     """The dense baseline equals the filtered path with every token kept (same kernels, same
-    numerics, dmode FULL) and the oracle's ordinary backward."""
+    numerics, dmode FULL) and the oracle's ordinary backward, in either weight layout."""
     cfg = synth.get_config(name)
     inp = synth.make_layer_inputs(cfg, keep=np.ones(cfg.M, np.uint8))
     weights, saved, dy = _upload_layer(inp)
-    g_unf = tfb.layer_bwd(tfb.layer_cfg(cfg, unfiltered=True), weights, saved, dy,
+    if layout == tfb.WEIGHTS_IN_OUT:
+        weights = tfb.to_in_out(weights)
+    g_unf = tfb.layer_bwd(tfb.layer_cfg(cfg, unfiltered=True, weight_layout=layout), weights, saved, dy,
                           tfb.dense_index(cfg.B, cfg.S))
     ix = tfb.build_index(_dev_keep(inp["keep"]), cfg.B, cfg.S)
-    g_all = tfb.layer_bwd(tfb.layer_cfg(cfg, dmode=tfb.ATTN_D_FULL), weights, saved, dy, ix)
+    g_all = tfb.layer_bwd(tfb.layer_cfg(cfg, dmode=tfb.ATTN_D_FULL, weight_layout=layout), weights, saved,
+                          dy, ix)
     for k in g_unf:
         assert torch.equal(g_unf[k], g_all[k]), k
     ref = oracle.layer_bwd(cfg, upcast(inp["weights"]), upcast(inp["saved"]),
                            synth.bf16_bits_to_f32(inp["dy"]), inp["keep"], "full_d")
     for gname, oname in GRAD_NAMES[cfg.kind].items():
-        assert rel_err(to64(g_unf[gname]), ref[oname]) <= BF16_TOL, gname
+        got = to64(g_unf[gname])
+        if layout == tfb.WEIGHTS_IN_OUT and gname.startswith("dw_"):
+            got = got.T
+        assert rel_err(got, ref[oname]) <= BF16_TOL, gname
