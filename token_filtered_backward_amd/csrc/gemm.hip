@@ -505,20 +505,20 @@ __device__ __forceinline__ void dma16(rsrc_t rs, uint32_t m0, uint32_t voff, uin
                : "memory", "m0");
 }
 
-// Direct loads of one operand tile, [R x KT] (K-major) or [KT x R] (MN-major) in LDS.  Wave w
-// issues loads q = w, w + 4, ...; load q fills LDS bytes [1024 q, 1024 q + 1024) of the tile.  The
-// per-lane byte offsets (relative to the k-tile's source, see ktile_src) are computed once per
+// Direct loads of one operand tile, [R x KT] (K-major) or [KT x R] (MN-major) in LDS.  Wave w of
+// NW issues loads q = w, w + NW, ...; load q fills LDS bytes [1024 q, 1024 q + 1024) of the tile.
+// The per-lane byte offsets (relative to the k-tile's source, see ktile_src) are computed once per
 // output tile.
-template <int R, bool KMAJ, int KT>
+template <int R, bool KMAJ, int KT, int NW>
 struct TileDMA {
-  static constexpr int NI = R * KT * 2 / 1024, PW = NI / 4;
-  static_assert(NI % 4 == 0, "every wave issues the same number of loads");
+  static constexpr int NI = R * KT * 2 / 1024, PW = NI / NW;
+  static_assert(NI % NW == 0, "every wave issues the same number of loads");
   uint32_t off[PW];
   // mn0: first row (K-major) or first column (MN-major) of the tile in the operand
   __device__ __forceinline__ void init(int64_t ld, int mn0, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
-      const int b = (wave + 4 * i) * 1024 + lane * 16;
+      const int b = (wave + NW * i) * 1024 + lane * 16;
       if constexpr (KMAJ) {
         const int r = b / (2 * KT), pos = (b >> 4) & (KT / 8 - 1);
         const int c = pos ^ ((r >> 1) & (KT / 8 - 1));
@@ -533,17 +533,25 @@ struct TileDMA {
   // load I (< PW) of this wave; mw = LDS byte address of the wave's first slot in the tile
   template <int I>
   __device__ __forceinline__ void issue_one(const KSrc& s, uint32_t mw) const {
-    dma16(s.rs, mw + (uint32_t)I * 4096u, off[I], s.soff);
+    dma16(s.rs, mw + (uint32_t)I * (uint32_t)(NW * 1024), off[I], s.soff);
   }
 };
+
+// Wavefronts per workgroup of the direct-to-LDS kernel: 8 (two per SIMD, so that one wavefront's
+// waits are covered by the other's MFMAs) for 256 x 256 tiles, 4 otherwise.
+constexpr int lds_waves(int bm, int bn) { return (bm == 256 && bn == 256) ? 8 : 4; }
+// Wavefront grid over a BM x BN tile: 2 x (NW / 2) when BM / 2 is a multiple of 32, else 1 x 4
+// (BM = 160, 224: each wavefront covers all rows and a quarter of the columns).
+constexpr int wave_rows(int bm, int bn) { return (bm % 64 == 0) ? 2 : 1; }
+constexpr int wave_cols(int bm, int bn) { return lds_waves(bm, bn) / wave_rows(bm, bn); }
 
 // The loads of one k-tile (A then B) into an LDS stage, one instruction at a time, so that they can
 // be spread between MFMAs: a burst of 1 KB loads from every wavefront would queue at the CU's vector
 // memory unit and stall the wavefronts' MFMA issue behind it.
 template <int BM, int BN, bool AK, bool BKM, int KT>
 struct StageLoader {
-  using TA = TileDMA<BM, AK, KT>;
-  using TB = TileDMA<BN, BKM, KT>;
+  using TA = TileDMA<BM, AK, KT, lds_waves(BM, BN)>;
+  using TB = TileDMA<BN, BKM, KT, lds_waves(BM, BN)>;
   static constexpr int N = TA::PW + TB::PW;
   const TA& da;
   const TB& db;
@@ -624,21 +632,17 @@ struct FragOffsets {
 #define VMCNT_WAIT(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 0xf) | (((n) >> 4) << 14) | (0x7 << 4) | (0xf << 8))
 
-// Wavefront layout of a BM x BN tile: 2 x 2 wavefronts when BM / 2 is a multiple of 32, else
-// 1 x 4 (BM = 160, 224: each wavefront covers all rows and a quarter of the columns).
-constexpr int wave_rows(int bm) { return (bm % 64 == 0) ? 2 : 1; }
-
 // MFMAs of one k-tile (KT / 16 steps of k = 16) from one LDS stage; fragments of step kk+1 are read
 // while the MFMAs of step kk run (two register sets), interleaved with them.  With LOAD, the loads of a later k-tile (`ld`)
 // go out one instruction at a time between the MFMAs, within the first SPN / SPD of them.
 template <int BM, int BN, bool AK, bool BKM, int KT, int SPN, int SPD, bool LOAD>
 __device__ __forceinline__ void mma_ktile(
     uint32_t As, uint32_t Bs,
-    f32x16 (&acc)[BM / wave_rows(BM) / 32][BN / (4 / wave_rows(BM)) / 32],
-    const FragOffsets<BM, AK, KT, BM / wave_rows(BM) / 32>& fa,
-    const FragOffsets<BN, BKM, KT, BN / (4 / wave_rows(BM)) / 32>& fb,
+    f32x16 (&acc)[BM / wave_rows(BM, BN) / 32][BN / wave_cols(BM, BN) / 32],
+    const FragOffsets<BM, AK, KT, BM / wave_rows(BM, BN) / 32>& fa,
+    const FragOffsets<BN, BKM, KT, BN / wave_cols(BM, BN) / 32>& fb,
     const StageLoader<BM, BN, AK, BKM, KT>& ld) {
-  constexpr int WGM = wave_rows(BM), WGN = 4 / WGM;
+  constexpr int WGM = wave_rows(BM, BN), WGN = wave_cols(BM, BN);
   constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32, KS = KT / 16;
   constexpr int NQ = StageLoader<BM, BN, AK, BKM, KT>::N, MT = KS * TM * TN;
   static_assert(MT * SPN >= NQ * SPD && SPN <= SPD, "every load gets an MFMA slot");
@@ -703,14 +707,15 @@ __device__ __forceinline__ void mma_ktile(
 // epilogue.  No workgroup waits on another, and every sum has a fixed order, so results are
 // deterministic.
 template <int BM, int BN, int KT, bool AK, bool BKM, int EPI, int NS>
-__global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
+__global__ __launch_bounds__(64 * lds_waves(BM, BN)) void gemm_lds_kernel(GemmParams p) {
   constexpr int BK = KT;
-  constexpr int WGM = wave_rows(BM), WGN = 4 / WGM;
+  constexpr int NW = lds_waves(BM, BN), NT = 64 * NW;
+  constexpr int WGM = wave_rows(BM, BN), WGN = wave_cols(BM, BN);
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wavefront blocks of whole 32 x 32 MFMA tiles");
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
-  constexpr int LPW = (A_BYTES + B_BYTES) / 1024 / 4;  // load instructions per wave per k-tile
+  constexpr int LPW = (A_BYTES + B_BYTES) / 1024 / NW;  // load instructions per wave per k-tile
   static_assert(NS <= 3 && LPW * (NS - 2) < 64, "vmcnt range");
   extern __shared__ __align__(16) char lds[];
 
@@ -727,7 +732,7 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
   const uint32_t b0_bytes = (uint32_t)((int64_t)(BKM ? p.N : kseg) * p.ldb * 2);
   const uint32_t b1_bytes = (uint32_t)((int64_t)(BKM ? p.N : p.K - kseg) * p.ldb * 2);
   // the loads of the k-tile starting at reduction index k into the LDS stage at byte address st
-  auto loader = [&](const TileDMA<BM, AK, KT>& da, const TileDMA<BN, BKM, KT>& db, int k,
+  auto loader = [&](const TileDMA<BM, AK, KT, NW>& da, const TileDMA<BN, BKM, KT, NW>& db, int k,
                     uint32_t st, bool on) {
     const bool seg1 = two_seg && k >= kseg;
     const uint32_t mw = st + (uint32_t)wave * 1024u;
@@ -780,8 +785,8 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
     const int m0 = tm * BM, n0 = tn * BN;
     const int nk = kt1 - kt0;
     const int kbeg = kt0 * BK;
-    TileDMA<BM, AK, KT> da;
-    TileDMA<BN, BKM, KT> db;
+    TileDMA<BM, AK, KT, NW> da;
+    TileDMA<BN, BKM, KT, NW> db;
     da.init(p.lda, m0, wave, lane);
     db.init(p.ldb, n0, wave, lane);
 
@@ -790,12 +795,12 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmParams p) {
     constexpr int LDE = BN + 8;  // +8 floats: the two lane halves' rows land 32 banks apart
     // rows per pass: a divisor of BM that fits the stage buffers; epilogues with two 16-byte side
     // inputs per 8 outputs take shorter passes (registers)
-    constexpr int EROWS_REG = (EPI == EPI_SWIGLU || EPI == EPI_F32) ? 32 : 64;
+    constexpr int EROWS_REG = (EPI == EPI_SWIGLU || EPI == EPI_F32 || NW == 8) ? 32 : 64;
     constexpr int EROWS = (BM <= EROWS_REG && BM * LDE * 4 <= NS * STAGE) ? BM
                           : (BM % 64 == 0 && 64 <= EROWS_REG && 64 * LDE * 4 <= NS * STAGE) ? 64 : 32;
     static_assert(BM % EROWS == 0 && EROWS % 32 == 0, "epilogue passes cover whole accumulator blocks");
     static_assert(EROWS * LDE * 4 <= NS * STAGE, "epilogue pass must fit in the stage buffers");
-    constexpr int CPR = BN / 8, RSTEP = 256 / CPR, GPT = EROWS / RSTEP;
+    constexpr int CPR = BN / 8, RSTEP = NT / CPR, GPT = EROWS / RSTEP;
     static_assert(EROWS % RSTEP == 0, "epilogue rows per pass");
     const int cg = threadIdx.x % CPR, rsub = threadIdx.x / CPR;
     const int n = n0 + cg * 8;
@@ -1120,7 +1125,8 @@ collider_status launch_lds(const GemmParams& gp, int grid, const char* name, hip
   auto kern = gemm_lds_kernel<BM, BN, KT, AK, BKM, EPI, NS>;
   static std::atomic<uint64_t> attr_set{0};  // devices whose LDS limit is raised for this kernel
   set_lds_limit_once((const void*)kern, (int)lds, attr_set);
-  COLLIDER_LAUNCH(name, s, hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, gp));
+  COLLIDER_LAUNCH(name, s,
+                  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * lds_waves(BM, BN)), lds, s, gp));
   collider_status st = last_hip_status();
   if (st != COLLIDER_OK || gp.sk_tiles == 0) return st;
   COLLIDER_LAUNCH("gemm_sk_fixup", s,
