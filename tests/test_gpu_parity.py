@@ -360,14 +360,16 @@ def test_layer_parity_gemm_policies(gemm_policy, policy, name):
     run_layer_and_compare(inp, 0)
 
 
-@pytest.mark.parametrize("name", ["small_llama", "small_phi"])
-def test_layer_all_filtered(name):
+@pytest.mark.parametrize("name,layout", [("small_llama", 0), ("small_phi", 0), ("small_llama", 1)])
+def test_layer_all_filtered(name, layout):
     cfg = synth.get_config(name)
     inp = synth.make_layer_inputs(cfg, keep=np.zeros(cfg.M, np.uint8))
     weights, saved, dy = _upload_layer(inp)
+    if layout == tfb.WEIGHTS_IN_OUT:
+        weights = tfb.to_in_out(weights)
     ix = tfb.build_index(_dev_keep(inp["keep"]), cfg.B, cfg.S)
     assert ix.M_kept == 0
-    lcfg = tfb.layer_cfg(cfg)
+    lcfg = tfb.layer_cfg(cfg, weight_layout=layout)
     grads = tfb.make_grads(lcfg, cfg.M, 0, "cuda")
     for g in grads.values():
         g.fill_(float("nan"))
@@ -376,13 +378,16 @@ def test_layer_all_filtered(name):
         assert torch.all(g == 0).item(), k
 
 
-def test_layer_compact_chain_matches_full_layout():
+@pytest.mark.parametrize("layout", [0, 1])
+def test_layer_compact_chain_matches_full_layout(layout):
     """dx_compact of the upper layer feeding dy_compact of the lower one equals the full-layout path."""
     cfg = synth.get_config("small_llama")
     inp = synth.make_layer_inputs(cfg)
     weights, saved, dy = _upload_layer(inp)
+    if layout == tfb.WEIGHTS_IN_OUT:
+        weights = tfb.to_in_out(weights)
     ix = tfb.build_index(_dev_keep(inp["keep"]), cfg.B, cfg.S)
-    lcfg = tfb.layer_cfg(cfg)
+    lcfg = tfb.layer_cfg(cfg, weight_layout=layout)
     g_full = tfb.make_grads(lcfg, cfg.M, ix.M_kept, "cuda")
     tfb.layer_bwd(lcfg, weights, saved, dy, ix, g_full)
     g_c = tfb.make_grads(lcfg, cfg.M, ix.M_kept, "cuda", dx_compact=True)
