@@ -569,8 +569,17 @@ size_t attn_workspace_bytes(const collider_attn_cfg& c, int B, int S, int M_kept
   return carve_attn(c, B, S, M_kept, nullptr).bytes;
 }
 
+collider_status attn_rope_prepare(const collider_attn_cfg& c, const collider_index& ix, void* ws,
+                                  size_t ws_bytes, hipStream_t s) {
+  if (ix.M_kept <= 0 || c.rot_dims <= 0) return COLLIDER_OK;
+  AttnWs w = carve_attn(c, ix.B, ix.S, ix.M_kept, ws);
+  if (ws_bytes < w.bytes) return COLLIDER_ERR_WORKSPACE;
+  return launch_rope_table(w.rope, ix.S, c.rot_dims, c.rope_base, s);
+}
+
 collider_status attn_bwd(const collider_attn_cfg& c, const collider_index& ix,
-                         const collider_attn_io& io, void* ws, size_t ws_bytes, hipStream_t s) {
+                         const collider_attn_io& io, void* ws, size_t ws_bytes, hipStream_t s,
+                         bool rope_ready) {
   const int B = ix.B, S = ix.S, Mk = ix.M_kept;
   if (Mk <= 0) return COLLIDER_OK;
   AttnWs w = carve_attn(c, B, S, Mk, ws);
@@ -611,7 +620,7 @@ collider_status attn_bwd(const collider_attn_cfg& c, const collider_index& ix,
   p.ld_dv = io.ld_dv;
 
   collider_status st = COLLIDER_OK;
-  if (c.rot_dims > 0) {
+  if (c.rot_dims > 0 && !rope_ready) {
     st = launch_rope_table(w.rope, S, c.rot_dims, c.rope_base, s);
     if (st != COLLIDER_OK) return st;
   }

@@ -148,14 +148,16 @@ __device__ __forceinline__ void store8_partial(const GemmParams& p, int split, i
 // n .. n+7): the saved pre-activations (SwiGLU: gate in sa, up in sb; GELU: f in sa) or the fp32
 // values being accumulated into (sa, sb = columns n .. n+3, n+4 .. n+7).  All loads of a call are
 // issued before any is used, so one memory latency covers the whole batch.
+// side_rows gives the source rows (the index lookup, -1 past the edge), side_load issues the row
+// loads; the direct-to-LDS kernel looks up the rows one epilogue pass before it loads them, so
+// that each pass waits on one memory latency instead of two dependent ones.
 template <int EPI, int GPT>
-__device__ __forceinline__ void prefetch_side(const GemmParams& p, int mfirst, int mstep, int n,
-                                              uint4 (&sa)[GPT], uint4 (&sb)[GPT]) {
+__device__ __forceinline__ void side_rows(const GemmParams& p, int mfirst, int mstep, int n,
+                                          int (&r)[GPT]) {
   if constexpr (EPI == EPI_BF16) return;
   if constexpr (EPI == EPI_F32) {
     if (!p.accumulate) return;
   }
-  int64_t r[GPT];
 #pragma unroll
   for (int i = 0; i < GPT; ++i) {
     const int m = mfirst + i * mstep;
@@ -163,20 +165,37 @@ __device__ __forceinline__ void prefetch_side(const GemmParams& p, int mfirst, i
     if constexpr (EPI == EPI_F32)
       r[i] = ok ? m : -1;
     else
-      r[i] = ok ? (p.rowmap ? (int64_t)p.rowmap[m] : (int64_t)m) : -1;
+      r[i] = ok ? (p.rowmap ? p.rowmap[m] : m) : -1;
+  }
+}
+
+template <int EPI, int GPT>
+__device__ __forceinline__ void side_load(const GemmParams& p, const int (&r)[GPT], int n,
+                                          uint4 (&sa)[GPT], uint4 (&sb)[GPT]) {
+  if constexpr (EPI == EPI_BF16) return;
+  if constexpr (EPI == EPI_F32) {
+    if (!p.accumulate) return;
   }
 #pragma unroll
   for (int i = 0; i < GPT; ++i) {
     if (r[i] < 0) continue;
     if constexpr (EPI == EPI_F32) {
-      const uint4* c = (const uint4*)((const float*)p.C + r[i] * p.ldc + n);
+      const uint4* c = (const uint4*)((const float*)p.C + (int64_t)r[i] * p.ldc + n);
       sa[i] = c[0];
       sb[i] = c[1];
     } else {
-      sa[i] = *(const uint4*)(p.g + r[i] * p.ld_g + n);
-      if constexpr (EPI == EPI_SWIGLU) sb[i] = *(const uint4*)(p.up + r[i] * p.ld_g + n);
+      sa[i] = *(const uint4*)(p.g + (int64_t)r[i] * p.ld_g + n);
+      if constexpr (EPI == EPI_SWIGLU) sb[i] = *(const uint4*)(p.up + (int64_t)r[i] * p.ld_g + n);
     }
   }
+}
+
+template <int EPI, int GPT>
+__device__ __forceinline__ void prefetch_side(const GemmParams& p, int mfirst, int mstep, int n,
+                                              uint4 (&sa)[GPT], uint4 (&sb)[GPT]) {
+  int r[GPT];
+  side_rows<EPI, GPT>(p, mfirst, mstep, n, r);
+  side_load<EPI, GPT>(p, r, n, sa, sb);
 }
 
 // Final epilogue of 8 outputs with the side inputs already in registers.
@@ -804,11 +823,18 @@ __global__ __launch_bounds__(64 * lds_waves(BM, BN)) void gemm_lds_kernel(GemmPa
     static_assert(EROWS % RSTEP == 0, "epilogue rows per pass");
     const int cg = threadIdx.x % CPR, rsub = threadIdx.x / CPR;
     const int n = n0 + cg * 8;
-    // side inputs of the first epilogue pass (SwiGLU / GELU rows, or C when accumulating): loaded
-    // now, so that their latency overlaps the k-loop (loads return in order, so the k-loop's own
-    // waits never stop short of them)
+    // side inputs of the first epilogue pass (SwiGLU / GELU rows, or C when accumulating) and the
+    // source rows of the second pass's: loaded now, so that their latency overlaps the k-loop
+    // (loads return in order, so the k-loop's own waits never stop short of them)
+    constexpr int NPASS = BM / EROWS;
     uint4 sa[GPT], sb[GPT];
-    if (mode == 0) prefetch_side<EPI, GPT>(p, m0 + rsub, RSTEP, n, sa, sb);
+    int rn[GPT];  // source rows of the next pass's side inputs
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) rn[i] = -1;
+    if (mode == 0) {
+      prefetch_side<EPI, GPT>(p, m0 + rsub, RSTEP, n, sa, sb);
+      if (NPASS > 1) side_rows<EPI, GPT>(p, m0 + EROWS + rsub, RSTEP, n, rn);
+    }
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -846,11 +872,13 @@ __global__ __launch_bounds__(64 * lds_waves(BM, BN)) void gemm_lds_kernel(GemmPa
     float* E = (float*)lds;
 #pragma unroll
     for (int pass = 0; pass < BM / EROWS; ++pass) {
-      // side inputs of the next pass go out now; their latency (an index load, then the rows)
-      // overlaps this pass
+      // side inputs of the next pass go out now (their rows were looked up during the previous
+      // pass), and the rows of the pass after it are looked up; both latencies overlap this pass
       uint4 na[GPT], nb[GPT];
-      if (pass + 1 < BM / EROWS && mode == 0)
-        prefetch_side<EPI, GPT>(p, m0 + (pass + 1) * EROWS + rsub, RSTEP, n, na, nb);
+      if (pass + 1 < NPASS && mode == 0) {
+        side_load<EPI, GPT>(p, rn, n, na, nb);
+        if (pass + 2 < NPASS) side_rows<EPI, GPT>(p, m0 + (pass + 2) * EROWS + rsub, RSTEP, n, rn);
+      }
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < TM; ++i) {

@@ -181,7 +181,14 @@ collider_status gemm_f32(const GemmProblem& p, hipStream_t s);
 
 // attn.hip
 size_t attn_workspace_bytes(const collider_attn_cfg& c, int B, int S, int M_kept);
+// rope_ready: the (cos, sin) table in the workspace was already written by attn_rope_prepare
+// (on a stream this call's stream has waited for); otherwise attn_bwd writes it first.
 collider_status attn_bwd(const collider_attn_cfg& c, const collider_index& ix,
-                         const collider_attn_io& io, void* ws, size_t ws_bytes, hipStream_t s);
+                         const collider_attn_io& io, void* ws, size_t ws_bytes, hipStream_t s,
+                         bool rope_ready = false);
+// Writes the RoPE (cos, sin) table of attn_bwd's workspace (it depends on S and the rotary
+// configuration only), so that a caller can build it off the critical path.
+collider_status attn_rope_prepare(const collider_attn_cfg& c, const collider_index& ix, void* ws,
+                                  size_t ws_bytes, hipStream_t s);
 
 }  // namespace collider

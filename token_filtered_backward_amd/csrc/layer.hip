@@ -257,6 +257,9 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
   CHECK(handoff(5, s, s1));  // fork: dY' ready
   if (dx_full)  // the filtered rows of dx: +0.0 (the kept rows come from the last norm backward)
     CHECK(launch_scatter_bytes(nullptr, 0, gr->dx, (int64_t)H * 2, ix.inv, M, H * 2, 2, s1));
+  // the rotary table attention reads (S and the rotary configuration only), off the critical path;
+  // attention waits on the event recorded after the gathers below
+  CHECK(attn_rope_prepare(ac, aix, b.attn_ws, b.attn_ws_bytes, s1));
   if (Mk > 0 && !unf) {  // 2. saved tensors attention and dW_o read as compacted operands
     GatherDesc gd[5];
     int nd = 0;
@@ -300,7 +303,7 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dgamma2, c.accumulate, s1));
     CHECK(gemm_bf16(g_dO, b.gemm_ws, b.gemm_ws_bytes, s));
     if (side && hipStreamWaitEvent(s, side->ev[6], 0) != hipSuccess) return COLLIDER_ERR_HIP;
-    CHECK(attn_bwd(ac, aix, io, b.attn_ws, b.attn_ws_bytes, s));
+    CHECK(attn_bwd(ac, aix, io, b.attn_ws, b.attn_ws_bytes, s, true));
     CHECK(handoff(3, s, s1));  // [dq|dk|dv] ready
     CHECK(launch_norm_recompute((const uint16_t*)sv->x, nullptr, sv->rstd1, w->gamma1, nullptr, idx,
                                 Mk, H, b.xn_c, s1));
@@ -321,7 +324,7 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     CHECK(gemm_bf16(g_dA, b.gemm_ws, b.gemm_ws_bytes, s));
     CHECK(gemm_bf16(g_dO, b.gemm_ws, b.gemm_ws_bytes, s));
     if (side && hipStreamWaitEvent(s, side->ev[6], 0) != hipSuccess) return COLLIDER_ERR_HIP;
-    CHECK(attn_bwd(ac, aix, io, b.attn_ws, b.attn_ws_bytes, s));
+    CHECK(attn_bwd(ac, aix, io, b.attn_ws, b.attn_ws_bytes, s, true));
     CHECK(handoff(1, s, s1));  // [dq|dk|dv|dF] ready
     CHECK(gemm_bf16(g_dwqkv, b.gemm_ws2, b.gemm_ws2_bytes, s1));
     CHECK(gemm_bf16(g_dwfc1, b.gemm_ws2, b.gemm_ws2_bytes, s1));
