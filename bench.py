@@ -14,6 +14,7 @@ scatter, D = dO . O), the reduced-GEMM roofline (bf16 MFMA) from per-kernel HIP 
 CPU oracle timed on a bounded sample.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config tinyllama] [--r 40]
+                    [--seq S [--tokens T]]      (long-context sweep: S per sequence, B = T / S)
 """
 import argparse
 import json
@@ -79,7 +80,7 @@ def measured_traffic(cfg, r_pct):
     taken on another workload or on a GEMM source other than the one built here."""
     import hashlib
     import re
-    if (cfg.name, r_pct) != ("tinyllama", 40):
+    if (cfg.name, cfg.B, cfg.S, r_pct) != ("tinyllama", 4, 2048, 40):
         return None
     path = os.path.join(ROOT, "profiles", "gemm_bf16_tinyllama_b4s2048_r40_traffic.md")
     src = os.path.join(ROOT, "token_filtered_backward_amd", "csrc", "gemm.hip")
@@ -135,6 +136,10 @@ def main():
     ap.add_argument("--config", default="tinyllama")
     ap.add_argument("--r", type=int, default=40, help="filtered percentage")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--seq", type=int, default=0,
+                    help="sequence length S (long-context sweep); the batch becomes tokens / S")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="tokens per batch B*S with --seq (default: the config's own B*S)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfiltered", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch every kernel eagerly each step")
@@ -159,6 +164,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda"
     cfg = synth.get_config(args.config)
+    if args.seq:
+        tokens = args.tokens or cfg.M
+        if tokens % args.seq:
+            print(f"--tokens {tokens} is not a multiple of --seq {args.seq}", file=sys.stderr)
+            sys.exit(2)
+        cfg = cfg.with_(B=tokens // args.seq, S=args.seq)
     log(f"[bench] generating inputs for {cfg.name} (B={cfg.B} S={cfg.S} r={args.r}%) ...")
     t0 = time.perf_counter()
     inp = synth.make_layer_inputs(cfg, seed=args.seed, r_pct=args.r)
@@ -399,9 +410,9 @@ def main():
             "avg_launch_ms": round(gemm_ms / max(gemm_launches, 1), 5),
         },
     }
-    if not args.no_cpu_baseline and L > 1:
-        log("[bench] no CPU oracle timing for a layer stack (one float64 layer at this size alone "
-            "takes minutes)")
+    if not args.no_cpu_baseline and (L > 1 or S > 4096):
+        log("[bench] no CPU oracle timing for a layer stack or a sequence longer than 4096 (one "
+            "float64 sequence of the layer at this size alone takes minutes)")
     elif not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(cfg, inp)

@@ -80,6 +80,10 @@ CONFIGS = {
     # 22 TinyLlama-shaped layers at batch 1 x seq 8192
     "tinyllama_22l": LayerShape("tinyllama_22l", "llama", B=1, S=8192, H=2048, nq=32, nkv=4,
                                 d=64, I=5632, rot=64, rope_base=1.0e4, eps=1e-5, n_layers=22),
+    # Long-context attention check: one sequence of 16384 tokens with few heads (the kernels' work
+    # per sequence grows with S; the head count only multiplies it), small hidden size
+    "longctx_attn": LayerShape("longctx_attn", "llama", B=1, S=16384, H=256, nq=4, nkv=1, d=64,
+                               I=256, rot=64, rope_base=1.0e4, eps=1e-5),
     # Small shapes that still span several GEMM / attention tiles and a ragged tail.
     "small_llama": LayerShape("small_llama", "llama", B=2, S=200, H=256, nq=4, nkv=2, d=64,
                               I=384, rot=64, rope_base=1.0e4, eps=1e-5),

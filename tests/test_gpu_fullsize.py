@@ -14,7 +14,7 @@ import oracle
 import synth
 import token_filtered_backward_amd as tfb
 from tests.helpers import BF16_TOL, to64, upcast
-from tests.test_gpu_parity import GRAD_NAMES, _dev_keep, _upload_layer
+from tests.test_gpu_parity import GRAD_NAMES, _dev_keep, _upload_layer, check_attention
 
 pytestmark = pytest.mark.gpu
 
@@ -89,6 +89,15 @@ def test_layer_long_context_fullsize():
     ref = oracle.layer_bwd(cfg, upcast(inp["weights"]), upcast(inp["saved"]),
                            synth.bf16_bits_to_f32(inp["dy"]), inp["keep"], "filtered")
     _compare(cfg, got, ref, inp["keep"])
+
+
+@pytest.mark.timeout(900)
+def test_attention_long_context():
+    """Filtered attention backward over one sequence of 16384 tokens (4 query heads on 1 KV head,
+    head_dim 64, 40% filtered: 9831 kept rows, about 4.8e7 kept causal pairs per head) against the
+    float64 oracle: the long-context end of the sequence-length sweep."""
+    print("attention long context: B 1 x S 16384, oracle on the host (about a minute)", flush=True)
+    check_attention("longctx_attn", 40, 0)
 
 
 def test_stack_compact_chain_fullsize():

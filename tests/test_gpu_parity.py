@@ -226,6 +226,12 @@ def _attn_case(name, r, dmode, seed=0):
 @pytest.mark.parametrize("dmode", [0, 1])
 @pytest.mark.parametrize("r", [0, 40, 90])
 def test_attention_parity(name, dmode, r):
+    check_attention(name, r, dmode)
+
+
+def check_attention(name, r, dmode):
+    """collider_attn_bwd_filtered on compacted q, k, v, o, lse, dO against the oracle's attention
+    backward (then its RoPE backward) on the full token layout, at the kept rows."""
     cfg, inp, dob, ref = _attn_case(name, r, dmode)
     keep = inp["keep"]
     ix = tfb.build_index(_dev_keep(keep), cfg.B, cfg.S)
