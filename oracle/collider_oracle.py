@@ -37,6 +37,7 @@ __all__ = [
     "silu", "sigmoid", "gelu_tanh", "gelu_tanh_bwd", "swiglu_bwd",
     "rmsnorm_bwd", "layernorm_bwd", "rope_bwd", "attention_bwd",
     "llama_layer_bwd", "phi_layer_bwd", "layer_bwd", "model_bwd", "MODES",
+    "select_topk", "ce_logits_bwd", "lm_head_bwd", "embedding_bwd",
 ]
 
 MODES = ("filtered", "full_d", "loss_only")
@@ -336,3 +337,56 @@ def model_bwd(cfg, layers, dy, keep, mode="filtered"):
         outs.append(out)
         g = out["dx"]
     return outs[::-1]
+
+
+# ---------------------------------------------------------------------------------------------
+# loss side of the backward (Figure 2(b): the per-token training loss decides which tokens are
+# filtered; the loss of a filtered token is dropped, so it sends no gradient into the LM head,
+# the layers below it or the token embedding)
+# ---------------------------------------------------------------------------------------------
+
+
+def select_topk(score, n_keep):
+    """Token selection on per-token scores: keep the n_keep tokens with the largest score.
+
+    Order: by descending score, equal scores by ascending position; -0.0 equals +0.0; NaN ranks
+    below every number (NaN scores are filtered first).  Returns a uint8 mask (1 = kept)."""
+    s = np.asarray(score, dtype=np.float64).reshape(-1)
+    M = s.size
+    n_keep = max(0, min(int(n_keep), M))
+    nan = np.isnan(s)
+    # lexsort: the last key is the primary one
+    order = np.lexsort((np.arange(M), -np.where(nan, 0.0, s), nan))
+    keep = np.zeros(M, dtype=np.uint8)
+    keep[order[:n_keep]] = 1
+    return keep
+
+
+def ce_logits_bwd(logits, labels, keep, scale):
+    """Gradient of L = scale * sum over kept t of CE(logits_t, labels_t) with respect to the
+    logits, CE(z, y) = logsumexp(z) - z_y:  dL/dz_t = scale * (softmax(z_t) - onehot(y_t)) for a
+    kept token, 0 for a filtered one (its loss is dropped)."""
+    z = _f64(logits)
+    k = _keep_bool(keep)
+    zmax = z.max(axis=1, keepdims=True)
+    e = np.exp(z - zmax)
+    p = e / e.sum(axis=1, keepdims=True)
+    p[np.arange(z.shape[0]), np.asarray(labels, dtype=np.int64)] -= 1.0
+    return float(scale) * p * k[:, None]
+
+
+def lm_head_bwd(logits, labels, h, w_lm, keep, scale):
+    """Backward of the LM head logits = h @ w_lm.T (w_lm [V, H], torch layout) under the per-token
+    loss of ce_logits_bwd: dh = dlogits @ w_lm, dw_lm = dlogits^T @ h.  Rows of filtered tokens of
+    dlogits are zero, so dh's filtered rows are exactly zero and dw_lm sums over kept tokens only."""
+    g = ce_logits_bwd(logits, labels, keep, scale)
+    return {"dlogits": g, "dh": g @ _f64(w_lm), "dw_lm": g.T @ _f64(h)}
+
+
+def embedding_bwd(dx, token_ids, keep, V):
+    """Gradient of the token embedding table E [V, H] under x_t = E[id_t]: row v of dE is the sum of
+    dx_t over the kept tokens t with id_t = v (a filtered token's dx is zero)."""
+    g = _f64(dx) * _keep_bool(keep)[:, None]
+    dE = np.zeros((int(V), g.shape[1]))
+    np.add.at(dE, np.asarray(token_ids, dtype=np.int64), g)
+    return dE
