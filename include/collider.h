@@ -255,6 +255,60 @@ collider_status collider_layer_bwd(const collider_layer_cfg* cfg, const collider
                                    size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Loss side of the backward (Figure 2(b): the per-token training loss decides which tokens are
+ * filtered; a filtered token's loss is dropped, so it sends no gradient into the LM head, the
+ * layers or the token embedding).
+ *
+ * collider_select_keep: token selection on per-token scores (float32 [M], e.g. the per-token loss
+ * or any importance score).  keep[t] = 1 for the n_keep tokens with the largest score, else 0;
+ * equal scores keep the lower position first; -0.0 ranks as +0.0; NaN ranks below every number.
+ * n_keep <= 0 keeps nothing, n_keep >= M keeps every token.  keep is uint8 [M] (the mask
+ * collider_build_index takes).  One workgroup, five passes over the scores: meant for per-batch
+ * token counts (M <= 2^30 accepted; time grows linearly with M).  Bit-exact, deterministic.
+ * Errors: NULL pointer, M < 1 or M > 2^30.
+ * ------------------------------------------------------------------------------------------- */
+collider_status collider_select_keep(const float* score, int32_t M, int32_t n_keep, uint8_t* keep,
+                                     hipStream_t stream);
+
+/* collider_lm_head_bwd: per-token cross-entropy backward through the LM head, over kept tokens.
+ * The forward computed logits = h @ w_lm^T (w_lm [V, H] bf16, [out, in]) and kept them, bf16
+ * [M, V] in the full token layout (row stride ld_logits).  The loss is
+ *   L = loss_scale * sum over kept t with 0 <= labels[t] < V of (logsumexp(logits_t) - logits_t[labels[t]])
+ * (loss_scale = 1 / M_kept gives the mean over kept tokens; a label outside [0, V), such as
+ * torch's ignore index -100, marks a token without a target).  Computes, for kept rows only:
+ *   dlogits' = loss_scale * (softmax(logits') - onehot(labels'))   (bf16, in the workspace)
+ *   dh' = dlogits' @ w_lm            -> dh: bf16 [M_kept, H] (dh_compact != 0) or [M, H] with the
+ *                                       rows of filtered tokens +0.0 (dh_compact == 0)
+ *   dw_lm = dlogits'^T @ h'          -> float32 [V, H], overwritten (accumulate == 0) or added to
+ * h is the bf16 [M, H] input of the LM head (full layout, row stride ld_h); labels int32 [M].
+ * Requirements: H and V multiples of 8, 16-byte alignment of every bf16 pointer and leading
+ * dimension (COLLIDER_ERR_ALIGN otherwise), ix from collider_build_index with M_kept set.
+ * The workspace (collider_lm_head_workspace_bytes) holds h' and dlogits' ([M_kept, V] bf16) and
+ * GEMM partials; it must not alias any input or output. */
+size_t collider_lm_head_workspace_bytes(int32_t M_kept, int32_t H, int32_t V);
+collider_status collider_lm_head_bwd(const void* logits, int64_t ld_logits, const int32_t* labels,
+                                     const void* h, int64_t ld_h, const void* w_lm,
+                                     const collider_index* ix, int32_t H, int32_t V,
+                                     float loss_scale, void* dh, int32_t dh_compact, float* dw_lm,
+                                     int32_t accumulate, void* ws, size_t ws_bytes,
+                                     hipStream_t stream);
+
+/* collider_embedding_bwd: gradient of the token embedding table E [V, H] under x_t = E[ids[t]]:
+ *   dE[v, :] = sum of dx[t, :] over the kept tokens t with ids[t] == v, summed in ascending t
+ * (deterministic: the kept tokens are bucketed by id with a stable counting sort, then each row
+ * is summed by one wavefront; no float atomics).  dx is bf16: compacted [M_kept, H] (dx_compact
+ * != 0, e.g. the bottom layer's compact dx) or the full [M, H] layout (read at idx rows); ids is
+ * int32 [M]; dE is float32 [V, H], every row written (rows no kept token uses: 0) unless
+ * accumulate != 0 (then added to, and untouched rows left as they are).  Ids outside [0, V) are
+ * skipped.  H a multiple of 8, 16-byte alignment as above.  Workspace:
+ * collider_embedding_workspace_bytes. */
+size_t collider_embedding_workspace_bytes(int32_t M_kept, int32_t V);
+collider_status collider_embedding_bwd(const void* dx, int64_t ld_dx, int32_t dx_compact,
+                                       const int32_t* ids, const collider_index* ix, int32_t H,
+                                       int32_t V, float* dE, int32_t accumulate, void* ws,
+                                       size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Measurement and diagnostics.
  * collider_profile_enable(1): from then on every kernel the library enqueues is bracketed by a
  * pair of HIP events recorded on the same stream.  collider_profile_collect waits for them and,

@@ -365,13 +365,18 @@ def select_topk(score, n_keep):
 def ce_logits_bwd(logits, labels, keep, scale):
     """Gradient of L = scale * sum over kept t of CE(logits_t, labels_t) with respect to the
     logits, CE(z, y) = logsumexp(z) - z_y:  dL/dz_t = scale * (softmax(z_t) - onehot(y_t)) for a
-    kept token, 0 for a filtered one (its loss is dropped)."""
+    kept token, 0 for a filtered one (its loss is dropped).  A label outside [0, V) (torch's ignore
+    index -100, say) marks a token without a target: no loss, zero gradient."""
     z = _f64(logits)
-    k = _keep_bool(keep)
+    y = np.asarray(labels, dtype=np.int64).reshape(-1)
+    V = z.shape[1]
+    valid = (y >= 0) & (y < V)
+    k = _keep_bool(keep) & valid
     zmax = z.max(axis=1, keepdims=True)
     e = np.exp(z - zmax)
     p = e / e.sum(axis=1, keepdims=True)
-    p[np.arange(z.shape[0]), np.asarray(labels, dtype=np.int64)] -= 1.0
+    rows = np.flatnonzero(valid)
+    p[rows, y[rows]] -= 1.0
     return float(scale) * p * k[:, None]
 
 
@@ -385,8 +390,11 @@ def lm_head_bwd(logits, labels, h, w_lm, keep, scale):
 
 def embedding_bwd(dx, token_ids, keep, V):
     """Gradient of the token embedding table E [V, H] under x_t = E[id_t]: row v of dE is the sum of
-    dx_t over the kept tokens t with id_t = v (a filtered token's dx is zero)."""
-    g = _f64(dx) * _keep_bool(keep)[:, None]
-    dE = np.zeros((int(V), g.shape[1]))
-    np.add.at(dE, np.asarray(token_ids, dtype=np.int64), g)
+    dx_t over the kept tokens t with id_t = v (a filtered token's dx is zero).  Ids outside [0, V)
+    have no embedding row and are skipped."""
+    ids = np.asarray(token_ids, dtype=np.int64).reshape(-1)
+    use = _keep_bool(keep) & (ids >= 0) & (ids < int(V))
+    g = _f64(dx)[use]
+    dE = np.zeros((int(V), _f64(dx).shape[1]))
+    np.add.at(dE, ids[use], g)
     return dE

@@ -143,3 +143,23 @@ def test_gemm_plans_fill_the_cus_on_ragged_token_counts():
     assert L.collider_gemm_describe_plan(0, 8, 8, 0, 0, out) == 2
     assert L.collider_gemm_describe_plan(8, 12, 8, 0, 0, out) == 2
     assert L.collider_gemm_describe_plan(8, 8, 8, 2, 0, out) == 2
+
+
+def test_loss_side_validation():
+    L = tfb.lib()
+    p = ctypes.c_void_p(0x10000)
+    assert L.collider_select_keep(None, 8, 4, p, None) == 1
+    assert L.collider_select_keep(p, 0, 4, p, None) == 2
+    ix = tfb.CollIndex(p, p, p, p, 2, 64, 77)
+    # V not a multiple of 8, then a missing workspace
+    assert L.collider_lm_head_bwd(p, 1004, p, p, 256, p, ctypes.byref(ix), 256, 1004, 1.0, p, 0, p, 0,
+                                  None, 0, None) == 3
+    assert L.collider_lm_head_bwd(p, 1000, p, p, 256, p, ctypes.byref(ix), 256, 1000, 1.0, p, 0, p, 0,
+                                  None, 0, None) == 5
+    assert L.collider_lm_head_bwd(p, 1000, None, p, 256, p, ctypes.byref(ix), 256, 1000, 1.0, p, 0, p, 0,
+                                  None, 0, None) == 1
+    assert L.collider_lm_head_workspace_bytes(77, 256, 1000) >= 77 * 1000 * 2 + 2 * 77 * 256 * 2
+    assert L.collider_embedding_bwd(p, 256, 1, None, ctypes.byref(ix), 256, 1000, p, 0, None, 0, None) == 1
+    assert L.collider_embedding_bwd(p, 256, 1, p, ctypes.byref(ix), 252, 1000, p, 0, None, 0, None) == 3
+    assert L.collider_embedding_bwd(p, 256, 1, p, ctypes.byref(ix), 256, 1000, p, 0, None, 0, None) == 5
+    assert L.collider_embedding_workspace_bytes(77, 1000) >= (3 * 1000 + 1 + 77) * 4

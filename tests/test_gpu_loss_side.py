@@ -1,0 +1,166 @@
+"""GPU parity of the loss-side steps through the C ABI: token selection (bit-exact), the LM-head
+cross-entropy backward over kept tokens (bf16 bar) and the embedding gradient (float32 sums of
+bf16 rows in a fixed order), against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import token_filtered_backward_amd as tfb
+from tests.helpers import BF16_TOL, bf16_dev, rel_err, to64
+from tests.test_gpu_parity import _dev_keep
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------------------------------------
+# selection
+# ------------------------------------------------------------------------------------------------
+
+
+def _scores(M, kind, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "lognormal":
+        return np.exp(rng.standard_normal(M)).astype(np.float32)
+    if kind == "ties":  # few distinct values, signed zeros, infinities, NaN
+        vals = np.array([-1.5, -0.0, 0.0, 0.25, 2.0, np.inf, -np.inf, np.nan], np.float32)
+        return rng.choice(vals, size=M)
+    if kind == "const":
+        return np.full(M, 0.75, np.float32)
+    if kind == "normal":
+        return rng.standard_normal(M).astype(np.float32)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("M,kind", [(1, "lognormal"), (7, "ties"), (1000, "ties"), (8192, "lognormal"),
+                                    (8192, "const"), (70001, "normal"), (70001, "ties")])
+def test_select_keep_bit_exact(M, kind):
+    score = _scores(M, kind, M)
+    dev = torch.from_numpy(score).cuda()
+    for n_keep in sorted({0, 1, M // 3, M // 2, M - 1, M}):
+        got = tfb.select_keep(dev, n_keep).cpu().numpy()
+        ref = oracle.select_topk(score, n_keep)
+        assert np.array_equal(got, ref), (M, kind, n_keep, int(np.sum(got != ref)))
+
+
+def test_select_keep_matches_the_layer_inputs_mask():
+    """On the generator's LogNormal scores (as float32) the device selection gives the 40% mask the
+    layer benchmarks use."""
+    M = 8192
+    score = np.exp(synth.rng_for(0, "score").standard_normal(M))
+    s32 = score.astype(np.float32)
+    got = tfb.select_keep(torch.from_numpy(s32).cuda(), M - synth.n_filtered(M, 40)).cpu().numpy()
+    assert np.array_equal(got, oracle.select_topk(s32, M - synth.n_filtered(M, 40)))
+    # float32 rounding of these scores creates no tie, so the mask is the generator's
+    assert np.array_equal(got, synth.make_keep(M, 40, 0))
+
+
+# ------------------------------------------------------------------------------------------------
+# LM head cross-entropy backward
+# ------------------------------------------------------------------------------------------------
+
+
+def _lm_case(B, S, H, V, r, seed, pattern="topk"):
+    rng = np.random.default_rng(seed)
+    M = B * S
+    logits = synth.f32_to_bf16_bits((rng.standard_normal((M, V)) * 2.0).astype(np.float32))
+    h = synth.f32_to_bf16_bits(rng.standard_normal((M, H)).astype(np.float32))
+    w = synth.f32_to_bf16_bits((rng.standard_normal((V, H)) * 0.02).astype(np.float32))
+    labels = rng.integers(0, V, M).astype(np.int32)
+    labels[rng.random(M) < 0.05] = -100  # tokens without a target
+    keep = synth.make_keep(M, r, seed) if pattern == "topk" else np.zeros(M, np.uint8)
+    return logits, labels, h, w, keep
+
+
+@pytest.mark.parametrize("B,S,H,V,r", [(2, 200, 256, 1000, 40), (1, 64, 64, 40000, 40),
+                                       (1, 48, 64, 72000, 25), (2, 130, 128, 8, 0)])
+@pytest.mark.parametrize("dh_compact", [False, True])
+def test_lm_head_bwd_parity(B, S, H, V, r, dh_compact):
+    logits, labels, h, w, keep = _lm_case(B, S, H, V, r, seed=V + S)
+    M = B * S
+    ix = tfb.build_index(_dev_keep(keep), B, S)
+    mk = ix.M_kept
+    scale = 1.0 / max(mk, 1)
+    dh = torch.full((mk if dh_compact else M, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dw = torch.full((V, H), float("nan"), dtype=torch.float32, device="cuda")
+    tfb.collider_lm_head_bwd(bf16_dev(logits), torch.from_numpy(labels).cuda(), bf16_dev(h), bf16_dev(w),
+                             ix.c(), scale, dh, dw, dh_compact=dh_compact)
+    torch.cuda.synchronize()
+    f = synth.bf16_bits_to_f32
+    ref = oracle.lm_head_bwd(f(logits), labels, f(h), f(w), keep, scale)
+    got_dh = to64(dh)
+    ref_dh = ref["dh"][keep != 0] if dh_compact else ref["dh"]
+    assert rel_err(got_dh, ref_dh) <= BF16_TOL
+    assert rel_err(to64(dw), ref["dw_lm"]) <= BF16_TOL
+    if not dh_compact:
+        assert np.all(got_dh[keep == 0] == 0.0)
+
+
+def test_lm_head_bwd_all_filtered_and_accumulate():
+    B, S, H, V = 1, 96, 64, 512
+    logits, labels, h, w, _ = _lm_case(B, S, H, V, 40, seed=7)
+    keep = np.zeros(B * S, np.uint8)
+    ix = tfb.build_index(_dev_keep(keep), B, S)
+    dh = torch.full((B * S, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dw = torch.full((V, H), 3.0, dtype=torch.float32, device="cuda")
+    args = (bf16_dev(logits), torch.from_numpy(labels).cuda(), bf16_dev(h), bf16_dev(w), ix.c(), 1.0)
+    tfb.collider_lm_head_bwd(*args, dh, dw, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.all(dh.float() == 0.0) and torch.all(dw == 3.0)
+    tfb.collider_lm_head_bwd(*args, dh, dw)
+    torch.cuda.synchronize()
+    assert torch.all(dw == 0.0)
+    # accumulate on a real mask adds the overwrite result
+    keep = synth.make_keep(B * S, 40, 7)
+    ix = tfb.build_index(_dev_keep(keep), B, S)
+    args = (bf16_dev(logits), torch.from_numpy(labels).cuda(), bf16_dev(h), bf16_dev(w), ix.c(), 0.25)
+    dw1 = torch.empty((V, H), dtype=torch.float32, device="cuda")
+    tfb.collider_lm_head_bwd(*args, dh, dw1)
+    dw2 = torch.full((V, H), 1.5, dtype=torch.float32, device="cuda")
+    tfb.collider_lm_head_bwd(*args, dh, dw2, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.allclose(dw2, dw1 + 1.5, rtol=0, atol=1e-6)
+
+
+# ------------------------------------------------------------------------------------------------
+# embedding gradient
+# ------------------------------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("B,S,H,V,r", [(2, 200, 256, 1000, 40), (1, 3000, 64, 50, 20), (4, 2048, 128, 32000, 40),
+                                       (1, 77, 64, 16, 100)])
+@pytest.mark.parametrize("dx_compact", [False, True])
+def test_embedding_bwd_parity(B, S, H, V, r, dx_compact):
+    rng = np.random.default_rng(S + V)
+    M = B * S
+    keep = synth.make_keep(M, r, 1)
+    ids = rng.integers(0, V, M).astype(np.int32)
+    ids[: M // 10] = V // 2                     # a frequent token
+    ids[rng.random(M) < 0.01] = -1             # ids outside [0, V) are skipped
+    ix = tfb.build_index(_dev_keep(keep), B, S)
+    mk = ix.M_kept
+    dxf = synth.f32_to_bf16_bits(rng.standard_normal((M, H)).astype(np.float32))
+    dx_dev = bf16_dev(dxf[keep != 0] if dx_compact else dxf)
+    if mk == 0 and dx_compact:
+        dx_dev = torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    dE = torch.full((V, H), float("nan"), dtype=torch.float32, device="cuda")
+    tfb.collider_embedding_bwd(dx_dev, torch.from_numpy(ids).cuda(), ix.c(), dE, dx_compact=dx_compact)
+    torch.cuda.synchronize()
+    ref = oracle.embedding_bwd(synth.bf16_bits_to_f32(dxf), ids, keep, V)
+    got = to64(dE)
+    assert np.all(np.isfinite(got))
+    assert rel_err(got, ref) <= 1e-5
+    used = np.zeros(V, bool)
+    ok = (ids >= 0) & (ids < V) & (keep != 0)
+    used[ids[ok]] = True
+    assert np.all(got[~used] == 0.0)
+    # deterministic: a second call gives the same bits; accumulate adds
+    dE2 = torch.empty_like(dE)
+    tfb.collider_embedding_bwd(dx_dev, torch.from_numpy(ids).cuda(), ix.c(), dE2, dx_compact=dx_compact)
+    dE3 = torch.ones_like(dE)
+    tfb.collider_embedding_bwd(dx_dev, torch.from_numpy(ids).cuda(), ix.c(), dE3, dx_compact=dx_compact,
+                               accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dE, dE2)
+    assert torch.allclose(dE3, dE + 1.0, rtol=0, atol=1e-5)

@@ -96,6 +96,22 @@ def test_ce_logits_bwd_autograd_fd():
     assert np.all(got[keep == 0] == 0.0)
 
 
+def test_ce_ignored_labels_match_torch_ignore_index():
+    rng = np.random.default_rng(6)
+    M, V = 12, 10
+    z = rng.standard_normal((M, V))
+    y = rng.integers(0, V, M)
+    y[[1, 4, 9]] = -100
+    keep = np.ones(M, np.uint8)
+    keep[2] = 0
+    got = oracle.ce_logits_bwd(z, y, keep, 0.5)
+    zt = torch.tensor(z, requires_grad=True)
+    lz = torch.nn.functional.cross_entropy(zt, torch.tensor(y), reduction="none", ignore_index=-100)
+    (0.5 * (lz * torch.tensor(keep, dtype=torch.float64)).sum()).backward()
+    np.testing.assert_allclose(got, zt.grad.numpy(), rtol=1e-12, atol=1e-14)
+    assert np.all(got[[1, 2, 4, 9]] == 0.0)
+
+
 def test_lm_head_bwd_autograd():
     rng = np.random.default_rng(4)
     M, H, V = 13, 8, 19
@@ -125,20 +141,24 @@ def test_embedding_bwd_brute_force_and_autograd():
     dx = rng.standard_normal((M, H))
     ids = rng.integers(0, V, M)
     ids[:5] = 3  # a frequent token
+    ids[7], ids[8] = -1, V + 2  # no embedding row: skipped
     keep = (rng.random(M) < 0.6).astype(np.uint8)
+    keep[7] = keep[8] = 1
     got = oracle.embedding_bwd(dx, ids, keep, V)
     ref = np.zeros((V, H))
     for t in range(M):
-        if keep[t]:
+        if keep[t] and 0 <= ids[t] < V:
             for j in range(H):
                 ref[ids[t], j] += dx[t, j]
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
     E = torch.tensor(rng.standard_normal((V, H)), requires_grad=True)
-    x = torch.nn.functional.embedding(torch.tensor(ids), E)
-    (x * torch.tensor(dx) * torch.tensor(keep, dtype=torch.float64)[:, None]).sum().backward()
+    ok = (ids >= 0) & (ids < V)
+    x = torch.nn.functional.embedding(torch.tensor(np.where(ok, ids, 0)), E)
+    w = torch.tensor(keep * ok, dtype=torch.float64)[:, None]
+    (x * torch.tensor(dx) * w).sum().backward()
     np.testing.assert_allclose(got, E.grad.numpy(), rtol=1e-12, atol=1e-12)
     # ids no kept token uses get an exactly zero row
-    used = set(ids[keep != 0].tolist())
+    used = set(ids[(keep != 0) & ok].tolist())
     for v in range(V):
         if v not in used:
             assert np.all(got[v] == 0.0)

@@ -99,6 +99,13 @@ def lib():
         "collider_gemm_set_policy": (st, [_i32]),
         "collider_gemm_describe_plan": (st, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_i32)]),
         "collider_profile_collect": (_i32, [ctypes.c_char_p, _i32, P(ctypes.c_double), P(_i32), _i32]),
+        "collider_select_keep": (st, [_c_p, _i32, _i32, _c_p, _c_p]),
+        "collider_lm_head_workspace_bytes": (sz, [_i32, _i32, _i32]),
+        "collider_lm_head_bwd": (st, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, P(CollIndex), _i32, _i32,
+                                      ctypes.c_float, _c_p, _i32, _c_p, _i32, _c_p, sz, _c_p]),
+        "collider_embedding_workspace_bytes": (sz, [_i32, _i32]),
+        "collider_embedding_bwd": (st, [_c_p, _i64, _i32, _c_p, P(CollIndex), _i32, _i32, _c_p, _i32,
+                                        _c_p, sz, _c_p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -210,6 +217,55 @@ def collider_attn_bwd_filtered(cfg: AttnCfg, ix: CollIndex, io: AttnIO, ws, stre
     _check(lib().collider_attn_bwd_filtered(ctypes.byref(cfg), ctypes.byref(ix), ctypes.byref(io),
                                             _ptr(ws), ws.numel(), _stream(stream)),
            "collider_attn_bwd_filtered")
+
+
+def collider_select_keep(score, n_keep, keep, stream=None):
+    """keep[t] = 1 for the n_keep largest scores (float32 [M]; ties: lower t first), else 0."""
+    _check(lib().collider_select_keep(_ptr(score), score.numel(), int(n_keep), _ptr(keep),
+                                      _stream(stream)), "collider_select_keep")
+
+
+def select_keep(score: torch.Tensor, n_keep: int, stream=None) -> torch.Tensor:
+    keep = torch.empty(score.numel(), dtype=torch.uint8, device=score.device)
+    collider_select_keep(score, n_keep, keep, stream)
+    return keep
+
+
+def collider_lm_head_workspace_bytes(M_kept, H, V) -> int:
+    return int(lib().collider_lm_head_workspace_bytes(M_kept, H, V))
+
+
+def collider_lm_head_bwd(logits, labels, h, w_lm, ix: CollIndex, loss_scale, dh, dw_lm,
+                         dh_compact=False, accumulate=False, ws=None, stream=None):
+    """Cross-entropy backward through the LM head over kept tokens: logits bf16 [M, V] (full
+    layout), labels int32 [M], h bf16 [M, H], w_lm bf16 [V, H] -> dh bf16 ([M_kept, H] when
+    dh_compact, else [M, H] with zero filtered rows) and dw_lm float32 [V, H]."""
+    V, H = w_lm.shape
+    if ws is None:
+        ws = torch.empty(max(1, collider_lm_head_workspace_bytes(ix.M_kept, H, V)), dtype=torch.uint8,
+                         device=h.device)
+    _check(lib().collider_lm_head_bwd(_ptr(logits), _ld(logits), _ptr(labels), _ptr(h), _ld(h),
+                                      _ptr(w_lm), ctypes.byref(ix), H, V, float(loss_scale), _ptr(dh),
+                                      int(bool(dh_compact)), _ptr(dw_lm), int(bool(accumulate)),
+                                      _ptr(ws), ws.numel(), _stream(stream)), "collider_lm_head_bwd")
+
+
+def collider_embedding_workspace_bytes(M_kept, V) -> int:
+    return int(lib().collider_embedding_workspace_bytes(M_kept, V))
+
+
+def collider_embedding_bwd(dx, ids, ix: CollIndex, dE, dx_compact=False, accumulate=False, ws=None,
+                           stream=None):
+    """dE[v] (+)= sum of dx rows of the kept tokens with ids == v (token order); dx bf16 [M_kept, H]
+    (dx_compact) or [M, H], ids int32 [M], dE float32 [V, H]."""
+    V, H = dE.shape
+    if ws is None:
+        ws = torch.empty(max(1, collider_embedding_workspace_bytes(ix.M_kept, V)), dtype=torch.uint8,
+                         device=dE.device)
+    _check(lib().collider_embedding_bwd(_ptr(dx), _ld(dx) if dx is not None else H,
+                                        int(bool(dx_compact)), _ptr(ids), ctypes.byref(ix), H, V,
+                                        _ptr(dE), int(bool(accumulate)), _ptr(ws), ws.numel(),
+                                        _stream(stream)), "collider_embedding_bwd")
 
 
 def collider_layer_workspace_bytes(cfg: LayerCfg, B, S, M_kept) -> int:

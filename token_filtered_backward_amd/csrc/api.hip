@@ -408,4 +408,122 @@ int32_t collider_profile_collect(char* names, int32_t name_cap, double* total_ms
   return n;
 }
 
+// ------------------------------------------------------------------------------------------
+// loss side: token selection, LM-head cross-entropy backward, embedding gradient
+// ------------------------------------------------------------------------------------------
+collider_status collider_select_keep(const float* score, int32_t M, int32_t n_keep, uint8_t* keep,
+                                     hipStream_t stream) {
+  if (!score || !keep) return COLLIDER_ERR_NULL;
+  if (M < 1 || M > (1 << 30)) return COLLIDER_ERR_SHAPE;
+  return launch_select_topk(score, M, n_keep, keep, stream);
+}
+
+}  // extern "C"
+
+namespace {
+struct LmHeadWs {
+  uint16_t *h_c, *dl, *dh_c;
+  char* gws;
+  size_t gws_bytes, bytes;
+};
+
+LmHeadWs carve_lm_head(int32_t Mk, int32_t H, int32_t V, void* base) {
+  GemmProblem a, b;
+  linear_problems(COLLIDER_BF16, Mk, H, V, nullptr, H, nullptr, V, nullptr, nullptr, nullptr, 0, &a,
+                  &b);
+  Carver cv(base);
+  LmHeadWs w;
+  w.h_c = cv.take<uint16_t>((size_t)Mk * H);
+  w.dl = cv.take<uint16_t>((size_t)Mk * V);
+  w.dh_c = cv.take<uint16_t>((size_t)Mk * H);
+  w.gws_bytes = std::max(gemm_bf16_workspace_bytes(a), gemm_bf16_workspace_bytes(b));
+  w.gws = cv.take<char>(w.gws_bytes);
+  w.bytes = cv.bytes();
+  return w;
+}
+}  // namespace
+
+extern "C" {
+
+size_t collider_lm_head_workspace_bytes(int32_t M_kept, int32_t H, int32_t V) {
+  if (M_kept < 0 || H < 1 || V < 1) return 0;
+  return carve_lm_head(M_kept, H, V, nullptr).bytes;
+}
+
+collider_status collider_lm_head_bwd(const void* logits, int64_t ld_logits, const int32_t* labels,
+                                     const void* h, int64_t ld_h, const void* w_lm,
+                                     const collider_index* ix, int32_t H, int32_t V,
+                                     float loss_scale, void* dh, int32_t dh_compact, float* dw_lm,
+                                     int32_t accumulate, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+  collider_status st = check_index(ix);
+  if (st != COLLIDER_OK) return st;
+  if (!logits || !labels || !h || !w_lm || !dh || !dw_lm) return COLLIDER_ERR_NULL;
+  if (H < 1 || V < 1 || ld_logits < V || ld_h < H) return COLLIDER_ERR_SHAPE;
+  if (H % 8 || V % 8 || ld_logits % 8 || ld_h % 8) return COLLIDER_ERR_ALIGN;
+  if (!aligned16(logits) || !aligned16(h) || !aligned16(w_lm) || !aligned16(dh) || !aligned16(dw_lm))
+    return COLLIDER_ERR_ALIGN;
+  const int32_t Mk = ix->M_kept, M = ix->B * ix->S;
+  LmHeadWs w = carve_lm_head(Mk, H, V, ws);
+  if (!ws || ws_bytes < w.bytes) return COLLIDER_ERR_WORKSPACE;
+  uint16_t* dh_c = dh_compact ? (uint16_t*)dh : w.dh_c;
+  if (Mk > 0) {
+    GatherDesc gd{h, w.h_c, ld_h * 2 / 16, (int64_t)H * 2 / 16, H * 2 / 16, 0};
+    if ((st = launch_gather_rows(&gd, 1, ix->idx, Mk, stream)) != COLLIDER_OK) return st;
+    st = launch_ce_grad((const uint16_t*)logits, ld_logits, labels, ix->idx, Mk, V, loss_scale, w.dl,
+                        V, stream);
+    if (st != COLLIDER_OK) return st;
+  }
+  GemmProblem pdh, pdw;
+  linear_problems(COLLIDER_BF16, Mk, H, V, w.h_c, H, w.dl, V, w_lm, dh_c, dw_lm, accumulate, &pdh, &pdw);
+  pdh.name = "lm_head_dh";
+  pdw.name = "lm_head_dw";
+  if (Mk > 0 && (st = gemm_bf16(pdh, w.gws, w.gws_bytes, stream)) != COLLIDER_OK) return st;
+  if ((st = gemm_bf16(pdw, w.gws, w.gws_bytes, stream)) != COLLIDER_OK) return st;
+  if (!dh_compact)  // full layout: kept rows from dh', filtered rows +0.0
+    st = launch_scatter_bytes(dh_c, (int64_t)H * 2, dh, (int64_t)H * 2, ix->inv, M, H * 2, 1, stream);
+  return st;
+}
+
+}  // extern "C"
+
+namespace {
+struct EmbWs {
+  int32_t *cnt, *off, *cursor, *sorted;
+  size_t bytes;
+};
+EmbWs carve_emb(int32_t Mk, int32_t V, void* base) {
+  Carver cv(base);
+  EmbWs w;
+  w.cnt = cv.take<int32_t>((size_t)V);
+  w.off = cv.take<int32_t>((size_t)V + 1);
+  w.cursor = cv.take<int32_t>((size_t)V);
+  w.sorted = cv.take<int32_t>((size_t)(Mk > 0 ? Mk : 1));
+  w.bytes = cv.bytes();
+  return w;
+}
+}  // namespace
+
+extern "C" {
+
+size_t collider_embedding_workspace_bytes(int32_t M_kept, int32_t V) {
+  if (M_kept < 0 || V < 1) return 0;
+  return carve_emb(M_kept, V, nullptr).bytes;
+}
+
+collider_status collider_embedding_bwd(const void* dx, int64_t ld_dx, int32_t dx_compact,
+                                       const int32_t* ids, const collider_index* ix, int32_t H,
+                                       int32_t V, float* dE, int32_t accumulate, void* ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+  collider_status st = check_index(ix);
+  if (st != COLLIDER_OK) return st;
+  if (!ids || !dE || (ix->M_kept > 0 && !dx)) return COLLIDER_ERR_NULL;
+  if (H < 1 || V < 1 || V > (1 << 30) || ld_dx < H) return COLLIDER_ERR_SHAPE;
+  if (H % 8 || ld_dx % 8 || (dx && !aligned16(dx)) || !aligned16(dE)) return COLLIDER_ERR_ALIGN;
+  EmbWs w = carve_emb(ix->M_kept, V, ws);
+  if (!ws || ws_bytes < w.bytes) return COLLIDER_ERR_WORKSPACE;
+  return launch_embedding_bwd((const uint16_t*)dx, ld_dx, dx_compact, ids, ix->idx, ix->M_kept, V, H,
+                              dE, accumulate, w.cnt, w.off, w.cursor, w.sorted, stream);
+}
+
 }  // extern "C"

@@ -91,6 +91,18 @@ collider_status launch_build_index(const uint8_t* keep, int B, int S, int32_t* i
                                    int32_t* cu, int32_t* count, int expect, int32_t* mismatch,
                                    hipStream_t s);
 
+// loss.hip
+collider_status launch_select_topk(const float* score, int M, int n_keep, uint8_t* keep,
+                                   hipStream_t s);
+collider_status launch_ce_grad(const uint16_t* logits, int64_t ld, const int32_t* labels,
+                               const int32_t* rowmap, int rows, int V, float scale, uint16_t* dl,
+                               int64_t ldd, hipStream_t s);
+// cnt, cursor: [V]; off: [V + 1]; sorted: [rows]
+collider_status launch_embedding_bwd(const uint16_t* dx, int64_t ld, int dx_compact,
+                                     const int32_t* ids, const int32_t* idx, int rows, int V, int H,
+                                     float* dE, int accumulate, int32_t* cnt, int32_t* off,
+                                     int32_t* cursor, int32_t* sorted, hipStream_t s);
+
 // rows.hip
 struct GatherDesc {
   const void* src;

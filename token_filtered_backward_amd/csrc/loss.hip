@@ -1,0 +1,406 @@
+// Loss side of the filtered backward (Collider paper, Figure 2(b): the per-token training loss
+// decides which tokens are filtered, and a filtered token's loss is dropped, so it sends no
+// gradient into the LM head, the layers or the token embedding):
+//   select_topk_kernel      per-token scores -> keep mask (the n_keep largest scores kept)
+//   ce_grad_kernel          dlogits' = scale * (softmax(logits') - onehot(label')) over kept rows
+//   embed_*_kernel          dE[v] = sum of dx over the kept tokens with id v, in token order
+// The LM head's two reduced GEMMs reuse the bf16 GEMM (gemm.hip).
+#include "internal.h"
+
+namespace collider {
+
+// ------------------------------------------------------------------------------------------
+// top-k selection: one workgroup, radix select on 32-bit order-preserving keys
+// ------------------------------------------------------------------------------------------
+// Larger score -> larger key; -0.0 ranks as +0.0; NaN ranks below every number (key 0, below
+// -inf's 0x007fffff).
+__device__ __forceinline__ uint32_t score_key(float x) {
+  uint32_t b = __float_as_uint(x);
+  if (x != x) return 0u;
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+constexpr int kSelThreads = 1024;
+
+// keep[t] = 1 for the n_keep tokens of largest score (equal scores: lower t first), else 0.
+// Four passes pick the threshold key byte by byte from the top (a 256-bin histogram of the keys
+// that match the bytes chosen so far); a last pass keeps every key above the threshold and the
+// first `need` keys equal to it in token order (a block-wide running count).
+__global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* __restrict__ score,
+                                                                  int M, int n_keep,
+                                                                  uint8_t* __restrict__ keep) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_sel[2];
+  __shared__ uint32_t s_wsum[kSelThreads / 64];
+  __shared__ uint32_t s_carry;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (n_keep <= 0 || n_keep >= M) {
+    const uint8_t v = n_keep <= 0 ? 0 : 1;
+    for (int t = tid; t < M; t += kSelThreads) keep[t] = v;
+    return;
+  }
+  uint32_t prefix = 0, pmask = 0, need = (uint32_t)n_keep;
+  for (int d = 3; d >= 0; --d) {
+    for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+    __syncthreads();
+    for (int t = tid; t < M; t += kSelThreads) {
+      const uint32_t k = score_key(score[t]);
+      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> (8 * d)) & 255u], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane l holds bins 255 - 4l - q (q = 0..3), i.e. the bins in descending order
+      uint32_t loc[4], sum = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        loc[q] = hist[255 - 4 * lane - q];
+        sum += loc[q];
+      }
+      uint32_t incl = sum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+      }
+      const uint32_t excl = incl - sum;
+      if (excl < need && need <= incl) {  // exactly one lane: the total is at least `need`
+        uint32_t acc = excl;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (acc + loc[q] >= need) {
+            s_sel[0] = (uint32_t)(255 - 4 * lane - q);
+            s_sel[1] = need - acc;
+            break;
+          }
+          acc += loc[q];
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= s_sel[0] << (8 * d);
+    need = s_sel[1];
+    pmask |= 255u << (8 * d);
+    __syncthreads();  // s_sel is rewritten by the next pass
+  }
+  // prefix is now the threshold key T; keep keys > T and the first `need` keys == T
+  const uint32_t T = prefix;
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  constexpr int PER = 8;
+  for (int base = 0; base < M; base += kSelThreads * PER) {
+    const int t0 = base + tid * PER;
+    uint32_t kk[PER], eq = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      kk[q] = t0 + q < M ? score_key(score[t0 + q]) : 0u;
+      eq += (t0 + q < M && kk[q] == T) ? 1u : 0u;
+    }
+    uint32_t incl = eq;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    uint32_t before = s_carry + incl - eq;
+    for (int w = 0; w < wave; ++w) before += s_wsum[w];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      if (t0 + q >= M) break;
+      bool kp = kk[q] > T;
+      if (kk[q] == T) {
+        kp = before < need;
+        ++before;
+      }
+      keep[t0 + q] = kp ? 1 : 0;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t tot = 0;
+      for (int w = 0; w < kSelThreads / 64; ++w) tot += s_wsum[w];
+      s_carry += tot;
+    }
+    __syncthreads();
+  }
+}
+
+collider_status launch_select_topk(const float* score, int M, int n_keep, uint8_t* keep,
+                                   hipStream_t s) {
+  if (M <= 0) return COLLIDER_OK;
+  COLLIDER_LAUNCH("select_topk", s,
+                  hipLaunchKernelGGL(select_topk_kernel, dim3(1), dim3(kSelThreads), 0, s, score, M,
+                                     n_keep, keep));
+  return last_hip_status();
+}
+
+// ------------------------------------------------------------------------------------------
+// cross-entropy gradient over the kept rows: one workgroup per row
+// ------------------------------------------------------------------------------------------
+constexpr float kLog2eF = 1.4426950408889634f;
+
+struct MaxSum {
+  float m, s;  // running max of z * log2(e) and sum of 2^(z log2(e) - m)
+};
+__device__ __forceinline__ MaxSum ms_merge(MaxSum a, MaxSum b) {
+  const float m = fmaxf(a.m, b.m);
+  return MaxSum{m, a.s * __builtin_amdgcn_exp2f(a.m - m) + b.s * __builtin_amdgcn_exp2f(b.m - m)};
+}
+__device__ __forceinline__ MaxSum ms_add8(MaxSum a, uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float z[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    z[2 * i] = bflo(w[i]) * kLog2eF;
+    z[2 * i + 1] = bfhi(w[i]) * kLog2eF;
+  }
+  float m8 = z[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) m8 = fmaxf(m8, z[i]);
+  const float m = fmaxf(a.m, m8);
+  float s = a.s * __builtin_amdgcn_exp2f(a.m - m);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += __builtin_amdgcn_exp2f(z[i] - m);
+  return MaxSum{m, s};
+}
+
+// RV > 0: the row stays in registers (RV 16-byte vectors per thread, V <= 2048 RV); RV == 0: the
+// row is read twice (the second read mostly from cache).
+template <int RV>
+__global__ __launch_bounds__(256) void ce_grad_kernel(const uint16_t* __restrict__ logits,
+                                                      int64_t ld, const int32_t* __restrict__ labels,
+                                                      const int32_t* __restrict__ rowmap, int V,
+                                                      float scale, uint16_t* __restrict__ dl,
+                                                      int64_t ldd) {
+  __shared__ MaxSum s_ms[4];
+  const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t = rowmap ? rowmap[c] : c;
+  const int y = labels[t];
+  const int nvec = V >> 3;
+  const uint4* src = (const uint4*)(logits + t * ld);
+  uint4* dst = (uint4*)(dl + (int64_t)c * ldd);
+  if (y < 0 || y >= V) {  // no target: no loss, no gradient
+    for (int i = tid; i < nvec; i += 256) dst[i] = make_uint4(0, 0, 0, 0);
+    return;
+  }
+  MaxSum ms{-INFINITY, 0.f};
+  uint4 row[RV > 0 ? RV : 1];
+  if constexpr (RV > 0) {
+#pragma unroll
+    for (int j = 0; j < RV; ++j) {
+      const int i = tid + 256 * j;
+      row[j] = i < nvec ? src[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < RV; ++j)
+      if (tid + 256 * j < nvec) ms = ms_add8(ms, row[j]);
+  } else {
+    for (int i = tid; i < nvec; i += 256) ms = ms_add8(ms, src[i]);
+  }
+  // the first merge may combine two empty states (m = -inf): keep s = 0 there
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    MaxSum o{__shfl_xor(ms.m, off, 64), __shfl_xor(ms.s, off, 64)};
+    if (o.m == -INFINITY) continue;
+    ms = ms.m == -INFINITY ? o : ms_merge(ms, o);
+  }
+  if (lane == 0) s_ms[wave] = ms;
+  __syncthreads();
+  ms = s_ms[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) ms = ms_merge(ms, s_ms[w]);
+  const float m = ms.m, sc = scale / ms.s;
+  auto grad8 = [&](int i, uint4 v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float g[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      g[2 * e] = __builtin_amdgcn_exp2f(bflo(w[e]) * kLog2eF - m) * sc;
+      g[2 * e + 1] = __builtin_amdgcn_exp2f(bfhi(w[e]) * kLog2eF - m) * sc;
+    }
+    const int d = y - 8 * i;
+    if (d >= 0 && d < 8) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e == d) g[e] -= scale;
+    }
+    dst[i] = make_uint4(pack2bf(g[0], g[1]), pack2bf(g[2], g[3]), pack2bf(g[4], g[5]),
+                        pack2bf(g[6], g[7]));
+  };
+  if constexpr (RV > 0) {
+#pragma unroll
+    for (int j = 0; j < RV; ++j)
+      if (tid + 256 * j < nvec) grad8(tid + 256 * j, row[j]);
+  } else {
+    for (int i = tid; i < nvec; i += 256) grad8(i, src[i]);
+  }
+}
+
+collider_status launch_ce_grad(const uint16_t* logits, int64_t ld, const int32_t* labels,
+                               const int32_t* rowmap, int rows, int V, float scale, uint16_t* dl,
+                               int64_t ldd, hipStream_t s) {
+  if (rows <= 0) return COLLIDER_OK;
+  const int nvec = V / 8;
+  if (nvec <= 256 * 16)
+    COLLIDER_LAUNCH("ce_grad", s, hipLaunchKernelGGL(ce_grad_kernel<16>, dim3(rows), dim3(256), 0, s,
+                                                     logits, ld, labels, rowmap, V, scale, dl, ldd));
+  else if (nvec <= 256 * 32)
+    COLLIDER_LAUNCH("ce_grad", s, hipLaunchKernelGGL(ce_grad_kernel<32>, dim3(rows), dim3(256), 0, s,
+                                                     logits, ld, labels, rowmap, V, scale, dl, ldd));
+  else
+    COLLIDER_LAUNCH("ce_grad", s, hipLaunchKernelGGL(ce_grad_kernel<0>, dim3(rows), dim3(256), 0, s,
+                                                     logits, ld, labels, rowmap, V, scale, dl, ldd));
+  return last_hip_status();
+}
+
+// ------------------------------------------------------------------------------------------
+// embedding gradient: kept tokens bucketed by id (stable counting sort), then one wavefront per
+// vocabulary row sums its bucket's dx rows in token order.  No float atomics: every sum has a
+// fixed order.
+// ------------------------------------------------------------------------------------------
+__global__ void fill_i32_kernel(int32_t* __restrict__ p, int n, int32_t v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// id of kept token c (-1 when outside [0, V): such tokens have no embedding row)
+__device__ __forceinline__ int kept_id(const int32_t* ids, const int32_t* idx, int c, int V) {
+  const int id = ids[idx[c]];
+  return (id >= 0 && id < V) ? id : -1;
+}
+
+__global__ void embed_count_kernel(const int32_t* __restrict__ ids, const int32_t* __restrict__ idx,
+                                   int rows, int V, int32_t* __restrict__ cnt) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= rows) return;
+  const int id = kept_id(ids, idx, c, V);
+  if (id >= 0) atomicAdd(&cnt[id], 1);  // integer counts: the same totals in any order
+}
+
+// off[v] = sum of cnt[u] for u < v, off[V] = total; one workgroup of 1024 threads
+__global__ __launch_bounds__(1024) void embed_scan_kernel(const int32_t* __restrict__ cnt, int V,
+                                                          int32_t* __restrict__ off) {
+  __shared__ int32_t s_w[16];
+  __shared__ int32_t s_carry;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  for (int base = 0; base < V; base += 1024) {
+    const int v = base + tid;
+    const int x = v < V ? cnt[v] : 0;
+    int incl = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) s_w[wave] = incl;
+    __syncthreads();
+    int before = s_carry + incl - x;
+    for (int w = 0; w < wave; ++w) before += s_w[w];
+    if (v < V) off[v] = before;
+    __syncthreads();
+    if (tid == 0) {
+      int tot = 0;
+      for (int w = 0; w < 16; ++w) tot += s_w[w];
+      s_carry += tot;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) off[V] = s_carry;
+}
+
+// sorted[off[id] + r] = c, r = number of kept tokens before c with the same id (stable).  One
+// workgroup walks the kept tokens in chunks of 1024: a token's rank inside its chunk comes from the
+// chunk's ids in LDS, its rank across earlier chunks from cursor[id], which is raised once the
+// whole chunk has read it.
+__global__ __launch_bounds__(1024) void embed_place_kernel(const int32_t* __restrict__ ids,
+                                                           const int32_t* __restrict__ idx, int rows,
+                                                           int V, const int32_t* __restrict__ off,
+                                                           int32_t* cursor,
+                                                           int32_t* __restrict__ sorted) {
+  __shared__ int32_t s_id[1024];
+  const int tid = threadIdx.x;
+  for (int base = 0; base < rows; base += 1024) {
+    const int c = base + tid;
+    const int id = c < rows ? kept_id(ids, idx, c, V) : -1;
+    s_id[tid] = id;
+    __syncthreads();
+    if (id >= 0) {
+      int r = 0;
+      for (int j = 0; j < tid; ++j) r += s_id[j] == id ? 1 : 0;
+      const int cur = __hip_atomic_load(&cursor[id], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sorted[off[id] + cur + r] = c;
+    }
+    __syncthreads();  // every token of the chunk has read cursor[] before any update
+    if (id >= 0) atomicAdd(&cursor[id], 1);
+    __threadfence();
+    __syncthreads();
+  }
+}
+
+// dE[v, :] (+)= sum over j < off[v+1] - off[v] of dx[row(sorted[off[v] + j]), :]; one wavefront per
+// vocabulary row, 8 columns per lane per step; rows with no kept token are written as zeros
+// (or left as they are when accumulating).
+__global__ __launch_bounds__(256) void embed_rowsum_kernel(const uint16_t* __restrict__ dx,
+                                                           int64_t ld, const int32_t* __restrict__ idx,
+                                                           const int32_t* __restrict__ off,
+                                                           const int32_t* __restrict__ sorted, int V,
+                                                           int H, float* __restrict__ dE,
+                                                           int accumulate) {
+  const int v = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (v >= V) return;
+  const int b = off[v], n = off[v + 1] - b;
+  if (n == 0 && accumulate) return;
+  float* out = dE + (int64_t)v * H;
+  for (int col = lane * 8; col < H; col += 512) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < n; ++j) {
+      const int c = sorted[b + j];
+      const int64_t r = idx ? idx[c] : c;
+      const uint4 u = *(const uint4*)(dx + r * ld + col);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += bflo(w[e]);
+        acc[2 * e + 1] += bfhi(w[e]);
+      }
+    }
+    float4* o = (float4*)(out + col);
+    float4 a = make_float4(acc[0], acc[1], acc[2], acc[3]), c4 = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    if (accumulate) {
+      const float4 p0 = o[0], p1 = o[1];
+      a.x += p0.x; a.y += p0.y; a.z += p0.z; a.w += p0.w;
+      c4.x += p1.x; c4.y += p1.y; c4.z += p1.z; c4.w += p1.w;
+    }
+    o[0] = a;
+    o[1] = c4;
+  }
+}
+
+collider_status launch_embedding_bwd(const uint16_t* dx, int64_t ld, int dx_compact,
+                                     const int32_t* ids, const int32_t* idx, int rows, int V, int H,
+                                     float* dE, int accumulate, int32_t* cnt, int32_t* off,
+                                     int32_t* cursor, int32_t* sorted, hipStream_t s) {
+  COLLIDER_LAUNCH("embed_fill", s,
+                  hipLaunchKernelGGL(fill_i32_kernel, dim3((V + 255) / 256), dim3(256), 0, s, cnt, V, 0));
+  COLLIDER_LAUNCH("embed_fill", s,
+                  hipLaunchKernelGGL(fill_i32_kernel, dim3((V + 255) / 256), dim3(256), 0, s, cursor, V, 0));
+  if (rows > 0)
+    COLLIDER_LAUNCH("embed_count", s,
+                    hipLaunchKernelGGL(embed_count_kernel, dim3((rows + 255) / 256), dim3(256), 0, s,
+                                       ids, idx, rows, V, cnt));
+  COLLIDER_LAUNCH("embed_scan", s,
+                  hipLaunchKernelGGL(embed_scan_kernel, dim3(1), dim3(1024), 0, s, cnt, V, off));
+  if (rows > 0)
+    COLLIDER_LAUNCH("embed_place", s,
+                    hipLaunchKernelGGL(embed_place_kernel, dim3(1), dim3(1024), 0, s, ids, idx, rows,
+                                       V, off, cursor, sorted));
+  COLLIDER_LAUNCH("embed_rowsum", s,
+                  hipLaunchKernelGGL(embed_rowsum_kernel, dim3((V + 3) / 4), dim3(256), 0, s, dx, ld,
+                                     dx_compact ? nullptr : idx, off, sorted, V, H, dE, accumulate));
+  return last_hip_status();
+}
+
+}  // namespace collider
