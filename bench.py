@@ -15,6 +15,7 @@ CPU oracle timed on a bounded sample.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config tinyllama] [--r 40]
                     [--seq S [--tokens T]]      (long-context sweep: S per sequence, B = T / S)
+                    [--loss-side [--vocab V]]   (the loss-side steps instead of the layer)
 """
 import argparse
 import json
@@ -128,6 +129,134 @@ def cpu_baseline(cfg, inp, min_seconds=8.0):
                       f"scaled x{cfg.B / done:g} (the layer's work is linear in the sequence count)"}
 
 
+def loss_side_bench(args, cfg):
+    """The loss-side steps of one batch: per-token scores -> keep mask (device top-k) -> index ->
+    LM-head cross-entropy backward over the kept tokens (dh stays compact for the top layer) ->
+    embedding gradient from the bottom layer's compact dx.  Unfiltered: the same LM-head and
+    embedding backward over every token."""
+    import numpy as np
+    import torch
+
+    import synth
+    import token_filtered_backward_amd as tfb
+
+    dev = "cuda"
+    B, S, M, H, V = cfg.B, cfg.S, cfg.M, cfg.H, args.vocab
+    n_keep = M - synth.n_filtered(M, args.r)
+    log(f"[bench] loss side: M={M} H={H} V={V} r={args.r}% (kept {n_keep})")
+    rng = np.random.default_rng(args.seed)
+    score = torch.from_numpy(np.exp(synth.rng_for(args.seed, "score").standard_normal(M)).astype(np.float32)).to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    logits = (torch.randn((M, V), generator=g, device=dev) * 2.0).to(torch.bfloat16)
+    h = torch.randn((M, H), generator=g, device=dev).to(torch.bfloat16)
+    w_lm = (torch.randn((V, H), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    labels = torch.from_numpy(rng.integers(0, V, M).astype(np.int32)).to(dev)
+    ids = torch.from_numpy(rng.integers(0, V, M).astype(np.int32)).to(dev)
+    dx = torch.randn((n_keep, H), generator=g, device=dev).to(torch.bfloat16)
+    dx_full = torch.randn((M, H), generator=g, device=dev).to(torch.bfloat16)
+    keep = torch.empty(M, dtype=torch.uint8, device=dev)
+    ixp = tfb.build_index(torch.ones(M, dtype=torch.uint8, device=dev), B, S)
+    dh = torch.empty((n_keep, H), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((V, H), dtype=torch.float32, device=dev)
+    dE = torch.empty((V, H), dtype=torch.float32, device=dev)
+    ws_lm = torch.empty(tfb.collider_lm_head_workspace_bytes(M, H, V), dtype=torch.uint8, device=dev)
+    ws_e = torch.empty(tfb.collider_embedding_workspace_bytes(M, V), dtype=torch.uint8, device=dev)
+    # every token kept (a real index: the LM-head path reads rows through it, so the unfiltered
+    # step also copies h once, about 1% of its time)
+    uix = tfb.build_index(torch.ones(M, dtype=torch.uint8, device=dev), B, S)
+    dh_u = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        tfb.collider_select_keep(score, n_keep, keep)
+        ix = tfb.build_index(keep, B, S, out=ixp, expect=n_keep)
+        c = ix.c()
+        tfb.collider_lm_head_bwd(logits, labels, h, w_lm, c, 1.0 / n_keep, dh, dw, dh_compact=True, ws=ws_lm)
+        tfb.collider_embedding_bwd(dx, ids, c, dE, dx_compact=True, ws=ws_e)
+
+    def step_unf():
+        c = uix.c()
+        tfb.collider_lm_head_bwd(logits, labels, h, w_lm, c, 1.0 / M, dh_u, dw, dh_compact=True, ws=ws_lm)
+        tfb.collider_embedding_bwd(dx_full, ids, c, dE, dx_compact=True, ws=ws_e)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) * 1e3 / args.steps
+
+    ms_f = timed(step)
+    ixp.check()
+    ms_u = timed(step_unf)
+    log(f"[bench] loss side filtered {ms_f:.3f} ms, unfiltered {ms_u:.3f} ms")
+
+    def kernels(fn):
+        n = max(3, min(args.steps, 10))
+        torch.cuda.synchronize()
+        tfb.collider_profile_collect()
+        tfb.collider_profile_enable(True)
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        prof = tfb.collider_profile_collect()
+        tfb.collider_profile_enable(False)
+        return {k: v[0] / n for k, v in prof.items()}
+
+    kf, ku = kernels(step), kernels(step_unf)
+    gemm_ms = kf.get("lm_head_dh", 0.0) + kf.get("lm_head_dw", 0.0)
+    gemm_flops = 2 * 2.0 * n_keep * H * V
+    ce_bytes = 2.0 * n_keep * V * 2
+    emb_ms = sum(v for k, v in kf.items() if k.startswith("embed_"))
+    emb_bytes = 4.0 * V * H + 2.0 * n_keep * H
+    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None
+    out = {
+        "metric": "loss-side bwd ms (token selection, LM-head cross-entropy bwd, embedding grad) at "
+                  f"{args.r}% filter",
+        "value": round(ms_f, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_f, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"loss side of a {cfg.name}-shaped model, B{B}xS{S}, hidden {H}, vocab {V}, "
+                               f"{args.r}% filtered", "M": M, "M_kept": n_keep, "hidden": H, "vocab": V},
+        "ms_unfiltered": round(ms_u, 4), "speedup_vs_unfiltered": round(ms_u / ms_f, 3),
+        "kernel_ms_per_step": {k: round(v, 4) for k, v in sorted(kf.items(), key=lambda kv: -kv[1])},
+        "kernel_ms_per_step_unfiltered": {k: round(v, 4) for k, v in sorted(ku.items(), key=lambda kv: -kv[1])},
+        "ce_grad_gbs": round(ce_bytes / (kf["ce_grad"] * 1e-3) / 1e9, 1) if kf.get("ce_grad") else None,
+        "embedding_gbs": round(emb_bytes / (emb_ms * 1e-3) / 1e9, 1) if emb_ms else None,
+        "select_ms": round(kf.get("select_topk", 0.0), 4),
+        "roofline": {"kernel": "gemm_bf16 (the LM head's dh and dW reduced GEMMs)", "bound": "mfma",
+                     "achieved": None if gemm_tflops is None else round(gemm_tflops, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": None if gemm_tflops is None else round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "flops_per_launch": gemm_flops / 2,
+                     "avg_launch_ms": round(gemm_ms / 2, 5)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            cores = len(os.sched_getaffinity(0))
+        rows = 512  # kept rows of the sample (the LM-head work is linear in the kept-row count)
+        sel = np.arange(rows)
+        lg = logits[:rows].float().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.lm_head_bwd(lg, labels[:rows].cpu().numpy(), h[:rows].float().cpu().numpy(),
+                           w_lm.float().cpu().numpy(), np.ones(rows, np.uint8), 1.0 / rows)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(dt * 1e3 * n_keep / rows, 1), "unit": "ms", "cores": int(cores),
+                               "kind": "oracle",
+                               "sample": f"LM-head backward of {rows} kept rows (float64 NumPy), scaled x"
+                                         f"{n_keep / rows:g} to the {n_keep} kept rows; selection and "
+                                         "embedding gradient not included"}
+        del sel
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +275,10 @@ def main():
     ap.add_argument("--weight-layout", choices=("in_out", "out_in"), default="in_out",
                     help="projection weights stored [in, out] (y = x W, the pages' notation) or "
                          "[out, in] (torch nn.Linear); LLAMA-kind layers only take in_out")
+    ap.add_argument("--loss-side", action="store_true",
+                    help="time the loss-side steps (token selection, LM-head cross-entropy backward, "
+                         "embedding gradient) at the config's token count and hidden size")
+    ap.add_argument("--vocab", type=int, default=32000, help="vocabulary size for --loss-side")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a plain copy of "
                          "known size, to calibrate HBM byte counters in a profiler run)")
@@ -164,6 +297,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda"
     cfg = synth.get_config(args.config)
+    if args.loss_side:
+        loss_side_bench(args, cfg)
+        return
     if args.seq:
         tokens = args.tokens or cfg.M
         if tokens % args.seq:

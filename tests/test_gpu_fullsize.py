@@ -131,3 +131,49 @@ def test_stack_compact_chain_fullsize():
     dx = to64(out_c["dx"])
     assert np.all(np.isfinite(dx)) and np.all(dx[inp["keep"] == 0] == 0.0)
     assert np.abs(dx[inp["keep"] != 0]).max() > 0
+
+
+@pytest.mark.timeout(900)
+def test_loss_side_fullsize():
+    """The loss-side steps at the benchmark's shape (B 4 x S 2048, hidden 2048, vocab 32000, 40%
+    filtered by the device's own top-k on the LogNormal scores): LM-head cross-entropy backward
+    and embedding gradient against the float64 oracle."""
+    from tests.helpers import bf16_dev, rel_err
+    B, S, H, V = 4, 2048, 2048, 32000
+    M = B * S
+    rng = np.random.default_rng(11)
+    score = np.exp(synth.rng_for(0, "score").standard_normal(M)).astype(np.float32)
+    keep_d = tfb.select_keep(torch.from_numpy(score).cuda(), M - synth.n_filtered(M, 40))
+    keep = keep_d.cpu().numpy()
+    assert np.array_equal(keep, oracle.select_topk(score, M - synth.n_filtered(M, 40)))
+    ix = tfb.build_index(keep_d, B, S)
+    mk = ix.M_kept
+    logits = synth.f32_to_bf16_bits((rng.standard_normal((M, V)) * 2.0).astype(np.float32))
+    h = synth.f32_to_bf16_bits(rng.standard_normal((M, H)).astype(np.float32))
+    w = synth.f32_to_bf16_bits((rng.standard_normal((V, H)) * 0.02).astype(np.float32))
+    labels = rng.integers(0, V, M).astype(np.int32)
+    dh = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty((V, H), dtype=torch.float32, device="cuda")
+    print("loss side full size: LM head", flush=True)
+    tfb.collider_lm_head_bwd(bf16_dev(logits), torch.from_numpy(labels).cuda(), bf16_dev(h), bf16_dev(w),
+                             ix.c(), 1.0 / mk, dh, dw)
+    torch.cuda.synchronize()
+    f = synth.bf16_bits_to_f32
+    ref = oracle.lm_head_bwd(f(logits), labels, f(h), f(w), keep, 1.0 / mk)
+    got_dh = to64(dh)
+    errs = {"dh": rel_err(got_dh, ref["dh"]), "dw_lm": rel_err(to64(dw), ref["dw_lm"])}
+    print(errs, flush=True)
+    assert np.all(got_dh[keep == 0] == 0.0)
+    assert all(e <= BF16_TOL for e in errs.values()), errs
+    del ref, logits
+    print("loss side full size: embedding", flush=True)
+    ids = rng.integers(0, V, M).astype(np.int32)
+    dxc = synth.f32_to_bf16_bits(rng.standard_normal((mk, H)).astype(np.float32))
+    dE = torch.empty((V, H), dtype=torch.float32, device="cuda")
+    tfb.collider_embedding_bwd(bf16_dev(dxc), torch.from_numpy(ids).cuda(), ix.c(), dE, dx_compact=True)
+    torch.cuda.synchronize()
+    dx_full = np.zeros((M, H))
+    dx_full[keep != 0] = f(dxc)
+    e = rel_err(to64(dE), oracle.embedding_bwd(dx_full, ids, keep, V))
+    print("embedding", e, flush=True)
+    assert e <= 1e-5

@@ -278,18 +278,26 @@ __global__ void embed_count_kernel(const int32_t* __restrict__ ids, const int32_
   if (id >= 0) atomicAdd(&cnt[id], 1);  // integer counts: the same totals in any order
 }
 
-// off[v] = sum of cnt[u] for u < v, off[V] = total; one workgroup of 1024 threads
+// off[v] = sum of cnt[u] for u < v, off[V] = total.  One workgroup of 1024 threads walks the ids
+// in tiles of kScanTile: the tile is loaded into LDS with coalesced reads, thread i scans its 16
+// consecutive entries there, a block scan of the thread sums (plus the carry of earlier tiles) gives
+// each run's start, and the offsets go back out coalesced.
+constexpr int kScanTile = 16384;
 __global__ __launch_bounds__(1024) void embed_scan_kernel(const int32_t* __restrict__ cnt, int V,
                                                           int32_t* __restrict__ off) {
+  __shared__ int32_t s_t[kScanTile];
   __shared__ int32_t s_w[16];
   __shared__ int32_t s_carry;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int PER = kScanTile / 1024;
   if (tid == 0) s_carry = 0;
-  __syncthreads();
-  for (int base = 0; base < V; base += 1024) {
-    const int v = base + tid;
-    const int x = v < V ? cnt[v] : 0;
-    int incl = x;
+  for (int base = 0; base < V; base += kScanTile) {
+    for (int i = tid; i < kScanTile; i += 1024) s_t[i] = base + i < V ? cnt[base + i] : 0;
+    __syncthreads();
+    int sum = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) sum += s_t[tid * PER + q];
+    int incl = sum;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int y = __shfl_up(incl, o, 64);
@@ -297,15 +305,18 @@ __global__ __launch_bounds__(1024) void embed_scan_kernel(const int32_t* __restr
     }
     if (lane == 63) s_w[wave] = incl;
     __syncthreads();
-    int before = s_carry + incl - x;
-    for (int w = 0; w < wave; ++w) before += s_w[w];
-    if (v < V) off[v] = before;
-    __syncthreads();
-    if (tid == 0) {
-      int tot = 0;
-      for (int w = 0; w < 16; ++w) tot += s_w[w];
-      s_carry += tot;
+    int run = s_carry + incl - sum;
+    for (int w = 0; w < wave; ++w) run += s_w[w];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int x = s_t[tid * PER + q];
+      s_t[tid * PER + q] = run;
+      run += x;
     }
+    __syncthreads();
+    for (int i = tid; i < kScanTile; i += 1024)
+      if (base + i < V) off[base + i] = s_t[i];
+    if (tid == 1023) s_carry = run;  // the tile's last run ends at the tile's total
     __syncthreads();
   }
   if (tid == 0) off[V] = s_carry;
@@ -313,15 +324,23 @@ __global__ __launch_bounds__(1024) void embed_scan_kernel(const int32_t* __restr
 
 // sorted[off[id] + r] = c, r = number of kept tokens before c with the same id (stable).  One
 // workgroup walks the kept tokens in chunks of 1024: a token's rank inside its chunk comes from the
-// chunk's ids in LDS, its rank across earlier chunks from cursor[id], which is raised once the
-// whole chunk has read it.
+// chunk's ids in LDS (four ids per LDS read), its rank across earlier chunks from cursor[id], which
+// is raised once the whole chunk has read it.  LDS_CURSOR: the cursors live in LDS (V <= 32768);
+// otherwise in global memory (an atomic read and add per token and chunk).
+constexpr int kCursorLds = 32768;
+template <bool LDS_CURSOR>
 __global__ __launch_bounds__(1024) void embed_place_kernel(const int32_t* __restrict__ ids,
                                                            const int32_t* __restrict__ idx, int rows,
                                                            int V, const int32_t* __restrict__ off,
                                                            int32_t* cursor,
                                                            int32_t* __restrict__ sorted) {
-  __shared__ int32_t s_id[1024];
+  extern __shared__ __align__(16) int32_t s_dyn[];
+  __shared__ __align__(16) int32_t s_id[1024];
   const int tid = threadIdx.x;
+  if constexpr (LDS_CURSOR) {
+    for (int i = tid; i < V; i += 1024) s_dyn[i] = 0;
+    __syncthreads();
+  }
   for (int base = 0; base < rows; base += 1024) {
     const int c = base + tid;
     const int id = c < rows ? kept_id(ids, idx, c, V) : -1;
@@ -329,13 +348,27 @@ __global__ __launch_bounds__(1024) void embed_place_kernel(const int32_t* __rest
     __syncthreads();
     if (id >= 0) {
       int r = 0;
-      for (int j = 0; j < tid; ++j) r += s_id[j] == id ? 1 : 0;
-      const int cur = __hip_atomic_load(&cursor[id], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int4* s4 = (const int4*)s_id;
+      for (int j4 = 0; j4 < (tid >> 2); ++j4) {
+        const int4 q = s4[j4];
+        r += (q.x == id) + (q.y == id) + (q.z == id) + (q.w == id);
+      }
+      for (int j = tid & ~3; j < tid; ++j) r += s_id[j] == id ? 1 : 0;
+      int cur;
+      if constexpr (LDS_CURSOR)
+        cur = s_dyn[id];
+      else
+        cur = __hip_atomic_load(&cursor[id], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       sorted[off[id] + cur + r] = c;
     }
-    __syncthreads();  // every token of the chunk has read cursor[] before any update
-    if (id >= 0) atomicAdd(&cursor[id], 1);
-    __threadfence();
+    __syncthreads();  // every token of the chunk has read its cursor before any update
+    if (id >= 0) {
+      if constexpr (LDS_CURSOR)
+        atomicAdd(&s_dyn[id], 1);
+      else
+        atomicAdd(&cursor[id], 1);
+    }
+    if constexpr (!LDS_CURSOR) __threadfence();
     __syncthreads();
   }
 }
@@ -393,10 +426,19 @@ collider_status launch_embedding_bwd(const uint16_t* dx, int64_t ld, int dx_comp
                                        ids, idx, rows, V, cnt));
   COLLIDER_LAUNCH("embed_scan", s,
                   hipLaunchKernelGGL(embed_scan_kernel, dim3(1), dim3(1024), 0, s, cnt, V, off));
-  if (rows > 0)
+  if (rows > 0 && V <= kCursorLds) {
+    static const bool attr_ok =
+        hipFuncSetAttribute((const void*)embed_place_kernel<true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kCursorLds * 4) == hipSuccess;
+    if (!attr_ok) return COLLIDER_ERR_HIP;
     COLLIDER_LAUNCH("embed_place", s,
-                    hipLaunchKernelGGL(embed_place_kernel, dim3(1), dim3(1024), 0, s, ids, idx, rows,
-                                       V, off, cursor, sorted));
+                    hipLaunchKernelGGL(embed_place_kernel<true>, dim3(1), dim3(1024), V * 4, s, ids, idx,
+                                       rows, V, off, cursor, sorted));
+  } else if (rows > 0) {
+    COLLIDER_LAUNCH("embed_place", s,
+                    hipLaunchKernelGGL(embed_place_kernel<false>, dim3(1), dim3(1024), 0, s, ids, idx,
+                                       rows, V, off, cursor, sorted));
+  }
   COLLIDER_LAUNCH("embed_rowsum", s,
                   hipLaunchKernelGGL(embed_rowsum_kernel, dim3((V + 3) / 4), dim3(256), 0, s, dx, ld,
                                      dx_compact ? nullptr : idx, off, sorted, V, H, dE, accumulate));
