@@ -129,7 +129,7 @@ def cpu_baseline(cfg, inp, min_seconds=8.0):
                       f"scaled x{cfg.B / done:g} (the layer's work is linear in the sequence count)"}
 
 
-def loss_side_bench(args, cfg):
+def loss_side_bench(args, cfg, emit=True):
     """The loss-side steps of one batch: per-token scores -> keep mask (device top-k) -> index ->
     LM-head cross-entropy backward over the kept tokens (dh stays compact for the top layer) ->
     embedding gradient from the bottom layer's compact dx.  Unfiltered: the same LM-head and
@@ -254,7 +254,9 @@ def loss_side_bench(args, cfg):
                                          f"{n_keep / rows:g} to the {n_keep} kept rows; selection and "
                                          "embedding gradient not included"}
         del sel
-    print(json.dumps(out), flush=True)
+    if emit:
+        print(json.dumps(out), flush=True)
+    return out
 
 
 def main():
@@ -279,6 +281,8 @@ def main():
                     help="time the loss-side steps (token selection, LM-head cross-entropy backward, "
                          "embedding gradient) at the config's token count and hidden size")
     ap.add_argument("--vocab", type=int, default=32000, help="vocabulary size for --loss-side")
+    ap.add_argument("--no-loss-side", action="store_true",
+                    help="skip the loss-side summary the default layer run appends")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a plain copy of "
                          "known size, to calibrate HBM byte counters in a profiler run)")
@@ -546,6 +550,19 @@ def main():
             "avg_launch_ms": round(gemm_ms / max(gemm_launches, 1), 5),
         },
     }
+    if L == 1 and cfg.name == "tinyllama" and not args.seq and not args.no_loss_side:
+        # the loss-side steps of the same batch (selection, LM-head cross-entropy backward,
+        # embedding gradient), timed on their own; not part of `value`
+        try:
+            la = argparse.Namespace(seed=args.seed, r=args.r, vocab=args.vocab, steps=10, warmup=3,
+                                    no_cpu_baseline=True)
+            ls = loss_side_bench(la, cfg, emit=False)
+            out["loss_side"] = {k: ls[k] for k in ("value", "unit", "ms_unfiltered", "speedup_vs_unfiltered",
+                                                    "ce_grad_gbs", "embedding_gbs", "select_ms")}
+            out["loss_side"]["workload"] = ls["config"]["workload"]
+            out["loss_side"]["gemm_tflops"] = ls["roofline"]["achieved"]
+        except Exception as e:  # reported, never fatal to the layer measurement
+            out["loss_side"] = {"error": f"{type(e).__name__}: {e}"}
     if not args.no_cpu_baseline and (L > 1 or S > 4096):
         log("[bench] no CPU oracle timing for a layer stack or a sequence longer than 4096 (one "
             "float64 sequence of the layer at this size alone takes minutes)")
