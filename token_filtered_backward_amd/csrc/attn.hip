@@ -15,8 +15,9 @@
 //     over a slice of the query heads sharing its KV head; slices go to fp32 partial buffers.
 //  3. attn_dkv_finalize: sums the slices in a fixed order, applies the rotary backward to dK and
 //     stores bf16 dk, dv.
-// Token tiles [64 rows x D] live in LDS once, row-major with padded rows.  Operands that need the
-// token index as the MFMA reduction index (K in dS K; Q and dO in P^T dO and dS^T Q) are read with
+// Token tiles [64 rows x D] live in LDS once, row-major (XOR-swizzled chunks for D = 64, padded
+// rows for D = 128).  Operands that need the token index as the MFMA reduction index (K in dS K;
+// Q and dO in P^T dO and dS^T Q) are read with
 // ds_read_b64_tr_b16: within a group of 16 lanes, lane j addresses row k0 + j/4 at columns
 // n + 4*(j%4) and lane i receives rows k0 .. k0+3 of column n + i.  The row order of the two
 // transpose reads per fragment follows the 32x32 accumulator layout (rows 8*(r/4) + 4*(lane/32) +
@@ -79,14 +80,28 @@ __device__ __forceinline__ bf16x8 to_frag(const float* v8) {
   return a;
 }
 
-// [64 x D] bf16 token tile in LDS, row-major with padded rows.  Pitch (in 4-byte banks) is 36 for
-// D = 64 and 76 for D = 128: 16 consecutive rows of a 16-byte fragment read start on distinct
-// 4-bank groups, and the 4 consecutive rows of a transpose-read group on distinct 8-bank groups.
+// [64 x D] bf16 token tile in LDS, row-major.
+// D = 64: 128-byte rows whose 16-byte chunks sit at chunk ^ swz(r), so that both read patterns are
+// free of bank conflicts (64 banks of 4 bytes) - a 16-byte fragment read (16 lanes, 16 consecutive
+// rows, one chunk) and a transpose read (32 lanes, 4 consecutive rows, 4 consecutive chunks) - and
+// so are the tile stores: swz takes distinct values on the 8 even and on the 8 odd rows of any 16,
+// and its bit 2 differs between rows r and r + 2 for r = 0, 1 mod 4.  A padded pitch left the
+// transpose reads 2-way conflicted; the swizzle took the dQ kernel from 108 to 104 us (TinyLlama
+// layer, 40%).
+// D = 128: padded 304-byte rows (76 banks): 16 consecutive rows of a fragment read start on
+// distinct 4-bank groups.  The same swizzle (4 bits) measured 10% slower there: the extra address
+// arithmetic outweighed the conflicts it removed.
 template <int D>
 struct TokTile {
-  static constexpr int PITCH = D == 64 ? 144 : 304;  // bytes
-  static constexpr int BYTES = 64 * PITCH;
-  static constexpr int NV = 64 * (D / 8) / 256;       // 16-byte chunks per thread
+  static constexpr int ROWB = D == 64 ? 128 : 304;  // bytes per row
+  static constexpr int BYTES = 64 * ROWB;
+  static constexpr int NV = 64 * (D / 8) / 256;      // 16-byte chunks per thread
+  static __device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+  // byte offset of byte `b` of row r
+  static __device__ __forceinline__ int off(int r, int b) {
+    if constexpr (D == 64) return r * ROWB + ((((b >> 4) ^ swz(r))) << 4) + (b & 15);
+    return r * ROWB + b;
+  }
 };
 
 template <int D>
@@ -108,7 +123,7 @@ struct TileRegs {
     for (int i = 0; i < TokTile<D>::NV; ++i) {
       const int c = threadIdx.x + 256 * i;
       const int r = c / (D / 8), dc = c % (D / 8);
-      *(uint4*)(T + r * TokTile<D>::PITCH + dc * 16) = v[i];
+      *(uint4*)(T + TokTile<D>::off(r, dc * 16)) = v[i];
     }
   }
 };
@@ -117,7 +132,7 @@ struct TileRegs {
 // d = kk*16 .. kk*16+15 (16-byte read per lane)
 template <int D>
 __device__ __forceinline__ bf16x8 frag_rows(const char* T, int rbase, int kk, int lane) {
-  return *(const bf16x8*)(T + (rbase + (lane & 31)) * TokTile<D>::PITCH + (kk * 16 + (lane >> 5) * 8) * 2);
+  return *(const bf16x8*)(T + TokTile<D>::off(rbase + (lane & 31), (kk * 16 + (lane >> 5) * 8) * 2));
 }
 
 // B operand with the token index as the reduction index: 16 tokens tbase .. tbase+15 in the
@@ -128,10 +143,10 @@ __device__ __forceinline__ bf16x8 frag_tr(const char* T, int tbase, int dbase, i
   const int g = lane >> 4, j = lane & 15;
   const int col = dbase + 16 * (g & 1) + 4 * (j & 3);
   const int row = tbase + 4 * (g >> 1) + (j >> 2);
-  const char* a0 = T + row * TokTile<D>::PITCH + col * 2;
+  const char* a0 = T + TokTile<D>::off(row, col * 2);
+  const char* a1 = T + TokTile<D>::off(row + 8, col * 2);
   const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s __attribute__((address_space(3)))*)a0);
-  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (v4s __attribute__((address_space(3)))*)(a0 + 8 * TokTile<D>::PITCH));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s __attribute__((address_space(3)))*)a1);
   const v8s both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, both);
 }
