@@ -242,7 +242,6 @@ def loss_side_bench(args, cfg, emit=True):
         except Exception:  # pragma: no cover
             cores = len(os.sched_getaffinity(0))
         rows = 512  # kept rows of the sample (the LM-head work is linear in the kept-row count)
-        sel = np.arange(rows)
         lg = logits[:rows].float().cpu().numpy()
         t0 = time.perf_counter()
         oracle.lm_head_bwd(lg, labels[:rows].cpu().numpy(), h[:rows].float().cpu().numpy(),
@@ -253,7 +252,6 @@ def loss_side_bench(args, cfg, emit=True):
                                "sample": f"LM-head backward of {rows} kept rows (float64 NumPy), scaled x"
                                          f"{n_keep / rows:g} to the {n_keep} kept rows; selection and "
                                          "embedding gradient not included"}
-        del sel
     if emit:
         print(json.dumps(out), flush=True)
     return out

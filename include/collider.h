@@ -277,8 +277,9 @@ collider_status collider_select_keep(const float* score, int32_t M, int32_t n_ke
  * (loss_scale = 1 / M_kept gives the mean over kept tokens; a label outside [0, V), such as
  * torch's ignore index -100, marks a token without a target).  Computes, for kept rows only:
  *   dlogits' = loss_scale * (softmax(logits') - onehot(labels'))   (bf16, in the workspace)
- *   dh' = dlogits' @ w_lm            -> dh: bf16 [M_kept, H] (dh_compact != 0) or [M, H] with the
- *                                       rows of filtered tokens +0.0 (dh_compact == 0)
+ *   dh' = dlogits' @ w_lm            -> dh: bf16 [M_kept, H] (dh_compact != 0; may be NULL when
+ *                                       M_kept = 0) or [M, H] with the rows of filtered tokens +0.0
+ *                                       (dh_compact == 0)
  *   dw_lm = dlogits'^T @ h'          -> float32 [V, H], overwritten (accumulate == 0) or added to
  * h is the bf16 [M, H] input of the LM head (full layout, row stride ld_h); labels int32 [M].
  * Requirements: H and V multiples of 8, 16-byte alignment of every bf16 pointer and leading

@@ -111,6 +111,12 @@ def test_lm_head_bwd_all_filtered_and_accumulate():
     tfb.collider_lm_head_bwd(*args, dh, dw)
     torch.cuda.synchronize()
     assert torch.all(dw == 0.0)
+    # nothing kept, compact dh: an empty output is accepted
+    dw0 = torch.full((V, H), 2.0, dtype=torch.float32, device="cuda")
+    tfb.collider_lm_head_bwd(*args, torch.empty((0, H), dtype=torch.bfloat16, device="cuda"), dw0,
+                             dh_compact=True)
+    torch.cuda.synchronize()
+    assert torch.all(dw0 == 0.0)
     # accumulate on a real mask adds the overwrite result
     keep = synth.make_keep(B * S, 40, 7)
     ix = tfb.build_index(_dev_keep(keep), B, S)

@@ -459,12 +459,15 @@ collider_status collider_lm_head_bwd(const void* logits, int64_t ld_logits, cons
                                      hipStream_t stream) {
   collider_status st = check_index(ix);
   if (st != COLLIDER_OK) return st;
-  if (!logits || !labels || !h || !w_lm || !dh || !dw_lm) return COLLIDER_ERR_NULL;
+  const int32_t Mk = ix->M_kept, M = ix->B * ix->S;
+  // a compact dh has no rows when nothing is kept: NULL is accepted there
+  const bool dh_none = dh_compact && Mk == 0;
+  if (!logits || !labels || !h || !w_lm || !dw_lm || (!dh && !dh_none)) return COLLIDER_ERR_NULL;
   if (H < 1 || V < 1 || ld_logits < V || ld_h < H) return COLLIDER_ERR_SHAPE;
   if (H % 8 || V % 8 || ld_logits % 8 || ld_h % 8) return COLLIDER_ERR_ALIGN;
-  if (!aligned16(logits) || !aligned16(h) || !aligned16(w_lm) || !aligned16(dh) || !aligned16(dw_lm))
+  if (!aligned16(logits) || !aligned16(h) || !aligned16(w_lm) || (dh && !aligned16(dh)) ||
+      !aligned16(dw_lm))
     return COLLIDER_ERR_ALIGN;
-  const int32_t Mk = ix->M_kept, M = ix->B * ix->S;
   LmHeadWs w = carve_lm_head(Mk, H, V, ws);
   if (!ws || ws_bytes < w.bytes) return COLLIDER_ERR_WORKSPACE;
   uint16_t* dh_c = dh_compact ? (uint16_t*)dh : w.dh_c;
