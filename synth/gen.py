@@ -10,6 +10,7 @@ LogNormal(0, 1) score (a stand-in for the per-token loss a filter ranks by) and 
 floor(M * r_pct / 100) lowest-scoring tokens of the flattened batch are filtered; among equal scores
 the lower flat position is kept.  The paper leaves its selector open (it cites one, Figure 4 caption).
 """
+import sys
 import zlib
 
 import numpy as np
@@ -133,6 +134,9 @@ def _attention_fwd(q, k, v, B, S, nq, nkv, d, chunk=1024):
     for b in range(B):
         r0 = b * S
         for h in range(nq):
+            if S >= 16384 and h % 8 == 0:  # long sequences take minutes on the host: say where we are
+                print(f"[synth] attention forward: sequence {b + 1}/{B}, head {h + 1}/{nq} (S={S})",
+                      file=sys.stderr, flush=True)
             g = h // G
             kk = k3[r0:r0 + S, g, :]
             vv = v3[r0:r0 + S, g, :]
