@@ -514,6 +514,10 @@ def test_unfiltered_baseline(name, layout):
                           dy, ix)
     for k in g_unf:
         assert torch.equal(g_unf[k], g_all[k]), k
+    # with every token kept the filtered row term is the full one (the layer takes the cheaper form)
+    g_def = tfb.layer_bwd(tfb.layer_cfg(cfg, weight_layout=layout), weights, saved, dy, ix)
+    for k in g_unf:
+        assert torch.equal(g_unf[k], g_def[k]), k
     ref = oracle.layer_bwd(cfg, upcast(inp["weights"]), upcast(inp["saved"]),
                            synth.bf16_bits_to_f32(inp["dy"]), inp["keep"], "full_d")
     for gname, oname in GRAD_NAMES[cfg.kind].items():

@@ -226,6 +226,8 @@ def collider_select_keep(score, n_keep, keep, stream=None):
 
 
 def select_keep(score: torch.Tensor, n_keep: int, stream=None) -> torch.Tensor:
+    if score.dtype != torch.float32 or not score.is_contiguous():
+        raise TypeError("score must be a contiguous float32 tensor")
     keep = torch.empty(score.numel(), dtype=torch.uint8, device=score.device)
     collider_select_keep(score, n_keep, keep, stream)
     return keep
@@ -241,6 +243,10 @@ def collider_lm_head_bwd(logits, labels, h, w_lm, ix: CollIndex, loss_scale, dh,
     layout), labels int32 [M], h bf16 [M, H], w_lm bf16 [V, H] -> dh bf16 ([M_kept, H] when
     dh_compact, else [M, H] with zero filtered rows) and dw_lm float32 [V, H]."""
     V, H = w_lm.shape
+    for name, t, dt in (("logits", logits, torch.bfloat16), ("h", h, torch.bfloat16), ("w_lm", w_lm, torch.bfloat16),
+                        ("labels", labels, torch.int32), ("dh", dh, torch.bfloat16), ("dw_lm", dw_lm, torch.float32)):
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
     if ws is None:
         ws = torch.empty(max(1, collider_lm_head_workspace_bytes(ix.M_kept, H, V)), dtype=torch.uint8,
                          device=h.device)
@@ -259,6 +265,8 @@ def collider_embedding_bwd(dx, ids, ix: CollIndex, dE, dx_compact=False, accumul
     """dE[v] (+)= sum of dx rows of the kept tokens with ids == v (token order); dx bf16 [M_kept, H]
     (dx_compact) or [M, H], ids int32 [M], dE float32 [V, H]."""
     V, H = dE.shape
+    if dE.dtype != torch.float32 or ids.dtype != torch.int32 or (dx is not None and dx.dtype != torch.bfloat16):
+        raise TypeError("dx must be bfloat16, ids int32 and dE float32")
     if ws is None:
         ws = torch.empty(max(1, collider_embedding_workspace_bytes(ix.M_kept, V)), dtype=torch.uint8,
                          device=dE.device)

@@ -212,7 +212,9 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
   ac.rot_dims = c.rot_dims;
   ac.rope_base = c.rope_base;
   ac.softmax_scale = 0.f;
-  ac.dmode = unf ? COLLIDER_ATTN_D_FULL : c.dmode;
+  // with every token kept the two row terms are the same quantity: D~_i = sum_j P_ij dO_i . v_j =
+  // dO_i . O_i, the forward's output over all (here all kept) keys; the second costs no key sweep
+  ac.dmode = (unf || Mk == M) ? COLLIDER_ATTN_D_FULL : c.dmode;
   collider_index aix = ix;
   if (unf) {  // every token kept: the attention kernels take cs = b*S and position = row mod S
     aix.idx = nullptr;
