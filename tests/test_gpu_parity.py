@@ -525,3 +525,34 @@ def test_unfiltered_baseline(name, layout):
         if layout == tfb.WEIGHTS_IN_OUT and gname.startswith("dw_"):
             got = got.T
         assert rel_err(got, ref[oname]) <= BF16_TOL, gname
+
+
+def _degenerate_keep(B, S, kind):
+    keep = np.zeros((B, S), np.uint8)
+    if kind == "one_token":            # a single kept token, in the middle of the batch
+        keep[B // 2, S // 2] = 1
+    elif kind == "middle_sequence_empty":  # sequences kept whole except an empty one between them
+        keep[:] = 1
+        keep[B // 2] = 0
+    elif kind == "first_tokens":       # only each sequence's first token (the shortest causal rows)
+        keep[:, 0] = 1
+    elif kind == "last_tokens":        # only each sequence's last token (the longest causal rows)
+        keep[:, -1] = 1
+    elif kind == "alternate":          # every other token
+        keep[:, ::2] = 1
+    return keep.reshape(-1)
+
+
+@pytest.mark.parametrize("name", ["small_llama", "small_llama_d128", "small_phi"])
+@pytest.mark.parametrize("B,S", [(1, 1), (3, 5), (2, 129)])
+@pytest.mark.parametrize("kind", ["one_token", "middle_sequence_empty", "first_tokens", "last_tokens",
+                                  "alternate"])
+def test_layer_degenerate_shapes(name, B, S, kind):
+    """Very short sequences (S = 1, 5; 129 crosses one 128-row attention block), a single kept token,
+    an empty sequence between kept ones, only first or only last tokens kept, every other token."""
+    cfg = synth.get_config(name).with_(B=B, S=S)
+    keep = _degenerate_keep(B, S, kind)
+    if keep.sum() == 0:
+        keep[0] = 1
+    inp = synth.make_layer_inputs(cfg, keep=keep)
+    run_layer_and_compare(inp, 0)
