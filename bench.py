@@ -275,6 +275,9 @@ def main():
     ap.add_argument("--weight-layout", choices=("in_out", "out_in"), default="in_out",
                     help="projection weights stored [in, out] (y = x W, the pages' notation) or "
                          "[out, in] (torch nn.Linear); LLAMA-kind layers only take in_out")
+    ap.add_argument("--dmode", choices=("filtered", "full"), default="filtered",
+                    help="softmax-backward row term of the filtered attention: sum over kept keys of "
+                         "P~ dP (filtered, the default) or dO . O (full)")
     ap.add_argument("--loss-side", action="store_true",
                     help="time the loss-side steps (token selection, LM-head cross-entropy backward, "
                          "embedding gradient) at the config's token count and hidden size")
@@ -336,7 +339,8 @@ def main():
     if layout == tfb.WEIGHTS_IN_OUT:
         weights = tfb.to_in_out(weights)
 
-    lcfg = tfb.layer_cfg(cfg, weight_layout=layout)
+    dmode = tfb.ATTN_D_FULL if args.dmode == "full" else tfb.ATTN_D_FILTERED
+    lcfg = tfb.layer_cfg(cfg, dmode=dmode, weight_layout=layout)
     lb = tfb.LayerBackward(lcfg, B, S, dev)
     ix0 = tfb.build_index(keep, B, S)
     grads = tfb.make_grads(lcfg, M, ix0.M_kept, dev)
@@ -517,6 +521,7 @@ def main():
                    "layers": L,
                    "B": B, "S": S, "hidden": cfg.H, "heads": f"{cfg.nq}/{cfg.nkv}x{cfg.d}",
                    "inter": cfg.I, "M": M, "M_kept": ix.M_kept, "parallelism": "single GPU",
+                   "attn_row_term": args.dmode,
                    "weight_layout": "in_out" if layout == tfb.WEIGHTS_IN_OUT else "out_in"},
         "launch_mode": {"filtered": mode_f, "unfiltered": mode_u},
         "ms_by_launch_mode": {"filtered": modes_f, "unfiltered": modes_u},
