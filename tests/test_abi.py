@@ -29,6 +29,11 @@ def test_header_declares_the_entry_points():
         assert n in names
 
 
+def test_library_resolves_every_symbol_at_load():
+    """Loading with immediate binding fails on any symbol the library uses but does not define."""
+    ctypes.CDLL(tfb.LIB_PATH, mode=os.RTLD_NOW | os.RTLD_LOCAL)
+
+
 def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(tfb.LIB_PATH)
     missing = [n for n in declared_functions() if not hasattr(L, n)]

@@ -5,6 +5,8 @@
 //   ce_grad_kernel          dlogits' = scale * (softmax(logits') - onehot(label')) over kept rows
 //   embed_*_kernel          dE[v] = sum of dx over the kept tokens with id v, in token order
 // The LM head's two reduced GEMMs reuse the bf16 GEMM (gemm.hip).
+#include <atomic>
+
 #include "internal.h"
 
 namespace collider {
@@ -412,6 +414,20 @@ __global__ __launch_bounds__(256) void embed_rowsum_kernel(const uint16_t* __res
   }
 }
 
+// Raises embed_place_kernel<true>'s dynamic-LDS limit to the cursor array's size, once per device.
+static bool place_lds_limit_set() {
+  static std::atomic<uint64_t> done{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  const uint64_t bit = 1ull << dev;
+  if (done.load(std::memory_order_acquire) & bit) return true;
+  if (hipFuncSetAttribute((const void*)embed_place_kernel<true>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kCursorLds * 4) != hipSuccess)
+    return false;
+  done.fetch_or(bit, std::memory_order_acq_rel);
+  return true;
+}
+
 collider_status launch_embedding_bwd(const uint16_t* dx, int64_t ld, int dx_compact,
                                      const int32_t* ids, const int32_t* idx, int rows, int V, int H,
                                      float* dE, int accumulate, int32_t* cnt, int32_t* off,
@@ -427,10 +443,7 @@ collider_status launch_embedding_bwd(const uint16_t* dx, int64_t ld, int dx_comp
   COLLIDER_LAUNCH("embed_scan", s,
                   hipLaunchKernelGGL(embed_scan_kernel, dim3(1), dim3(1024), 0, s, cnt, V, off));
   if (rows > 0 && V <= kCursorLds) {
-    static const bool attr_ok =
-        hipFuncSetAttribute((const void*)embed_place_kernel<true>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kCursorLds * 4) == hipSuccess;
-    if (!attr_ok) return COLLIDER_ERR_HIP;
+    if (!place_lds_limit_set()) return COLLIDER_ERR_HIP;
     COLLIDER_LAUNCH("embed_place", s,
                     hipLaunchKernelGGL(embed_place_kernel<true>, dim3(1), dim3(1024), V * 4, s, ids, idx,
                                        rows, V, off, cursor, sorted));
