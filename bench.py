@@ -129,6 +129,42 @@ def cpu_baseline(cfg, inp, min_seconds=8.0):
                       f"scaled x{cfg.B / done:g} (the layer's work is linear in the sequence count)"}
 
 
+def calibration_copy(mb):
+    """One elementwise kernel over `mb` MiB (reads mb MiB, writes mb MiB): a plain copy of known size
+    that calibrates HBM byte counters in a profiler run."""
+    if mb <= 0:
+        return
+    import torch
+    n = mb << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    log(f"[bench] calibration copy of {mb} MiB done")
+
+
+def lm_head_traffic(cfg, r_pct, vocab):
+    """HBM bytes per LM-head GEMM launch from the committed counter runs, or None for another
+    workload or another GEMM / entry-point source than the one built here."""
+    import hashlib
+    import re
+    if (cfg.name, cfg.B, cfg.S, r_pct, vocab) != ("tinyllama", 4, 2048, 40, 32000):
+        return None
+    path = os.path.join(ROOT, "profiles", "gemm_bf16_lm_head_b4s2048_v32000_r40_traffic.md")
+    csrc = os.path.join(ROOT, "token_filtered_backward_amd", "csrc")
+    try:
+        text = open(path).read()
+        shas = {n: hashlib.sha256(open(os.path.join(csrc, n), "rb").read()).hexdigest()
+                for n in ("gemm.hip", "api.hip")}
+    except OSError:
+        return None
+    m = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    ok = all(re.search(rf"{re.escape(n)}_sha256: {h}", text) for n, h in shas.items())
+    return float(m.group(1)) if m and ok else None
+
+
 def loss_side_bench(args, cfg, emit=True):
     """The loss-side steps of one batch: per-token scores -> keep mask (device top-k) -> index ->
     LM-head cross-entropy backward over the kept tokens (dh stays compact for the top layer) ->
@@ -141,6 +177,7 @@ def loss_side_bench(args, cfg, emit=True):
     import token_filtered_backward_amd as tfb
 
     dev = "cuda"
+    calibration_copy(getattr(args, "copy_calibration_mb", 0))
     B, S, M, H, V = cfg.B, cfg.S, cfg.M, cfg.H, args.vocab
     n_keep = M - synth.n_filtered(M, args.r)
     log(f"[bench] loss side: M={M} H={H} V={V} r={args.r}% (kept {n_keep})")
@@ -231,7 +268,9 @@ def loss_side_bench(args, cfg, emit=True):
                      "achieved": None if gemm_tflops is None else round(gemm_tflops, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": None if gemm_tflops is None else round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "flops_per_launch": gemm_flops / 2,
+                     "traffic": lm_head_traffic(cfg, args.r, V), "flops_per_launch": gemm_flops / 2,
+                     "algorithmic_bytes_per_launch": (2.0 * n_keep * V + 2.0 * V * H + 2.0 * n_keep * H
+                                                      + 2.0 * n_keep * V + 2.0 * n_keep * H + 4.0 * V * H) / 2,
                      "avg_launch_ms": round(gemm_ms / 2, 5)},
     }
     if not args.no_cpu_baseline:
@@ -384,15 +423,7 @@ def main():
             ub(weights, saved, ugrads[(layer - 1) % 2]["dx"], uix, ugrads[layer % 2])
 
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)  # > 256 MB MALL
-    if args.copy_calibration_mb > 0:
-        n = args.copy_calibration_mb << 20
-        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.neg(src, out=dst)  # one elementwise kernel: reads n bytes, writes n bytes
-        torch.cuda.synchronize()
-        del src, dst
-        log(f"[bench] calibration copy of {args.copy_calibration_mb} MiB done")
+    calibration_copy(args.copy_calibration_mb)
 
     def timed(fn, K, W_):
         for _ in range(W_):
