@@ -24,3 +24,26 @@ def test_help_lists_the_workload_options():
     assert r.returncode == 0
     for opt in ("--config", "--r", "--seq", "--tokens", "--loss-side", "--no-loss-side", "--steps", "--warmup"):
         assert opt in r.stdout
+
+
+def test_algorithmic_work_counts():
+    """The work counts behind the roofline figures, recomputed from the layer shapes by hand."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import synth
+    cfg = synth.get_config("tinyllama")
+    Mk, H, I, d, nq, nkv = 4916, 2048, 5632, 64, 32, 4
+    counts = [1229, 1229, 1229, 1229]
+    w = bench.algorithmic_work(cfg, Mk, counts)
+    # weights: qkv [2560 x 2048], o [2048 x 2048], gate/up [11264 x 2048], down [2048 x 5632]
+    proj = 2560 * 2048 + 2048 * 2048 + 11264 * 2048 + 2048 * 5632
+    assert w["gemm_flops"] == 4.0 * Mk * proj                     # dX and dW, 2 M' K N each
+    assert abs(w["gemm_flops"] - 8.66e11) / 8.66e11 < 2e-3       # the layer's 866 GFLOP
+    pairs = 4 * 1229 * 1230 // 2
+    assert w["pairs"] == pairs
+    assert w["attn_flops"] == 10.0 * d * nq * pairs
+    assert w["attn_dt_flops"] == 4.0 * d * nq * pairs
+    # gathered per kept token: dY (2H B) + q, o (2 x 2 nq d B) + k, v (2 x 2 nkv d B) + lse (4 nq B)
+    row = 2 * H + 2 * 2 * nq * d + 2 * 2 * nkv * d + 4 * nq
+    assert row == 13440 and w["gather_bytes"] == 2.0 * Mk * row
+    assert w["gemm_launches"] == 8
