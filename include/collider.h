@@ -83,7 +83,10 @@ collider_status collider_build_index(const uint8_t* keep, int32_t B, int32_t S, 
  * cu_seqlens (clamped), so that every consumer sized for expected_count rows stays in bounds
  * whatever the mask holds.  *mismatch (device int32, written by every call) = 1 if the mask keeps
  * another number of tokens - the gradients computed from such an index are then not the filtered
- * gradient and must be discarded - else 0; *count holds the true count either way.
+ * gradient and must be discarded - else 0; *count holds the true count either way.  On a mismatch
+ * every output of a call that used the index is unspecified but the call stays within its buffers,
+ * and collider_layer_bwd writes each full-layout dx row from one kernel only (the rows past the
+ * true count are left to the zero fill of filtered rows).
  * COLLIDER_ERR_SHAPE if expected_count < 0 or > B*S; COLLIDER_ERR_NULL for a null pointer. */
 collider_status collider_build_index_expect(const uint8_t* keep, int32_t B, int32_t S,
                                             int32_t expected_count, int32_t* idx, int32_t* inv,
@@ -103,7 +106,8 @@ collider_status collider_gather_rows(const void* src, int64_t ld_src, void* dst,
                                      collider_dtype dt, hipStream_t stream);
 
 /* Row scatter back to the full token layout, for t < M:
- *   dst[t, :] = src[inv[t], :] if inv[t] >= 0; else +0.0 (zero_fill_filtered != 0) or untouched.
+ *   dst[t, :] = src[inv[t], :] if inv[t] >= 0; else +0.0 (zero_fill_filtered != 0, any non-zero
+ *   value) or untouched (zero_fill_filtered == 0).
  * The rows of filtered tokens therefore stay exactly zero (abstract: sparsity is maintained). */
 collider_status collider_scatter_rows(const void* src, int64_t ld_src, void* dst, int64_t ld_dst,
                                       const int32_t* inv, int32_t M, int32_t row_elems,
@@ -259,6 +263,19 @@ collider_status collider_layer_bwd(const collider_layer_cfg* cfg, const collider
  * filtered; a filtered token's loss is dropped, so it sends no gradient into the LM head, the
  * layers or the token embedding).
  *
+ * collider_ce_loss: per-token cross-entropy loss of every token from the LM head's logits (bf16
+ * [M, V], row stride ld_logits, full token layout) and labels (int32 [M]):
+ *   loss[t] = logsumexp(logits_t) - logits_t[labels[t]]   (natural log, float32 [M])
+ *   loss[t] = 0 when labels[t] is outside [0, V) (no target, e.g. torch's ignore index -100).
+ * This is the score token selection ranks by (collider_select_keep on `loss` keeps the tokens
+ * with the largest loss).  Max and exp-sum in float32, one pass over each row; logits equal to
+ * -inf (masked vocabulary entries) contribute nothing.  V and ld_logits multiples of 8, logits
+ * 16-byte aligned (COLLIDER_ERR_ALIGN); M in [1, 2^30] (COLLIDER_ERR_SHAPE); NULL pointers
+ * COLLIDER_ERR_NULL. */
+collider_status collider_ce_loss(const void* logits, int64_t ld_logits, const int32_t* labels,
+                                 int32_t M, int32_t V, float* loss, hipStream_t stream);
+
+/*
  * collider_select_keep: token selection on per-token scores (float32 [M], e.g. the per-token loss
  * or any importance score).  keep[t] = 1 for the n_keep tokens with the largest score, else 0;
  * equal scores keep the lower position first; -0.0 ranks as +0.0; NaN ranks below every number.
@@ -311,8 +328,9 @@ collider_status collider_embedding_bwd(const void* dx, int64_t ld_dx, int32_t dx
 
 /* ---------------------------------------------------------------------------------------------
  * Measurement and diagnostics.
- * collider_profile_enable(1): from then on every kernel the library enqueues is bracketed by a
- * pair of HIP events recorded on the same stream.  collider_profile_collect waits for them and,
+ * collider_profile_enable(1): from then on every kernel the library enqueues from the calling host
+ * thread is bracketed by a pair of HIP events recorded on the same stream (the switch is per host
+ * thread; other threads' launches are not timed).  collider_profile_collect waits for them and,
  * for each kernel name, returns the summed duration (ms) and the number of launches; it then
  * clears the record.  names receives up to max_kernels NUL-separated names (name_cap bytes).
  * Returns the number of distinct kernels, or -1 on error.
@@ -324,8 +342,9 @@ collider_status collider_profile_enable(int32_t on);
  *   0  default: a cost model picks the tile shape and whole tiles, K-splits or stream-K;
  *   1  whole tiles and K-splits only;   2  stream-K wherever the direct-to-LDS kernel applies;
  *   3  whole tiles only.
- * Process-wide.  Workspace sizes depend on it: query *_workspace_bytes after setting it.  Returns
- * COLLIDER_ERR_SHAPE for any other value. */
+ * Per host thread: it applies to the calls (and *_workspace_bytes queries) the calling thread
+ * makes afterwards, and never to another thread's.  Workspace sizes depend on it: query
+ * *_workspace_bytes after setting it.  Returns COLLIDER_ERR_SHAPE for any other value. */
 collider_status collider_gemm_set_policy(int32_t policy);
 
 /* The work decomposition the current policy picks for one bf16 GEMM C[M, N] = A B with reduction
@@ -339,6 +358,18 @@ collider_status collider_gemm_describe_plan(int32_t M, int32_t N, int32_t K, int
                                            int32_t concurrent, int32_t* out);
 int32_t collider_profile_collect(char* names, int32_t name_cap, double* total_ms, int32_t* launches,
                                  int32_t max_kernels);
+
+/* Library-held HIP objects.  collider_layer_bwd forks part of its work onto a side stream (default
+ * priority) and joins it back with events; it leases the stream and its events from a per-device
+ * pool for the duration of one call and returns them when its launches are enqueued, so the pool
+ * holds as many sets as calls have ever run at once on a device, however many host threads call
+ * (a set still part of an open graph capture is not leased again until that capture ends).
+ * collider_side_streams_live returns the number of sets alive (leased or idle, all devices).
+ * collider_release_resources destroys every idle set and the pooled timing events (the next call
+ * creates what it needs again); call it before unloading the library.  Sets leased by calls in
+ * progress on other threads are left alone. */
+int32_t collider_side_streams_live(void);
+collider_status collider_release_resources(void);
 const char* collider_status_string(collider_status s);
 
 #ifdef __cplusplus

@@ -37,14 +37,39 @@ __all__ = [
     "silu", "sigmoid", "gelu_tanh", "gelu_tanh_bwd", "swiglu_bwd",
     "rmsnorm_bwd", "layernorm_bwd", "rope_bwd", "attention_bwd",
     "llama_layer_bwd", "phi_layer_bwd", "layer_bwd", "model_bwd", "MODES",
-    "select_topk", "ce_logits_bwd", "lm_head_bwd", "embedding_bwd",
+    "select_topk", "ce_loss", "ce_logits_bwd", "lm_head_bwd", "embedding_bwd", "precision",
 ]
 
 MODES = ("filtered", "full_d", "loss_only")
 
 
+# Floating-point type of the oracle's arithmetic.  float64 everywhere the oracle is pinned and
+# compared; `precision(np.float32)` switches it for a timed float32 run (the CPU baseline of the
+# benchmark), whose results tests check against the float64 ones.
+_DTYPE = np.float64
+
+
+class precision:
+    """Context manager: run the oracle's float arithmetic in `dtype` (float64 or float32)."""
+
+    def __init__(self, dtype):
+        if np.dtype(dtype) not in (np.dtype(np.float64), np.dtype(np.float32)):
+            raise ValueError(dtype)
+        self.dtype, self.prev = np.dtype(dtype).type, None
+
+    def __enter__(self):
+        global _DTYPE
+        self.prev, _DTYPE = _DTYPE, self.dtype
+        return self
+
+    def __exit__(self, *exc):
+        global _DTYPE
+        _DTYPE = self.prev
+        return False
+
+
 def _f64(a):
-    return np.asarray(a, dtype=np.float64)
+    return np.asarray(a, dtype=_DTYPE)
 
 
 def _keep_bool(keep):
@@ -98,7 +123,7 @@ def scatter_rows(src_compact, idx, M):
 def linear_bwd(x, dy, w, keep, bias=False):
     """y = x @ w.T with the loss of filtered tokens dropped: dY~ = diag(keep) dY,
     dX = dY~ @ w, dW = dY~^T @ x (stored [out, in]), db = column sums of dY~."""
-    k = _keep_bool(keep).astype(np.float64)[:, None]
+    k = _keep_bool(keep).astype(_DTYPE)[:, None]
     dyk = _f64(dy) * k
     out = {"dx": dyk @ _f64(w), "dw": dyk.T @ _f64(x)}
     if bias:
@@ -211,13 +236,13 @@ def attention_bwd(q, k, v, o, lse, dout, keep, B, S, nq, nkv, d, mode="filtered"
     keepb = _keep_bool(keep)
     q3, k3, v3 = _f64(q).reshape(M, nq, d), _f64(k).reshape(M, nkv, d), _f64(v).reshape(M, nkv, d)
     o3, do3, lse2 = _f64(o).reshape(M, nq, d), _f64(dout).reshape(M, nq, d), _f64(lse).reshape(M, nq)
-    dq = np.zeros((M, nq, d))
-    dk = np.zeros((M, nkv, d))
-    dv = np.zeros((M, nkv, d))
+    dq = np.zeros((M, nq, d), _DTYPE)
+    dk = np.zeros((M, nkv, d), _DTYPE)
+    dv = np.zeros((M, nkv, d), _DTYPE)
     causal = np.tril(np.ones((S, S), dtype=bool))
     for b in range(B):
         rows = slice(b * S, (b + 1) * S)
-        kb = keepb[rows].astype(np.float64)
+        kb = keepb[rows].astype(_DTYPE)
         for h in range(nq):
             g = h // G
             qq, kk, vv = q3[rows, h, :], k3[rows, g, :], v3[rows, g, :]
@@ -254,7 +279,7 @@ def llama_layer_bwd(cfg, w, saved, dy, keep, mode="filtered"):
     Returns dx and the weight / gain gradients (all float64, full token layout)."""
     B, S, H, nq, nkv, d, I = _split_cfg(cfg)
     M = B * S
-    kf = _keep_bool(keep).astype(np.float64)[:, None]
+    kf = _keep_bool(keep).astype(_DTYPE)[:, None]
     pos = np.arange(M) % S
     dYp = _f64(dy) * kf
     gate, up = _f64(saved["gate"]), _f64(saved["up"])
@@ -293,7 +318,7 @@ def phi_layer_bwd(cfg, w, saved, dy, keep, mode="filtered"):
     saved: x, mean, rstd, q, k (post-rotary), v, o, lse, f (fc1 pre-activation)."""
     B, S, H, nq, nkv, d, I = _split_cfg(cfg)
     M = B * S
-    kf = _keep_bool(keep).astype(np.float64)[:, None]
+    kf = _keep_bool(keep).astype(_DTYPE)[:, None]
     pos = np.arange(M) % S
     dYp = _f64(dy) * kf
     f = _f64(saved["f"])
@@ -362,6 +387,21 @@ def select_topk(score, n_keep):
     return keep
 
 
+def ce_loss(logits, labels):
+    """Per-token cross-entropy loss of every token (Figure 2(b): the training loss whose per-token
+    values decide which tokens backward filtering drops): loss_t = logsumexp(z_t) - z_t[y_t], natural
+    log.  A label outside [0, V) marks a token without a target: loss 0.  -inf logits (masked
+    vocabulary entries) contribute exp(-inf) = 0 to the sum."""
+    z = _f64(logits)
+    y = np.asarray(labels, dtype=np.int64).reshape(-1)
+    V = z.shape[1]
+    valid = (y >= 0) & (y < V)
+    zmax = z.max(axis=1)
+    lse = zmax + np.log(np.exp(z - zmax[:, None]).sum(axis=1))
+    zy = z[np.arange(z.shape[0]), np.where(valid, y, 0)]
+    return np.where(valid, lse - zy, 0.0)
+
+
 def ce_logits_bwd(logits, labels, keep, scale):
     """Gradient of L = scale * sum over kept t of CE(logits_t, labels_t) with respect to the
     logits, CE(z, y) = logsumexp(z) - z_y:  dL/dz_t = scale * (softmax(z_t) - onehot(y_t)) for a
@@ -395,6 +435,6 @@ def embedding_bwd(dx, token_ids, keep, V):
     ids = np.asarray(token_ids, dtype=np.int64).reshape(-1)
     use = _keep_bool(keep) & (ids >= 0) & (ids < int(V))
     g = _f64(dx)[use]
-    dE = np.zeros((int(V), _f64(dx).shape[1]))
+    dE = np.zeros((int(V), _f64(dx).shape[1]), _DTYPE)
     np.add.at(dE, ids[use], g)
     return dE

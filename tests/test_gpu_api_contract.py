@@ -1,0 +1,135 @@
+"""GPU checks of the C ABI's contract beyond numerics: flag values, the side-stream pool shared by
+host threads, graph replay on the caller's stream, and an index built with a wrong announced
+count (outputs unspecified, but every full-layout dx row written by one kernel only)."""
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import token_filtered_backward_amd as tfb
+from tests.helpers import bf16_dev
+from tests.test_gpu_parity import _dev_keep, _keep, _upload_layer
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+
+def test_scatter_any_nonzero_flag_zero_fills():
+    B, S, cols = 2, 300, 64
+    M = B * S
+    keep = _keep(M, "topk", seed=3)
+    ix = tfb.build_index(_dev_keep(keep), B, S)
+    rng = np.random.default_rng(3)
+    src = bf16_dev(rng.integers(0, 2 ** 16, size=(ix.M_kept, cols), dtype=np.uint16))
+    outs = []
+    for flag in (1, 2, 5, -1):
+        dst = torch.full((M, cols), 7.0, dtype=torch.bfloat16, device="cuda")
+        tfb.lib().collider_scatter_rows(tfb._ptr(src), cols, tfb._ptr(dst), cols, tfb._ptr(ix.inv), M, cols,
+                                        flag, tfb.BF16, tfb._stream())
+        outs.append(dst)
+    torch.cuda.synchronize()
+    ref = oracle.scatter_rows(src.cpu().view(torch.int16).numpy(), oracle.build_index(keep, B, S)["idx"], M)
+    for o in outs:
+        assert np.array_equal(o.cpu().view(torch.int16).numpy(), ref)
+
+
+def _layer_setup(name="small_llama"):
+    cfg = synth.get_config(name)
+    inp = synth.make_layer_inputs(cfg, r_pct=40)
+    weights, saved, dy = _upload_layer(inp)
+    ix = tfb.build_index(_dev_keep(inp["keep"]), cfg.B, cfg.S)
+    return cfg, inp, weights, saved, dy, ix, tfb.layer_cfg(cfg)
+
+
+def test_side_stream_pool_shared_by_threads():
+    """Several host threads, each on its own stream, run the layer at once: every result equals the
+    single-thread one bit for bit, and the library's side-stream sets stay bounded by the calls in
+    flight at once (no set per thread); releasing the resources frees the idle sets."""
+    cfg, inp, weights, saved, dy, ix, lcfg = _layer_setup()
+    ref = tfb.layer_bwd(lcfg, weights, saved, dy, ix)
+    torch.cuda.synchronize()
+    n_threads, rounds = 6, 3
+    results, errors = [None] * n_threads, []
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream()
+            lb = tfb.LayerBackward(lcfg, cfg.B, cfg.S, "cuda")
+            g = tfb.make_grads(lcfg, cfg.M, ix.M_kept, "cuda")
+            with torch.cuda.stream(s):
+                for _ in range(rounds):
+                    lb(weights, saved, dy, ix, g, stream=s)
+            s.synchronize()
+            results[i] = g
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    for wave in range(2):  # a second wave of new threads must reuse the pool
+        ts = [threading.Thread(target=work, args=(i,)) for i in range(n_threads)]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+        assert not errors, errors
+        live = tfb.collider_side_streams_live()
+        assert 1 <= live <= n_threads + 1, live
+        for g in results:
+            for k in ref:
+                assert torch.equal(_bits(g[k]), _bits(ref[k])), k
+    torch.cuda.synchronize()
+    tfb.collider_release_resources()
+    assert tfb.collider_side_streams_live() == 0
+    again = tfb.layer_bwd(lcfg, weights, saved, dy, ix)  # the pool is rebuilt on demand
+    torch.cuda.synchronize()
+    for k in ref:
+        assert torch.equal(_bits(again[k]), _bits(ref[k])), k
+
+
+def test_graph_replay_on_callers_stream():
+    """graph=True with an explicit stream captures and replays on that stream, after the work the
+    caller queued there (here: a kernel that rewrites dy just before the replay)."""
+    cfg, inp, weights, saved, dy, ix, lcfg = _layer_setup()
+    dy2 = (dy.float() * 0.5).to(torch.bfloat16)
+    ref = tfb.layer_bwd(lcfg, weights, saved, dy2, ix)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    lb = tfb.LayerBackward(lcfg, cfg.B, cfg.S, "cuda")
+    dyb = dy.clone()
+    g = tfb.make_grads(lcfg, cfg.M, ix.M_kept, "cuda")
+    for rep in range(3):
+        with torch.cuda.stream(s):
+            dyb.copy_(dy)
+        lb(weights, saved, dyb, ix, g, stream=s, graph=True)  # first call captures
+        with torch.cuda.stream(s):
+            dyb.copy_(dy2)
+        lb(weights, saved, dyb, ix, g, stream=s, graph=True)  # must see dy2
+        s.synchronize()
+        for k in ref:
+            assert torch.equal(_bits(g[k]), _bits(ref[k])), (rep, k)
+
+
+@pytest.mark.parametrize("delta", [5, -5])
+def test_wrong_announced_count_keeps_filtered_rows_zero(delta):
+    """An index built with an announced count the mask does not meet: the call stays in bounds,
+    flags the mismatch, and every row of the full-layout dx that the zero fill owns (the filtered
+    tokens, and kept tokens past the announced count) is exactly zero - no other kernel writes it."""
+    cfg, inp, weights, saved, dy, ix0, lcfg = _layer_setup()
+    keep = inp["keep"]
+    n = int(keep.sum())
+    ix = tfb.build_index(_dev_keep(keep), cfg.B, cfg.S, expect=n + delta)
+    g = tfb.make_grads(lcfg, cfg.M, ix.M_kept, "cuda")
+    for rep in range(3):
+        g["dx"].fill_(float("nan"))
+        tfb.LayerBackward(lcfg, cfg.B, cfg.S, "cuda")(weights, saved, dy, ix, g)
+        torch.cuda.synchronize()
+        with pytest.raises(tfb.ColliderError):
+            ix.check()
+        inv = ix.inv.cpu().numpy()
+        dx = g["dx"].float().cpu().numpy()
+        assert np.all(dx[inv < 0] == 0.0), rep

@@ -171,3 +171,96 @@ def test_embedding_bwd_parity(B, S, H, V, r, dx_compact):
     torch.cuda.synchronize()
     assert torch.equal(dE, dE2)
     assert torch.allclose(dE3, dE + 1.0, rtol=0, atol=1e-5)
+
+
+# ------------------------------------------------------------------------------------------------
+# per-token loss -> selection -> index, on the device
+# ------------------------------------------------------------------------------------------------
+
+
+def _logits_case(M, V, seed, minus_inf=False):
+    rng = np.random.default_rng(seed)
+    z = (rng.standard_normal((M, V)) * 2.0).astype(np.float32)
+    labels = rng.integers(0, V, M).astype(np.int32)
+    labels[rng.random(M) < 0.05] = -100
+    if M > 3:
+        labels[3] = V + 3  # past the vocabulary: no target either
+    if minus_inf:
+        # whole 8-wide blocks of -inf (masked vocabulary entries), at the start of a row, in the
+        # middle, at the end, and runs long enough to cover a thread's whole share of a row; every
+        # row keeps at least one finite 8-wide block (a row of -inf only has no defined loss)
+        def blocks(n):
+            return max(0, min(n, V - 8)) // 8 * 8
+        z[0, :blocks(64)] = -np.inf
+        if M > 1:
+            z[1, 8:8 + blocks(min(8 * 300, V - 16))] = -np.inf
+        if M > 2:
+            z[2, V - blocks(16):] = -np.inf
+        z[4::5, :blocks(V // 2)] = -np.inf
+        # labels on finite entries
+        for t in range(min(M, 5)):
+            fin = np.flatnonzero(np.isfinite(z[t]))
+            if labels[t] >= 0 and labels[t] < V and fin.size:
+                labels[t] = fin[len(fin) // 2]
+        rows = np.arange(4, M, 5)
+        labels[rows] = np.where(labels[rows] >= 0, V - 1, labels[rows])
+    return synth.f32_to_bf16_bits(z), labels
+
+
+@pytest.mark.parametrize("M,V", [(400, 1000), (64, 40000), (37, 72000), (130, 8), (1, 32000)])
+@pytest.mark.parametrize("minus_inf", [False, True])
+def test_ce_loss_parity(M, V, minus_inf):
+    bits, labels = _logits_case(M, V, seed=M + V, minus_inf=minus_inf)
+    got = tfb.ce_loss(bf16_dev(bits), torch.from_numpy(labels).cuda()).cpu().numpy().astype(np.float64)
+    ref = oracle.ce_loss(synth.bf16_bits_to_f32(bits), labels)
+    assert np.all(np.isfinite(got))
+    assert rel_err(got, ref) <= 1e-5, rel_err(got, ref)
+    assert np.all(got[(labels < 0) | (labels >= V)] == 0.0)
+
+
+def test_loss_select_index_chain():
+    """logits -> per-token loss -> keep the 60% largest -> index, all on the device (the loss side
+    of Figure 2(b) up to the layers): the mask is the oracle's selection of the device's own loss
+    values bit for bit, and the index the oracle's index of that mask."""
+    B, S, V = 4, 512, 4096
+    M = B * S
+    bits, labels = _logits_case(M, V, seed=5)
+    loss = tfb.ce_loss(bf16_dev(bits), torch.from_numpy(labels).cuda())
+    n_keep = M - synth.n_filtered(M, 40)
+    keep = tfb.select_keep(loss, n_keep)
+    ix = tfb.build_index(keep, B, S)
+    loss_np = loss.cpu().numpy()
+    assert rel_err(loss_np, oracle.ce_loss(synth.bf16_bits_to_f32(bits), labels)) <= 1e-5
+    keep_ref = oracle.select_topk(loss_np, n_keep)
+    assert np.array_equal(keep.cpu().numpy(), keep_ref)
+    ref = oracle.build_index(keep_ref, B, S)
+    assert ix.M_kept == ref["count"] == n_keep
+    assert np.array_equal(ix.idx.cpu().numpy()[:n_keep], ref["idx"])
+    assert np.array_equal(ix.inv.cpu().numpy(), ref["inv"])
+    # tokens without a target have loss 0 and are ranked below every token with a positive loss
+    assert np.all(keep_ref[(labels < 0) | (labels >= V)] == 0)
+
+
+@pytest.mark.parametrize("V", [1000, 40000, 72000])
+def test_lm_head_bwd_minus_inf_blocks(V):
+    """LM-head backward on logit rows holding whole 8-wide blocks of -inf: finite gradients equal to
+    the oracle's (the -inf entries get exactly zero gradient)."""
+    B, S, H = 1, 64, 128
+    M = B * S
+    bits, labels = _logits_case(M, V, seed=V, minus_inf=True)
+    rng = np.random.default_rng(V + 1)
+    h = synth.f32_to_bf16_bits(rng.standard_normal((M, H)).astype(np.float32))
+    w = synth.f32_to_bf16_bits((rng.standard_normal((V, H)) * 0.02).astype(np.float32))
+    keep = np.ones(M, np.uint8)
+    keep[1::3] = 0
+    ix = tfb.build_index(_dev_keep(keep), B, S)
+    dh = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty((V, H), dtype=torch.float32, device="cuda")
+    tfb.collider_lm_head_bwd(bf16_dev(bits), torch.from_numpy(labels).cuda(), bf16_dev(h), bf16_dev(w),
+                             ix.c(), 1.0 / ix.M_kept, dh, dw)
+    torch.cuda.synchronize()
+    f = synth.bf16_bits_to_f32
+    ref = oracle.lm_head_bwd(f(bits), labels, f(h), f(w), keep, 1.0 / ix.M_kept)
+    got_dh, got_dw = to64(dh), to64(dw)
+    assert np.all(np.isfinite(got_dh)) and np.all(np.isfinite(got_dw))
+    assert rel_err(got_dh, ref["dh"]) <= BF16_TOL and rel_err(got_dw, ref["dw_lm"]) <= BF16_TOL

@@ -162,3 +162,72 @@ def test_embedding_bwd_brute_force_and_autograd():
     for v in range(V):
         if v not in used:
             assert np.all(got[v] == 0.0)
+
+
+# ------------------------------------------------------------------------------------------------
+# per-token loss (the score token selection ranks by) and masked vocabulary entries
+# ------------------------------------------------------------------------------------------------
+
+
+def test_ce_loss_matches_torch_and_brute_force():
+    import math
+    rng = np.random.default_rng(7)
+    M, V = 19, 23
+    z = rng.standard_normal((M, V)) * 3
+    y = rng.integers(0, V, M)
+    y[[2, 11]] = -100
+    got = oracle.ce_loss(z, y)
+    ref = torch.nn.functional.cross_entropy(torch.tensor(z), torch.tensor(y), reduction="none",
+                                            ignore_index=-100).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-13)
+    for t in range(M):  # the definition, one token at a time
+        want = 0.0 if not 0 <= y[t] < V else math.log(sum(math.exp(v) for v in z[t])) - z[t, y[t]]
+        assert abs(got[t] - want) <= 1e-12 * max(1.0, abs(want))
+    # labels past the vocabulary also mean "no target"
+    y2 = y.copy()
+    y2[5] = V + 3
+    assert oracle.ce_loss(z, y2)[5] == 0.0
+    # a constant shift of a row's logits leaves its loss unchanged; the loss is never negative
+    np.testing.assert_allclose(oracle.ce_loss(z + 17.0, y), got, rtol=0, atol=1e-11)
+    assert np.all(got >= 0.0)
+
+
+def test_masked_logits_minus_inf():
+    """Whole runs of -inf logits (masked vocabulary entries) drop out of the softmax: the loss and
+    its gradient equal those of the row without them (and torch's, which handles -inf the same)."""
+    rng = np.random.default_rng(8)
+    M, V = 6, 40
+    z = rng.standard_normal((M, V)) * 2
+    z[0, :16] = -np.inf       # two 8-wide blocks at the start of the row
+    z[1, 8:32] = -np.inf      # three blocks in the middle
+    z[2, 32:] = -np.inf       # the tail
+    y = np.array([20, 3, 5, 7, 9, 11])
+    keep = np.ones(M, np.uint8)
+    g = oracle.ce_logits_bwd(z, y, keep, 1.0)
+    zt = torch.tensor(z, requires_grad=True)
+    torch.nn.functional.cross_entropy(zt, torch.tensor(y), reduction="sum").backward()
+    np.testing.assert_allclose(g, zt.grad.numpy(), rtol=1e-12, atol=1e-14)
+    assert np.all(g[np.isinf(z)] == 0.0)
+    loss = oracle.ce_loss(z, y)
+    for t in range(3):
+        fin = np.isfinite(z[t])
+        keep_cols = np.flatnonzero(fin)
+        want = oracle.ce_loss(z[t:t + 1, fin], [int(np.searchsorted(keep_cols, y[t]))])[0]
+        assert abs(loss[t] - want) <= 1e-12
+
+
+def test_oracle_float32_precision_close_to_float64():
+    """The float32 run of the oracle (the benchmark's CPU baseline) agrees with the float64 one
+    on a small layer within 1e-4 of each gradient's largest entry."""
+    cfg = synth.get_config("small_llama")
+    inp = synth.make_layer_inputs(cfg)
+    args = (cfg, synth.floats(inp["weights"]), synth.floats(inp["saved"]),
+            synth.bf16_bits_to_f32(inp["dy"]), inp["keep"])
+    ref = oracle.layer_bwd(*args)
+    with oracle.precision(np.float32):
+        got = oracle.layer_bwd(*args)
+    for k, r in ref.items():
+        assert got[k].dtype == np.float32, k
+        err = np.abs(got[k].astype(np.float64) - r).max() / np.abs(r).max()
+        assert err <= 1e-4, (k, err)
+    assert oracle.layer_bwd(*args)["dx"].dtype == np.float64  # the switch is scoped

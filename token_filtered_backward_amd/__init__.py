@@ -100,6 +100,9 @@ def lib():
         "collider_gemm_describe_plan": (st, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_i32)]),
         "collider_profile_collect": (_i32, [ctypes.c_char_p, _i32, P(ctypes.c_double), P(_i32), _i32]),
         "collider_select_keep": (st, [_c_p, _i32, _i32, _c_p, _c_p]),
+        "collider_ce_loss": (st, [_c_p, _i64, _c_p, _i32, _i32, _c_p, _c_p]),
+        "collider_side_streams_live": (_i32, []),
+        "collider_release_resources": (st, []),
         "collider_lm_head_workspace_bytes": (sz, [_i32, _i32, _i32]),
         "collider_lm_head_bwd": (st, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, P(CollIndex), _i32, _i32,
                                       ctypes.c_float, _c_p, _i32, _c_p, _i32, _c_p, sz, _c_p]),
@@ -225,6 +228,34 @@ def collider_select_keep(score, n_keep, keep, stream=None):
                                       _stream(stream)), "collider_select_keep")
 
 
+def collider_ce_loss(logits, labels, loss, stream=None):
+    """loss[t] = logsumexp(logits[t]) - logits[t, labels[t]] (0 for a label outside [0, V)) for
+    every token: logits bf16 [M, V], labels int32 [M], loss float32 [M]."""
+    M, V = logits.shape
+    if logits.dtype != torch.bfloat16 or labels.dtype != torch.int32 or loss.dtype != torch.float32:
+        raise TypeError("logits must be bfloat16, labels int32 and loss float32")
+    if labels.numel() != M or loss.numel() != M:
+        raise ValueError("labels and loss need one entry per logits row")
+    _check(lib().collider_ce_loss(_ptr(logits), _ld(logits), _ptr(labels), M, V, _ptr(loss),
+                                  _stream(stream)), "collider_ce_loss")
+
+
+def ce_loss(logits: torch.Tensor, labels: torch.Tensor, stream=None) -> torch.Tensor:
+    loss = torch.empty(logits.shape[0], dtype=torch.float32, device=logits.device)
+    collider_ce_loss(logits, labels, loss, stream)
+    return loss
+
+
+def collider_side_streams_live() -> int:
+    """Side-stream sets the library holds (leased or idle, every device)."""
+    return int(lib().collider_side_streams_live())
+
+
+def collider_release_resources():
+    """Destroy the library's idle side streams and pooled timing events."""
+    _check(lib().collider_release_resources(), "collider_release_resources")
+
+
 def select_keep(score: torch.Tensor, n_keep: int, stream=None) -> torch.Tensor:
     if score.dtype != torch.float32 or not score.is_contiguous():
         raise TypeError("score must be a contiguous float32 tensor")
@@ -292,8 +323,8 @@ GEMM_POLICY_AUTO, GEMM_POLICY_SPLITK, GEMM_POLICY_STREAMK, GEMM_POLICY_TILES = 0
 
 
 def collider_gemm_set_policy(policy: int):
-    """Process-wide GEMM work decomposition (0 cost model, 1 tiles + K-splits, 2 stream-K,
-    3 whole tiles only).  Query workspace sizes after changing it."""
+    """GEMM work decomposition for the calling thread (0 cost model, 1 tiles + K-splits,
+    2 stream-K, 3 whole tiles only).  Query workspace sizes after changing it."""
     _check(lib().collider_gemm_set_policy(int(policy)), "collider_gemm_set_policy")
 
 
@@ -473,16 +504,20 @@ class LayerBackward:
         if not graph:
             _check(lib().collider_layer_bwd(*args, _stream(stream)), "collider_layer_bwd")
             return grads
-        if getattr(self, "_graph_key", None) != self._key:
+        run_on = torch.cuda.current_stream() if stream is None else stream
+        key = (self._key, run_on.cuda_stream)
+        if getattr(self, "_graph_key", None) != key:
             # one eager call first: the library's one-time set-up (side stream, kernel attributes)
             # must not happen inside the capture
-            _check(lib().collider_layer_bwd(*args, _stream(stream)), "collider_layer_bwd")
+            _check(lib().collider_layer_bwd(*args, _stream(run_on)), "collider_layer_bwd")
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 _check(lib().collider_layer_bwd(*args, _stream()), "collider_layer_bwd")
-            self._graph, self._graph_key = g, self._key
-        self._graph.replay()
+            self._graph, self._graph_key = g, key
+        # the replay goes on the caller's stream, after the work already queued there
+        with torch.cuda.stream(run_on):
+            self._graph.replay()
         return grads
 
 

@@ -25,7 +25,8 @@ struct ProfRec {
   hipEvent_t a, b;
 };
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+// per host thread: one thread's timing switch does not change how another thread's launches run
+thread_local bool t_prof_on = false;
 std::vector<ProfRec> g_prof_recs;
 std::vector<hipEvent_t> g_prof_pool;
 
@@ -41,14 +42,11 @@ hipEvent_t pool_get() {
 }
 }  // namespace
 
-bool profiling_on() {
-  std::lock_guard<std::mutex> lk(g_prof_mu);
-  return g_prof_on;
-}
+bool profiling_on() { return t_prof_on; }
 
 ProfScope::ProfScope(const char* n, hipStream_t s) : name(n), stream(s), slot(-1) {
+  if (!t_prof_on) return;
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  if (!g_prof_on) return;
   hipEvent_t a = pool_get(), b = pool_get();
   if (!a || !b) return;
   (void)hipEventRecord(a, s);
@@ -157,8 +155,9 @@ collider_status collider_scatter_rows(const void* src, int64_t ld_src, void* dst
   if (M == 0 || row_elems == 0) return COLLIDER_OK;
   if (!src || !dst || !inv) return COLLIDER_ERR_NULL;
   if (((uintptr_t)src | (uintptr_t)dst) & (es - 1)) return COLLIDER_ERR_ALIGN;
+  // any non-zero flag zero-fills the filtered rows (the kernels' mode 2, zeros only, is internal)
   return launch_scatter_bytes(src, ld_src * es, dst, ld_dst * es, inv, M, row_elems * es,
-                              zero_fill_filtered, stream);
+                              zero_fill_filtered ? 1 : 0, stream);
 }
 
 static void linear_problems(collider_dtype dt, int32_t Mk, int32_t K, int32_t N, const void* x,
@@ -367,8 +366,18 @@ collider_status collider_gemm_describe_plan(int32_t M, int32_t N, int32_t K, int
 }
 
 collider_status collider_profile_enable(int32_t on) {
+  t_prof_on = on != 0;
+  return COLLIDER_OK;
+}
+
+int32_t collider_side_streams_live(void) { return side_sets_live(); }
+
+collider_status collider_release_resources(void) {
+  (void)side_release_idle();
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  g_prof_on = on != 0;
+  if (!g_prof_recs.empty()) return COLLIDER_OK;  // events still awaiting collection stay
+  for (hipEvent_t e : g_prof_pool) (void)hipEventDestroy(e);
+  g_prof_pool.clear();
   return COLLIDER_OK;
 }
 
@@ -411,6 +420,14 @@ int32_t collider_profile_collect(char* names, int32_t name_cap, double* total_ms
 // ------------------------------------------------------------------------------------------
 // loss side: token selection, LM-head cross-entropy backward, embedding gradient
 // ------------------------------------------------------------------------------------------
+collider_status collider_ce_loss(const void* logits, int64_t ld_logits, const int32_t* labels,
+                                 int32_t M, int32_t V, float* loss, hipStream_t stream) {
+  if (!logits || !labels || !loss) return COLLIDER_ERR_NULL;
+  if (M < 1 || M > (1 << 30) || V < 1 || ld_logits < V) return COLLIDER_ERR_SHAPE;
+  if (V % 8 || ld_logits % 8 || !aligned16(logits)) return COLLIDER_ERR_ALIGN;
+  return launch_ce_loss((const uint16_t*)logits, ld_logits, labels, M, V, loss, stream);
+}
+
 collider_status collider_select_keep(const float* score, int32_t M, int32_t n_keep, uint8_t* keep,
                                      hipStream_t stream) {
   if (!score || !keep) return COLLIDER_ERR_NULL;
@@ -533,5 +550,6 @@ collider_status collider_embedding_bwd(const void* dx, int64_t ld_dx, int32_t dx
   return launch_embedding_bwd((const uint16_t*)dx, ld_dx, dx_compact, ids, ix->idx, ix->M_kept, V, H,
                               dE, accumulate, w.cnt, w.off, w.cursor, w.sorted, stream);
 }
+
 
 }  // extern "C"

@@ -992,7 +992,8 @@ namespace {
 constexpr int kBK = 64;
 constexpr int kMaxDevices = 64;
 
-std::atomic<int> g_policy{0};
+// per host thread: one thread's choice does not change another thread's launches
+thread_local int t_policy = 0;
 
 // Raises a kernel's dynamic-LDS limit once per device (the call costs microseconds of host time,
 // and every launch would otherwise repeat it).
@@ -1080,7 +1081,7 @@ double epi_bytes(const GemmProblem& p) {
 Plan make_plan(const GemmProblem& p) {
   const int ncu = cu_count();
   const bool lds = lds_eligible(p);
-  int policy = g_policy.load(std::memory_order_relaxed);
+  int policy = t_policy;
   if (policy == 0 && p.concurrent) policy = 3;
   const double bw = 8.0e6, bw_cu = bw / ncu;  // bytes per microsecond
   const double eb = epi_bytes(p);
@@ -1258,7 +1259,7 @@ int tile_group_rows(int tiles_m, int tiles_n, int bm, int bn) {
 
 }  // namespace
 
-void gemm_set_policy(int policy) { g_policy.store(policy, std::memory_order_relaxed); }
+void gemm_set_policy(int policy) { t_policy = policy; }
 
 void gemm_describe_plan(const GemmProblem& p, int* out) {
   const Plan pl = make_plan(p);

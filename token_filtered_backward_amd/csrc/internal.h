@@ -40,8 +40,11 @@ __device__ __forceinline__ float bfhi(uint32_t w) { return __uint_as_float(w & 0
 // ------------------------------------------------------------------------------------------
 // launch bookkeeping: error check + optional per-kernel event timing
 // ------------------------------------------------------------------------------------------
-// true while per-kernel event timing is enabled (collider_profile_enable)
+// true while per-kernel event timing is enabled (collider_profile_enable) on the calling thread
 bool profiling_on();
+// layer.hip: side-stream sets alive (leased or idle), and destruction of the idle ones
+int side_sets_live();
+int side_release_idle();
 
 struct ProfScope {
   const char* name;
@@ -94,6 +97,8 @@ collider_status launch_build_index(const uint8_t* keep, int B, int S, int32_t* i
 // loss.hip
 collider_status launch_select_topk(const float* score, int M, int n_keep, uint8_t* keep,
                                    hipStream_t s);
+collider_status launch_ce_loss(const uint16_t* logits, int64_t ld, const int32_t* labels, int M, int V,
+                               float* loss, hipStream_t s);
 collider_status launch_ce_grad(const uint16_t* logits, int64_t ld, const int32_t* labels,
                                const int32_t* rowmap, int rows, int V, float scale, uint16_t* dl,
                                int64_t ldd, hipStream_t s);
@@ -129,11 +134,11 @@ collider_status launch_norm_recompute(const uint16_t* x, const float* mean, cons
 collider_status launch_act_recompute(const uint16_t* g, const uint16_t* up, const int32_t* rowmap,
                                      int rows, int I, uint16_t* a, hipStream_t s);
 // dx = dres + norm_bwd(dxn; x[rowmap], stats): row c of dx, or row rowmap[c] when dx_full != 0
-// (the full token layout)
+// (the full token layout); row_limit (device int, may be null): rows c >= *row_limit are skipped
 collider_status launch_norm_bwd(const uint16_t* dxn, const uint16_t* dres, const uint16_t* x,
                                 const float* mean, const float* rstd, const float* gamma,
                                 const int32_t* rowmap, int rows, int H, uint16_t* dx, int dx_full,
-                                hipStream_t s);
+                                hipStream_t s, const int32_t* row_limit = nullptr);
 // partial column sums for dgamma = sum dxn * xhat (and dbeta = sum dxn when part_dbeta != null):
 // n_part rows of H floats each, summed by launch_colsum_parts
 collider_status launch_norm_grad_parts(const uint16_t* dxn, const uint16_t* x, const float* mean,

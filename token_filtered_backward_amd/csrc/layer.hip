@@ -19,6 +19,8 @@
 // through the index; the SwiGLU / GELU backward is fused into the epilogue of the GEMM producing dA.
 #include <algorithm>
 #include <cstdlib>
+#include <mutex>
+#include <vector>
 
 #include "internal.h"
 
@@ -26,34 +28,111 @@ namespace collider {
 
 namespace {
 
-// One side stream (default priority) and its fork / join events per host thread and device,
-// created on first use and kept for the life of the process.  Everything runs on the caller's
-// stream with COLLIDER_SINGLE_STREAM=1 set, and while per-kernel timing is on (so that each
-// kernel's events bracket it alone).
+// Side streams (default priority) with their fork / join events, leased per call from a pool per
+// device: a call takes an idle set (or creates one when every set is leased, so the pool never
+// outgrows the number of calls in flight at once on that device) and returns it when its launches
+// are enqueued.  A set whose stream still belongs to an open graph capture (it joined the capture
+// through the fork event) is not leased again until that capture has ended.  The pool holds no
+// per-thread state; collider_release_resources destroys the idle sets.  Everything runs on the
+// caller's stream with COLLIDER_SINGLE_STREAM=1 set, and while per-kernel timing is on (so that
+// each kernel's events bracket it alone).
 struct Side {
   hipStream_t s = nullptr;
   hipEvent_t ev[8] = {};
+  int dev = -1;
 };
 
-collider_status side_stream(Side** out) {
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+std::vector<Side*> g_side_idle[kMaxDevices];
+int g_side_live = 0;
+
+void side_destroy(Side* sd) {
+  for (hipEvent_t e : sd->ev)
+    if (e) (void)hipEventDestroy(e);
+  if (sd->s) (void)hipStreamDestroy(sd->s);
+  delete sd;
+}
+
+bool side_capturing(const Side* sd) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(sd->s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone;
+}
+
+collider_status side_acquire(Side** out) {
   static const bool single = getenv("COLLIDER_SINGLE_STREAM") != nullptr;
   *out = nullptr;
   if (single || profiling_on()) return COLLIDER_OK;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return COLLIDER_ERR_HIP;
-  thread_local Side sides[64];
-  Side& sd = sides[dev];
-  if (!sd.s) {
-    for (hipEvent_t& e : sd.ev)
-      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return COLLIDER_ERR_HIP;
-    if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess) {
-      sd.s = nullptr;
-      return COLLIDER_ERR_HIP;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return COLLIDER_ERR_HIP;
+  {
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    std::vector<Side*>& idle = g_side_idle[dev];
+    for (size_t i = idle.size(); i-- > 0;) {
+      if (side_capturing(idle[i])) continue;
+      *out = idle[i];
+      idle.erase(idle.begin() + (std::ptrdiff_t)i);
+      return COLLIDER_OK;
     }
   }
-  *out = &sd;
+  Side* sd = new Side;
+  sd->dev = dev;
+  bool ok = hipStreamCreateWithFlags(&sd->s, hipStreamNonBlocking) == hipSuccess;
+  for (hipEvent_t& e : sd->ev)
+    ok = ok && hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
+    side_destroy(sd);
+    return COLLIDER_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  ++g_side_live;
+  *out = sd;
   return COLLIDER_OK;
 }
+
+// Returns a leased set to its device's pool on scope exit (the events may be recorded again at
+// once: every wait on them is already enqueued, and a wait takes the event's state at enqueue).
+struct SideLease {
+  Side* sd = nullptr;
+  ~SideLease() {
+    if (!sd) return;
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    g_side_idle[sd->dev].push_back(sd);
+  }
+};
+
+}  // namespace
+
+int side_sets_live() {
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  return g_side_live;
+}
+
+int side_release_idle() {
+  std::vector<Side*> doomed;
+  {
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    for (std::vector<Side*>& idle : g_side_idle) {
+      for (Side* sd : idle)
+        if (!side_capturing(sd)) doomed.push_back(sd);
+      std::vector<Side*> keep;
+      for (Side* sd : idle)
+        if (std::find(doomed.begin(), doomed.end(), sd) == doomed.end()) keep.push_back(sd);
+      idle.swap(keep);
+    }
+    g_side_live -= (int)doomed.size();
+  }
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  for (Side* sd : doomed) {
+    (void)hipSetDevice(sd->dev);
+    side_destroy(sd);
+  }
+  (void)hipSetDevice(cur);
+  return (int)doomed.size();
+}
+
+namespace {
 
 struct LayerBufs {
 
@@ -244,8 +323,9 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
   // caller's stream with events: the memory-bound work there overlaps the dX chain's GEMMs, and
   // the critical path dA -> dX -> norm bwd -> dO -> attention -> dX -> norm bwd -> scatter stays
   // on `s`.
-  Side* side = nullptr;
-  CHECK(side_stream(&side));
+  SideLease lease;
+  CHECK(side_acquire(&lease.sd));
+  Side* side = lease.sd;
   hipStream_t s1 = side ? side->s : s;
   auto handoff = [&](int e, hipStream_t from, hipStream_t to) -> collider_status {
     if (!side) return COLLIDER_OK;
@@ -316,7 +396,7 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
                                  b.part_g, nullptr, parts, s1));
     CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dgamma1, c.accumulate, s1));
     CHECK(launch_norm_bwd(b.dxn1, b.dh, (const uint16_t*)sv->x, nullptr, sv->rstd1, w->gamma1, idx, Mk,
-                          H, b.dx_c, dx_full, s));
+                          H, b.dx_c, dx_full, s, dx_full ? ix.count : nullptr));
   } else {
     CHECK(launch_act_recompute((const uint16_t*)sv->f, nullptr, idx, Mk, I, b.act_c, s1));
     CHECK(launch_norm_recompute((const uint16_t*)sv->x, sv->mean, sv->rstd1, w->ln_gamma, w->ln_beta,
@@ -337,7 +417,7 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dln_gamma, c.accumulate, s1));
     CHECK(launch_colsum_parts(b.part_b, Mk > 0 ? parts : 0, H, gr->dln_beta, c.accumulate, s1));
     CHECK(launch_norm_bwd(b.dxn, b.dy_c, (const uint16_t*)sv->x, sv->mean, sv->rstd1, w->ln_gamma,
-                          idx, Mk, H, b.dx_c, dx_full, s));
+                          idx, Mk, H, b.dx_c, dx_full, s, dx_full ? ix.count : nullptr));
   }
   CHECK(handoff(4, s1, s));  // join: every weight gradient is complete on the caller's stream
 #undef CHECK

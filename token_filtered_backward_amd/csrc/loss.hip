@@ -1,6 +1,7 @@
 // Loss side of the filtered backward (Collider paper, Figure 2(b): the per-token training loss
 // decides which tokens are filtered, and a filtered token's loss is dropped, so it sends no
 // gradient into the LM head, the layers or the token embedding):
+//   ce_loss_kernel          per-token cross-entropy loss of every token (the score to rank by)
 //   select_topk_kernel      per-token scores -> keep mask (the n_keep largest scores kept)
 //   ce_grad_kernel          dlogits' = scale * (softmax(logits') - onehot(label')) over kept rows
 //   embed_*_kernel          dE[v] = sum of dx over the kept tokens with id v, in token order
@@ -145,7 +146,11 @@ constexpr float kLog2eF = 1.4426950408889634f;
 struct MaxSum {
   float m, s;  // running max of z * log2(e) and sum of 2^(z log2(e) - m)
 };
+// An empty state (no finite logit seen yet) has m = -inf and s = 0; merging it must not form
+// exp2(-inf - (-inf)) = exp2(NaN), so either side being empty returns the other.
 __device__ __forceinline__ MaxSum ms_merge(MaxSum a, MaxSum b) {
+  if (a.m == -INFINITY) return b;
+  if (b.m == -INFINITY) return a;
   const float m = fmaxf(a.m, b.m);
   return MaxSum{m, a.s * __builtin_amdgcn_exp2f(a.m - m) + b.s * __builtin_amdgcn_exp2f(b.m - m)};
 }
@@ -161,7 +166,8 @@ __device__ __forceinline__ MaxSum ms_add8(MaxSum a, uint4 v) {
 #pragma unroll
   for (int i = 1; i < 8; ++i) m8 = fmaxf(m8, z[i]);
   const float m = fmaxf(a.m, m8);
-  float s = a.s * __builtin_amdgcn_exp2f(a.m - m);
+  if (m == -INFINITY) return a;  // every logit so far is -inf (masked entries): nothing to add
+  float s = a.m == -INFINITY ? 0.f : a.s * __builtin_amdgcn_exp2f(a.m - m);
 #pragma unroll
   for (int i = 0; i < 8; ++i) s += __builtin_amdgcn_exp2f(z[i] - m);
   return MaxSum{m, s};
@@ -200,13 +206,9 @@ __global__ __launch_bounds__(256) void ce_grad_kernel(const uint16_t* __restrict
   } else {
     for (int i = tid; i < nvec; i += 256) ms = ms_add8(ms, src[i]);
   }
-  // the first merge may combine two empty states (m = -inf): keep s = 0 there
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    MaxSum o{__shfl_xor(ms.m, off, 64), __shfl_xor(ms.s, off, 64)};
-    if (o.m == -INFINITY) continue;
-    ms = ms.m == -INFINITY ? o : ms_merge(ms, o);
-  }
+  for (int off = 32; off > 0; off >>= 1)
+    ms = ms_merge(ms, MaxSum{__shfl_xor(ms.m, off, 64), __shfl_xor(ms.s, off, 64)});
   if (lane == 0) s_ms[wave] = ms;
   __syncthreads();
   ms = s_ms[0];
@@ -253,6 +255,54 @@ collider_status launch_ce_grad(const uint16_t* logits, int64_t ld, const int32_t
   else
     COLLIDER_LAUNCH("ce_grad", s, hipLaunchKernelGGL(ce_grad_kernel<0>, dim3(rows), dim3(256), 0, s,
                                                      logits, ld, labels, rowmap, V, scale, dl, ldd));
+  return last_hip_status();
+}
+
+// ------------------------------------------------------------------------------------------
+// per-token cross-entropy loss over every token: loss_t = logsumexp(z_t) - z_t[y_t] (0 without a
+// target).  It is the score backward token filtering ranks tokens by (Figure 2(b)).  One
+// workgroup per row; the row is read once, four 16-byte vectors in flight per thread.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void ce_loss_kernel(const uint16_t* __restrict__ logits, int64_t ld,
+                                                      const int32_t* __restrict__ labels, int V,
+                                                      float* __restrict__ loss) {
+  __shared__ MaxSum s_ms[4];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int y = labels[t];
+  if (y < 0 || y >= V) {
+    if (tid == 0) loss[t] = 0.f;
+    return;
+  }
+  const int nvec = V >> 3;
+  const uint4* src = (const uint4*)(logits + t * ld);
+  MaxSum ms{-INFINITY, 0.f};
+  int i = tid;
+  for (; i + 3 * 256 < nvec; i += 4 * 256) {
+    const uint4 a = src[i], b = src[i + 256], c = src[i + 512], d = src[i + 768];
+    ms = ms_add8(ms_add8(ms_add8(ms_add8(ms, a), b), c), d);
+  }
+  for (; i < nvec; i += 256) ms = ms_add8(ms, src[i]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1)
+    ms = ms_merge(ms, MaxSum{__shfl_xor(ms.m, off, 64), __shfl_xor(ms.s, off, 64)});
+  if (lane == 0) s_ms[wave] = ms;
+  __syncthreads();
+  if (tid == 0) {
+    ms = s_ms[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) ms = ms_merge(ms, s_ms[w]);
+    // log-sum-exp in natural-log units: (m + log2 s) ln 2, m and s in base-2 units
+    const float lse = (ms.m + __builtin_amdgcn_logf(ms.s)) * 0.6931471805599453f;
+    loss[t] = lse - bf2f(logits[t * ld + y]);
+  }
+}
+
+collider_status launch_ce_loss(const uint16_t* logits, int64_t ld, const int32_t* labels, int M, int V,
+                               float* loss, hipStream_t s) {
+  if (M <= 0) return COLLIDER_OK;
+  COLLIDER_LAUNCH("ce_loss", s, hipLaunchKernelGGL(ce_loss_kernel, dim3(M), dim3(256), 0, s, logits,
+                                                   ld, labels, V, loss));
   return last_hip_status();
 }
 

@@ -362,10 +362,13 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(
     const uint16_t* __restrict__ dxn, const uint16_t* __restrict__ dres,
     const uint16_t* __restrict__ x, const float* __restrict__ mean, const float* __restrict__ rstd,
     const float* __restrict__ gamma, const int32_t* __restrict__ rowmap, int rows, int H,
-    uint16_t* __restrict__ dx, int dx_full) {
+    uint16_t* __restrict__ dx, int dx_full, const int32_t* __restrict__ row_limit) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = blockIdx.x * 4 + wave;
   if (c >= rows) return;
+  // rows at or past the device's kept count map to filtered positions (an index built with a
+  // wrong announced count): their full-layout rows belong to the zero fill alone
+  if (row_limit && c >= *row_limit) return;
   const int nvec = H >> 3;
   const int64_t r = rowmap ? rowmap[c] : c;
   const float mu = mean ? mean[r] : 0.f;
@@ -489,7 +492,7 @@ int norm_grad_parts(int rows, int H) {
 collider_status launch_norm_bwd(const uint16_t* dxn, const uint16_t* dres, const uint16_t* x,
                                 const float* mean, const float* rstd, const float* gamma,
                                 const int32_t* rowmap, int rows, int H, uint16_t* dx, int dx_full,
-                                hipStream_t s) {
+                                hipStream_t s, const int32_t* row_limit) {
   if (rows <= 0) return COLLIDER_OK;
   const int nv = (H / 8 + 63) / 64;
   dim3 grid((rows + 3) / 4), block(256);
@@ -497,7 +500,8 @@ collider_status launch_norm_bwd(const uint16_t* dxn, const uint16_t* dres, const
   case N:                                                                                       \
     COLLIDER_LAUNCH("norm_bwd", s,                                                              \
                     hipLaunchKernelGGL((norm_bwd_kernel<N>), grid, block, 0, s, dxn, dres, x,   \
-                                       mean, rstd, gamma, rowmap, rows, H, dx, dx_full));       \
+                                       mean, rstd, gamma, rowmap, rows, H, dx, dx_full,         \
+                                       row_limit));                                             \
     break;
   switch (nv) {
     NB_CASE(1) NB_CASE(2) NB_CASE(3) NB_CASE(4) NB_CASE(5) NB_CASE(6) NB_CASE(7) NB_CASE(8)
