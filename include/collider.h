@@ -326,6 +326,21 @@ collider_status collider_embedding_bwd(const void* dx, int64_t ld_dx, int32_t dx
                                        int32_t V, float* dE, int32_t accumulate, void* ws,
                                        size_t ws_bytes, hipStream_t stream);
 
+/* collider_embedding_bwd_noalloc: collider_embedding_bwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).  The
+ * same arguments without the workspace, the same kernels and the same result bit for bit; the
+ * counting sort's scratch (per-id counts, offsets and cursors, the sorted token list) lives in a
+ * library-owned device array of 7 MiB per GPU, held until the process ends.  Limits: V <=
+ * 262144 and M_kept <= 1048576, else COLLIDER_ERR_WORKSPACE (nothing enqueued).  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).  Every call on a GPU
+ * shares that GPU's scratch array and clears what it needs itself: calls that overlap on one GPU
+ * (on different streams, or from several host threads without ordering) race and give undefined
+ * results; calls ordered on one stream are safe.  Other errors as collider_embedding_bwd. */
+collider_status collider_embedding_bwd_noalloc(const void* dx, int64_t ld_dx, int32_t dx_compact,
+                                               const int32_t* ids, const collider_index* ix,
+                                               int32_t H, int32_t V, float* dE, int32_t accumulate,
+                                               hipStream_t stream);
+
 /* ---------------------------------------------------------------------------------------------
  * Measurement and diagnostics.
  * collider_profile_enable(1): from then on every kernel the library enqueues from the calling host

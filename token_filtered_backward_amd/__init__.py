@@ -107,6 +107,8 @@ def lib():
         "collider_lm_head_bwd": (st, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, P(CollIndex), _i32, _i32,
                                       ctypes.c_float, _c_p, _i32, _c_p, _i32, _c_p, sz, _c_p]),
         "collider_embedding_workspace_bytes": (sz, [_i32, _i32]),
+        "collider_embedding_bwd_noalloc": (st, [_c_p, _i64, _i32, _c_p, P(CollIndex), _i32, _i32, _c_p,
+                                                _i32, _c_p]),
         "collider_embedding_bwd": (st, [_c_p, _i64, _i32, _c_p, P(CollIndex), _i32, _i32, _c_p, _i32,
                                         _c_p, sz, _c_p]),
     }
@@ -305,6 +307,19 @@ def collider_embedding_bwd(dx, ids, ix: CollIndex, dE, dx_compact=False, accumul
                                         int(bool(dx_compact)), _ptr(ids), ctypes.byref(ix), H, V,
                                         _ptr(dE), int(bool(accumulate)), _ptr(ws), ws.numel(),
                                         _stream(stream)), "collider_embedding_bwd")
+
+
+def collider_embedding_bwd_noalloc(dx, ids, ix: CollIndex, dE, dx_compact=False, accumulate=False,
+                                   stream=None):
+    """collider_embedding_bwd without a workspace (the library's fixed device scratch; V <= 262144,
+    M_kept <= 1048576; calls that overlap on one GPU race)."""
+    V, H = dE.shape
+    if dE.dtype != torch.float32 or ids.dtype != torch.int32 or (dx is not None and dx.dtype != torch.bfloat16):
+        raise TypeError("dx must be bfloat16, ids int32 and dE float32")
+    _check(lib().collider_embedding_bwd_noalloc(_ptr(dx), _ld(dx) if dx is not None else H,
+                                                int(bool(dx_compact)), _ptr(ids), ctypes.byref(ix), H, V,
+                                                _ptr(dE), int(bool(accumulate)), _stream(stream)),
+           "collider_embedding_bwd_noalloc")
 
 
 def collider_layer_workspace_bytes(cfg: LayerCfg, B, S, M_kept) -> int:

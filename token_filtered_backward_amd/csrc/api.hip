@@ -551,5 +551,20 @@ collider_status collider_embedding_bwd(const void* dx, int64_t ld_dx, int32_t dx
                               dE, accumulate, w.cnt, w.off, w.cursor, w.sorted, stream);
 }
 
+collider_status collider_embedding_bwd_noalloc(const void* dx, int64_t ld_dx, int32_t dx_compact,
+                                               const int32_t* ids, const collider_index* ix,
+                                               int32_t H, int32_t V, float* dE, int32_t accumulate,
+                                               hipStream_t stream) {
+  collider_status st = check_index(ix);
+  if (st != COLLIDER_OK) return st;
+  if (!ids || !dE || (ix->M_kept > 0 && !dx)) return COLLIDER_ERR_NULL;
+  if (H < 1 || V < 1 || ld_dx < H) return COLLIDER_ERR_SHAPE;
+  if (H % 8 || ld_dx % 8 || (dx && !aligned16(dx)) || !aligned16(dE)) return COLLIDER_ERR_ALIGN;
+  if (V > kEmbScratchMaxV || ix->M_kept > kEmbScratchMaxRows) return COLLIDER_ERR_WORKSPACE;
+  int32_t *cnt, *off, *cursor, *sorted;
+  if ((st = embedding_scratch(&cnt, &off, &cursor, &sorted)) != COLLIDER_OK) return st;
+  return launch_embedding_bwd((const uint16_t*)dx, ld_dx, dx_compact, ids, ix->idx, ix->M_kept, V, H,
+                              dE, accumulate, cnt, off, cursor, sorted, stream);
+}
 
 }  // extern "C"

@@ -102,6 +102,12 @@ collider_status launch_ce_loss(const uint16_t* logits, int64_t ld, const int32_t
 collider_status launch_ce_grad(const uint16_t* logits, int64_t ld, const int32_t* labels,
                                const int32_t* rowmap, int rows, int V, float scale, uint16_t* dl,
                                int64_t ldd, hipStream_t s);
+// The allocation-free embedding gradient's scratch (a file-scope device array in loss.hip):
+// device addresses, on the current device, of cnt / cursor [kEmbScratchMaxV], off
+// [kEmbScratchMaxV + 1] and sorted [kEmbScratchMaxRows]
+constexpr int kEmbScratchMaxV = 1 << 18;
+constexpr int kEmbScratchMaxRows = 1 << 20;
+collider_status embedding_scratch(int32_t** cnt, int32_t** off, int32_t** cursor, int32_t** sorted);
 // cnt, cursor: [V]; off: [V + 1]; sorted: [rows]
 collider_status launch_embedding_bwd(const uint16_t* dx, int64_t ld, int dx_compact,
                                      const int32_t* ids, const int32_t* idx, int rows, int V, int H,

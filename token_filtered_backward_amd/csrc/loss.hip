@@ -7,6 +7,7 @@
 //   embed_*_kernel          dE[v] = sum of dx over the kept tokens with id v, in token order
 // The LM head's two reduced GEMMs reuse the bf16 GEMM (gemm.hip).
 #include <atomic>
+#include <mutex>
 
 #include "internal.h"
 
@@ -476,6 +477,38 @@ static bool place_lds_limit_set() {
     return false;
   done.fetch_or(bit, std::memory_order_acq_rel);
   return true;
+}
+
+// ------------------------------------------------------------------------------------------
+// Scratch of the allocation-free embedding gradient: the counting sort's counts, offsets,
+// cursors and sorted token list for up to kEmbScratchMaxV vocabulary rows and kEmbScratchMaxRows
+// kept tokens (7 MiB per GPU, held until the process ends).  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol): the device address of each
+// GPU's copy is looked up once per device with hipGetSymbolAddress and used from then on.
+// ------------------------------------------------------------------------------------------
+constexpr int kEmbScratchInts = 3 * kEmbScratchMaxV + 1 + kEmbScratchMaxRows;
+static __device__ __align__(256) int32_t scratch[kEmbScratchInts];
+
+collider_status embedding_scratch(int32_t** cnt, int32_t** off, int32_t** cursor, int32_t** sorted) {
+  static std::mutex mu;
+  static int32_t* ptr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return COLLIDER_ERR_HIP;
+  int32_t* base = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    if (!ptr[dev]) {
+      void* p = nullptr;
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return COLLIDER_ERR_HIP;
+      ptr[dev] = (int32_t*)p;
+    }
+    base = ptr[dev];
+  }
+  *cnt = base;
+  *off = base + kEmbScratchMaxV;
+  *cursor = base + 2 * kEmbScratchMaxV + 1;
+  *sorted = base + 3 * kEmbScratchMaxV + 1;
+  return COLLIDER_OK;
 }
 
 collider_status launch_embedding_bwd(const uint16_t* dx, int64_t ld, int dx_compact,
