@@ -337,10 +337,11 @@ def sparse_sweep_bench(args, cfg):
     filter-ratio sweep, computed three ways:
       dense   torch.matmul (hipBLASLt) on all M rows, filtered rows of dG zeroed - what filtering
               only the loss costs;
-      sparse  torch.sparse.mm with dG in CSR (rows of filtered tokens empty) - PyTorch's sparse
-              GEMM, the comparison of the Figure 4 caption;
+      sparse  torch.sparse.mm with dG in CSR (rows of filtered tokens empty), float32 - PyTorch's
+              sparse GEMM, the comparison of the Figure 4 caption;
       reduced this library: gather of the kept rows of dG and X, then collider_linear_bwd_reduced
-              (dense GEMMs over the M' kept rows).
+              (dense GEMMs over the M' kept rows); beside it torch.matmul on the same compacted
+              rows (the vendor GEMM on the reduced shapes).
     Each is dX = dG w plus dW = dG^T X.  Context only (no target)."""
     import numpy as np
     import torch
@@ -371,17 +372,14 @@ def sparse_sweep_bench(args, cfg):
             ts.append(e0.elapsed_time(e1))
         return float(np.median(ts))
 
-    def sparse_ms(a, b, dt):
-        """ms of torch.sparse.mm(a as CSR, b) in dtype dt, or None when unsupported."""
-        try:
-            a_sp = a.to(dt).to_sparse_csr()
-            b_ = b.to(dt)
-            torch.sparse.mm(a_sp, b_)
-            torch.cuda.synchronize()
-            return t_ms(lambda: torch.sparse.mm(a_sp, b_))
-        except (RuntimeError, NotImplementedError) as e:
-            log(f"[bench] torch.sparse.mm in {dt}: {type(e).__name__}: {str(e).splitlines()[0][:120]}")
-            return None
+    # The sparse leg runs in float32 only: the ROCm sparse library's SpMM documents no type
+    # combination with bf16 inputs and a bf16 result (bf16 inputs need a float32 result), which is
+    # what torch.sparse.mm on two bf16 operands would ask for.
+    def sparse_ms(a, b):
+        """ms of torch.sparse.mm(a as float32 CSR, b as float32)."""
+        a_sp = a.float().to_sparse_csr()
+        b_ = b.float()
+        return t_ms(lambda: torch.sparse.mm(a_sp, b_))
 
     rows = []
     for r in (0, 10, 20, 30, 40, 50, 60, 70, 80, 90, 95, 99):
@@ -395,9 +393,7 @@ def sparse_sweep_bench(args, cfg):
         row["dense_bf16_ms"] = t_ms(lambda: (torch.matmul(dGm, w), torch.matmul(dGmT, X)))
         dGf, dGfT, Xf, wf = dGm.float(), dGmT.float(), X.float(), w.float()
         row["dense_f32_ms"] = t_ms(lambda: (torch.matmul(dGf, wf), torch.matmul(dGfT, Xf)))
-        for name, dt in (("sparse_bf16_ms", torch.bfloat16), ("sparse_f32_ms", torch.float32)):
-            a_ms, b_ms = sparse_ms(dGm, w, dt), sparse_ms(dGmT, X, dt)
-            row[name] = None if a_ms is None or b_ms is None else a_ms + b_ms
+        row["sparse_f32_ms"] = sparse_ms(dGm, w) + sparse_ms(dGmT, X)
         dGk = torch.empty((max(mk, 1), N), dtype=torch.bfloat16, device=dev)
         Xk = torch.empty((max(mk, 1), H), dtype=torch.bfloat16, device=dev)
         dx = torch.empty((max(mk, 1), H), dtype=torch.bfloat16, device=dev)
@@ -413,14 +409,22 @@ def sparse_sweep_bench(args, cfg):
 
         row["reduced_ms"] = t_ms(reduced)
         row["reduced_gemms_only_ms"] = t_ms(lambda: reduced(False))
+        # the vendor GEMM (torch.matmul, hipBLASLt) on the same compacted rows: dX = dG' w and
+        # dW = dG'^T X' with dG'^T made contiguous beforehand (untimed)
+        if mk:
+            dGkT = dGk[:mk].t().contiguous()
+            row["reduced_rows_hipblaslt_ms"] = t_ms(lambda: (torch.matmul(dGk[:mk], w), torch.matmul(dGkT, Xk[:mk])))
+            del dGkT
+        else:
+            row["reduced_rows_hipblaslt_ms"] = 0.0
         rows.append(row)
         log(f"[bench] sparse sweep r={r}%: " + ", ".join(
             f"{k} {v:.3f}" if isinstance(v, float) else f"{k} {v}" for k, v in row.items() if k != "r_pct"))
         del dGm, dGmT, dGf, dGfT, Xf, wf
 
-    def crossover(key):
+    def crossover(key, dense_key):
         for row in rows:
-            if row[key] is not None and row[key] < row["dense_bf16_ms" if "bf16" in key else "dense_f32_ms"]:
+            if row[key] < row[dense_key]:
                 return row["r_pct"]
         return None
 
@@ -430,7 +434,9 @@ def sparse_sweep_bench(args, cfg):
            "config": {"workload": f"{cfg.name}-shaped gate/up projection backward, dG [{M}, {N}], X [{M}, {H}], "
                                   f"w [{N}, {H}]", "M": M, "N": N, "K": H},
            "rows": rows,
-           "sparse_beats_dense_from_r_pct": {"bf16": crossover("sparse_bf16_ms"), "f32": crossover("sparse_f32_ms")},
+           "sparse_f32_beats_dense_from_r_pct": {"dense_f32": crossover("sparse_f32_ms", "dense_f32_ms"),
+                                                 "dense_bf16": crossover("sparse_f32_ms", "dense_bf16_ms")},
+           "reduced_beats_dense_bf16_from_r_pct": crossover("reduced_ms", "dense_bf16_ms"),
            "torch": torch.__version__}
     print(json.dumps(out), flush=True)
     return out

@@ -154,7 +154,9 @@ typedef struct {
   const void* q; int64_t ld_q;     /* [M_kept, nq*d]  */
   const void* k; int64_t ld_k;     /* [M_kept, nkv*d] */
   const void* v; int64_t ld_v;     /* [M_kept, nkv*d] */
-  const void* o; int64_t ld_o;     /* [M_kept, nq*d]; read only with COLLIDER_ATTN_D_FULL */
+  const void* o; int64_t ld_o;     /* [M_kept, nq*d] forward output: required with
+                                      COLLIDER_ATTN_D_FULL; optional with FILTERED, where it only
+                                      improves the rounding of dq (NULL allowed) */
   const float* lse; int64_t ld_lse;/* [M_kept, nq] float32 */
   const void* dout; int64_t ld_do; /* [M_kept, nq*d] gradient of o */
   void* dq; int64_t ld_dq;         /* [M_kept, nq*d] out */

@@ -246,14 +246,14 @@ collider_status collider_attn_bwd_filtered(const collider_attn_cfg* cfg, const c
   if (cfg->dmode == COLLIDER_ATTN_D_FULL && !io->o) return COLLIDER_ERR_NULL;
   if (io->ld_q < nqd || io->ld_k < nkvd || io->ld_v < nkvd || io->ld_do < nqd || io->ld_dq < nqd ||
       io->ld_dk < nkvd || io->ld_dv < nkvd || io->ld_lse < cfg->n_q_heads ||
-      (cfg->dmode == COLLIDER_ATTN_D_FULL && io->ld_o < nqd))
+      (io->o && io->ld_o < nqd))
     return COLLIDER_ERR_SHAPE;
   const void* p16[] = {io->q, io->k, io->v, io->dout, io->dq, io->dk, io->dv};
   for (const void* p : p16)
     if (bad_ptr16(p)) return COLLIDER_ERR_ALIGN;
   if ((io->ld_q | io->ld_k | io->ld_v | io->ld_do | io->ld_dq | io->ld_dk | io->ld_dv) % 8)
     return COLLIDER_ERR_ALIGN;
-  if (cfg->dmode == COLLIDER_ATTN_D_FULL && (bad_ptr16(io->o) || io->ld_o % 8)) return COLLIDER_ERR_ALIGN;
+  if (io->o && (bad_ptr16(io->o) || io->ld_o % 8)) return COLLIDER_ERR_ALIGN;
   const size_t need = attn_workspace_bytes(*cfg, ix->B, ix->S, ix->M_kept);
   if (!ws || ws_bytes < need) return COLLIDER_ERR_WORKSPACE;
   return attn_bwd(*cfg, *ix, *io, ws, ws_bytes, stream);

@@ -5,9 +5,11 @@
 // the kept rows only, with the forward's log-sum-exp (over all keys) kept as the normaliser.
 //
 // Three kernels, all on CDNA4 bf16 MFMA 32x32x16 with fp32 accumulation, P recomputed from Q, K:
-//  1. attn_dq   (query-block outer, 4 wavefronts x 32 queries): with dmode FILTERED it first sweeps
-//     the kept keys to form D~_i = sum_j P_ij dP_ij; with FULL it forms D_i = dO_i . O_i.  It then
-//     sweeps the keys again for dQ = tau * dS K, applies the rotary backward and stores bf16 dq.
+//  1. attn_dq   (query-block outer, 4 wavefronts x 32 queries): one sweep over the kept keys for
+//     dQ = tau * dS K.  With dmode FULL the row term D_i = dO_i . O_i is known before the sweep;
+//     with FILTERED the sweep also forms D~_i = sum_j P_ij dP_ij and the products that let dQ be
+//     finished from it afterwards (see the kernel).  It applies the rotary backward, stores bf16 dq
+//     and the row term for the dK/dV kernel.
 //     It computes S^T = K Q^T so that each lane owns one query: its lse and D are scalars, and the
 //     S^T accumulator registers are directly the A operand of dS K.
 //  2. attn_dkv  (key-block outer, 4 wavefronts x 32 keys): S = Q K^T so each lane owns one key and
@@ -40,6 +42,9 @@ struct AttnParams {
   int64_t ld_lse;
   const int32_t* cu;
   const int32_t* idx;
+  // row of compacted token c in q, k, v, o and lse: srcmap[c] (the full-layout saved tensors read
+  // through the index), or c when null (compacted inputs); dout, the outputs and Dbuf are compacted
+  const int32_t* srcmap;
   int M_kept, S, nq, nkv, G, HS;
   float scale, scale_log2;
   int rot;
@@ -104,6 +109,26 @@ struct TokTile {
   }
 };
 
+__device__ __forceinline__ int64_t src_row(const AttnParams& p, int c) {
+  return p.srcmap ? (int64_t)p.srcmap[c] : (int64_t)c;
+}
+
+// Source rows of this thread's 16-byte chunks of a 64-row tile (tile rows row0 .. row0+63 of a
+// sequence starting at compacted row `base`; -1 past its nrows rows), looked up through `map` -
+// one tile ahead of the loads that use them, so that the lookup's latency is hidden.
+template <int D>
+struct TileRows {
+  int64_t r[TokTile<D>::NV];
+  __device__ __forceinline__ void set(const int32_t* __restrict__ map, int base, int row0, int nrows) {
+#pragma unroll
+    for (int i = 0; i < TokTile<D>::NV; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int rr = row0 + c / (D / 8);
+      r[i] = rr < nrows ? (map ? (int64_t)map[base + rr] : (int64_t)(base + rr)) : -1;
+    }
+  }
+};
+
 template <int D>
 struct TileRegs {
   uint4 v[TokTile<D>::NV];
@@ -116,6 +141,15 @@ struct TileRegs {
       const int r = c / (D / 8), dc = c % (D / 8);
       v[i] = (row0 + r < nrows) ? *(const uint4*)(src + (int64_t)(row0 + r) * ld + col0 + dc * 8)
                                 : make_uint4(0, 0, 0, 0);
+    }
+  }
+  // the tile whose rows `t` lists
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int64_t ld, int col0,
+                                       const TileRows<D>& t) {
+#pragma unroll
+    for (int i = 0; i < TokTile<D>::NV; ++i) {
+      const int dc = (threadIdx.x + 256 * i) % (D / 8);
+      v[i] = t.r[i] >= 0 ? *(const uint4*)(src + t.r[i] * ld + col0 + dc * 8) : make_uint4(0, 0, 0, 0);
     }
   }
   __device__ __forceinline__ void store(char* T) const {
@@ -170,13 +204,25 @@ __device__ __forceinline__ void score_tiles(const char* Ks, const char* Vs, cons
   }
 }
 
+// One sweep over the kept keys of the query block.  dS_ij = P_ij (dP_ij - D_i) needs the row term
+// D_i before any of it can be formed.  With D = dO . O (FULLD) it is known up front.  With the
+// filtered row term D~_i = sum_j P_ij dP_ij (a sum over the same sweep) the kernel instead uses,
+// for a per-query constant c_i known up front,
+//   sum_j dS_ij K_j = sum_j P_ij (dP_ij - c_i) K_j  -  (D~_i - c_i) sum_j P_ij K_j,
+// accumulating both products and D~ in the one sweep (each score exponentiated once instead of
+// twice) and combining them at the end.  c_i = dO_i . O_i, the full softmax's row term: it equals
+// D~_i when no causal key of query i is filtered, so the correction stays small and the bf16
+// operands of the first product are the usual dS values.  Without O (it is optional for the
+// filtered row term) c_i = 0.
 template <int D, bool FULLD>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_dq_kernel(AttnParams p) {
+__global__ __launch_bounds__(256, D == 64 ? (FULLD ? 3 : 2) : 1) void attn_dq_kernel(AttnParams p) {
   constexpr int BQ = 128, BKV = 64, KK = D / 16, DT = D / 32;
   constexpr int TB = TokTile<D>::BYTES;
   constexpr int LDE = D + 4;  // fp32 epilogue tile [BQ][LDE] reuses the same LDS
   constexpr int KV_BYTES = 4 * TB, EPI_BYTES = BQ * LDE * 4;
-  __shared__ __align__(16) char smem[KV_BYTES > EPI_BYTES ? KV_BYTES : EPI_BYTES];
+  constexpr int CORR_OFF = KV_BYTES > EPI_BYTES ? KV_BYTES : EPI_BYTES;
+  // + the per-query correction D~ - c of the filtered row term, [BQ] floats
+  __shared__ __align__(16) char smem[CORR_OFF + (FULLD ? 0 : BQ * 4)];
   // buffers: K in smem + buf*2*TB, V right after it
   // grid (head, sequence, block rank): blocks are dispatched x-fastest, so every sequence's and
   // head's largest query block (the last one, which sees the most keys) starts first
@@ -192,119 +238,95 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_dq_kernel(AttnParam
   const bool qvalid = iq < nb;
   const int qw = q0 + wave * 32;     // first query of this wave
   const bool qall = qw + 31 < nb;    // all 32 queries of the wave exist
-  const uint16_t* kseq = p.k + (int64_t)cs * p.ld_k;  // rows of this sequence
-  const uint16_t* vseq = p.v + (int64_t)cs * p.ld_v;
+  const int64_t qrow = qvalid ? src_row(p, cs + iq) : 0;  // this lane's query in q, o, lse
 
   bf16x8 qf[KK], dof[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     if (qvalid) {
-      qf[kk] = *(const bf16x8*)(p.q + (int64_t)(cs + iq) * p.ld_q + h * D + kk * 16 + hl * 8);
+      qf[kk] = *(const bf16x8*)(p.q + qrow * p.ld_q + h * D + kk * 16 + hl * 8);
       dof[kk] = *(const bf16x8*)(p.dout + (int64_t)(cs + iq) * p.ld_do + h * D + kk * 16 + hl * 8);
     } else {
       qf[kk] = zero_frag();
       dof[kk] = zero_frag();
     }
   }
-  const float lse2 = qvalid ? p.lse[(int64_t)(cs + iq) * p.ld_lse + h] * kLog2e : 0.f;
+  const float lse2 = qvalid ? p.lse[qrow * p.ld_lse + h] * kLog2e : 0.f;
   const int kv_end = min(nb, q0 + BQ);
   const int nkvb = (kv_end + BKV - 1) / BKV;
   TileRegs<D> rk, rv;
+  TileRows<D> tkv;  // rows of the next K / V tile
 
-  float Dv = 0.f;
-  if constexpr (FULLD) {
-    float part = 0.f;
-    if (qvalid) {
+  // cref = c_i = dO_i . O_i (this lane's query; both lane halves hold the full sum)
+  float cref = 0.f;
+  if (p.o && qvalid) {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const bf16x8 of = *(const bf16x8*)(p.o + (int64_t)(cs + iq) * p.ld_o + h * D + kk * 16 + hl * 8);
+    for (int kk = 0; kk < KK; ++kk) {
+      const bf16x8 of = *(const bf16x8*)(p.o + qrow * p.ld_o + h * D + kk * 16 + hl * 8);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) part += (float)of[e] * (float)dof[kk][e];
-      }
+      for (int e = 0; e < 8; ++e) cref += (float)of[e] * (float)dof[kk][e];
     }
-    Dv = part + __shfl_xor(part, 32, 64);
-  } else {
-    // pass 1: D~_i = sum over kept keys j <= i of P_ij dP_ij
-    float dacc = 0.f;
-    rk.load(kseq, p.ld_k, g * D, 0, nb);
-    rv.load(vseq, p.ld_v, g * D, 0, nb);
-    rk.store(smem);
-    rv.store(smem + TB);
-    __syncthreads();
-    for (int kb = 0; kb < nkvb; ++kb) {
-      const char* Ks = smem + (kb & 1) * 2 * TB;
-      if (kb + 1 < nkvb) {
-        rk.load(kseq, p.ld_k, g * D, (kb + 1) * BKV, nb);
-        rv.load(vseq, p.ld_v, g * D, (kb + 1) * BKV, nb);
-      }
-#pragma unroll
-      for (int jt = 0; jt < BKV / 32; ++jt) {
-        f32x16 st, dpt;
-        score_tiles<D>(Ks, Ks + TB, qf, dof, jt, lane, st, dpt);
-        if (kb * BKV + jt * 32 + 31 <= qw && qall) {  // below the diagonal: no mask
-#pragma unroll
-          for (int r = 0; r < 16; ++r) dacc += fast_exp2(fmaf(st[r], p.scale_log2, -lse2)) * dpt[r];
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = kb * BKV + jt * 32 + acc_row(r, lane);
-            const float pr = (qvalid && j <= iq) ? fast_exp2(fmaf(st[r], p.scale_log2, -lse2)) : 0.f;
-            dacc += pr * dpt[r];
-          }
-        }
-      }
-      if (kb + 1 < nkvb) {
-        char* nx = smem + ((kb + 1) & 1) * 2 * TB;
-        rk.store(nx);
-        rv.store(nx + TB);
-      }
-      __syncthreads();
-    }
-    Dv = dacc + __shfl_xor(dacc, 32, 64);
   }
-  if (hl == 0 && qvalid) p.Dbuf[(int64_t)(cs + iq) * p.nq + h] = Dv;
+  cref += __shfl_xor(cref, 32, 64);
 
-  // pass 2: dQ = sum_j dS_ij K_j
-  f32x16 dqa[DT];
+  // dqa = sum_j P_ij (dP_ij - c_i) K_j; dqb = sum_j P_ij K_j (filtered row term only)
+  f32x16 dqa[DT], dqb[FULLD ? 1 : DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqa[t][r] = 0.f;
-  rk.load(kseq, p.ld_k, g * D, 0, nb);
-  rv.load(vseq, p.ld_v, g * D, 0, nb);
+  if constexpr (!FULLD) {
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dqb[t][r] = 0.f;
+  }
+  float dacc = 0.f;  // this lane's part of D~_i = sum_j P_ij dP_ij
+  tkv.set(p.srcmap, cs, 0, nb);
+  rk.load(p.k, p.ld_k, g * D, tkv);
+  rv.load(p.v, p.ld_v, g * D, tkv);
+  if (nkvb > 1) tkv.set(p.srcmap, cs, BKV, nb);
   rk.store(smem);
   rv.store(smem + TB);
   __syncthreads();
   for (int kb = 0; kb < nkvb; ++kb) {
     const char* Ks = smem + (kb & 1) * 2 * TB;
     if (kb + 1 < nkvb) {
-      rk.load(kseq, p.ld_k, g * D, (kb + 1) * BKV, nb);
-      rv.load(vseq, p.ld_v, g * D, (kb + 1) * BKV, nb);
+      rk.load(p.k, p.ld_k, g * D, tkv);
+      rv.load(p.v, p.ld_v, g * D, tkv);
+      if (kb + 2 < nkvb) tkv.set(p.srcmap, cs, (kb + 2) * BKV, nb);
     }
 #pragma unroll
     for (int jt = 0; jt < BKV / 32; ++jt) {
       f32x16 st, dpt;
       score_tiles<D>(Ks, Ks + TB, qf, dof, jt, lane, st, dpt);
-      float ds[16];
+      float pr[16], x[16];
       if (kb * BKV + jt * 32 + 31 <= qw && qall) {  // below the diagonal: no mask
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          ds[r] = fast_exp2(fmaf(st[r], p.scale_log2, -lse2)) * (dpt[r] - Dv);
+        for (int r = 0; r < 16; ++r) {
+          pr[r] = fast_exp2(fmaf(st[r], p.scale_log2, -lse2));
+          x[r] = pr[r] * (dpt[r] - cref);
+          if constexpr (!FULLD) dacc = fmaf(pr[r], dpt[r], dacc);
+        }
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = kb * BKV + jt * 32 + acc_row(r, lane);
-          const float pr = (qvalid && j <= iq) ? fast_exp2(fmaf(st[r], p.scale_log2, -lse2)) : 0.f;
-          ds[r] = pr * (dpt[r] - Dv);
+          pr[r] = (qvalid && j <= iq) ? fast_exp2(fmaf(st[r], p.scale_log2, -lse2)) : 0.f;
+          x[r] = pr[r] * (dpt[r] - cref);
+          if constexpr (!FULLD) dacc = fmaf(pr[r], dpt[r], dacc);
         }
       }
 #pragma unroll
       for (int step = 0; step < 2; ++step) {
-        const bf16x8 a = to_frag(ds + 8 * step);
+        const bf16x8 a = to_frag(x + 8 * step);
+        bf16x8 ap;
+        if constexpr (!FULLD) ap = to_frag(pr + 8 * step);
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
           const bf16x8 bk = frag_tr<D>(Ks, jt * 32 + 16 * step, t * 32, lane);
           dqa[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bk, dqa[t], 0, 0, 0);
+          if constexpr (!FULLD) dqb[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap, bk, dqb[t], 0, 0, 0);
         }
       }
     }
@@ -314,6 +336,26 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_dq_kernel(AttnParam
       rv.store(nx + TB);
     }
     __syncthreads();
+  }
+  float Dv = cref;
+  if constexpr (!FULLD) {
+    Dv = dacc + __shfl_xor(dacc, 32, 64);
+    if (hl == 0) ((float*)(smem + CORR_OFF))[wave * 32 + l32] = Dv - cref;
+  }
+  if (hl == 0 && qvalid) p.Dbuf[(int64_t)(cs + iq) * p.nq + h] = Dv;
+  if constexpr (!FULLD) {
+    __syncthreads();  // the corrections of the wave's 32 queries are in LDS
+    // dQ accumulator rows are queries acc_row(r, lane): D~ - c of row r comes from LDS
+    const float* corr = (const float*)(smem + CORR_OFF) + wave * 32;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const float4 c4 = *(const float4*)(corr + 8 * r4 + 4 * hl);
+      const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dqa[t][4 * r4 + q] = fmaf(-cv[q], dqb[t][4 * r4 + q], dqa[t][4 * r4 + q]);
+    }
   }
 
   // epilogue: tau * dQ through LDS (fp32), rotary backward, bf16 store
@@ -375,15 +417,15 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_dkv_kernel(AttnPara
   const bool kvalid = jk < nb;
   const int kw = k0 + wave * 32;     // first key of this wave
   const bool kall = kw + 31 < nb;    // all 32 keys of the wave exist
-  const uint16_t* qseq = p.q + (int64_t)cs * p.ld_q;  // rows of this sequence
-  const uint16_t* doseq = p.dout + (int64_t)cs * p.ld_do;
+  const uint16_t* doseq = p.dout + (int64_t)cs * p.ld_do;  // compacted rows of this sequence
+  const int64_t krow = kvalid ? src_row(p, cs + jk) : 0;     // this lane's key in k, v
 
   bf16x8 kf[KK], vf[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     if (kvalid) {
-      kf[kk] = *(const bf16x8*)(p.k + (int64_t)(cs + jk) * p.ld_k + g * D + kk * 16 + hl * 8);
-      vf[kk] = *(const bf16x8*)(p.v + (int64_t)(cs + jk) * p.ld_v + g * D + kk * 16 + hl * 8);
+      kf[kk] = *(const bf16x8*)(p.k + krow * p.ld_k + g * D + kk * 16 + hl * 8);
+      vf[kk] = *(const bf16x8*)(p.v + krow * p.ld_v + g * D + kk * 16 + hl * 8);
     } else {
       kf[kk] = zero_frag();
       vf[kk] = zero_frag();
@@ -402,16 +444,24 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_dkv_kernel(AttnPara
   const int n_iter = GH * per_head;  // (head, query block) pairs, head-major
   TileRegs<D> rq, ro;
   float sl = 0.f, sd = 0.f;
-
+  // source rows of the Q tile and of the lse entry (threads < BQ) the next fetch reads, looked up
+  // one iteration ahead of it
+  TileRows<D> tq;
+  int64_t lrow = -1;
+  auto rows_of = [&](int it) {
+    const int i0 = (qb0 + it % per_head) * BQ;
+    tq.set(p.srcmap, cs, i0, nb);
+    if (threadIdx.x < BQ) lrow = i0 + (int)threadIdx.x < nb ? src_row(p, cs + i0 + threadIdx.x) : -1;
+  };
   auto fetch = [&](int it) {
     const int h = g * p.G + hs * GH + it / per_head;
     const int i0 = (qb0 + it % per_head) * BQ;
-    rq.load(qseq, p.ld_q, h * D, i0, nb);
+    rq.load(p.q, p.ld_q, h * D, tq);
     ro.load(doseq, p.ld_do, h * D, i0, nb);
     if (threadIdx.x < BQ) {
       const int i = i0 + threadIdx.x;
-      sl = i < nb ? p.lse[(int64_t)(cs + i) * p.ld_lse + h] * kLog2e : 0.f;
-      sd = i < nb ? p.Dbuf[(int64_t)(cs + i) * p.nq + h] : 0.f;
+      sl = lrow >= 0 ? p.lse[lrow * p.ld_lse + h] * kLog2e : 0.f;
+      sd = i < nb ? -p.Dbuf[(int64_t)(cs + i) * p.nq + h] : 0.f;  // -D: the dP accumulator's start
     }
   };
   auto put = [&](int buf) {
@@ -425,7 +475,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_dkv_kernel(AttnPara
   };
 
   if (n_iter > 0) {
+    rows_of(0);
     fetch(0);
+    if (n_iter > 1) rows_of(1);
     put(0);
   }
   __syncthreads();
@@ -436,12 +488,25 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_dkv_kernel(AttnPara
     const float* Ls = (const float*)(base + 2 * TB);
     const float* Ds = Ls + BQ;
     const int i0 = (qb0 + it % per_head) * BQ;
-    if (it + 1 < n_iter) fetch(it + 1);
+    if (it + 1 < n_iter) {
+      fetch(it + 1);
+      if (it + 2 < n_iter) rows_of(it + 2);
+    }
 #pragma unroll
     for (int t2 = 0; t2 < BQ / 32; ++t2) {
+      // dP accumulates onto -D_i (rows of the tile are queries 8*r4 + 4*hl + q), so that it comes
+      // out of the MFMAs as dP - D
       f32x16 s, dp;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 d4 = *(const float4*)(Ds + t2 * 32 + 8 * r4 + 4 * hl);
+        dp[4 * r4] = d4.x;
+        dp[4 * r4 + 1] = d4.y;
+        dp[4 * r4 + 2] = d4.z;
+        dp[4 * r4 + 3] = d4.w;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const bf16x8 qa = frag_rows<D>(Qs, t2 * 32, kk, lane);
@@ -450,30 +515,29 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_dkv_kernel(AttnPara
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kk], dp, 0, 0, 0);
       }
       float pr[16], ds[16];
-      // every query of this 32-block is valid and after every key of the wave: no mask
-      const bool interior = (i0 + t2 * 32 >= kw + 31) && (i0 + t2 * 32 + 31 < nb) && kall;
+      float lv[16];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int ib = t2 * 32 + 8 * r4 + 4 * hl;  // 4 consecutive queries
-        const float4 l4 = *(const float4*)(Ls + ib);
-        const float4 d4 = *(const float4*)(Ds + ib);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
-        if (interior) {
+        const float4 l4 = *(const float4*)(Ls + t2 * 32 + 8 * r4 + 4 * hl);
+        lv[4 * r4] = l4.x;
+        lv[4 * r4 + 1] = l4.y;
+        lv[4 * r4 + 2] = l4.z;
+        lv[4 * r4 + 3] = l4.w;
+      }
+      // every query of this 32-block is valid and after every key of the wave: no mask
+      if ((i0 + t2 * 32 >= kw + 31) && (i0 + t2 * 32 + 31 < nb) && kall) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = 4 * r4 + q;
-            pr[r] = fast_exp2(fmaf(s[r], p.scale_log2, -lv[q]));
-            ds[r] = pr[r] * (dp[r] - dvv[q]);
-          }
-        } else {
+        for (int r = 0; r < 16; ++r) {
+          pr[r] = fast_exp2(fmaf(s[r], p.scale_log2, -lv[r]));
+          ds[r] = pr[r] * dp[r];
+        }
+      } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = 4 * r4 + q;
-            const int i = i0 + ib + q;
-            const float pv = (kvalid && i < nb && jk <= i) ? fast_exp2(fmaf(s[r], p.scale_log2, -lv[q])) : 0.f;
-            pr[r] = pv;
-            ds[r] = pv * (dp[r] - dvv[q]);
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int i = i0 + t2 * 32 + acc_row(r, lane);
+          const float pv = (kvalid && i < nb && jk <= i) ? fast_exp2(fmaf(s[r], p.scale_log2, -lv[r])) : 0.f;
+          pr[r] = pv;
+          ds[r] = pv * dp[r];
         }
       }
 #pragma unroll
@@ -594,7 +658,7 @@ collider_status attn_rope_prepare(const collider_attn_cfg& c, const collider_ind
 
 collider_status attn_bwd(const collider_attn_cfg& c, const collider_index& ix,
                          const collider_attn_io& io, void* ws, size_t ws_bytes, hipStream_t s,
-                         bool rope_ready) {
+                         bool rope_ready, const int32_t* srcmap) {
   const int B = ix.B, S = ix.S, Mk = ix.M_kept;
   if (Mk <= 0) return COLLIDER_OK;
   AttnWs w = carve_attn(c, B, S, Mk, ws);
@@ -614,6 +678,7 @@ collider_status attn_bwd(const collider_attn_cfg& c, const collider_index& ix,
   p.ld_lse = io.ld_lse;
   p.cu = ix.cu_seqlens;
   p.idx = ix.idx;
+  p.srcmap = srcmap;
   p.M_kept = Mk;
   p.S = S;
   p.nq = c.n_q_heads;

@@ -1057,8 +1057,9 @@ struct Plan {
 // The direct-to-LDS kernel needs whole 64-wide k-tiles along every K-contiguous operand row
 // (buffer loads only zero-fill past the end of a buffer) and 32-bit byte offsets.
 bool lds_eligible(const GemmProblem& p) {
-  if (p.a_kmajor && p.K % kBK) return false;
-  if (p.b_kmajor && p.K % kBK) return false;
+  const int64_t kpad = ((int64_t)p.K + kBK - 1) / kBK * kBK;
+  if (p.a_kmajor && p.K % kBK && !(p.a_kpad && p.lda >= kpad)) return false;
+  if (p.b_kmajor && p.K % kBK && !(p.b_kpad && p.ldb >= kpad)) return false;
   if (p.B1 && p.kseg % kBK) return false;
   const int64_t a_rows = p.a_kmajor ? p.M : p.K, b_rows = p.b_kmajor ? p.N : p.K;
   return a_rows * p.lda * 2 < (1ll << 31) && b_rows * p.ldb * 2 < (1ll << 31);
@@ -1217,6 +1218,13 @@ collider_status launch_cfg(const GemmParams& gp, const GemmProblem& pr, const Pl
       if (pl.lds) return launch_lds<BM, BN, EPI_F32, false, false>(gp, pl.grid, name, s);
       if constexpr (kStaged) return launch_one<BM, BN, EPI_F32, false, false>(gp, name, s);
     }
+  }
+  // weight gradients with one token-contiguous operand (the transposed normalised input /
+  // activation): A = X^T (weights [in, out]) or B = X^T (weights [out, in]); direct-to-LDS only
+  if (pr.epi == EPI_F32 && pl.lds) {
+    if (pr.a_kmajor && !pr.b_kmajor) return launch_lds<BM, BN, EPI_F32, true, false>(gp, pl.grid, name, s);
+    if constexpr (kMnA)
+      if (!pr.a_kmajor && pr.b_kmajor) return launch_lds<BM, BN, EPI_F32, false, true>(gp, pl.grid, name, s);
   }
   return COLLIDER_ERR_UNSUPPORTED;
 }

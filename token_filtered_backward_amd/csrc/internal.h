@@ -132,13 +132,15 @@ collider_status launch_scatter_bytes(const void* src, int64_t ld_src_b, void* ds
                                      const int32_t* inv, int M, int row_bytes, int zero_fill,
                                      hipStream_t s);
 
-// xn = norm(x[rowmap[c]]) as bf16 (RMSNorm when mean == nullptr, else LayerNorm with beta)
-collider_status launch_norm_recompute(const uint16_t* x, const float* mean, const float* rstd,
-                                      const float* gamma, const float* beta, const int32_t* rowmap,
-                                      int rows, int H, uint16_t* xn, hipStream_t s);
-// a = act(gate/f [rowmap[c]]) as bf16: SwiGLU (up != nullptr) or GELU-tanh (up == nullptr)
-collider_status launch_act_recompute(const uint16_t* g, const uint16_t* up, const int32_t* rowmap,
-                                     int rows, int I, uint16_t* a, hipStream_t s);
+// out[col * ldT + c] = bf16(op(row rowmap[c] of x (and x2), col)) for c < rows, 0 up to ldT (a
+// multiple of 8 >= rows): the transposed (token-contiguous) operand of a weight-gradient GEMM.
+// op: COL_COPY x; COL_NORM (x - mean) rstd gamma + beta (mean, beta may be null: RMSNorm);
+// COL_SWIGLU silu(x) x2; COL_GELU gelu_tanh(x).  x, x2 row stride ld_x elements.
+enum ColOp { COL_COPY = 0, COL_NORM = 1, COL_SWIGLU = 2, COL_GELU = 3 };
+collider_status launch_cols_recompute(int op, const uint16_t* x, int64_t ld_x, const uint16_t* x2,
+                                      const float* mean, const float* rstd, const float* gamma,
+                                      const float* beta, const int32_t* rowmap, int rows, int C,
+                                      uint16_t* out, int64_t ldT, hipStream_t s);
 // dx = dres + norm_bwd(dxn; x[rowmap], stats): row c of dx, or row rowmap[c] when dx_full != 0
 // (the full token layout); row_limit (device int, may be null): rows c >= *row_limit are skipped
 collider_status launch_norm_bwd(const uint16_t* dxn, const uint16_t* dres, const uint16_t* x,
@@ -176,6 +178,10 @@ struct GemmProblem {
   int kseg;
   int64_t ldb;
   bool b_kmajor;  // B(k,n) = B[n*ldb + k] (true) or B[k*ldb + n] (false)
+  // a K-major operand whose rows hold zeros from K up to the next multiple of 64 (within its
+  // leading dimension): its ragged reduction length needs no masking (token-contiguous operands
+  // of the weight-gradient GEMMs, written with that padding)
+  bool a_kpad, b_kpad;
   // epilogue
   int epi;
   void* C;
@@ -206,9 +212,11 @@ collider_status gemm_f32(const GemmProblem& p, hipStream_t s);
 size_t attn_workspace_bytes(const collider_attn_cfg& c, int B, int S, int M_kept);
 // rope_ready: the (cos, sin) table in the workspace was already written by attn_rope_prepare
 // (on a stream this call's stream has waited for); otherwise attn_bwd writes it first.
+// srcmap: when not null, row c of io.q, k, v, o and lse is row srcmap[c] (the full-layout saved
+// tensors read through the index); dout and the outputs are compacted either way.
 collider_status attn_bwd(const collider_attn_cfg& c, const collider_index& ix,
                          const collider_attn_io& io, void* ws, size_t ws_bytes, hipStream_t s,
-                         bool rope_ready = false);
+                         bool rope_ready = false, const int32_t* srcmap = nullptr);
 // Writes the RoPE (cos, sin) table of attn_bwd's workspace (it depends on S and the rotary
 // configuration only), so that a caller can build it off the critical path.
 collider_status attn_rope_prepare(const collider_attn_cfg& c, const collider_index& ix, void* ws,

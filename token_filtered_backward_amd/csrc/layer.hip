@@ -2,7 +2,8 @@
 // filtered across all layers; every linear backward becomes a dense GEMM over the kept tokens).
 //
 // The sequence of launches for one layer, all on one stream, no host synchronisation:
-//   gather   dY', O', Q', K', V', lse' (one multi-tensor launch; saved tensors are full-layout)
+//   gather   dY' (the saved tensors stay in the full layout; their consumers read them through
+//            the index)
 //   LLAMA                                         PHI (parallel block)
 //   a'  = silu(gate')*up'   (recompute)           g' = gelu_tanh(f')       (recompute)
 //   dA  = dY' w_down   -> SwiGLU bwd epilogue     dF = dY' w_fc2 -> GELU bwd epilogue
@@ -136,9 +137,11 @@ namespace {
 
 struct LayerBufs {
 
-  uint16_t *dy_c, *o_c, *q_c, *k_c, *v_c;
-  float* lse_c;
-  uint16_t *act_c, *xn_c, *dmid, *dqkv, *dxn, *dh, *do_c, *dx_c;
+  uint16_t* dy_c;
+  // token-contiguous (transposed, [C, ldT]) operands of the weight-gradient GEMMs: the
+  // activation, the normalised input, the attention output
+  uint16_t *actT, *xnT, *oT;
+  uint16_t *dmid, *dqkv, *dxn, *dh, *do_c, *dx_c;
   float *part_g, *part_b;
   uint16_t* dxn1;
   void* gemm_ws;   // split-K partials of the GEMMs on the caller's stream
@@ -164,23 +167,17 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
 
   Carver cv(dry ? nullptr : ws);
   LayerBufs b{};
-  if (unf) {  // saved tensors are read in place
+  // the upstream gradient's kept rows are gathered (the first GEMM's operand); the saved tensors
+  // attention reads (q, k, v, o, lse) stay in the full layout and are read through the index
+  if (unf)
     b.dy_c = (uint16_t*)dy;
-    b.o_c = sv ? (uint16_t*)sv->o : nullptr;
-    b.q_c = sv ? (uint16_t*)sv->q : nullptr;
-    b.k_c = sv ? (uint16_t*)sv->k : nullptr;
-    b.v_c = sv ? (uint16_t*)sv->v : nullptr;
-    b.lse_c = sv ? (float*)sv->lse : nullptr;
-  } else {
+  else
     b.dy_c = dy_compact ? (uint16_t*)dy : cv.take<uint16_t>((size_t)Mk * H);
-    b.o_c = cv.take<uint16_t>((size_t)Mk * nqd);
-    b.q_c = cv.take<uint16_t>((size_t)Mk * nqd);
-    b.k_c = cv.take<uint16_t>((size_t)Mk * nkvd);
-    b.v_c = cv.take<uint16_t>((size_t)Mk * nkvd);
-    b.lse_c = cv.take<float>((size_t)Mk * nq);
-  }
-  b.act_c = cv.take<uint16_t>((size_t)Mk * I);
-  b.xn_c = cv.take<uint16_t>((size_t)Mk * H);
+  // tokens of the transposed operands, padded with zero columns to whole 64-token k-tiles
+  const int ldT = (Mk + 63) / 64 * 64;
+  b.actT = cv.take<uint16_t>((size_t)I * ldT);
+  b.xnT = cv.take<uint16_t>((size_t)H * ldT);
+  b.oT = cv.take<uint16_t>((size_t)nqd * ldT);
   b.dmid = cv.take<uint16_t>((size_t)Mk * mid);
   // [dq|dk|dv]: its own buffer for LLAMA (attention must not overwrite [dgate|dup] while the
   // side stream's dw_gateup GEMM may still read it); for PHI the first columns of dmid
@@ -217,18 +214,23 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     p.B0 = Bm; p.ldb = w_io ? k : ldb; p.b_kmajor = w_io;
     p.epi = epi; p.C = C; p.ldc = ldc;
   };
-  auto dw_gemm = [&](GemmProblem& p, int m, int n, const void* A, int64_t lda, const void* Bm,
-                     int64_t ldb, float* C) {
-    // dw [m = out, n = in] = dY^T [m, M'] X [M', n]; with [in, out] weights the transpose
+  auto dw_gemm = [&](GemmProblem& p, int m, int n, const void* G, int64_t ldg, const void* XT,
+                     float* C) {
+    // dw [m = out, n = in] = dY^T [m, M'] X [M', n], with the gradient dY token-major (row stride
+    // ldg) and X given transposed, XT [n, ldT] (token-contiguous, zero past the kept tokens).
+    // [in, out] weights: dW [in, out] = X^T dY, A = XT read along the reduction; [out, in]:
+    // dw = dY^T X, B = XT read along the reduction.
+    p.K = Mk;
     if (w_io) {
-      std::swap(m, n);
-      std::swap(A, Bm);
-      std::swap(lda, ldb);
+      p.M = n; p.N = m;
+      p.A = XT; p.lda = ldT; p.a_kmajor = true; p.a_kpad = true;
+      p.B0 = G; p.ldb = ldg; p.b_kmajor = false;
+    } else {
+      p.M = m; p.N = n;
+      p.A = G; p.lda = ldg; p.a_kmajor = false;
+      p.B0 = XT; p.ldb = ldT; p.b_kmajor = true; p.b_kpad = true;
     }
-    p.M = m; p.N = n; p.K = Mk;
-    p.A = A; p.lda = lda; p.a_kmajor = false;
-    p.B0 = Bm; p.ldb = ldb; p.b_kmajor = false;
-    p.epi = EPI_F32; p.C = C; p.ldc = n; p.accumulate = c.accumulate;
+    p.epi = EPI_F32; p.C = C; p.ldc = p.N; p.accumulate = c.accumulate;
   };
   if (llama) {
     dx_gemm(g_dA, I, H, b.dy_c, H, w ? w->w_down : nullptr, I, EPI_SWIGLU, b.dmid, mid);
@@ -238,27 +240,27 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     g_dA.rowmap = idx;
     g_dA.out2 = b.dmid ? b.dmid + I : nullptr;
     g_dA.ld_out2 = mid;
-    dw_gemm(g_dw2, H, I, b.dy_c, H, b.act_c, I, gr ? gr->dw_down : nullptr);
+    dw_gemm(g_dw2, H, I, b.dy_c, H, b.actT, gr ? gr->dw_down : nullptr);
     dx_gemm(g_dXmid, H, 2 * I, b.dmid, mid, w ? w->w_gateup : nullptr, H, EPI_BF16, b.dxn, H);
-    dw_gemm(g_dwmid, 2 * I, H, b.dmid, mid, b.xn_c, H, gr ? gr->dw_gateup : nullptr);
+    dw_gemm(g_dwmid, 2 * I, H, b.dmid, mid, b.xnT, gr ? gr->dw_gateup : nullptr);
     dx_gemm(g_dO, nqd, H, b.dh, H, w ? w->w_o : nullptr, nqd, EPI_BF16, b.do_c, nqd);
-    dw_gemm(g_dwo, H, nqd, b.dh, H, b.o_c, nqd, gr ? gr->dw_o : nullptr);
+    dw_gemm(g_dwo, H, nqd, b.dh, H, b.oT, gr ? gr->dw_o : nullptr);
     dx_gemm(g_dXin, H, nqkv, b.dqkv, ldq, w ? w->w_qkv : nullptr, H, EPI_BF16, b.dxn1, H);
-    dw_gemm(g_dwqkv, nqkv, H, b.dqkv, ldq, b.xn_c, H, gr ? gr->dw_qkv : nullptr);
+    dw_gemm(g_dwqkv, nqkv, H, b.dqkv, ldq, b.xnT, gr ? gr->dw_qkv : nullptr);
   } else {
     uint16_t* dF = b.dmid ? b.dmid + nqkv : nullptr;
     dx_gemm(g_dA, I, H, b.dy_c, H, w ? w->w_fc2 : nullptr, I, EPI_GELU, dF, mid);
     g_dA.g = sv ? (const uint16_t*)sv->f : nullptr;
     g_dA.ld_g = I;
     g_dA.rowmap = idx;
-    dw_gemm(g_dw2, H, I, b.dy_c, H, b.act_c, I, gr ? gr->dw_fc2 : nullptr);
+    dw_gemm(g_dw2, H, I, b.dy_c, H, b.actT, gr ? gr->dw_fc2 : nullptr);
     dx_gemm(g_dO, nqd, H, b.dy_c, H, w ? w->w_o : nullptr, nqd, EPI_BF16, b.do_c, nqd);
-    dw_gemm(g_dwo, H, nqd, b.dy_c, H, b.o_c, nqd, gr ? gr->dw_o : nullptr);
+    dw_gemm(g_dwo, H, nqd, b.dy_c, H, b.oT, gr ? gr->dw_o : nullptr);
     dx_gemm(g_dXin, H, nqkv + I, b.dmid, mid, w ? w->w_qkv : nullptr, H, EPI_BF16, b.dxn, H);
     g_dXin.B1 = w ? w->w_fc1 : nullptr;
     g_dXin.kseg = nqkv;
-    dw_gemm(g_dwqkv, nqkv, H, b.dmid, mid, b.xn_c, H, gr ? gr->dw_qkv : nullptr);
-    dw_gemm(g_dwfc1, I, H, dF, mid, b.xn_c, H, gr ? gr->dw_fc1 : nullptr);
+    dw_gemm(g_dwqkv, nqkv, H, b.dmid, mid, b.xnT, gr ? gr->dw_qkv : nullptr);
+    dw_gemm(g_dwfc1, I, H, dF, mid, b.xnT, gr ? gr->dw_fc1 : nullptr);
   }
   g_dA.name = llama ? "gemm_dA_swiglu" : "gemm_dA_gelu";
   g_dw2.name = llama ? "gemm_dw_down" : "gemm_dw_fc2";
@@ -342,35 +344,22 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
   // the rotary table attention reads (S and the rotary configuration only), off the critical path;
   // attention waits on the event recorded after the gathers below
   CHECK(attn_rope_prepare(ac, aix, b.attn_ws, b.attn_ws_bytes, s1));
-  if (Mk > 0 && !unf) {  // 2. saved tensors attention and dW_o read as compacted operands
-    GatherDesc gd[5];
-    int nd = 0;
-    auto add = [&](const void* src, void* dst, int row_bytes) {
-      gd[nd++] = GatherDesc{src, dst, row_bytes / 16, row_bytes / 16, row_bytes / 16, 0};
-    };
-    add(sv->o, b.o_c, nqd * 2);
-    add(sv->q, b.q_c, nqd * 2);
-    add(sv->k, b.k_c, nkvd * 2);
-    add(sv->v, b.v_c, nkvd * 2);
-    add(sv->lse, b.lse_c, nq * 4);
-    CHECK(launch_gather_rows(gd, nd, idx, Mk, s1));
-  }
   if (side && hipEventRecord(side->ev[6], s1) != hipSuccess) return COLLIDER_ERR_HIP;
-  collider_attn_io io{};
-  io.q = b.q_c; io.ld_q = nqd;
-  io.k = b.k_c; io.ld_k = nkvd;
-  io.v = b.v_c; io.ld_v = nkvd;
-  io.o = b.o_c; io.ld_o = nqd;
-  io.lse = b.lse_c; io.ld_lse = nq;
+  collider_attn_io io{};  // saved tensors in the full layout, rows idx[c] (all rows when unfiltered)
+  io.q = sv ? sv->q : nullptr; io.ld_q = nqd;
+  io.k = sv ? sv->k : nullptr; io.ld_k = nkvd;
+  io.v = sv ? sv->v : nullptr; io.ld_v = nkvd;
+  io.o = sv ? sv->o : nullptr; io.ld_o = nqd;
+  io.lse = sv ? sv->lse : nullptr; io.ld_lse = nq;
   io.dout = b.do_c; io.ld_do = nqd;
   io.dq = b.dqkv; io.ld_dq = ldq;
   io.dk = b.dqkv + nqd; io.ld_dk = ldq;
   io.dv = b.dqkv + nqd + nkvd; io.ld_dv = ldq;
   if (llama) {
-    CHECK(launch_act_recompute((const uint16_t*)sv->gate, (const uint16_t*)sv->up, idx, Mk, I,
-                               b.act_c, s1));
-    CHECK(launch_norm_recompute((const uint16_t*)sv->h, nullptr, sv->rstd2, w->gamma2, nullptr, idx,
-                                Mk, H, b.xn_c, s1));
+    CHECK(launch_cols_recompute(COL_SWIGLU, (const uint16_t*)sv->gate, I, (const uint16_t*)sv->up,
+                                nullptr, nullptr, nullptr, nullptr, idx, Mk, I, b.actT, ldT, s1));
+    CHECK(launch_cols_recompute(COL_NORM, (const uint16_t*)sv->h, H, nullptr, nullptr, sv->rstd2,
+                                w->gamma2, nullptr, idx, Mk, H, b.xnT, ldT, s1));
     CHECK(gemm_bf16(g_dw2, b.gemm_ws2, b.gemm_ws2_bytes, s1));
     CHECK(gemm_bf16(g_dA, b.gemm_ws, b.gemm_ws_bytes, s));
     CHECK(handoff(1, s, s1));  // [dgate|dup] ready
@@ -378,6 +367,8 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     CHECK(gemm_bf16(g_dXmid, b.gemm_ws, b.gemm_ws_bytes, s));
     CHECK(launch_norm_bwd(b.dxn, b.dy_c, (const uint16_t*)sv->h, nullptr, sv->rstd2, w->gamma2, idx,
                           Mk, H, b.dh, 0, s));
+    CHECK(launch_cols_recompute(COL_COPY, (const uint16_t*)sv->o, nqd, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, idx, Mk, nqd, b.oT, ldT, s1));
     CHECK(handoff(2, s, s1));  // dh ready (and dXn2, for the gain gradient)
     CHECK(gemm_bf16(g_dwo, b.gemm_ws2, b.gemm_ws2_bytes, s1));
     CHECK(launch_norm_grad_parts(b.dxn, (const uint16_t*)sv->h, nullptr, sv->rstd2, idx, Mk, H,
@@ -385,10 +376,10 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dgamma2, c.accumulate, s1));
     CHECK(gemm_bf16(g_dO, b.gemm_ws, b.gemm_ws_bytes, s));
     if (side && hipStreamWaitEvent(s, side->ev[6], 0) != hipSuccess) return COLLIDER_ERR_HIP;
-    CHECK(attn_bwd(ac, aix, io, b.attn_ws, b.attn_ws_bytes, s, true));
+    CHECK(attn_bwd(ac, aix, io, b.attn_ws, b.attn_ws_bytes, s, true, idx));
     CHECK(handoff(3, s, s1));  // [dq|dk|dv] ready
-    CHECK(launch_norm_recompute((const uint16_t*)sv->x, nullptr, sv->rstd1, w->gamma1, nullptr, idx,
-                                Mk, H, b.xn_c, s1));
+    CHECK(launch_cols_recompute(COL_NORM, (const uint16_t*)sv->x, H, nullptr, nullptr, sv->rstd1,
+                                w->gamma1, nullptr, idx, Mk, H, b.xnT, ldT, s1));
     CHECK(gemm_bf16(g_dwqkv, b.gemm_ws2, b.gemm_ws2_bytes, s1));
     CHECK(gemm_bf16(g_dXin, b.gemm_ws, b.gemm_ws_bytes, s));
     CHECK(handoff(7, s, s1));  // dXn1 ready: the gain gradient on the side stream
@@ -398,15 +389,18 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     CHECK(launch_norm_bwd(b.dxn1, b.dh, (const uint16_t*)sv->x, nullptr, sv->rstd1, w->gamma1, idx, Mk,
                           H, b.dx_c, dx_full, s, dx_full ? ix.count : nullptr));
   } else {
-    CHECK(launch_act_recompute((const uint16_t*)sv->f, nullptr, idx, Mk, I, b.act_c, s1));
-    CHECK(launch_norm_recompute((const uint16_t*)sv->x, sv->mean, sv->rstd1, w->ln_gamma, w->ln_beta,
-                                idx, Mk, H, b.xn_c, s1));
+    CHECK(launch_cols_recompute(COL_GELU, (const uint16_t*)sv->f, I, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, idx, Mk, I, b.actT, ldT, s1));
+    CHECK(launch_cols_recompute(COL_NORM, (const uint16_t*)sv->x, H, nullptr, sv->mean, sv->rstd1,
+                                w->ln_gamma, w->ln_beta, idx, Mk, H, b.xnT, ldT, s1));
+    CHECK(launch_cols_recompute(COL_COPY, (const uint16_t*)sv->o, nqd, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, idx, Mk, nqd, b.oT, ldT, s1));
     CHECK(gemm_bf16(g_dw2, b.gemm_ws2, b.gemm_ws2_bytes, s1));
     CHECK(gemm_bf16(g_dwo, b.gemm_ws2, b.gemm_ws2_bytes, s1));
     CHECK(gemm_bf16(g_dA, b.gemm_ws, b.gemm_ws_bytes, s));
     CHECK(gemm_bf16(g_dO, b.gemm_ws, b.gemm_ws_bytes, s));
     if (side && hipStreamWaitEvent(s, side->ev[6], 0) != hipSuccess) return COLLIDER_ERR_HIP;
-    CHECK(attn_bwd(ac, aix, io, b.attn_ws, b.attn_ws_bytes, s, true));
+    CHECK(attn_bwd(ac, aix, io, b.attn_ws, b.attn_ws_bytes, s, true, idx));
     CHECK(handoff(1, s, s1));  // [dq|dk|dv|dF] ready
     CHECK(gemm_bf16(g_dwqkv, b.gemm_ws2, b.gemm_ws2_bytes, s1));
     CHECK(gemm_bf16(g_dwfc1, b.gemm_ws2, b.gemm_ws2_bytes, s1));

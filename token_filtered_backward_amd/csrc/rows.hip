@@ -213,70 +213,7 @@ collider_status launch_scatter_bytes(const void* src, int64_t ld_src_b, void* ds
 }
 
 // ------------------------------------------------------------------------------------------
-// norm recompute: xn[c] = bf16(norm(x[rowmap[c]])), RMSNorm (mean == nullptr) or LayerNorm
-// ------------------------------------------------------------------------------------------
-// One wavefront per row; all of the row's loads are issued before any arithmetic (NV 16-byte
-// vectors per lane, H <= 512 * NV).
-template <int NV>
-__global__ __launch_bounds__(256) void norm_recompute_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ mean, const float* __restrict__ rstd,
-    const float* __restrict__ gamma, const float* __restrict__ beta,
-    const int32_t* __restrict__ rowmap, int rows, int H, uint16_t* __restrict__ xn) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int c = blockIdx.x * 4 + wave;
-  if (c >= rows) return;
-  const int64_t r = rowmap ? rowmap[c] : c;
-  const float mu = mean ? mean[r] : 0.f;
-  const float rs = rstd[r];
-  const uint4* xr = (const uint4*)(x + r * H);
-  uint4* out = (uint4*)(xn + (int64_t)c * H);
-  const int nvec = H / 8;
-  uint4 xv[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i)
-    if (lane + 64 * i < nvec) xv[i] = xr[lane + 64 * i];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int v = lane + 64 * i;
-    if (v >= nvec) continue;
-    const float4 g0 = ((const float4*)gamma)[2 * v], g1 = ((const float4*)gamma)[2 * v + 1];
-    float4 b0 = make_float4(0, 0, 0, 0), b1 = b0;
-    if (beta) {
-      b0 = ((const float4*)beta)[2 * v];
-      b1 = ((const float4*)beta)[2 * v + 1];
-    }
-    uint4 o;
-    o.x = pack2bf((bflo(xv[i].x) - mu) * rs * g0.x + b0.x, (bfhi(xv[i].x) - mu) * rs * g0.y + b0.y);
-    o.y = pack2bf((bflo(xv[i].y) - mu) * rs * g0.z + b0.z, (bfhi(xv[i].y) - mu) * rs * g0.w + b0.w);
-    o.z = pack2bf((bflo(xv[i].z) - mu) * rs * g1.x + b1.x, (bfhi(xv[i].z) - mu) * rs * g1.y + b1.y);
-    o.w = pack2bf((bflo(xv[i].w) - mu) * rs * g1.z + b1.z, (bfhi(xv[i].w) - mu) * rs * g1.w + b1.w);
-    out[v] = o;
-  }
-}
-
-collider_status launch_norm_recompute(const uint16_t* x, const float* mean, const float* rstd,
-                                      const float* gamma, const float* beta, const int32_t* rowmap,
-                                      int rows, int H, uint16_t* xn, hipStream_t s) {
-  if (rows <= 0) return COLLIDER_OK;
-  const int nv = (H / 8 + 63) / 64;
-  dim3 grid((rows + 3) / 4), block(256);
-#define NR_CASE(N)                                                                             \
-  case N:                                                                                      \
-    COLLIDER_LAUNCH("norm_recompute", s,                                                       \
-                    hipLaunchKernelGGL(norm_recompute_kernel<N>, grid, block, 0, s, x, mean, rstd, \
-                                       gamma, beta, rowmap, rows, H, xn));                     \
-    break;
-  switch (nv) {
-    NR_CASE(1) NR_CASE(2) NR_CASE(3) NR_CASE(4) NR_CASE(5) NR_CASE(6) NR_CASE(7) NR_CASE(8)
-    default:
-      return COLLIDER_ERR_UNSUPPORTED;
-  }
-#undef NR_CASE
-  return last_hip_status();
-}
-
-// ------------------------------------------------------------------------------------------
-// activation recompute: a[c] = bf16(silu(g)*up) or bf16(gelu_tanh(g)), rows rowmap[c]
+// activations recomputed from the saved pre-activations
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ float silu_f(float g) { return g * fast_sigmoid(g); }
 __device__ __forceinline__ float gelu_f(float f) {
@@ -285,57 +222,110 @@ __device__ __forceinline__ float gelu_f(float f) {
   return 0.5f * f * (1.f + fast_tanh(u));
 }
 
-// One wavefront per row, the row's loads issued first in batches of up to 8 vectors per lane.
-__global__ __launch_bounds__(256) void act_recompute_kernel(const uint16_t* __restrict__ g,
-                                                            const uint16_t* __restrict__ up,
-                                                            const int32_t* __restrict__ rowmap,
-                                                            int rows, int I,
-                                                            uint16_t* __restrict__ a) {
-  constexpr int NB = 8;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int c = blockIdx.x * 4 + wave;
-  if (c >= rows) return;
-  const int64_t r = rowmap ? rowmap[c] : c;
-  const uint4* gr = (const uint4*)(g + r * I);
-  const uint4* ur = up ? (const uint4*)(up + r * I) : nullptr;
-  uint4* out = (uint4*)(a + (int64_t)c * I);
-  const int nvec = I / 8;
-  for (int v0 = lane; v0 < nvec; v0 += 64 * NB) {
-    uint4 gv[NB], uv[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int v = v0 + 64 * b;
-      if (v < nvec) {
-        gv[b] = gr[v];
-        if (ur) uv[b] = ur[v];
-      }
+// ------------------------------------------------------------------------------------------
+// transposed recompute: out[col * ldT + c] = bf16(op(row rowmap[c], col)) for c < rows, 0 for
+// rows <= c < ldT.  The operands the weight-gradient GEMMs reduce over tokens (normalised inputs,
+// activations, the attention output) come out token-contiguous, so the GEMM reads them with
+// 16-byte LDS reads instead of transposing ones.  Ops: COL_COPY (a saved tensor as it is),
+// COL_NORM (RMSNorm / LayerNorm with the saved statistics: (x - mean) rstd gamma + beta),
+// COL_SWIGLU (silu(gate) up), COL_GELU (gelu_tanh(f)), each in fp32 and rounded to bf16 once.
+// Each thread takes an 8-token x 8-column block: eight 16-byte row loads (threads of one token
+// block read 16 consecutive chunks of a row), the op in fp32, a transpose in registers and eight
+// 16-byte stores of 8 consecutive tokens of one column (threads of one column block write 16
+// consecutive chunks of an output row).  A workgroup covers 128 tokens x 128 columns.
+// ------------------------------------------------------------------------------------------
+template <int OP>
+__global__ __launch_bounds__(256) void cols_recompute_kernel(
+    const uint16_t* __restrict__ x, int64_t ld_x, const uint16_t* __restrict__ x2,
+    const float* __restrict__ mean, const float* __restrict__ rstd, const float* __restrict__ gamma,
+    const float* __restrict__ beta, const int32_t* __restrict__ rowmap, int rows, int C,
+    uint16_t* __restrict__ out, int64_t ldT) {
+  const int tb = threadIdx.x & 15, cb = threadIdx.x >> 4;
+  const int c0 = blockIdx.x * 128 + tb * 8;   // first token of the block
+  const int col0 = blockIdx.y * 128 + cb * 8; // first column
+  if (c0 >= ldT || col0 >= C) return;
+  uint4 u[8];
+  float g[8] = {}, bt[8] = {};
+  if constexpr (OP == COL_NORM) {
+    const float4 g0 = ((const float4*)(gamma + col0))[0], g1 = ((const float4*)(gamma + col0))[1];
+    g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w; g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+    if (beta) {
+      const float4 b0 = ((const float4*)(beta + col0))[0], b1 = ((const float4*)(beta + col0))[1];
+      bt[0] = b0.x; bt[1] = b0.y; bt[2] = b0.z; bt[3] = b0.w; bt[4] = b1.x; bt[5] = b1.y; bt[6] = b1.z; bt[7] = b1.w;
     }
+  }
+  int64_t r[8];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int v = v0 + 64 * b;
-      if (v >= nvec) continue;
-      const uint32_t gw[4] = {gv[b].x, gv[b].y, gv[b].z, gv[b].w};
-      uint32_t ow[4];
-      if (ur) {
-        const uint32_t uw[4] = {uv[b].x, uv[b].y, uv[b].z, uv[b].w};
+  for (int e = 0; e < 8; ++e) r[e] = c0 + e < rows ? (rowmap ? rowmap[c0 + e] : c0 + e) : -1;
+  uint4 v[8], v2[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    v[e] = r[e] >= 0 ? *(const uint4*)(x + r[e] * ld_x + col0) : make_uint4(0, 0, 0, 0);
+    if constexpr (OP == COL_SWIGLU)
+      v2[e] = r[e] >= 0 ? *(const uint4*)(x2 + r[e] * ld_x + col0) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (r[e] < 0) {
+      u[e] = make_uint4(0, 0, 0, 0);
+      continue;
+    }
+    if constexpr (OP == COL_COPY) {
+      u[e] = v[e];
+    } else {
+      const uint32_t w[4] = {v[e].x, v[e].y, v[e].z, v[e].w};
+      uint32_t o[4];
+      if constexpr (OP == COL_NORM) {
+        const float mu = mean ? mean[r[e]] : 0.f, rs = rstd[r[e]];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          ow[i] = pack2bf(silu_f(bflo(gw[i])) * bflo(uw[i]), silu_f(bfhi(gw[i])) * bfhi(uw[i]));
+          o[i] = pack2bf((bflo(w[i]) - mu) * rs * g[2 * i] + bt[2 * i],
+                         (bfhi(w[i]) - mu) * rs * g[2 * i + 1] + bt[2 * i + 1]);
+      } else if constexpr (OP == COL_SWIGLU) {
+        const uint32_t w2[4] = {v2[e].x, v2[e].y, v2[e].z, v2[e].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o[i] = pack2bf(silu_f(bflo(w[i])) * bflo(w2[i]), silu_f(bfhi(w[i])) * bfhi(w2[i]));
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ow[i] = pack2bf(gelu_f(bflo(gw[i])), gelu_f(bfhi(gw[i])));
+        for (int i = 0; i < 4; ++i) o[i] = pack2bf(gelu_f(bflo(w[i])), gelu_f(bfhi(w[i])));
       }
-      out[v] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+      u[e] = make_uint4(o[0], o[1], o[2], o[3]);
     }
+  }
+  // transpose: t[j] holds column col0 + j of tokens c0 .. c0+7 (two tokens per dword)
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t d[4];
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr) {
+      const uint32_t lo = ((const uint32_t*)&u[2 * pr])[j >> 1];
+      const uint32_t hi = ((const uint32_t*)&u[2 * pr + 1])[j >> 1];
+      d[pr] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+    }
+    if (col0 + j < C) *(uint4*)(out + (int64_t)(col0 + j) * ldT + c0) = make_uint4(d[0], d[1], d[2], d[3]);
   }
 }
 
-collider_status launch_act_recompute(const uint16_t* g, const uint16_t* up, const int32_t* rowmap,
-                                     int rows, int I, uint16_t* a, hipStream_t s) {
-  if (rows <= 0) return COLLIDER_OK;
-  COLLIDER_LAUNCH("act_recompute", s,
-                  hipLaunchKernelGGL(act_recompute_kernel, dim3((rows + 3) / 4), dim3(256), 0, s,
-                                     g, up, rowmap, rows, I, a));
+collider_status launch_cols_recompute(int op, const uint16_t* x, int64_t ld_x, const uint16_t* x2,
+                                      const float* mean, const float* rstd, const float* gamma,
+                                      const float* beta, const int32_t* rowmap, int rows, int C,
+                                      uint16_t* out, int64_t ldT, hipStream_t s) {
+  if (ldT <= 0 || C <= 0) return COLLIDER_OK;
+  if (C % 8 || ldT % 8 || ld_x % 8 || ldT < rows) return COLLIDER_ERR_UNSUPPORTED;
+  dim3 grid((unsigned)((ldT + 127) / 128), (unsigned)((C + 127) / 128)), block(256);
+#define CR_CASE(OPV)                                                                          \
+  case OPV:                                                                                   \
+    COLLIDER_LAUNCH("cols_recompute", s,                                                      \
+                    hipLaunchKernelGGL(cols_recompute_kernel<OPV>, grid, block, 0, s, x, ld_x, x2, \
+                                       mean, rstd, gamma, beta, rowmap, rows, C, out, ldT));  \
+    break;
+  switch (op) {
+    CR_CASE(COL_COPY) CR_CASE(COL_NORM) CR_CASE(COL_SWIGLU) CR_CASE(COL_GELU)
+    default:
+      return COLLIDER_ERR_UNSUPPORTED;
+  }
+#undef CR_CASE
   return last_hip_status();
 }
 
