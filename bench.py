@@ -17,6 +17,7 @@ CPU oracle timed on a bounded sample.
                     [--seq S [--tokens T]]      (long-context sweep: S per sequence, B = T / S)
                     [--loss-side [--vocab V]]   (the loss-side steps instead of the layer)
                     [--sparse-sweep]            (Figure 4: torch.sparse vs dense vs reduced GEMMs)
+                    [--index-sweep]             (mask -> index build time from 8192 to 4M tokens)
 """
 import argparse
 import json
@@ -442,6 +443,42 @@ def sparse_sweep_bench(args, cfg):
     return out
 
 
+def index_sweep_bench(args):
+    """Mask -> index over growing token counts (one sequence per 8192 tokens, 40% filtered by the
+    generator's top-k): microseconds per build, from HIP events around 50 back-to-back builds."""
+    import numpy as np
+    import torch
+
+    import synth
+    import token_filtered_backward_amd as tfb
+
+    rows = []
+    for M in (8192, 65536, 262144, 1 << 20, 1 << 22):
+        S = 8192
+        B = M // S
+        keep = torch.from_numpy(synth.make_keep(M, 40, args.seed)).cuda()
+        ix = tfb.build_index(keep, B, S)
+        n_keep = ix.M_kept
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(5):
+            tfb.build_index(keep, B, S, out=ix, expect=n_keep)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(50):
+            tfb.build_index(keep, B, S, out=ix, expect=n_keep)
+        e1.record()
+        e1.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 50
+        rows.append({"M": M, "B": B, "S": S, "us_per_build": round(us, 2),
+                     "GB_per_s": round(9.0 * M / (us * 1e-6) / 1e9, 1)})
+        log(f"[bench] index build M={M}: {us:.2f} us")
+    out = {"metric": "mask -> index build, us per call (back to back, kept count announced)", "unit": "us",
+           "n_gpus": 1, "higher_is_better": False, "data": "synthetic", "rows": rows,
+           "config": {"workload": "keep mask of M tokens, sequences of 8192, 40% filtered"}}
+    print(json.dumps(out), flush=True)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -467,6 +504,8 @@ def main():
                     help="time the loss-side steps (token selection, LM-head cross-entropy backward, "
                          "embedding gradient) at the config's token count and hidden size")
     ap.add_argument("--vocab", type=int, default=32000, help="vocabulary size for --loss-side")
+    ap.add_argument("--index-sweep", action="store_true",
+                    help="time the mask -> index build from 8192 to 4M tokens")
     ap.add_argument("--sparse-sweep", action="store_true",
                     help="Figure 4 on this GPU: torch.sparse vs dense GEMM vs the reduced GEMMs over a "
                          "filter-ratio sweep (gate/up projection of the config's layer)")
@@ -495,6 +534,9 @@ def main():
         return
     if args.sparse_sweep:
         sparse_sweep_bench(args, cfg)
+        return
+    if args.index_sweep:
+        index_sweep_bench(args)
         return
     if args.seq:
         tokens = args.tokens or cfg.M

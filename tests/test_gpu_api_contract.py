@@ -1,6 +1,6 @@
 """GPU checks of the C ABI's contract beyond numerics: flag values, the side-stream pool shared by
-host threads, graph replay on the caller's stream, and an index built with a wrong announced
-count (outputs unspecified, but every full-layout dx row written by one kernel only)."""
+host threads, the graph mode's stream rule, and an index built with a wrong announced count
+(outputs unspecified, but every full-layout dx row written by one kernel only)."""
 import threading
 
 import numpy as np
@@ -91,27 +91,16 @@ def test_side_stream_pool_shared_by_threads():
         assert torch.equal(_bits(again[k]), _bits(ref[k])), k
 
 
-def test_graph_replay_on_callers_stream():
-    """graph=True with an explicit stream captures and replays on that stream, after the work the
-    caller queued there (here: a kernel that rewrites dy just before the replay)."""
+def test_graph_mode_refuses_an_explicit_stream():
+    """graph=True captures and replays on the current stream; an explicit other stream is refused
+    before any work is done (a replay of the captured layer on a caller-supplied stream once ended
+    in a host crash inside the graph launch, cause not found, so that combination is not offered)."""
     cfg, inp, weights, saved, dy, ix, lcfg = _layer_setup()
-    dy2 = (dy.float() * 0.5).to(torch.bfloat16)
-    ref = tfb.layer_bwd(lcfg, weights, saved, dy2, ix)
-    torch.cuda.synchronize()
     s = torch.cuda.Stream()
     lb = tfb.LayerBackward(lcfg, cfg.B, cfg.S, "cuda")
-    dyb = dy.clone()
     g = tfb.make_grads(lcfg, cfg.M, ix.M_kept, "cuda")
-    for rep in range(3):
-        with torch.cuda.stream(s):
-            dyb.copy_(dy)
-        lb(weights, saved, dyb, ix, g, stream=s, graph=True)  # first call captures
-        with torch.cuda.stream(s):
-            dyb.copy_(dy2)
-        lb(weights, saved, dyb, ix, g, stream=s, graph=True)  # must see dy2
-        s.synchronize()
-        for k in ref:
-            assert torch.equal(_bits(g[k]), _bits(ref[k])), (rep, k)
+    with pytest.raises(ValueError):
+        lb(weights, saved, dy, ix, g, stream=s, graph=True)
 
 
 @pytest.mark.parametrize("delta", [5, -5])

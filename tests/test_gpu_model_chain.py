@@ -10,6 +10,7 @@ growth with depth is visible.
 The oracle runs in float32 here (its float32 results are checked against float64 in
 tests/test_oracle_loss_side.py; the float32 rounding error, about 1e-6 relative, is far below
 the 2e-2 bar) so that three layers of S = 8192 attention fit the test's time."""
+import os
 import time
 
 import numpy as np
@@ -83,9 +84,11 @@ def run_chain(n_layers, seed=0, r_pct=40):
     return grad_err, dx_err
 
 
-@pytest.mark.timeout(1500)
+@pytest.mark.timeout(3000)
 def test_long_context_stack_against_oracle():
-    grad_err, dx_err = run_chain(3)
+    # three layers by default (about a minute of host time); COLLIDER_CHAIN_LAYERS=22 runs the whole
+    # 22-layer stack (about eight minutes, mostly the host forward and the oracle)
+    grad_err, dx_err = run_chain(int(os.environ.get("COLLIDER_CHAIN_LAYERS", "3")))
     bad = {(k, li): e for k, v in grad_err.items() for li, e in enumerate(v) if not e <= BF16_TOL}
     bad.update({("dx", li): e for li, e in enumerate(dx_err) if not e <= BF16_TOL})
     assert not bad, bad

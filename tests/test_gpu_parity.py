@@ -36,7 +36,9 @@ def _dev_keep(keep):
 
 @pytest.mark.parametrize("B,S,pattern", [(1, 1, "all"), (1, 1, "none"), (1, 7, "none"), (3, 11, "rand"),
                                          (4, 2048, "topk"), (2, 4096, "topk"), (1, 8192, "topk"),
-                                         (5, 3001, "rand"), (1, 70000, "rand"), (2, 5, "all")])
+                                         (5, 3001, "rand"), (1, 70000, "rand"), (2, 5, "all"),
+                                         (1, 16384, "topk"), (1, 16385, "rand"), (3, 400001, "rand"),
+                                         (1024, 1024, "topk"), (1, 1 << 22, "rand")])
 def test_build_index_bit_exact(B, S, pattern):
     keep = _keep(B * S, pattern, seed=B + S)
     ix = tfb.build_index(_dev_keep(keep), B, S)
@@ -50,7 +52,7 @@ def test_build_index_bit_exact(B, S, pattern):
 
 
 @pytest.mark.parametrize("B,S,pattern", [(4, 2048, "topk"), (5, 3001, "rand"), (1, 70000, "rand"),
-                                         (1, 7, "none"), (2, 5, "all")])
+                                         (1, 7, "none"), (2, 5, "all"), (3, 400001, "rand")])
 @pytest.mark.parametrize("delta", [0, -5, 3])
 def test_build_index_with_announced_count(B, S, pattern, delta):
     """The index build that takes the kept count from the caller: with the true count it equals the

@@ -514,25 +514,27 @@ class LayerBackward:
         """graph=True records the call into a HIP graph on first use and replays it while every
         pointer and the kept count stay the same (one launch instead of the layer's ~30; with
         top-k selection the kept count is the same every step).  The index buffers must then be
-        reused across steps (build_index(..., out=index))."""
+        reused across steps (build_index(..., out=index)).  The graph is captured and replayed on
+        the current stream: graph=True does not take an explicit `stream` (make the stream current
+        with torch.cuda.stream(...) instead)."""
+        if graph and stream is not None and stream != torch.cuda.current_stream():
+            raise ValueError("graph=True replays on the current stream; pass no other stream "
+                             "(wrap the call in torch.cuda.stream(s) instead)")
         args = self._args(weights, saved, dy, index, grads, dy_compact, dx_compact)
         if not graph:
             _check(lib().collider_layer_bwd(*args, _stream(stream)), "collider_layer_bwd")
             return grads
-        run_on = torch.cuda.current_stream() if stream is None else stream
-        key = (self._key, run_on.cuda_stream)
+        key = (self._key, torch.cuda.current_stream().cuda_stream)
         if getattr(self, "_graph_key", None) != key:
             # one eager call first: the library's one-time set-up (side stream, kernel attributes)
             # must not happen inside the capture
-            _check(lib().collider_layer_bwd(*args, _stream(run_on)), "collider_layer_bwd")
+            _check(lib().collider_layer_bwd(*args, _stream()), "collider_layer_bwd")
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 _check(lib().collider_layer_bwd(*args, _stream()), "collider_layer_bwd")
             self._graph, self._graph_key = g, key
-        # the replay goes on the caller's stream, after the work already queued there
-        with torch.cuda.stream(run_on):
-            self._graph.replay()
+        self._graph.replay()  # on the current stream, after the work already queued there
         return grads
 
 

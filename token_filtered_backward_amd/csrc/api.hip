@@ -514,7 +514,7 @@ collider_status collider_lm_head_bwd(const void* logits, int64_t ld_logits, cons
 
 namespace {
 struct EmbWs {
-  int32_t *cnt, *off, *cursor, *sorted;
+  int32_t *cnt, *off, *cursor, *sorted, *hist;
   size_t bytes;
 };
 EmbWs carve_emb(int32_t Mk, int32_t V, void* base) {
@@ -524,6 +524,8 @@ EmbWs carve_emb(int32_t Mk, int32_t V, void* base) {
   w.off = cv.take<int32_t>((size_t)V + 1);
   w.cursor = cv.take<int32_t>((size_t)V);
   w.sorted = cv.take<int32_t>((size_t)(Mk > 0 ? Mk : 1));
+  const int chunks = embedding_hist_chunks(Mk, V);  // parallel placement when its histograms fit
+  w.hist = chunks ? cv.take<int32_t>((size_t)chunks * V) : nullptr;
   w.bytes = cv.bytes();
   return w;
 }
@@ -548,7 +550,7 @@ collider_status collider_embedding_bwd(const void* dx, int64_t ld_dx, int32_t dx
   EmbWs w = carve_emb(ix->M_kept, V, ws);
   if (!ws || ws_bytes < w.bytes) return COLLIDER_ERR_WORKSPACE;
   return launch_embedding_bwd((const uint16_t*)dx, ld_dx, dx_compact, ids, ix->idx, ix->M_kept, V, H,
-                              dE, accumulate, w.cnt, w.off, w.cursor, w.sorted, stream);
+                              dE, accumulate, w.cnt, w.off, w.cursor, w.sorted, stream, w.hist);
 }
 
 collider_status collider_embedding_bwd_noalloc(const void* dx, int64_t ld_dx, int32_t dx_compact,

@@ -108,11 +108,15 @@ collider_status launch_ce_grad(const uint16_t* logits, int64_t ld, const int32_t
 constexpr int kEmbScratchMaxV = 1 << 18;
 constexpr int kEmbScratchMaxRows = 1 << 20;
 collider_status embedding_scratch(int32_t** cnt, int32_t** off, int32_t** cursor, int32_t** sorted);
-// cnt, cursor: [V]; off: [V + 1]; sorted: [rows]
+// cnt, cursor: [V]; off: [V + 1]; sorted: [rows]; hist (may be null): [embedding_hist_chunks(rows,
+// V) * V], the per-chunk histograms of the parallel placement (used when that count is non-zero)
+constexpr int64_t kEmbHistMax = 1 << 22;
+int embedding_hist_chunks(int rows, int V);
 collider_status launch_embedding_bwd(const uint16_t* dx, int64_t ld, int dx_compact,
                                      const int32_t* ids, const int32_t* idx, int rows, int V, int H,
                                      float* dE, int accumulate, int32_t* cnt, int32_t* off,
-                                     int32_t* cursor, int32_t* sorted, hipStream_t s);
+                                     int32_t* cursor, int32_t* sorted, hipStream_t s,
+                                     int32_t* hist = nullptr);
 
 // rows.hip
 struct GatherDesc {

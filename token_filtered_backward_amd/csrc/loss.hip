@@ -426,6 +426,61 @@ __global__ __launch_bounds__(1024) void embed_place_kernel(const int32_t* __rest
   }
 }
 
+// The same placement spread over workgroups, one per chunk of kEmbChunk kept tokens.  A token's
+// place is off[id] + (tokens with its id in earlier chunks) + (tokens with its id earlier in its
+// own chunk).  The first term's per-chunk part comes from per-chunk id histograms (integer atomics:
+// the counts, not their order, are what is kept), turned into per-chunk starting positions by a
+// prefix over chunks; the last term from the chunk's ids in LDS, as above.  Used when the
+// histograms (chunks x V ints) fit the workspace.
+constexpr int kEmbChunk = 1024;
+
+__global__ __launch_bounds__(kEmbChunk) void embed_hist_kernel(const int32_t* __restrict__ ids,
+                                                                const int32_t* __restrict__ idx,
+                                                                int rows, int V,
+                                                                int32_t* __restrict__ hist) {
+  int32_t* h = hist + (int64_t)blockIdx.x * V;
+  for (int v = threadIdx.x; v < V; v += kEmbChunk) h[v] = 0;
+  __syncthreads();
+  const int c = blockIdx.x * kEmbChunk + threadIdx.x;
+  const int id = c < rows ? kept_id(ids, idx, c, V) : -1;
+  if (id >= 0) atomicAdd(&h[id], 1);
+}
+
+// hist[j][v] <- off[v] + sum of hist[j'][v] over j' < j (exclusive prefix over chunks, in place)
+__global__ __launch_bounds__(256) void embed_hist_prefix_kernel(const int32_t* __restrict__ off,
+                                                                int V, int chunks,
+                                                                int32_t* __restrict__ hist) {
+  const int v = blockIdx.x * 256 + threadIdx.x;
+  if (v >= V) return;
+  int acc = off[v];
+  for (int j = 0; j < chunks; ++j) {
+    const int64_t e = (int64_t)j * V + v;
+    const int t = hist[e];
+    hist[e] = acc;
+    acc += t;
+  }
+}
+
+__global__ __launch_bounds__(kEmbChunk) void embed_place_chunks_kernel(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ idx, int rows, int V,
+    const int32_t* __restrict__ hist, int32_t* __restrict__ sorted) {
+  __shared__ __align__(16) int32_t s_id[kEmbChunk];
+  const int tid = threadIdx.x;
+  const int c = blockIdx.x * kEmbChunk + tid;
+  const int id = c < rows ? kept_id(ids, idx, c, V) : -1;
+  s_id[tid] = id;
+  __syncthreads();
+  if (id < 0) return;
+  int r = 0;
+  const int4* s4 = (const int4*)s_id;
+  for (int j4 = 0; j4 < (tid >> 2); ++j4) {
+    const int4 q = s4[j4];
+    r += (q.x == id) + (q.y == id) + (q.z == id) + (q.w == id);
+  }
+  for (int j = tid & ~3; j < tid; ++j) r += s_id[j] == id ? 1 : 0;
+  sorted[hist[(int64_t)blockIdx.x * V + id] + r] = c;
+}
+
 // dE[v, :] (+)= sum over j < off[v+1] - off[v] of dx[row(sorted[off[v] + j]), :]; one wavefront per
 // vocabulary row, 8 columns per lane per step; rows with no kept token are written as zeros
 // (or left as they are when accumulating).
@@ -511,21 +566,39 @@ collider_status embedding_scratch(int32_t** cnt, int32_t** off, int32_t** cursor
   return COLLIDER_OK;
 }
 
+int embedding_hist_chunks(int rows, int V) {
+  const int64_t chunks = ((int64_t)rows + kEmbChunk - 1) / kEmbChunk;
+  return (chunks >= 2 && chunks * V <= kEmbHistMax) ? (int)chunks : 0;
+}
+
 collider_status launch_embedding_bwd(const uint16_t* dx, int64_t ld, int dx_compact,
                                      const int32_t* ids, const int32_t* idx, int rows, int V, int H,
                                      float* dE, int accumulate, int32_t* cnt, int32_t* off,
-                                     int32_t* cursor, int32_t* sorted, hipStream_t s) {
+                                     int32_t* cursor, int32_t* sorted, hipStream_t s,
+                                     int32_t* hist) {
+  const int chunks = hist ? embedding_hist_chunks(rows, V) : 0;
   COLLIDER_LAUNCH("embed_fill", s,
                   hipLaunchKernelGGL(fill_i32_kernel, dim3((V + 255) / 256), dim3(256), 0, s, cnt, V, 0));
-  COLLIDER_LAUNCH("embed_fill", s,
-                  hipLaunchKernelGGL(fill_i32_kernel, dim3((V + 255) / 256), dim3(256), 0, s, cursor, V, 0));
+  if (chunks == 0)
+    COLLIDER_LAUNCH("embed_fill", s,
+                    hipLaunchKernelGGL(fill_i32_kernel, dim3((V + 255) / 256), dim3(256), 0, s, cursor, V, 0));
   if (rows > 0)
     COLLIDER_LAUNCH("embed_count", s,
                     hipLaunchKernelGGL(embed_count_kernel, dim3((rows + 255) / 256), dim3(256), 0, s,
                                        ids, idx, rows, V, cnt));
   COLLIDER_LAUNCH("embed_scan", s,
                   hipLaunchKernelGGL(embed_scan_kernel, dim3(1), dim3(1024), 0, s, cnt, V, off));
-  if (rows > 0 && V <= kCursorLds) {
+  if (chunks > 0) {
+    COLLIDER_LAUNCH("embed_place", s,
+                    hipLaunchKernelGGL(embed_hist_kernel, dim3(chunks), dim3(kEmbChunk), 0, s, ids, idx,
+                                       rows, V, hist));
+    COLLIDER_LAUNCH("embed_place", s,
+                    hipLaunchKernelGGL(embed_hist_prefix_kernel, dim3((V + 255) / 256), dim3(256), 0, s,
+                                       off, V, chunks, hist));
+    COLLIDER_LAUNCH("embed_place", s,
+                    hipLaunchKernelGGL(embed_place_chunks_kernel, dim3(chunks), dim3(kEmbChunk), 0, s,
+                                       ids, idx, rows, V, hist, sorted));
+  } else if (rows > 0 && V <= kCursorLds) {
     if (!place_lds_limit_set()) return COLLIDER_ERR_HIP;
     COLLIDER_LAUNCH("embed_place", s,
                     hipLaunchKernelGGL(embed_place_kernel<true>, dim3(1), dim3(1024), V * 4, s, ids, idx,
