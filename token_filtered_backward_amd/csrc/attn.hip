@@ -115,16 +115,20 @@ __device__ __forceinline__ int64_t src_row(const AttnParams& p, int c) {
 
 // Source rows of this thread's 16-byte chunks of a 64-row tile (tile rows row0 .. row0+63 of a
 // sequence starting at compacted row `base`; -1 past its nrows rows), looked up through `map` -
-// one tile ahead of the loads that use them, so that the lookup's latency is hidden.
+// one tile ahead of the loads that use them, so that the lookup's latency is hidden.  The rows stay
+// 32-bit until a load uses them: widening them here would make the wavefront wait for the lookup
+// (and for every load issued before it, the prefetch of the current tile included) at once.
 template <int D>
 struct TileRows {
-  int64_t r[TokTile<D>::NV];
+  int32_t r[TokTile<D>::NV];
   __device__ __forceinline__ void set(const int32_t* __restrict__ map, int base, int row0, int nrows) {
 #pragma unroll
     for (int i = 0; i < TokTile<D>::NV; ++i) {
       const int c = threadIdx.x + 256 * i;
       const int rr = row0 + c / (D / 8);
-      r[i] = rr < nrows ? (map ? (int64_t)map[base + rr] : (int64_t)(base + rr)) : -1;
+      int v = -1;
+      if (rr < nrows) v = map ? map[base + rr] : base + rr;
+      r[i] = v;
     }
   }
 };
@@ -149,7 +153,8 @@ struct TileRegs {
 #pragma unroll
     for (int i = 0; i < TokTile<D>::NV; ++i) {
       const int dc = (threadIdx.x + 256 * i) % (D / 8);
-      v[i] = t.r[i] >= 0 ? *(const uint4*)(src + t.r[i] * ld + col0 + dc * 8) : make_uint4(0, 0, 0, 0);
+      v[i] = t.r[i] >= 0 ? *(const uint4*)(src + (int64_t)t.r[i] * ld + col0 + dc * 8)
+                         : make_uint4(0, 0, 0, 0);
     }
   }
   __device__ __forceinline__ void store(char* T) const {
@@ -447,21 +452,29 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_dkv_kernel(AttnPara
   // source rows of the Q tile and of the lse entry (threads < BQ) the next fetch reads, looked up
   // one iteration ahead of it
   TileRows<D> tq;
-  int64_t lrow = -1;
+  int32_t lrow = -1;  // 32-bit until used, as in TileRows
   auto rows_of = [&](int it) {
     const int i0 = (qb0 + it % per_head) * BQ;
     tq.set(p.srcmap, cs, i0, nb);
-    if (threadIdx.x < BQ) lrow = i0 + (int)threadIdx.x < nb ? src_row(p, cs + i0 + threadIdx.x) : -1;
+    lrow = -1;
+    if (threadIdx.x < BQ && i0 + (int)threadIdx.x < nb) {
+      const int c = cs + i0 + (int)threadIdx.x;
+      lrow = p.srcmap ? p.srcmap[c] : c;
+    }
   };
   auto fetch = [&](int it) {
     const int h = g * p.G + hs * GH + it / per_head;
     const int i0 = (qb0 + it % per_head) * BQ;
     rq.load(p.q, p.ld_q, h * D, tq);
     ro.load(doseq, p.ld_do, h * D, i0, nb);
+    // raw values: scaling them here would make the wavefront wait for these loads, and for the
+    // tile loads above them, before the current tile's work
     if (threadIdx.x < BQ) {
       const int i = i0 + threadIdx.x;
-      sl = lrow >= 0 ? p.lse[lrow * p.ld_lse + h] * kLog2e : 0.f;
-      sd = i < nb ? -p.Dbuf[(int64_t)(cs + i) * p.nq + h] : 0.f;  // -D: the dP accumulator's start
+      sl = 0.f;
+      sd = 0.f;
+      if (lrow >= 0) sl = p.lse[(int64_t)lrow * p.ld_lse + h];
+      if (i < nb) sd = p.Dbuf[(int64_t)(cs + i) * p.nq + h];
     }
   };
   auto put = [&](int buf) {
@@ -469,8 +482,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_dkv_kernel(AttnPara
     rq.store(base);
     ro.store(base + TB);
     if (threadIdx.x < BQ) {
-      ((float*)(base + 2 * TB))[threadIdx.x] = sl;
-      ((float*)(base + 2 * TB + BQ * 4))[threadIdx.x] = sd;
+      ((float*)(base + 2 * TB))[threadIdx.x] = sl * kLog2e;
+      ((float*)(base + 2 * TB + BQ * 4))[threadIdx.x] = -sd;  // -D: the dP accumulator's start
     }
   };
 
