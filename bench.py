@@ -49,8 +49,12 @@ def algorithmic_work(cfg, M_kept, seq_counts):
     gemm_flops = 4.0 * M_kept * proj                      # dX and dW: 2 * M' * K * N each
     pairs = sum(n * (n + 1) // 2 for n in seq_counts)     # causal kept (query, key) pairs per head
     attn_flops = 10.0 * d * nq * pairs                    # S, dP, dV, dK, dQ
-    attn_dt_flops = 4.0 * d * nq * pairs                  # the filtered softmax-backward row term
-    gather_bytes = 2.0 * M_kept * (2 * H + 2 * 2 * nq * d + 2 * 2 * nkv * d + 4 * nq)
+    # the filtered softmax-backward row term (reading A): accumulated in the dQ kernel's one sweep,
+    # whose only extra matrix work is sum_j P_ij K_j
+    attn_dt_flops = 2.0 * d * nq * pairs
+    # the one gather left: dY's kept rows (read + write); attention and the recompute kernels read
+    # the other saved tensors through the index
+    gather_bytes = 2.0 * M_kept * 2 * H
     # reduced-GEMM bytes: bf16 operands read once, outputs written once (bf16 dX, fp32 dW), plus
     # the activation-backward epilogue's reads of the saved pre-activations
     Mk, nqd = M_kept, nq * d
@@ -71,7 +75,8 @@ def algorithmic_work(cfg, M_kept, seq_counts):
                       2 * (Mk * (nqkv + I) + (nqkv + I) * H + Mk * H),     # dX (qkv and fc1)
                       2 * Mk * nqkv + 2 * Mk * H + 4 * nqkv * H,           # dW qkv
                       2 * Mk * I + 2 * Mk * H + 4 * I * H]                 # dW fc1
-    scatter_bytes = 2.0 * M_kept * H + 2.0 * cfg.M * H  # kept rows read, every row written
+    # the scatter writes +0.0 to the filtered rows of dx; the last norm backward writes the kept rows
+    scatter_bytes = 2.0 * (cfg.M - M_kept) * H
     return {"gemm_flops": gemm_flops, "attn_flops": attn_flops, "attn_dt_flops": attn_dt_flops,
             "pairs": pairs, "gather_bytes": gather_bytes, "scatter_bytes": scatter_bytes,
             "gemm_bytes": float(sum(gemm_bytes)),
@@ -201,8 +206,8 @@ def loss_side_bench(args, cfg, emit=True):
     """The loss-side steps of one batch: logits -> per-token cross-entropy loss of every token ->
     keep mask (device top-k on the loss) -> index -> LM-head cross-entropy backward over the kept
     tokens (dh stays compact for the top layer) -> embedding gradient from the bottom layer's
-    compact dx.  Unfiltered: the same LM-head and embedding backward over every token (no per-token
-    loss, selection or index)."""
+    compact dx.  Unfiltered: the per-token loss (a training step computes it either way) and the
+    same LM-head and embedding backward over every token (no selection or index)."""
     import numpy as np
     import torch
 
@@ -246,6 +251,7 @@ def loss_side_bench(args, cfg, emit=True):
         tfb.collider_embedding_bwd(dx, ids, c, dE, dx_compact=True, ws=ws_e)
 
     def step_unf():
+        tfb.collider_ce_loss(logits, labels, loss)
         c = uix.c()
         tfb.collider_lm_head_bwd(logits, labels, h, w_lm, c, 1.0 / M, dh_u, dw, dh_compact=True, ws=ws_lm)
         tfb.collider_embedding_bwd(dx_full, ids, c, dE, dx_compact=True, ws=ws_e)
@@ -285,8 +291,8 @@ def loss_side_bench(args, cfg, emit=True):
     emb_bytes = 4.0 * V * H + 2.0 * n_keep * H
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None
     out = {
-        "metric": "loss-side bwd ms (token selection, LM-head cross-entropy bwd, embedding grad) at "
-                  f"{args.r}% filter",
+        "metric": "loss-side bwd ms (per-token loss, token selection, LM-head cross-entropy bwd, "
+                  f"embedding grad) at {args.r}% filter",
         "value": round(ms_f, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_f, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
@@ -719,15 +725,17 @@ def main():
     cu = ix.cu_seqlens.cpu().numpy()
     seq_counts = [int(cu[b + 1] - cu[b]) for b in range(B)]
     work = algorithmic_work(cfg, ix.M_kept, seq_counts)
-    if L > 1:  # every layer's GEMMs and attention; dY gathered by the top layer only
-        dy_bytes = 2.0 * ix.M_kept * 2 * cfg.H
+    if L > 1:  # every layer's GEMMs and attention; dY gathered by the top layer only, dx
+        # scattered by the bottom one
         work = dict(work, gemm_flops=L * work["gemm_flops"], attn_flops=L * work["attn_flops"],
                     attn_dt_flops=L * work["attn_dt_flops"],
-                    gather_bytes=L * (work["gather_bytes"] - dy_bytes) + dy_bytes,
                     gemm_bytes=L * work["gemm_bytes"], gemm_launches=L * work["gemm_launches"])
     gemm_tflops = work["gemm_flops"] / (gemm_ms * 1e-3) / 1e12
     attn_ms = sum(prof[k][0] for k in prof if k.startswith("attn_")) / n_prof
-    attn_tflops = (work["attn_flops"] + work["attn_dt_flops"]) / (attn_ms * 1e-3) / 1e12 if attn_ms else None
+    # the P K product runs only under reading A with some token filtered (with every token kept the
+    # layer takes D = dO . O, which then equals D~)
+    dt_flops = work["attn_dt_flops"] if (args.dmode == "filtered" and ix.M_kept < cfg.M) else 0.0
+    attn_tflops = (work["attn_flops"] + dt_flops) / (attn_ms * 1e-3) / 1e12 if attn_ms else None
     gather_ms = prof.get("gather_rows", (0.0, 1))[0] / n_prof
     gather_gbs = work["gather_bytes"] / (gather_ms * 1e-3) / 1e9 if gather_ms else None
     scatter_ms = prof.get("scatter_rows", (0.0, 1))[0] / n_prof
@@ -770,7 +778,7 @@ def main():
         "scatter_gbs": None if scatter_gbs is None else round(scatter_gbs, 1),
         "hbm_frac_gather": None if gather_gbs is None else round(gather_gbs / PEAK_HBM_GBS, 4),
         "hbm_frac_scatter": None if scatter_gbs is None else round(scatter_gbs / PEAK_HBM_GBS, 4),
-        "copy_gbs_cold_same_bytes_as_gather": round(copy_rate_cold(work["gather_bytes"] / max(L, 1)), 1),
+        "copy_gbs_cold_same_bytes_as_gather": round(copy_rate_cold(work["gather_bytes"]), 1),
         "kernel_ms_per_step": kernels,
         "kernel_ms_per_step_unfiltered": kernels_unf,
         "roofline": {

@@ -42,8 +42,9 @@ def test_algorithmic_work_counts():
     pairs = 4 * 1229 * 1230 // 2
     assert w["pairs"] == pairs
     assert w["attn_flops"] == 10.0 * d * nq * pairs
-    assert w["attn_dt_flops"] == 4.0 * d * nq * pairs
-    # gathered per kept token: dY (2H B) + q, o (2 x 2 nq d B) + k, v (2 x 2 nkv d B) + lse (4 nq B)
-    row = 2 * H + 2 * 2 * nq * d + 2 * 2 * nkv * d + 4 * nq
-    assert row == 13440 and w["gather_bytes"] == 2.0 * Mk * row
+    assert w["attn_dt_flops"] == 2.0 * d * nq * pairs             # the extra P K product
+    # gathered per kept token: dY's row (2H B), read and written; the rest is read through idx
+    assert w["gather_bytes"] == 2.0 * Mk * 2 * H
+    # scatter: +0.0 written to each filtered row of dx
+    assert w["scatter_bytes"] == 2.0 * (4 * 2048 - Mk) * H
     assert w["gemm_launches"] == 8

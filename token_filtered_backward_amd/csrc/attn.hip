@@ -243,6 +243,7 @@ __global__ __launch_bounds__(256, D == 64 ? (FULLD ? 3 : 2) : 1) void attn_dq_ke
   const bool qvalid = iq < nb;
   const int qw = q0 + wave * 32;     // first query of this wave
   const bool qall = qw + 31 < nb;    // all 32 queries of the wave exist
+  const int jlim = qw < nb ? min(qw + 31, nb - 1) : -1;  // last key any query of the wave sees
   const int64_t qrow = qvalid ? src_row(p, cs + iq) : 0;  // this lane's query in q, o, lse
 
   bf16x8 qf[KK], dof[KK];
@@ -303,6 +304,8 @@ __global__ __launch_bounds__(256, D == 64 ? (FULLD ? 3 : 2) : 1) void attn_dq_ke
     }
 #pragma unroll
     for (int jt = 0; jt < BKV / 32; ++jt) {
+      // 32 keys past every valid query of this wave: all masked, nothing to add (wave-uniform)
+      if (kb * BKV + jt * 32 > jlim) continue;
       f32x16 st, dpt;
       score_tiles<D>(Ks, Ks + TB, qf, dof, jt, lane, st, dpt);
       float pr[16], x[16];
@@ -507,6 +510,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_dkv_kernel(AttnPara
     }
 #pragma unroll
     for (int t2 = 0; t2 < BQ / 32; ++t2) {
+      // 32 queries that all precede every key of this wave, or none of which exists: all masked,
+      // nothing to add (wave-uniform)
+      if (i0 + t2 * 32 + 31 < kw || i0 + t2 * 32 >= nb) continue;
       // dP accumulates onto -D_i (rows of the tile are queries 8*r4 + 4*hl + q), so that it comes
       // out of the MFMAs as dP - D
       f32x16 s, dp;

@@ -262,8 +262,12 @@ collider_status launch_ce_grad(const uint16_t* logits, int64_t ld, const int32_t
 // ------------------------------------------------------------------------------------------
 // per-token cross-entropy loss over every token: loss_t = logsumexp(z_t) - z_t[y_t] (0 without a
 // target).  It is the score backward token filtering ranks tokens by (Figure 2(b)).  One
-// workgroup per row; the row is read once, four 16-byte vectors in flight per thread.
+// workgroup per row, the row read once.  Rows of up to NV * 2048 logits are loaded whole into
+// registers first (every load of the row in flight at once, together with the label's own logit);
+// longer rows (NV = 0) stream through four 16-byte vectors per thread at a time.  Each thread
+// folds its vectors in the same order either way, so the result does not depend on the path.
 // ------------------------------------------------------------------------------------------
+template <int NV>
 __global__ __launch_bounds__(256) void ce_loss_kernel(const uint16_t* __restrict__ logits, int64_t ld,
                                                       const int32_t* __restrict__ labels, int V,
                                                       float* __restrict__ loss) {
@@ -276,14 +280,29 @@ __global__ __launch_bounds__(256) void ce_loss_kernel(const uint16_t* __restrict
     return;
   }
   const int nvec = V >> 3;
-  const uint4* src = (const uint4*)(logits + t * ld);
+  const uint16_t* row = logits + t * ld;
+  const uint4* src = (const uint4*)row;
+  float zy = 0.f;
+  if (tid == 0) zy = bf2f(row[y]);
   MaxSum ms{-INFINITY, 0.f};
-  int i = tid;
-  for (; i + 3 * 256 < nvec; i += 4 * 256) {
-    const uint4 a = src[i], b = src[i + 256], c = src[i + 512], d = src[i + 768];
-    ms = ms_add8(ms_add8(ms_add8(ms_add8(ms, a), b), c), d);
+  if constexpr (NV > 0) {
+    uint4 v[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (tid + 256 * u < nvec) v[u] = src[tid + 256 * u];
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u)
+      if (tid + 256 * u < nvec) ms = ms_add8(ms, v[u]);
+  } else {
+    int i = tid;
+    for (; i + 3 * 256 < nvec; i += 4 * 256) {
+      const uint4 a = src[i], b = src[i + 256], c = src[i + 512], d = src[i + 768];
+      ms = ms_add8(ms_add8(ms_add8(ms_add8(ms, a), b), c), d);
+    }
+    for (; i < nvec; i += 256) ms = ms_add8(ms, src[i]);
   }
-  for (; i < nvec; i += 256) ms = ms_add8(ms, src[i]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1)
     ms = ms_merge(ms, MaxSum{__shfl_xor(ms.m, off, 64), __shfl_xor(ms.s, off, 64)});
@@ -295,15 +314,27 @@ __global__ __launch_bounds__(256) void ce_loss_kernel(const uint16_t* __restrict
     for (int w = 1; w < 4; ++w) ms = ms_merge(ms, s_ms[w]);
     // log-sum-exp in natural-log units: (m + log2 s) ln 2, m and s in base-2 units
     const float lse = (ms.m + __builtin_amdgcn_logf(ms.s)) * 0.6931471805599453f;
-    loss[t] = lse - bf2f(logits[t * ld + y]);
+    loss[t] = lse - zy;
   }
 }
 
 collider_status launch_ce_loss(const uint16_t* logits, int64_t ld, const int32_t* labels, int M, int V,
                                float* loss, hipStream_t s) {
   if (M <= 0) return COLLIDER_OK;
-  COLLIDER_LAUNCH("ce_loss", s, hipLaunchKernelGGL(ce_loss_kernel, dim3(M), dim3(256), 0, s, logits,
-                                                   ld, labels, V, loss));
+  const int nvec = V >> 3;
+  if (nvec <= 256 * 8) {
+    COLLIDER_LAUNCH("ce_loss", s, hipLaunchKernelGGL(ce_loss_kernel<8>, dim3(M), dim3(256), 0, s,
+                                                     logits, ld, labels, V, loss));
+  } else if (nvec <= 256 * 16) {
+    COLLIDER_LAUNCH("ce_loss", s, hipLaunchKernelGGL(ce_loss_kernel<16>, dim3(M), dim3(256), 0, s,
+                                                     logits, ld, labels, V, loss));
+  } else if (nvec <= 256 * 32) {
+    COLLIDER_LAUNCH("ce_loss", s, hipLaunchKernelGGL(ce_loss_kernel<32>, dim3(M), dim3(256), 0, s,
+                                                     logits, ld, labels, V, loss));
+  } else {
+    COLLIDER_LAUNCH("ce_loss", s, hipLaunchKernelGGL(ce_loss_kernel<0>, dim3(M), dim3(256), 0, s,
+                                                     logits, ld, labels, V, loss));
+  }
   return last_hip_status();
 }
 
