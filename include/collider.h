@@ -303,8 +303,9 @@ collider_status collider_select_keep(const float* score, int32_t M, int32_t n_ke
  * h is the bf16 [M, H] input of the LM head (full layout, row stride ld_h); labels int32 [M].
  * Requirements: H and V multiples of 8, 16-byte alignment of every bf16 pointer and leading
  * dimension (COLLIDER_ERR_ALIGN otherwise), ix from collider_build_index with M_kept set.
- * The workspace (collider_lm_head_workspace_bytes) holds h' and dlogits' ([M_kept, V] bf16) and
- * GEMM partials; it must not alias any input or output. */
+ * The workspace (collider_lm_head_workspace_bytes) holds h' transposed ([H, M_kept rounded up to
+ * 64] bf16, the weight gradient's operand with its tokens contiguous), dlogits' ([M_kept, V] bf16)
+ * and GEMM partials; it must not alias any input or output. */
 size_t collider_lm_head_workspace_bytes(int32_t M_kept, int32_t H, int32_t V);
 collider_status collider_lm_head_bwd(const void* logits, int64_t ld_logits, const int32_t* labels,
                                      const void* h, int64_t ld_h, const void* w_lm,

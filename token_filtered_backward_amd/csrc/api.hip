@@ -439,21 +439,37 @@ collider_status collider_select_keep(const float* score, int32_t M, int32_t n_ke
 
 namespace {
 struct LmHeadWs {
-  uint16_t *h_c, *dl, *dh_c;
+  uint16_t *hT, *dl, *dh_c;
+  int ldT;
   char* gws;
   size_t gws_bytes, bytes;
 };
 
+// The LM head's two reduced GEMMs: dh' = dlogits' w_lm (A K-contiguous, B = w_lm [V, H]) and
+// dW_lm = dlogits'^T h'.  h' reaches the second transposed, [H, ldT] with its tokens contiguous
+// (ldT = M' rounded up to 64, zero columns past M'), so that its reduction runs along memory.
+void lm_head_problems(int32_t Mk, int32_t H, int32_t V, const uint16_t* hT, int ldT,
+                      const uint16_t* dl, const void* w_lm, void* dh_c, float* dw_lm,
+                      int32_t accumulate, GemmProblem* pdh, GemmProblem* pdw) {
+  linear_problems(COLLIDER_BF16, Mk, H, V, nullptr, H, dl, V, w_lm, dh_c, dw_lm, accumulate, pdh, pdw);
+  pdw->B0 = hT; pdw->ldb = ldT; pdw->b_kmajor = true; pdw->b_kpad = true;
+  pdh->name = "lm_head_dh";
+  pdw->name = "lm_head_dw";
+  // whole-tile plans: for dh' the cost model (calibrated on the layer's reduction lengths) picks
+  // stream-K 256 x 256 tiles, but with the vocabulary-long reduction whole 160-row tiles measured
+  // 0.55 ms against 0.76 ms (B 4 x S 2048, hidden 2048, vocab 32000, 40% filtered)
+  pdh->concurrent = pdw->concurrent = true;
+}
+
 LmHeadWs carve_lm_head(int32_t Mk, int32_t H, int32_t V, void* base) {
-  GemmProblem a, b;
-  linear_problems(COLLIDER_BF16, Mk, H, V, nullptr, H, nullptr, V, nullptr, nullptr, nullptr, 0, &a,
-                  &b);
   Carver cv(base);
   LmHeadWs w;
-  w.h_c = cv.take<uint16_t>((size_t)Mk * H);
+  w.ldT = (Mk + 63) / 64 * 64;
+  w.hT = cv.take<uint16_t>((size_t)H * w.ldT);
   w.dl = cv.take<uint16_t>((size_t)Mk * V);
   w.dh_c = cv.take<uint16_t>((size_t)Mk * H);
-  a.concurrent = b.concurrent = true;  // the plans collider_lm_head_bwd runs
+  GemmProblem a, b;
+  lm_head_problems(Mk, H, V, nullptr, w.ldT, nullptr, nullptr, nullptr, nullptr, 0, &a, &b);
   w.gws_bytes = std::max(gemm_bf16_workspace_bytes(a), gemm_bf16_workspace_bytes(b));
   w.gws = cv.take<char>(w.gws_bytes);
   w.bytes = cv.bytes();
@@ -489,20 +505,16 @@ collider_status collider_lm_head_bwd(const void* logits, int64_t ld_logits, cons
   if (!ws || ws_bytes < w.bytes) return COLLIDER_ERR_WORKSPACE;
   uint16_t* dh_c = dh_compact ? (uint16_t*)dh : w.dh_c;
   if (Mk > 0) {
-    GatherDesc gd{h, w.h_c, ld_h * 2 / 16, (int64_t)H * 2 / 16, H * 2 / 16, 0};
-    if ((st = launch_gather_rows(&gd, 1, ix->idx, Mk, stream)) != COLLIDER_OK) return st;
+    // h's kept rows, transposed (the weight gradient's operand), read through the index
+    st = launch_cols_recompute(COL_COPY, (const uint16_t*)h, ld_h, nullptr, nullptr, nullptr, nullptr,
+                               nullptr, ix->idx, Mk, H, w.hT, w.ldT, stream);
+    if (st != COLLIDER_OK) return st;
     st = launch_ce_grad((const uint16_t*)logits, ld_logits, labels, ix->idx, Mk, V, loss_scale, w.dl,
                         V, stream);
     if (st != COLLIDER_OK) return st;
   }
   GemmProblem pdh, pdw;
-  linear_problems(COLLIDER_BF16, Mk, H, V, w.h_c, H, w.dl, V, w_lm, dh_c, dw_lm, accumulate, &pdh, &pdw);
-  pdh.name = "lm_head_dh";
-  pdw.name = "lm_head_dw";
-  // whole-tile plans: for dh' the cost model (calibrated on the layer's reduction lengths) picks
-  // stream-K 256 x 256 tiles, but with the vocabulary-long reduction whole 160-row tiles measured
-  // 0.55 ms against 0.76 ms (B 4 x S 2048, hidden 2048, vocab 32000, 40% filtered)
-  pdh.concurrent = pdw.concurrent = true;
+  lm_head_problems(Mk, H, V, w.hT, w.ldT, w.dl, w_lm, dh_c, dw_lm, accumulate, &pdh, &pdw);
   if (Mk > 0 && (st = gemm_bf16(pdh, w.gws, w.gws_bytes, stream)) != COLLIDER_OK) return st;
   if ((st = gemm_bf16(pdw, w.gws, w.gws_bytes, stream)) != COLLIDER_OK) return st;
   if (!dh_compact)  // full layout: kept rows from dh', filtered rows +0.0
