@@ -25,6 +25,8 @@
 // transpose reads per fragment follows the 32x32 accumulator layout (rows 8*(r/4) + 4*(lane/32) +
 // r%4), so the P / dS registers feed the MFMA without any data movement.  The next tile is fetched
 // into registers while the MFMAs of the current one run (two LDS buffers, one barrier per tile).
+// Inside the layer the kernels read q, k, v, o and lse of the full token layout through the index
+// (row idx[c] for compacted row c), looked up a tile ahead of the loads that use them.
 #include <cstdlib>
 
 #include "internal.h"

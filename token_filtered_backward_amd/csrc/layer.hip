@@ -1,7 +1,8 @@
 // Whole-layer filtered backward (Collider paper, abstract: the activations of filtered tokens are
 // filtered across all layers; every linear backward becomes a dense GEMM over the kept tokens).
 //
-// The sequence of launches for one layer, all on one stream, no host synchronisation:
+// The work of one layer, no host synchronisation (the weight-gradient side of it runs on a side
+// stream, see layer_run):
 //   gather   dY' (the saved tensors stay in the full layout; their consumers read them through
 //            the index)
 //   LLAMA                                         PHI (parallel block)
@@ -15,9 +16,12 @@
 //   attention bwd -> [dq|dk|dv]                   dx = dY' + LayerNorm bwd(dXn)
 //   dXn1 = [dq|dk|dv] w_qkv; dw_qkv = (...)^T xn1'
 //   dx = dh + RMSNorm1 bwd(dXn1)
-//   scatter dx to the full layout (filtered rows +0.0) unless the caller keeps it compact.
-// Normalised inputs (xn1', xn2') and activations (a', g') are recomputed from saved tensors read
-// through the index; the SwiGLU / GELU backward is fused into the epilogue of the GEMM producing dA.
+//   the last norm backward writes dx's kept rows (compact, or in place in the full layout, whose
+//   filtered rows get +0.0).
+// Normalised inputs (xn1', xn2'), activations (a', g') and the attention output O' are recomputed
+// or copied from saved tensors read through the index, and written transposed (tokens contiguous)
+// for the weight-gradient GEMMs; the SwiGLU / GELU backward is fused into the epilogue of the GEMM
+// producing dA.
 #include <algorithm>
 #include <cstdlib>
 #include <mutex>
@@ -320,11 +324,10 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     if (st != COLLIDER_OK) return st;  \
   } while (0)
 
-  // Weight-gradient GEMMs, the inputs only they read (normalised / activated saved tensors) and
-  // the gathers attention needs later run on a side stream, forked from and joined back to the
-  // caller's stream with events: the memory-bound work there overlaps the dX chain's GEMMs, and
-  // the critical path dA -> dX -> norm bwd -> dO -> attention -> dX -> norm bwd -> scatter stays
-  // on `s`.
+  // Weight-gradient GEMMs, the operands only they read (normalised / activated / copied saved
+  // tensors, written transposed) and the gain gradients run on a side stream, forked from and
+  // joined back to the caller's stream with events: that work fills what the dX chain leaves idle,
+  // and the critical path dA -> dX -> norm bwd -> dO -> attention -> dX -> norm bwd stays on `s`.
   SideLease lease;
   CHECK(side_acquire(&lease.sd));
   Side* side = lease.sd;
@@ -342,7 +345,7 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
   if (dx_full)  // the filtered rows of dx: +0.0 (the kept rows come from the last norm backward)
     CHECK(launch_scatter_bytes(nullptr, 0, gr->dx, (int64_t)H * 2, ix.inv, M, H * 2, 2, s1));
   // the rotary table attention reads (S and the rotary configuration only), off the critical path;
-  // attention waits on the event recorded after the gathers below
+  // attention waits on the event recorded after it
   CHECK(attn_rope_prepare(ac, aix, b.attn_ws, b.attn_ws_bytes, s1));
   if (side && hipEventRecord(side->ev[6], s1) != hipSuccess) return COLLIDER_ERR_HIP;
   collider_attn_io io{};  // saved tensors in the full layout, rows idx[c] (all rows when unfiltered)

@@ -1,9 +1,10 @@
-// Row-wise kernels: gather / scatter of token rows, activation and norm recomputation, norm
-// backward, column sums and rotary tables.  All are HBM-bound streaming kernels: rows are moved in
-// 16-byte vectors, one wavefront (or workgroup) per row, consecutive lanes on consecutive vectors.
+// Row-wise kernels: gather / scatter of token rows, the transposed recompute of the weight-gradient
+// operands, norm backward, column sums and rotary tables.  All are HBM-bound streaming kernels:
+// rows are moved in 16-byte vectors.
 //
 // Dimension reduction (Collider paper, abstract): the rows of kept tokens are gathered into dense
-// [M_kept, C] operands; the scatter puts results back with filtered rows exactly zero.
+// [M_kept, C] operands (or read through the index by their consumers); the scatter puts results
+// back with filtered rows exactly zero.
 #include "internal.h"
 
 #include <algorithm>
