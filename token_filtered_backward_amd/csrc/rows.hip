@@ -259,11 +259,17 @@ __global__ __launch_bounds__(256) void cols_recompute_kernel(
 #pragma unroll
   for (int e = 0; e < 8; ++e) r[e] = c0 + e < rows ? (rowmap ? rowmap[c0 + e] : c0 + e) : -1;
   uint4 v[8], v2[8];
+  float mu[8], rs[8];  // row statistics (COL_NORM), loaded with the rows rather than at their use
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     v[e] = r[e] >= 0 ? *(const uint4*)(x + r[e] * ld_x + col0) : make_uint4(0, 0, 0, 0);
     if constexpr (OP == COL_SWIGLU)
       v2[e] = r[e] >= 0 ? *(const uint4*)(x2 + r[e] * ld_x + col0) : make_uint4(0, 0, 0, 0);
+    if constexpr (OP == COL_NORM) {
+      const int64_t rr = r[e] >= 0 ? r[e] : 0;
+      mu[e] = mean ? mean[rr] : 0.f;
+      rs[e] = rstd[rr];
+    }
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -277,11 +283,10 @@ __global__ __launch_bounds__(256) void cols_recompute_kernel(
       const uint32_t w[4] = {v[e].x, v[e].y, v[e].z, v[e].w};
       uint32_t o[4];
       if constexpr (OP == COL_NORM) {
-        const float mu = mean ? mean[r[e]] : 0.f, rs = rstd[r[e]];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          o[i] = pack2bf((bflo(w[i]) - mu) * rs * g[2 * i] + bt[2 * i],
-                         (bfhi(w[i]) - mu) * rs * g[2 * i + 1] + bt[2 * i + 1]);
+          o[i] = pack2bf((bflo(w[i]) - mu[e]) * rs[e] * g[2 * i] + bt[2 * i],
+                         (bfhi(w[i]) - mu[e]) * rs[e] * g[2 * i + 1] + bt[2 * i + 1]);
       } else if constexpr (OP == COL_SWIGLU) {
         const uint32_t w2[4] = {v2[e].x, v2[e].y, v2[e].z, v2[e].w};
 #pragma unroll
@@ -345,9 +350,16 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Read-only stand-ins for absent optional inputs of norm_bwd_kernel (no row limit: INT_MAX; no
+// mean: 0), so that its loads need no branch.
+static __device__ const int32_t kNoRowLimit = 0x7fffffff;
+static __device__ const float kZeroMean = 0.f;
+
 // One wavefront per row (4 rows per workgroup), the row in registers (NV 8-element vectors per
 // lane, H <= 512 * NV); all of a row's loads are issued together and nothing is kept across rows,
-// so that many wavefronts per SIMD hide the loads' latency.
+// so that many wavefronts per SIMD hide the loads' latency.  The compacted rows (dxn, dres) go out
+// first and the row of x, which needs the index lookup, after them; the kept-count limit is loaded
+// beside them and only decides the store, so no load waits on another except x on its index.
 template <int NV>
 __global__ __launch_bounds__(256) void norm_bwd_kernel(
     const uint16_t* __restrict__ dxn, const uint16_t* __restrict__ dres,
@@ -358,28 +370,36 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(
   const int c = blockIdx.x * 4 + wave;
   if (c >= rows) return;
   // rows at or past the device's kept count map to filtered positions (an index built with a
-  // wrong announced count): their full-layout rows belong to the zero fill alone
-  if (row_limit && c >= *row_limit) return;
+  // wrong announced count): their full-layout rows belong to the zero fill alone (checked at the
+  // store; rowmap has an entry for every token, so the loads below stay in bounds)
+  // (an ordinary vector load, not a scalar one, so that nothing waits for it before the stores;
+  // vectors past the row's end are loaded from its last vector and left unused: no branch splits
+  // the loads, whose waits the compiler would otherwise put at each branch)
+  typedef __attribute__((address_space(1))) const int32_t gi32;  // global (not flat) loads
+  const int lim = *(gi32*)(row_limit ? row_limit : &kNoRowLimit);
   const int nvec = H >> 3;
-  const int64_t r = rowmap ? rowmap[c] : c;
-  const float mu = mean ? mean[r] : 0.f;
-  const float rs = rstd[r];
+  const int map_v = *(gi32*)(rowmap ? rowmap + c : &kNoRowLimit);
   uint4 dv[NV], xv[NV], rv[NV];
+  float4 ga[NV], gb[NV];  // gamma of this lane's columns, loaded once with the rows
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int v = lane + 64 * i;
-    if (v < nvec) {
-      dv[i] = ((const uint4*)(dxn + (int64_t)c * H))[v];
-      xv[i] = ((const uint4*)(x + r * H))[v];
-      rv[i] = ((const uint4*)(dres + (int64_t)c * H))[v];
-    }
+    const int v = min(lane + 64 * i, nvec - 1);
+    dv[i] = ((const uint4*)(dxn + (int64_t)c * H))[v];
+    rv[i] = ((const uint4*)(dres + (int64_t)c * H))[v];
+    ga[i] = ((const float4*)gamma)[2 * v];
+    gb[i] = ((const float4*)gamma)[2 * v + 1];
   }
+  const int64_t r = rowmap ? map_v : c;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) xv[i] = ((const uint4*)(x + r * H))[min(lane + 64 * i, nvec - 1)];
+  const float mu = *(__attribute__((address_space(1))) const float*)(mean ? mean + r : &kZeroMean);
+  const float rs = rstd[r];
   float s_g = 0.f, s_gx = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int v = lane + 64 * i;
     if (v < nvec) {
-      const float4 g0 = ((const float4*)gamma)[2 * v], g1 = ((const float4*)gamma)[2 * v + 1];
+      const float4 g0 = ga[i], g1 = gb[i];
       const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
       const uint32_t dw[4] = {dv[i].x, dv[i].y, dv[i].z, dv[i].w};
       const uint32_t xw[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
@@ -396,11 +416,12 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(
   s_g = wave_sum(s_g) / (float)H;
   s_gx = wave_sum(s_gx) / (float)H;
   if (!mean) s_g = 0.f;
+  if (c >= lim) return;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int v = lane + 64 * i;
     if (v < nvec) {
-      const float4 g0 = ((const float4*)gamma)[2 * v], g1 = ((const float4*)gamma)[2 * v + 1];
+      const float4 g0 = ga[i], g1 = gb[i];
       const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
       const uint32_t dw[4] = {dv[i].x, dv[i].y, dv[i].z, dv[i].w};
       const uint32_t xw[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
@@ -435,21 +456,44 @@ __global__ __launch_bounds__(256) void norm_grad_parts_kernel(
   float ag[8], ab[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) ag[j] = ab[j] = 0.f;
-#pragma unroll 2
-  for (int c = r0 + wave; c < r1; c += 4) {
-    const int64_t r = rowmap ? rowmap[c] : c;
-    const float mu = mean ? mean[r] : 0.f;
-    const float rs = rstd[r];
-    if (!on) continue;
-    const uint4 dv = *(const uint4*)(dxn + (int64_t)c * H + col);
-    const uint4 xv = *(const uint4*)(x + r * H + col);
-    const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w}, xw[4] = {xv.x, xv.y, xv.z, xv.w};
+  // rows c = r0 + wave, + 4, ... in batches of RB: the batch's index lookups, then all of its row
+  // and statistics loads, go out before any is used (indices clamped into range instead of
+  // branches, which would make the compiler wait at each one); the sums still take the rows in
+  // order
+  constexpr int RB = 4;
+  typedef __attribute__((address_space(1))) const float gf32;
+  typedef __attribute__((address_space(1))) const int32_t gi32;
+  const int colc = on ? col : 0;
+  for (int cb = r0 + wave; cb < r1; cb += 4 * RB) {
+    int64_t r[RB];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float d = (j & 1) ? bfhi(dw[j >> 1]) : bflo(dw[j >> 1]);
-      const float xh = (((j & 1) ? bfhi(xw[j >> 1]) : bflo(xw[j >> 1])) - mu) * rs;
-      ag[j] += d * xh;
-      if constexpr (LN) ab[j] += d;
+    for (int b = 0; b < RB; ++b) {
+      const int c = min(cb + 4 * b, r1 - 1);
+      const int m = *(gi32*)(rowmap ? rowmap + c : &kNoRowLimit);  // no branch around the load
+      r[b] = rowmap ? m : c;
+    }
+    uint4 dv[RB], xv[RB];
+    float mu[RB], rs[RB];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      const int c = min(cb + 4 * b, r1 - 1);
+      dv[b] = *(const uint4*)(dxn + (int64_t)c * H + colc);
+      xv[b] = *(const uint4*)(x + r[b] * H + colc);
+      mu[b] = *(gf32*)(mean ? mean + r[b] : &kZeroMean);
+      rs[b] = rstd[r[b]];
+    }
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      if (!on || cb + 4 * b >= r1) continue;
+      const uint32_t dw[4] = {dv[b].x, dv[b].y, dv[b].z, dv[b].w};
+      const uint32_t xw[4] = {xv[b].x, xv[b].y, xv[b].z, xv[b].w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float d = (j & 1) ? bfhi(dw[j >> 1]) : bflo(dw[j >> 1]);
+        const float xh = (((j & 1) ? bfhi(xw[j >> 1]) : bflo(xw[j >> 1])) - mu[b]) * rs[b];
+        ag[j] += d * xh;
+        if constexpr (LN) ab[j] += d;
+      }
     }
   }
   __shared__ float red[2][4][512];
