@@ -668,6 +668,22 @@ def main():
     if graph:
         vf["graph"] = lambda: step_filtered(True)
         vf["graph, host waits for count"] = lambda: step_filtered(True, True)
+        # the whole step (index build with the announced count, then the layer) as one HIP graph,
+        # captured after an eager step; one replay must reproduce the eager step bit for bit
+        step_filtered()
+        torch.cuda.synchronize()
+        ref = {k: v.clone() for k, v in grads.items()}
+        g_step = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_step):
+            step_filtered()
+        for v in grads.values():
+            v.fill_(float("nan"))
+        g_step.replay()
+        torch.cuda.synchronize()
+        for k, v in ref.items():
+            a, b = (grads[k].view(torch.int16), v.view(torch.int16)) if v.dtype == torch.bfloat16 else (grads[k], v)
+            assert torch.equal(a, b), f"whole-step graph replay differs from the eager step in {k}"
+        vf["graph of the whole step"] = g_step.replay
     ms_f, ms_f_cold, mode_f, modes_f = best_of(vf, "filtered")
     ixp.check()
     ms_u = ms_u_cold = mode_u = modes_u = None

@@ -487,6 +487,60 @@ def test_layer_graph_replay_matches_eager(name):
         ix.check()
 
 
+@pytest.mark.parametrize("name", ["small_llama", "small_phi"])
+def test_index_and_layer_in_one_graph(name):
+    """A whole step - the index build from the mask, with the kept count announced by the host, and
+    the layer - recorded into one HIP graph: every replay gives the eager result bit for bit, with a
+    new mask of the same kept count written into the captured mask buffer between replays, and eager
+    work and synchronisation in between."""
+    cfg = synth.get_config(name)
+    inp = synth.make_layer_inputs(cfg, r_pct=40)
+    weights, saved, dy = _upload_layer(inp)
+    lcfg = tfb.layer_cfg(cfg)
+    keep1 = inp["keep"]
+    keep2 = synth.make_keep(cfg.M, 40, 77)  # another mask, same kept count
+    n = int(keep1.sum())
+    assert n == int(keep2.sum())
+
+    def eager(keep):
+        ix = tfb.build_index(_dev_keep(keep), cfg.B, cfg.S)
+        g = tfb.make_grads(lcfg, cfg.M, ix.M_kept, "cuda")
+        tfb.LayerBackward(lcfg, cfg.B, cfg.S, "cuda")(weights, saved, dy, ix, g)
+        torch.cuda.synchronize()
+        return {k: v.clone() for k, v in g.items()}
+
+    ref1, ref2 = eager(keep1), eager(keep2)
+    keep_dev = _dev_keep(keep1)
+    ix = tfb.build_index(keep_dev, cfg.B, cfg.S)
+    lb = tfb.LayerBackward(lcfg, cfg.B, cfg.S, "cuda")
+    grads = tfb.make_grads(lcfg, cfg.M, n, "cuda")
+
+    def step():
+        tfb.build_index(keep_dev, cfg.B, cfg.S, out=ix, expect=n)
+        lb(weights, saved, dy, ix, grads)
+
+    step()  # eager first: workspace and mismatch flag exist before the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    junk = torch.zeros(1 << 20, device="cuda")
+    for rep, (keep, ref) in enumerate([(keep1, ref1), (keep2, ref2), (keep2, ref2), (keep1, ref1)]):
+        keep_dev.copy_(_dev_keep(keep))
+        for gt in grads.values():
+            gt.fill_(float("nan"))
+        graph.replay()
+        junk.add_(1.0)  # eager work between replays
+        torch.cuda.synchronize()
+        for k in ref:
+            a, b = grads[k], ref[k]
+            same = torch.equal(a.view(torch.int16), b.view(torch.int16)) if a.dtype == torch.bfloat16 \
+                else torch.equal(a, b)
+            assert same, (rep, k)
+        ix.check()
+
+
 def test_layer_repeat_is_deterministic():
     cfg = synth.get_config("small_llama")
     inp = synth.make_layer_inputs(cfg)
