@@ -70,7 +70,7 @@ def test_host_validation_errors():
     assert L.collider_attn_bwd_filtered(ctypes.byref(cfg), ctypes.byref(ix), ctypes.byref(io), None, 0, None) == 4
     cfg = tfb.AttnCfg(6, 4, 64, 0, 0.0, 0.0, 0)                                # nq % nkv != 0
     assert L.collider_attn_bwd_filtered(ctypes.byref(cfg), ctypes.byref(ix), ctypes.byref(io), None, 0, None) == 2
-    cfg = tfb.AttnCfg(8, 2, 64, 24, 1e4, 0.0, 0)                               # rot not multiple of 16
+    cfg = tfb.AttnCfg(8, 2, 64, 25, 1e4, 0.0, 0)                               # odd rotary width
     assert L.collider_attn_bwd_filtered(ctypes.byref(cfg), ctypes.byref(ix), ctypes.byref(io), None, 0, None) == 4
     cfg = tfb.AttnCfg(8, 2, 64, 64, 1e4, 0.0, 0)
     ix_bad = tfb.CollIndex(p, p, p, p, 1, 8, 9)                                # M_kept > M
@@ -96,7 +96,7 @@ def test_layer_validation_and_workspace_sizes():
         assert L.collider_layer_workspace_bytes(ctypes.byref(cfg), shape.B, shape.S, shape.M) >= need
         assert L.collider_layer_workspace_bytes(ctypes.byref(cfg), shape.B, shape.S, shape.M + 1) == 0
     shape = synth.get_config("tinyllama")
-    bad = tfb.layer_cfg(shape.with_(H=5000))
+    bad = tfb.layer_cfg(shape.with_(H=5004))                  # hidden not a multiple of 8
     assert L.collider_layer_workspace_bytes(ctypes.byref(bad), 1, 8, 8) == 0
     cfg = tfb.layer_cfg(shape)
     ix = tfb.CollIndex(0x1000, 0x1000, 0x1000, 0x1000, 4, 2048, 4916)

@@ -445,6 +445,22 @@ def test_stack_of_layers(name):
     assert np.all(to64(outs[-1]["dx"])[keep == 0] == 0.0)
 
 
+@pytest.mark.parametrize("base,changes", [
+    ("small_llama", dict(H=4608, B=1, S=160)),             # hidden > 4096: the two-sweep norm backward
+    ("small_phi", dict(H=4160, B=1, S=160)),               # ... with a ragged last 8-vector per lane
+    ("small_llama", dict(nq=6, nkv=2, rot=24)),            # head count not a multiple of 4, rotary
+    ("small_llama_d128", dict(nq=3, nkv=1, rot=40)),       # widths not multiples of 16 (rot/2 and
+    ("small_phi", dict(nq=6, nkv=6, rot=20)),              # rot fall inside groups of 8 columns)
+])
+@pytest.mark.parametrize("dmode", [0, 1])
+def test_layer_parity_wider_shapes(base, changes, dmode):
+    """Layer shapes outside the benchmark models' envelope: hidden sizes past 4096 and head counts /
+    rotary widths that do not divide into the kernels' vector widths, against the oracle."""
+    cfg = synth.get_config(base).with_(name=base + "_wide", **changes)
+    inp = synth.make_layer_inputs(cfg, r_pct=40)
+    run_layer_and_compare(inp, dmode)
+
+
 @pytest.mark.parametrize("name", ["small_llama", "small_phi"])
 def test_layer_graph_replay_matches_eager(name):
     """The layer recorded into a HIP graph and replayed gives the eager result bit for bit, on every

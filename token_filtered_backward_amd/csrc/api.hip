@@ -80,8 +80,7 @@ static collider_status check_attn_cfg(const collider_attn_cfg* c) {
   if (!c) return COLLIDER_ERR_NULL;
   if (c->n_q_heads < 1 || c->n_kv_heads < 1 || c->n_q_heads % c->n_kv_heads) return COLLIDER_ERR_SHAPE;
   if (c->head_dim != 64 && c->head_dim != 128) return COLLIDER_ERR_UNSUPPORTED;
-  if (c->n_q_heads % 4) return COLLIDER_ERR_UNSUPPORTED;  // lse rows are moved as 16-byte vectors
-  if (c->rot_dims < 0 || c->rot_dims > c->head_dim || c->rot_dims % 16) return COLLIDER_ERR_UNSUPPORTED;
+  if (c->rot_dims < 0 || c->rot_dims > c->head_dim || c->rot_dims % 2) return COLLIDER_ERR_UNSUPPORTED;
   if (c->rot_dims > 0 && !(c->rope_base > 1.f)) return COLLIDER_ERR_SHAPE;
   if (c->softmax_scale < 0.f) return COLLIDER_ERR_SHAPE;
   if (c->dmode != COLLIDER_ATTN_D_FILTERED && c->dmode != COLLIDER_ATTN_D_FULL) return COLLIDER_ERR_SHAPE;
@@ -263,7 +262,6 @@ static collider_status check_layer(const collider_layer_cfg* c) {
   if (!c) return COLLIDER_ERR_NULL;
   if (c->kind != COLLIDER_LAYER_LLAMA && c->kind != COLLIDER_LAYER_PHI) return COLLIDER_ERR_UNSUPPORTED;
   if (c->hidden < 8 || c->inter < 8 || c->hidden % 8 || c->inter % 8) return COLLIDER_ERR_SHAPE;
-  if (c->hidden > 4096) return COLLIDER_ERR_UNSUPPORTED;  // norm backward keeps a row in registers
   collider_attn_cfg ac{c->n_q_heads, c->n_kv_heads, c->head_dim, c->rot_dims, c->rope_base, 0.f, c->dmode};
   collider_status st = check_attn_cfg(&ac);
   if (st != COLLIDER_OK) return st;

@@ -384,15 +384,21 @@ __global__ __launch_bounds__(256, D == 64 ? (FULLD ? 3 : 2) : 1) void attn_dq_ke
     float out[8];
     const float* er = E + row * LDE;
     if (c0 < p.rot) {
+      // rotate-half pairs (m, m + rot/2) for m < rot/2; columns from rot on pass through (rot may
+      // end inside this group of 8, and rot/2 may fall inside it)
       const int pos = (p.idx ? p.idx[cs + i] : cs + i) % p.S;
-      const bool lower = c0 < half;
-      const int m0 = lower ? c0 : c0 - half;
-      const int pc = lower ? c0 + half : c0 - half;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float2 t = p.rope[(int64_t)pos * half + m0 + e];
-        const float x = er[c0 + e], y = er[pc + e];
-        out[e] = lower ? x * t.x + y * t.y : x * t.x - y * t.y;
+        const int col = c0 + e;
+        const float x = er[col];
+        if (col < p.rot) {
+          const bool lower = col < half;
+          const float2 t = p.rope[(int64_t)pos * half + (lower ? col : col - half)];
+          const float y = er[lower ? col + half : col - half];
+          out[e] = lower ? x * t.x + y * t.y : x * t.x - y * t.y;
+        } else {
+          out[e] = x;
+        }
       }
     } else {
 #pragma unroll

@@ -1355,7 +1355,7 @@ collider_status gemm_bf16(const GemmProblem& prob, void* ws, size_t ws_bytes, hi
 
 
 // ------------------------------------------------------------------------------------------
-// fp32 GEMM (CUDA-core style FMA, 64x64 tiles, 4x4 per thread) for the fp32 linear backward
+// fp32 GEMM (vector-ALU FMA, 64x64 tiles, 4x4 outputs per thread) for the fp32 linear backward
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, int64_t lda,
                                                        int ak, const float* __restrict__ B,

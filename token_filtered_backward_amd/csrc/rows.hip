@@ -440,6 +440,63 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(
   }
 }
 
+// Rows longer than 4096 elements (hidden > 4096): the same computation, in the same per-lane order,
+// in two sweeps over the row - the sums, then the output - the second re-reading the row that the
+// first has just brought into L2, so that no row has to fit in registers.
+__global__ __launch_bounds__(256) void norm_bwd_long_kernel(
+    const uint16_t* __restrict__ dxn, const uint16_t* __restrict__ dres,
+    const uint16_t* __restrict__ x, const float* __restrict__ mean, const float* __restrict__ rstd,
+    const float* __restrict__ gamma, const int32_t* __restrict__ rowmap, int rows, int H,
+    uint16_t* __restrict__ dx, int dx_full, const int32_t* __restrict__ row_limit) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 4 + wave;
+  if (c >= rows) return;
+  const int nvec = H >> 3;
+  const int64_t r = rowmap ? rowmap[c] : c;
+  const float mu = mean ? mean[r] : 0.f;
+  const float rs = rstd[r];
+  const uint4* drow = (const uint4*)(dxn + (int64_t)c * H);
+  const uint4* xrow = (const uint4*)(x + r * H);
+  const uint4* rrow = (const uint4*)(dres + (int64_t)c * H);
+  float s_g = 0.f, s_gx = 0.f;
+  for (int v = lane; v < nvec; v += 64) {
+    const float4 g0 = ((const float4*)gamma)[2 * v], g1 = ((const float4*)gamma)[2 * v + 1];
+    const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const uint4 dv = drow[v], xv = xrow[v];
+    const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w}, xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float d = (j & 1) ? bfhi(dw[j >> 1]) : bflo(dw[j >> 1]);
+      const float xh = (((j & 1) ? bfhi(xw[j >> 1]) : bflo(xw[j >> 1])) - mu) * rs;
+      const float gv = d * gm[j];
+      s_g += gv;
+      s_gx += gv * xh;
+    }
+  }
+  s_g = wave_sum(s_g) / (float)H;
+  s_gx = wave_sum(s_gx) / (float)H;
+  if (!mean) s_g = 0.f;
+  // rows at or past the device's kept count: their full-layout rows belong to the zero fill alone
+  if (row_limit && c >= *row_limit) return;
+  for (int v = lane; v < nvec; v += 64) {
+    const float4 g0 = ((const float4*)gamma)[2 * v], g1 = ((const float4*)gamma)[2 * v + 1];
+    const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const uint4 dv = drow[v], xv = xrow[v], rv = rrow[v];
+    const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w}, xw[4] = {xv.x, xv.y, xv.z, xv.w};
+    const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
+    uint32_t ow[4];
+#pragma unroll
+    for (int j2 = 0; j2 < 4; ++j2) {
+      const float g_a = bflo(dw[j2]) * gm[2 * j2], g_b = bfhi(dw[j2]) * gm[2 * j2 + 1];
+      const float x_a = (bflo(xw[j2]) - mu) * rs, x_b = (bfhi(xw[j2]) - mu) * rs;
+      const float a0 = bflo(rw[j2]) + rs * (g_a - s_g - x_a * s_gx);
+      const float a1 = bfhi(rw[j2]) + rs * (g_b - s_g - x_b * s_gx);
+      ow[j2] = pack2bf(a0, a1);
+    }
+    ((uint4*)(dx + (dx_full ? r : (int64_t)c) * H))[v] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+  }
+}
+
 // Partial column sums of dxn * xhat (and of dxn, LN) over one chunk of rows: workgroup
 // (column block cb, part p) covers 512 columns (8 per lane) and rows [p * rpp, (p + 1) * rpp), the
 // 4 wavefronts taking every fourth row; their sums are combined in a fixed order, so the result
@@ -540,8 +597,10 @@ collider_status launch_norm_bwd(const uint16_t* dxn, const uint16_t* dres, const
     break;
   switch (nv) {
     NB_CASE(1) NB_CASE(2) NB_CASE(3) NB_CASE(4) NB_CASE(5) NB_CASE(6) NB_CASE(7) NB_CASE(8)
-    default:
-      return COLLIDER_ERR_UNSUPPORTED;
+    default:  // rows longer than 4096
+      COLLIDER_LAUNCH("norm_bwd", s,
+                      hipLaunchKernelGGL(norm_bwd_long_kernel, grid, block, 0, s, dxn, dres, x, mean,
+                                         rstd, gamma, rowmap, rows, H, dx, dx_full, row_limit));
   }
 #undef NB_CASE
   return last_hip_status();
