@@ -500,9 +500,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfiltered", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch every kernel eagerly each step")
-    ap.add_argument("--weight-layout", choices=("in_out", "out_in"), default="in_out",
+    ap.add_argument("--weight-layout", choices=("in_out", "out_in"), default=None,
                     help="projection weights stored [in, out] (y = x W, the pages' notation) or "
-                         "[out, in] (torch nn.Linear); LLAMA-kind layers only take in_out")
+                         "[out, in] (torch nn.Linear); default: in_out for LLAMA-kind layers, "
+                         "out_in for PHI-kind ones")
     ap.add_argument("--dmode", choices=("filtered", "full"), default="filtered",
                     help="softmax-backward row term of the filtered attention: sum over kept keys of "
                          "P~ dP (filtered, the default) or dO . O (full)")
@@ -574,7 +575,8 @@ def main():
     keep = torch.from_numpy(inp["keep"]).to(dev)
     B, S, M = cfg.B, cfg.S, cfg.M
     # weight storage layout (set up once, before timing; the weight gradients come out in it)
-    layout = tfb.WEIGHTS_IN_OUT if (args.weight_layout == "in_out" and cfg.kind == "llama") else tfb.WEIGHTS_OUT_IN
+    wl = args.weight_layout or ("in_out" if cfg.kind == "llama" else "out_in")
+    layout = tfb.WEIGHTS_IN_OUT if wl == "in_out" else tfb.WEIGHTS_OUT_IN
     if layout == tfb.WEIGHTS_IN_OUT:
         weights = tfb.to_in_out(weights)
 

@@ -193,14 +193,15 @@ typedef struct {
                                    (only B, S), nothing is gathered or scattered, every GEMM and
                                    the attention run on the full layout, dmode is taken as FULL */
   int32_t weight_layout;        /* collider_weight_layout: how the projection weights and their
-                                   gradients are stored (LLAMA only may take IN_OUT) */
+                                   gradients are stored */
 } collider_layer_cfg;
 
 /* COLLIDER_WEIGHTS_OUT_IN: w [out, in], y = x w^T (torch nn.Linear), the layouts listed below.
  * COLLIDER_WEIGHTS_IN_OUT: W [in, out], y = x W (the notation of the Collider pages, dX = dY W^T):
  * every projection weight and its gradient is the transpose of the OUT_IN one - W_qkv [H, nqkv]
  * (q columns, then k, then v), W_o [nq*d, H], W_gateup [H, 2I] (gate columns then up), W_down
- * [I, H].  With IN_OUT each weight row is contiguous along the reduction of the activation-gradient
+ * [I, H]; PHI: W_fc1 [H, I], W_fc2 [I, H] (the PHI layer then stacks W_qkv and W_fc1 into one
+ * [H, nqkv + I] matrix in its workspace each call).  With IN_OUT each weight row is contiguous along the reduction of the activation-gradient
  * GEMM, so both of its operands are read with 16-byte LDS reads (OUT_IN needs the transposing
  * 8-byte reads, a third of the LDS bandwidth). */
 typedef enum { COLLIDER_WEIGHTS_OUT_IN = 0, COLLIDER_WEIGHTS_IN_OUT = 1 } collider_weight_layout;

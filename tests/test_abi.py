@@ -106,11 +106,11 @@ def test_layer_validation_and_workspace_sizes():
     cfg.kind = 7
     assert L.collider_layer_bwd(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(sv), ctypes.c_void_p(0x1000),
                                 0, ctypes.byref(ix), ctypes.byref(g), 0, None, 0, None) == 4
-    # weight layouts: [in, out] for LLAMA layers only; unknown layouts rejected
+    # weight layouts: [in, out] for both layer kinds; unknown layouts rejected
     io = tfb.layer_cfg(shape, weight_layout=tfb.WEIGHTS_IN_OUT)
     assert L.collider_layer_workspace_bytes(ctypes.byref(io), 4, 2048, 4916) > 0
     phi_io = tfb.layer_cfg(synth.get_config("phi15"), weight_layout=tfb.WEIGHTS_IN_OUT)
-    assert L.collider_layer_workspace_bytes(ctypes.byref(phi_io), 4, 2048, 4916) == 0
+    assert L.collider_layer_workspace_bytes(ctypes.byref(phi_io), 4, 2048, 4916) > 0
     io.weight_layout = 2
     assert L.collider_layer_workspace_bytes(ctypes.byref(io), 4, 2048, 4916) == 0
 

@@ -59,7 +59,7 @@ def _compare(cfg, got, ref, keep):
                                                  ("tinyllama", 40, 0, 1), ("qwen25", 40, 0, 0),
                                                  ("qwen25", 40, 0, 1), ("phi15", 0, 0, 0),
                                                  ("phi15", 20, 0, 0), ("phi15", 40, 0, 0),
-                                                 ("phi15", 60, 0, 0)])
+                                                 ("phi15", 60, 0, 0), ("phi15", 40, 0, 1)])
 def test_layer_fullsize(name, r, dmode, layout):
     cfg = synth.get_config(name)
     inp = synth.make_layer_inputs(cfg, seed=0, r_pct=r)

@@ -324,7 +324,7 @@ def test_layer_parity_small(name, dmode, r):
     run_layer_and_compare(inp, dmode)
 
 
-@pytest.mark.parametrize("name", ["small_llama", "small_llama_d128"])
+@pytest.mark.parametrize("name", ["small_llama", "small_llama_d128", "small_phi"])
 @pytest.mark.parametrize("r", [0, 40])
 def test_layer_weight_layouts(name, r):
     """Weights stored [in, out] give the same gradients as [out, in] - dx and the norm gains bit for
@@ -352,7 +352,7 @@ def test_layer_weight_layouts(name, r):
         assert same, k
     ref = oracle.layer_bwd(cfg, upcast(inp["weights"]), upcast(inp["saved"]),
                            synth.bf16_bits_to_f32(inp["dy"]), inp["keep"], "filtered")
-    for gname, oname in GRAD_NAMES["llama"].items():
+    for gname, oname in GRAD_NAMES[cfg.kind].items():
         got = to64(g1[gname])
         got = got.T if gname.startswith("dw_") else got
         assert rel_err(got, ref[oname]) <= BF16_TOL, gname
@@ -368,7 +368,8 @@ def test_layer_parity_gemm_policies(gemm_policy, policy, name):
     run_layer_and_compare(inp, 0)
 
 
-@pytest.mark.parametrize("name,layout", [("small_llama", 0), ("small_phi", 0), ("small_llama", 1)])
+@pytest.mark.parametrize("name,layout", [("small_llama", 0), ("small_phi", 0), ("small_llama", 1),
+                                         ("small_phi", 1)])
 def test_layer_all_filtered(name, layout):
     cfg = synth.get_config(name)
     inp = synth.make_layer_inputs(cfg, keep=np.zeros(cfg.M, np.uint8))
@@ -570,7 +571,7 @@ def test_layer_repeat_is_deterministic():
 
 
 @pytest.mark.parametrize("name,layout", [("small_llama", 0), ("small_llama_d128", 0), ("small_phi", 0),
-                                         ("small_llama", 1)])
+                                         ("small_llama", 1), ("small_phi", 1)])
 def test_unfiltered_baseline(name, layout):
     """The dense baseline equals the filtered path with every token kept (same kernels, same
     numerics, dmode FULL) and the oracle's ordinary backward, in either weight layout."""

@@ -269,10 +269,6 @@ static collider_status check_layer(const collider_layer_cfg* c) {
     return COLLIDER_ERR_UNSUPPORTED;
   if (c->weight_layout != COLLIDER_WEIGHTS_OUT_IN && c->weight_layout != COLLIDER_WEIGHTS_IN_OUT)
     return COLLIDER_ERR_UNSUPPORTED;
-  // [in, out] weights: LLAMA only (the PHI activation-gradient GEMM reads w_qkv and w_fc1 as two
-  // segments of one reduction, which needs their [out, in] rows)
-  if (c->weight_layout == COLLIDER_WEIGHTS_IN_OUT && c->kind != COLLIDER_LAYER_LLAMA)
-    return COLLIDER_ERR_UNSUPPORTED;
   return COLLIDER_OK;
 }
 

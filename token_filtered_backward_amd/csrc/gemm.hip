@@ -1212,6 +1212,10 @@ collider_status launch_cfg(const GemmParams& gp, const GemmProblem& pr, const Pl
         if (pl.lds) return launch_lds<BM, BN, EPI_SWIGLU, true, true>(gp, pl.grid, name, s);
         if constexpr (kStaged) return launch_one<BM, BN, EPI_SWIGLU, true, true>(gp, name, s);
         break;
+      case EPI_GELU:
+        if (pl.lds) return launch_lds<BM, BN, EPI_GELU, true, true>(gp, pl.grid, name, s);
+        if constexpr (kStaged) return launch_one<BM, BN, EPI_GELU, true, true>(gp, name, s);
+        break;
     }
   } else if (!pr.a_kmajor && !pr.b_kmajor && pr.epi == EPI_F32) {
     if constexpr (kMnA) {

@@ -136,6 +136,9 @@ collider_status launch_scatter_bytes(const void* src, int64_t ld_src_b, void* ds
                                      const int32_t* inv, int M, int row_bytes, int zero_fill,
                                      hipStream_t s);
 
+// dst[r, 0:cols] = src[r, 0:cols] for r < rows, bf16 with leading dimensions ld_src / ld_dst
+collider_status launch_copy_rows(const uint16_t* src, int64_t ld_src, uint16_t* dst, int64_t ld_dst,
+                                 int rows, int cols, hipStream_t s);
 // out[col * ldT + c] = bf16(op(row rowmap[c] of x (and x2), col)) for c < rows, 0 up to ldT (a
 // multiple of 8 >= rows): the transposed (token-contiguous) operand of a weight-gradient GEMM.
 // op: COL_COPY x; COL_NORM (x - mean) rstd gamma + beta (mean, beta may be null: RMSNorm);

@@ -148,6 +148,7 @@ struct LayerBufs {
   uint16_t *dmid, *dqkv, *dxn, *dh, *do_c, *dx_c;
   float *part_g, *part_b;
   uint16_t* dxn1;
+  uint16_t* w_stack;  // PHI, [in, out] weights: [W_qkv | W_fc1], [H, nqkv + I]
   void* gemm_ws;   // split-K partials of the GEMMs on the caller's stream
   void* gemm_ws2;  // ... and of the weight-gradient GEMMs on the side stream
   void* attn_ws;
@@ -199,6 +200,9 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
   const int dx_full = (!dx_compact && !unf) ? 1 : 0;
   b.part_g = cv.take<float>((size_t)parts * H);
   b.part_b = cv.take<float>((size_t)parts * H);
+  // PHI with [in, out] weights: W_qkv and W_fc1 stacked into one [H, nqkv + I] matrix
+  b.w_stack = (!llama && c.weight_layout == COLLIDER_WEIGHTS_IN_OUT)
+                  ? cv.take<uint16_t>((size_t)H * (nqkv + I)) : nullptr;
 
   // GEMM problems (pointers are only meaningful when not dry)
   const int32_t* idx = unf ? nullptr : ix.idx;  // row map of the saved tensors (null: identity)
@@ -261,8 +265,15 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     dx_gemm(g_dO, nqd, H, b.dy_c, H, w ? w->w_o : nullptr, nqd, EPI_BF16, b.do_c, nqd);
     dw_gemm(g_dwo, H, nqd, b.dy_c, H, b.oT, gr ? gr->dw_o : nullptr);
     dx_gemm(g_dXin, H, nqkv + I, b.dmid, mid, w ? w->w_qkv : nullptr, H, EPI_BF16, b.dxn, H);
-    g_dXin.B1 = w ? w->w_fc1 : nullptr;
-    g_dXin.kseg = nqkv;
+    if (w_io) {
+      // [in, out]: W_qkv [H, nqkv] and W_fc1 [H, I] have different row lengths, so they are
+      // stacked into one [H, nqkv + I] matrix (copied on the side stream, well before this GEMM),
+      // whose rows hold the whole reduction
+      g_dXin.B0 = b.w_stack;
+    } else {
+      g_dXin.B1 = w ? w->w_fc1 : nullptr;
+      g_dXin.kseg = nqkv;
+    }
     dw_gemm(g_dwqkv, nqkv, H, b.dmid, mid, b.xnT, gr ? gr->dw_qkv : nullptr);
     dw_gemm(g_dwfc1, I, H, dF, mid, b.xnT, gr ? gr->dw_fc1 : nullptr);
   }
@@ -347,6 +358,11 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
   // the rotary table attention reads (S and the rotary configuration only), off the critical path;
   // attention waits on the event recorded after it
   CHECK(attn_rope_prepare(ac, aix, b.attn_ws, b.attn_ws_bytes, s1));
+  if (b.w_stack) {  // the stacked [W_qkv | W_fc1] of a PHI layer with [in, out] weights
+    CHECK(launch_copy_rows((const uint16_t*)w->w_qkv, nqkv, b.w_stack, nqkv + I, H, nqkv, s1));
+    CHECK(launch_copy_rows((const uint16_t*)w->w_fc1, I, b.w_stack + nqkv, nqkv + I, H, I, s1));
+  }
+  // attention, and everything after it on `s`, waits on the event recorded here
   if (side && hipEventRecord(side->ev[6], s1) != hipSuccess) return COLLIDER_ERR_HIP;
   collider_attn_io io{};  // saved tensors in the full layout, rows idx[c] (all rows when unfiltered)
   io.q = sv ? sv->q : nullptr; io.ld_q = nqd;

@@ -111,6 +111,32 @@ collider_status launch_gather_rows(const GatherDesc* d, int n_desc, const int32_
   return last_hip_status();
 }
 
+// Row-by-row copy of a [rows, cols] bf16 matrix between leading dimensions (16-byte chunks; cols,
+// both leading dimensions and both addresses multiples of 8 elements / 16 bytes).
+__global__ __launch_bounds__(256) void copy_rows_kernel(const uint4* __restrict__ src, int64_t ld_src,
+                                                        uint4* __restrict__ dst, int64_t ld_dst,
+                                                        int rows, int per_row) {
+  const int64_t n = (int64_t)rows * per_row;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / per_row, c = i - r * per_row;
+    dst[r * ld_dst + c] = src[r * ld_src + c];
+  }
+}
+
+collider_status launch_copy_rows(const uint16_t* src, int64_t ld_src, uint16_t* dst, int64_t ld_dst,
+                                 int rows, int cols, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return COLLIDER_OK;
+  if (cols % 8 || ld_src % 8 || ld_dst % 8 || !aligned16(src) || !aligned16(dst))
+    return COLLIDER_ERR_UNSUPPORTED;
+  const int per_row = cols / 8;
+  const int64_t n = (int64_t)rows * per_row;
+  const int blocks = (int)std::min<int64_t>((n + 255) / 256, 4096);
+  COLLIDER_LAUNCH("copy_rows", s,
+                  hipLaunchKernelGGL(copy_rows_kernel, dim3(blocks), dim3(256), 0, s, (const uint4*)src,
+                                     ld_src / 8, (uint4*)dst, ld_dst / 8, rows, per_row));
+  return last_hip_status();
+}
+
 // Generic byte-granular gather / scatter (2-byte units) for rows that are not 16-byte multiples.
 __global__ void gather_u16_kernel(const uint16_t* __restrict__ src, int64_t ld_src,
                                   uint16_t* __restrict__ dst, int64_t ld_dst,
