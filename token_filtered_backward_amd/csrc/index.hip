@@ -1,22 +1,24 @@
 // Mask -> index: stable stream compaction of the per-token keep mask.
 //
 // Backward token filtering decides per token whether its loss is kept (Collider paper, Figure 2(b));
-// the kept tokens are the rows the dimension-reduced dense GEMMs run over (abstract).  A workgroup
-// of 1024 threads (16 wavefronts) walks the mask in chunks of 8 tokens per thread: wavefront prefix
-// sums via shuffles, then an LDS scan over the 16 wavefront totals.  Masks up to 16384 tokens take
-// one workgroup (the work is latency-bound); longer ones are split over up to 64 workgroups, each of
-// which finds its starting position by counting the kept tokens before its range itself.
+// the kept tokens are the rows the dimension-reduced dense GEMMs run over (abstract).  Each
+// workgroup owns a range of the mask and walks it in scan steps of 8 tokens per thread: wavefront
+// prefix sums via shuffles, then an LDS scan over the wavefront totals.  The call has no scratch
+// memory to exchange partial counts through, so every workgroup counts the kept tokens before its
+// range and in the whole mask itself (1 byte per token, served by L2 after the first workgroups).
+// The token ids of a scan step are placed in LDS in their compacted order (kept ones, then the
+// filtered ones) and written out as two contiguous runs of idx, so that the stores coalesce.
 #include "internal.h"
 
 namespace collider {
 
-static constexpr int kThreads = 1024;
 static constexpr int kPer = 8;
-static constexpr int kWaves = kThreads / 64;
-// masks up to kMwMin tokens: one workgroup (a few microseconds of latency, no gain from more);
-// longer masks: up to kMwGrid workgroups, each with a range of the mask
-static constexpr int64_t kMwMin = 16384;
-static constexpr int kMwGrid = 64;
+// masks up to kSmallMax tokens: workgroups of 256 threads, one 2048-token scan step each; longer
+// masks: up to kBigGrid workgroups of 1024 threads, each over a range of whole 8192-token scan
+// steps (at 65536 tokens 8 such workgroups built the index in 8.0 us against 9.2 us for 32 of the
+// small ones, whose count sweeps then take two memory round trips)
+static constexpr int64_t kSmallMax = 16384;
+static constexpr int kBigGrid = 64;
 
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = threadIdx.x & 63;
@@ -28,21 +30,23 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Exclusive scan of one int per thread over the block; also returns the block total.
+// Exclusive scan of one int per thread over the block of NT threads; also returns the block total.
+template <int NT>
 __device__ __forceinline__ int block_excl_scan(int v, int* total, int* s_wave) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = wave_incl_scan(v);
   if (lane == 63) s_wave[wave] = incl;
   __syncthreads();
   if (wave == 0) {
-    int w = lane < kWaves ? s_wave[lane] : 0;
+    int w = lane < NW ? s_wave[lane] : 0;
     int wi = wave_incl_scan(w);
-    if (lane < kWaves) s_wave[lane] = wi - w;  // exclusive wave offsets
-    if (lane == kWaves - 1) s_wave[kWaves] = wi;
+    if (lane < NW) s_wave[lane] = wi - w;  // exclusive wave offsets
+    if (lane == NW - 1) s_wave[NW] = wi;
   }
   __syncthreads();
   int r = s_wave[wave] + incl - v;
-  *total = s_wave[kWaves];
+  *total = s_wave[NW];
   __syncthreads();  // s_wave is reused by the next call
   return r;
 }
@@ -67,27 +71,29 @@ __device__ __forceinline__ unsigned load_bits(const uint8_t* __restrict__ keep, 
   return bits;
 }
 
-// Writes idx / inv / cu for tokens t0 .. t0+7, whose first kept token gets compacted position pre.
-// Compacted positions at or past lim are left out of inv and cu (lim = the count the caller
-// announced; INT_MAX when it announced none), so that no consumer sized for lim rows ever indexes
-// past them.
-__device__ __forceinline__ void scatter_group(unsigned bits, int t0, int pre, int n_kept, int M, int S,
-                                              int lim, int32_t* __restrict__ idx,
-                                              int32_t* __restrict__ inv, int32_t* __restrict__ cu) {
+// Writes inv and cu for tokens t0 .. t0+7 (t0 < M), whose first kept token gets compacted position
+// pre, and places their ids at their compacted slots of the scan step in LDS: kept token number k of
+// the step at loc[k], filtered token number f at loc[n_step_kept + f] (lpre / lpos: kept tokens and
+// tokens of the step before t0).  Compacted positions at or past lim are left out of inv and cu
+// (lim = the count the caller announced; INT_MAX when it announced none), so that no consumer sized
+// for lim rows ever indexes past them.
+__device__ __forceinline__ void place_group(unsigned bits, int t0, int pre, int lpre, int lpos,
+                                            int n_step_kept, int M, int S, int lim, int32_t* loc,
+                                            int32_t* __restrict__ inv, int32_t* __restrict__ cu) {
   int iv[kPer];
+  int r = t0 % S;  // position of token t0 in its sequence
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
     const int t = t0 + e;
     const bool k = (bits >> e) & 1u;
     iv[e] = (k && pre < lim) ? pre : -1;
     if (t < M) {
-      if (t % S == 0) cu[t / S] = min(pre, lim);
-      if (k)
-        idx[pre] = t;
-      else
-        idx[n_kept + (t - pre)] = t;
+      if (r == 0) cu[t / S] = min(pre, lim);
+      loc[k ? lpre : n_step_kept + (lpos + e - lpre)] = t;
     }
+    r = r + 1 == S ? 0 : r + 1;
     pre += k;
+    lpre += k;
   }
   if (t0 + 8 <= M && ((uintptr_t)(inv + t0) & 15) == 0) {
     ((int4*)(inv + t0))[0] = make_int4(iv[0], iv[1], iv[2], iv[3]);
@@ -98,15 +104,6 @@ __device__ __forceinline__ void scatter_group(unsigned bits, int t0, int pre, in
       if (t0 + e < M) inv[t0 + e] = iv[e];
   }
 }
-
-// Multi-workgroup form for long masks: workgroup g owns tokens [g*T, min(M, (g+1)*T)), T a multiple
-// of kChunkMW.  It needs the number of kept tokens before its range (its first compacted position)
-// and in the whole mask (the filtered positions' offset); rather than exchange partial counts
-// through memory (which would need scratch the call does not have), every workgroup counts them
-// itself in one sweep over the mask (1 byte per token, served by L2 after the first workgroups).
-// Then it scans its range chunk by chunk like the single-workgroup kernel.
-constexpr int kThreadsMW = kThreads;
-constexpr int kChunkMW = kThreadsMW * kPer;  // 8192 tokens per scan step
 
 __device__ __forceinline__ int count_kept_16(const uint8_t* __restrict__ keep, int t0, int M) {
   // kept tokens among t0 .. t0+15 (t0 a multiple of 16)
@@ -125,93 +122,64 @@ __device__ __forceinline__ int count_kept_16(const uint8_t* __restrict__ keep, i
   return n;
 }
 
-__device__ __forceinline__ int block_sum_mw(int v, int* s_wave) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  if (lane == 0) s_wave[wave] = v;
-  __syncthreads();
-  int t = 0;
-#pragma unroll
-  for (int w = 0; w < kThreadsMW / 64; ++w) t += s_wave[w];
-  __syncthreads();
-  return t;
-}
-
-__global__ __launch_bounds__(kThreadsMW) void build_index_mw_kernel(
-    const uint8_t* __restrict__ keep, int B, int S, int T, int32_t* __restrict__ idx,
-    int32_t* __restrict__ inv, int32_t* __restrict__ cu, int32_t* __restrict__ count, int expect,
-    int32_t* __restrict__ mismatch) {
-  __shared__ int s_wave[kWaves + 1];
+// Workgroup g of NT threads owns tokens [g T, min(M, (g + 1) T)), T a multiple of the scan step
+// NT * 8.
+template <int NT>
+__global__ __launch_bounds__(NT) void build_index_kernel(const uint8_t* __restrict__ keep, int B,
+                                                         int S, int T, int32_t* __restrict__ idx,
+                                                         int32_t* __restrict__ inv,
+                                                         int32_t* __restrict__ cu,
+                                                         int32_t* __restrict__ count, int expect,
+                                                         int32_t* __restrict__ mismatch) {
+  constexpr int NW = NT / 64, STEP = NT * kPer;
+  __shared__ int s_wave[NW + 1];
+  __shared__ int2 s_pair[NW];
+  __shared__ int32_t loc[STEP];
   const int M = B * S;
   const int lim = expect >= 0 ? expect : 0x7fffffff;
   const int g0 = blockIdx.x * T, g1 = min(M, g0 + T);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the first scan step's mask bytes go out with the count sweep's
+  unsigned bits = g0 + (int)threadIdx.x * kPer < g1 ? load_bits(keep, g0 + threadIdx.x * kPer, g1) : 0u;
   // kept tokens before this range and in the whole mask (16 tokens per thread per step, eight
   // steps' loads in flight)
-  int before = 0, all = 0;
+  int before = 0, n_kept = 0;
 #pragma unroll 8
-  for (int t = threadIdx.x * 16; t < M; t += kThreadsMW * 16) {
+  for (int t = threadIdx.x * 16; t < M; t += NT * 16) {
     const int n = count_kept_16(keep, t, M);
-    all += n;
+    n_kept += n;
     before += t < g0 ? n : 0;
   }
-  before = block_sum_mw(before, s_wave);
-  const int n_kept = block_sum_mw(all, s_wave);
-  for (int base = g0; base < g1; base += kChunkMW) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    before += __shfl_xor(before, off, 64);
+    n_kept += __shfl_xor(n_kept, off, 64);
+  }
+  if (lane == 0) s_pair[wave] = make_int2(before, n_kept);
+  __syncthreads();
+  before = 0;
+  n_kept = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    before += s_pair[w].x;
+    n_kept += s_pair[w].y;
+  }
+  for (int base = g0; base < g1; base += STEP) {
     const int t0 = base + threadIdx.x * kPer;
-    const unsigned bits = t0 < g1 ? load_bits(keep, t0, g1) : 0u;
-    int chunk_total = 0;
-    const int pre = before + block_excl_scan(__popc(bits), &chunk_total, s_wave);
-    if (t0 < g1) scatter_group(bits, t0, pre, n_kept, g1, S, lim, idx, inv, cu);
-    before += chunk_total;
+    if (base != g0) bits = t0 < g1 ? load_bits(keep, t0, g1) : 0u;
+    int step_kept = 0;
+    const int lpre = block_excl_scan<NT>(__popc(bits), &step_kept, s_wave);
+    if (t0 < g1)
+      place_group(bits, t0, before + lpre, lpre, threadIdx.x * kPer, step_kept, g1, S, lim, loc, inv, cu);
+    __syncthreads();
+    // kept ids to idx[before ..), filtered ids to idx[n_kept + filtered tokens before this step ..)
+    const int n_step = min(STEP, g1 - base);
+    const int fdst = n_kept + (base - before) - step_kept;
+    for (int j = threadIdx.x; j < n_step; j += NT) idx[(j < step_kept ? before : fdst) + j] = loc[j];
+    before += step_kept;
+    __syncthreads();  // loc is reused by the next scan step
   }
   if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) {
-    cu[B] = min(n_kept, lim);
-    count[0] = n_kept;
-    if (mismatch) mismatch[0] = (expect >= 0 && n_kept != expect) ? 1 : 0;
-  }
-}
-
-__global__ __launch_bounds__(kThreads) void build_index_kernel(const uint8_t* __restrict__ keep,
-                                                               int B, int S,
-                                                               int32_t* __restrict__ idx,
-                                                               int32_t* __restrict__ inv,
-                                                               int32_t* __restrict__ cu,
-                                                               int32_t* __restrict__ count,
-                                                               int expect,
-                                                               int32_t* __restrict__ mismatch) {
-  __shared__ int s_wave[kWaves + 1];
-  const int M = B * S;
-  const int lim = expect >= 0 ? expect : 0x7fffffff;
-  constexpr int CHUNK = kThreads * kPer;
-  int n_kept;
-  if (M <= CHUNK) {
-    // one chunk: the scan of the only chunk also gives the total
-    const int t0 = threadIdx.x * kPer;
-    const unsigned bits = load_bits(keep, t0, M);
-    int total = 0;
-    const int pre = block_excl_scan(__popc(bits), &total, s_wave);
-    n_kept = total;
-    scatter_group(bits, t0, pre, n_kept, M, S, lim, idx, inv, cu);
-  } else {
-    // pass 1: number of kept tokens (the filtered positions are placed after the kept ones)
-    int local = 0;
-    for (int t0 = threadIdx.x * kPer; t0 < M; t0 += CHUNK) local += __popc(load_bits(keep, t0, M));
-    int total = 0;
-    (void)block_excl_scan(local, &total, s_wave);
-    n_kept = total;
-    // pass 2: chunked exclusive scan and scatter
-    int before = 0;  // kept tokens before the current chunk
-    for (int base = 0; base < M; base += CHUNK) {
-      const int t0 = base + threadIdx.x * kPer;
-      const unsigned bits = load_bits(keep, t0, M);
-      int chunk_total = 0;
-      const int pre = before + block_excl_scan(__popc(bits), &chunk_total, s_wave);
-      scatter_group(bits, t0, pre, n_kept, M, S, lim, idx, inv, cu);
-      before += chunk_total;
-    }
-  }
-  if (threadIdx.x == 0) {
     cu[B] = min(n_kept, lim);
     count[0] = n_kept;
     if (mismatch) mismatch[0] = (expect >= 0 && n_kept != expect) ? 1 : 0;
@@ -222,20 +190,23 @@ collider_status launch_build_index(const uint8_t* keep, int B, int S, int32_t* i
                                    int32_t* cu, int32_t* count, int expect, int32_t* mismatch,
                                    hipStream_t s) {
   const int64_t M = (int64_t)B * S;
-  if (M <= kMwMin) {
+  if (M <= kSmallMax) {
+    constexpr int NT = 256, STEP = NT * kPer;
+    const int grid = (int)((M + STEP - 1) / STEP);
     COLLIDER_LAUNCH("build_index", s,
-                    hipLaunchKernelGGL(build_index_kernel, dim3(1), dim3(kThreads), 0, s, keep, B, S,
-                                       idx, inv, cu, count, expect, mismatch));
+                    hipLaunchKernelGGL(build_index_kernel<NT>, dim3(grid), dim3(NT), 0, s, keep, B, S,
+                                       STEP, idx, inv, cu, count, expect, mismatch));
   } else {
-    // ranges of whole 8192-token scan steps, at most kMwGrid workgroups (each also sweeps the
-    // whole mask once for its counts)
-    const int64_t chunks = (M + kChunkMW - 1) / kChunkMW;
-    const int64_t per = (chunks + kMwGrid - 1) / kMwGrid;
-    const int T = (int)(per * kChunkMW);
+    // ranges of whole scan steps, at most kBigGrid workgroups (each also sweeps the whole mask once
+    // for its counts)
+    constexpr int NT = 1024, STEP = NT * kPer;
+    const int64_t steps = (M + STEP - 1) / STEP;
+    const int64_t per = (steps + kBigGrid - 1) / kBigGrid;
+    const int T = (int)(per * STEP);
     const int grid = (int)((M + T - 1) / T);
     COLLIDER_LAUNCH("build_index", s,
-                    hipLaunchKernelGGL(build_index_mw_kernel, dim3(grid), dim3(kThreadsMW), 0, s, keep,
-                                       B, S, T, idx, inv, cu, count, expect, mismatch));
+                    hipLaunchKernelGGL(build_index_kernel<NT>, dim3(grid), dim3(NT), 0, s, keep, B, S,
+                                       T, idx, inv, cu, count, expect, mismatch));
   }
   return last_hip_status();
 }
