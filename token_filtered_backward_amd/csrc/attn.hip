@@ -383,9 +383,23 @@ __global__ __launch_bounds__(256, D == 64 ? (FULLD ? 3 : 2) : 1) void attn_dq_ke
     if (i >= nb) continue;
     float out[8];
     const float* er = E + row * LDE;
-    if (c0 < p.rot) {
-      // rotate-half pairs (m, m + rot/2) for m < rot/2; columns from rot on pass through (rot may
-      // end inside this group of 8, and rot/2 may fall inside it)
+    const bool one_side = c0 + 8 <= half || (c0 >= half && c0 + 8 <= p.rot);
+    if (c0 < p.rot && one_side) {
+      // rotate-half pairs (m, m + rot/2) for m < rot/2, the 8 columns all in one half: their
+      // partners and table entries are 8 consecutive values too (vector reads)
+      const int pos = (p.idx ? p.idx[cs + i] : cs + i) % p.S;
+      const bool lower = c0 < half;
+      const int m0 = lower ? c0 : c0 - half;
+      const int pc = lower ? c0 + half : c0 - half;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float2 t = p.rope[(int64_t)pos * half + m0 + e];
+        const float x = er[c0 + e], y = er[pc + e];
+        out[e] = lower ? x * t.x + y * t.y : x * t.x - y * t.y;
+      }
+    } else if (c0 < p.rot) {
+      // the general case: rot/2 or rot falls inside this group of 8 (columns from rot on pass
+      // through), paired per element
       const int pos = (p.idx ? p.idx[cs + i] : cs + i) % p.S;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
