@@ -252,7 +252,9 @@ typedef struct {                /* outputs (weight gradients in the weights' lay
 
 /* dy: bf16 [M, H] (dy_compact = 0) or already compacted [M_kept, H] (dy_compact != 0, e.g. the
  * dx of the layer above produced with dx_compact != 0).  The workspace must not alias any input
- * or output. */
+ * or output.  An index with M_kept = B*S (every token kept: its partition is the identity) runs the
+ * dense path of unfiltered = 1, with the same results and no gather or index lookups; the
+ * workspace size is queried with the same M_kept, so it follows. */
 size_t collider_layer_workspace_bytes(const collider_layer_cfg* cfg, int32_t B, int32_t S,
                                       int32_t M_kept);
 collider_status collider_layer_bwd(const collider_layer_cfg* cfg, const collider_layer_weights* w,

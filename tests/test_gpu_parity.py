@@ -413,6 +413,29 @@ def test_layer_compact_chain_matches_full_layout(layout):
 
 
 @pytest.mark.parametrize("name", ["small_llama", "small_phi"])
+def test_layer_every_token_kept_is_the_dense_path(name):
+    """An index that keeps every token gives exactly the unfiltered baseline's gradients, in the
+    full layout, compact (dx_compact) and from a compact dy alike."""
+    cfg = synth.get_config(name)
+    inp = synth.make_layer_inputs(cfg, r_pct=0)
+    weights, saved, dy = _upload_layer(inp)
+    keep = np.ones(cfg.M, dtype=np.uint8)
+    ix = tfb.build_index(_dev_keep(keep), cfg.B, cfg.S)
+    assert ix.M_kept == cfg.M
+    g_dense = tfb.make_grads(tfb.layer_cfg(cfg, unfiltered=True), cfg.M, cfg.M, "cuda")
+    tfb.layer_bwd(tfb.layer_cfg(cfg, unfiltered=True), weights, saved, dy, tfb.dense_index(cfg.B, cfg.S),
+                  g_dense)
+    lcfg = tfb.layer_cfg(cfg)
+    g_full = tfb.make_grads(lcfg, cfg.M, ix.M_kept, "cuda")
+    tfb.layer_bwd(lcfg, weights, saved, dy, ix, g_full)
+    g_c = tfb.make_grads(lcfg, cfg.M, ix.M_kept, "cuda", dx_compact=True)
+    tfb.layer_bwd(lcfg, weights, saved, dy, ix, g_c, dx_compact=True, dy_compact=True)
+    for k in g_dense:
+        assert torch.equal(g_full[k], g_dense[k]), k
+        assert torch.equal(g_c[k], g_dense[k]), k
+
+
+@pytest.mark.parametrize("name", ["small_llama", "small_phi"])
 def test_stack_of_layers(name):
     """Three layers from one consistent forward, chained top to bottom with compact gradients
     between layers (the same mask in every layer), against the oracle's stack backward."""

@@ -162,7 +162,9 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
                           const collider_index& ix, collider_layer_grads* gr, int dx_compact,
                           void* ws, size_t ws_bytes, hipStream_t s, size_t* need) {
   const bool llama = c.kind == COLLIDER_LAYER_LLAMA;
-  const bool unf = c.unfiltered != 0;  // dense baseline: full layout, no index
+  // dense: the unfiltered baseline, or an index that keeps every token (its partition is then the
+  // identity, so the full layout is the compacted one and no gather or index lookup is needed)
+  const bool unf = c.unfiltered != 0 || ix.M_kept == ix.B * ix.S;
   const int B = ix.B, S = ix.S, M = B * S, Mk = unf ? M : ix.M_kept;
   const int H = c.hidden, I = c.inter, d = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
   const int nqd = nq * d, nkvd = nkv * d, nqkv = nqd + 2 * nkvd;
