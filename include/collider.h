@@ -370,15 +370,11 @@ collider_status collider_gemm_set_policy(int32_t policy);
 
 /* The work decomposition the current policy picks for one bf16 GEMM C[M, N] = A B with reduction
  * length K, on the current device (host only, launches nothing).  layout 0: dX = dY w (A [M, K]
- * K-contiguous, B [K, N] N-contiguous, bf16 C); layout 1: dW = dY^T X (A and B token-major, fp32 C);
- * layout 2: dW = X^T dY with X given transposed (A [M, K] K-contiguous with K padded to a multiple
- * of 64, B token-major, fp32 C), as the layer's weight-gradient GEMMs with [in, out] weights.
- * concurrent 1: the plan for GEMMs that run beside another stream (the layer's: whole tiles only);
- * 2: the plan for such GEMMs that run beside longer work (the tile shape with the fewest
- * CU-microseconds, within 3x of the fastest plan's duration).  out[7] receives
+ * K-contiguous, B [K, N] N-contiguous, bf16 C); layout 1: dW = dY^T X (A and B token-major, fp32 C).
+ * concurrent != 0: the plan for GEMMs that run beside another stream (the layer's).  out[7] receives
  * tile rows, tile columns, K-splits, whole tiles, stream-K tiles, workgroups, and 1 when the
- * direct-to-LDS kernel runs (0: register-staged).  COLLIDER_ERR_SHAPE for M or N <= 0, K < 0,
- * N % 8 != 0, or layout / concurrent out of range; COLLIDER_ERR_NULL for out == NULL. */
+ * direct-to-LDS kernel runs (0: register-staged).  COLLIDER_ERR_SHAPE for M or N <= 0, K < 0 or
+ * N % 8 != 0; COLLIDER_ERR_NULL for out == NULL. */
 collider_status collider_gemm_describe_plan(int32_t M, int32_t N, int32_t K, int32_t layout,
                                            int32_t concurrent, int32_t* out);
 int32_t collider_profile_collect(char* names, int32_t name_cap, double* total_ms, int32_t* launches,

@@ -344,9 +344,7 @@ def collider_gemm_set_policy(policy: int):
 
 
 def collider_gemm_describe_plan(M, N, K, layout, concurrent=False):
-    """{bm, bn, splits, dp_tiles, sk_tiles, grid, lds} of the bf16 GEMM plan (host only).
-    layout 0 dX, 1 dW with token-major operands, 2 dW with the transposed operand; concurrent
-    0 / False alone, 1 / True beside another stream, 2 beside longer work (throughput plan)."""
+    """{bm, bn, splits, dp_tiles, sk_tiles, grid, lds} of the bf16 GEMM plan (host only)."""
     out = (_i32 * 7)()
     _check(lib().collider_gemm_describe_plan(int(M), int(N), int(K), int(layout), int(concurrent), out),
            "collider_gemm_describe_plan")

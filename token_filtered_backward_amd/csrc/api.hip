@@ -337,28 +337,19 @@ collider_status collider_gemm_set_policy(int32_t policy) {
 collider_status collider_gemm_describe_plan(int32_t M, int32_t N, int32_t K, int32_t layout,
                                            int32_t concurrent, int32_t* out) {
   if (!out) return COLLIDER_ERR_NULL;
-  if (M <= 0 || N <= 0 || K < 0 || N % 8 || layout < 0 || layout > 2 || concurrent < 0 ||
-      concurrent > 2)
-    return COLLIDER_ERR_SHAPE;
+  if (M <= 0 || N <= 0 || K < 0 || N % 8 || (layout != 0 && layout != 1)) return COLLIDER_ERR_SHAPE;
   GemmProblem g{};
   g.M = M;
   g.N = N;
   g.K = K;
   g.concurrent = concurrent != 0;
-  g.throughput = concurrent == 2;
   if (layout == 0) {  // dX = dY w: A [M, K] K-contiguous, B [K, N] N-contiguous, bf16 out
     g.a_kmajor = true;
     g.lda = K;
     g.ldb = N;
     g.epi = EPI_BF16;
-  } else if (layout == 1) {  // dW = dY^T X: both operands token-major [K, M] and [K, N], fp32 out
+  } else {  // dW = dY^T X: both operands token-major [K, M] and [K, N], fp32 out
     g.lda = M;
-    g.ldb = N;
-    g.epi = EPI_F32;
-  } else {  // dW = X^T dY with X given transposed: A [M, K padded to 64] K-contiguous, B [K, N]
-    g.a_kmajor = true;
-    g.a_kpad = true;
-    g.lda = (K + 63) / 64 * 64;
     g.ldb = N;
     g.epi = EPI_F32;
   }

@@ -1099,18 +1099,6 @@ Plan make_plan(const GemmProblem& p) {
     int r = 0, c = 0;
     return (e && sscanf(e, "%dx%d", &r, &c) == 2) ? r * 1000 + c : 0;
   }();
-  // Throughput plans (p.throughput, whole tiles): the tile shape whose tiles take the fewest
-  // CU-microseconds, provided the GEMM's duration stays within kTputSlack of the fastest plan's.
-  // Measured (TinyLlama-shaped layer, 40%): 256 x 256 tiles for the weight-gradient GEMMs of the
-  // down, gate/up and o projections (which run beside the dA, dX and attention work) took the
-  // layer 1.157 -> 1.134 ms, though the dW GEMM of o alone went 52 -> 103 us on its 64 tiles.
-  constexpr double kTputSlack = 3.0;
-  const bool tput = p.throughput && policy == 3;
-  struct TputPlan {
-    Plan plan;
-    double cu_us;
-  } tput_plans[2 * kNumCfgs];  // at most one per tile shape and pass
-  int n_tput = 0;
   // 256 x 256 only in the direct-to-LDS kernel (staged through registers it would spill)
   for (int pass = 0; pass < 2 && best.cost >= 1e300; ++pass)  // pass 1: the override does not apply
   for (int c = lds ? 0 : 1; c < kNumCfgs; ++c) {
@@ -1131,13 +1119,8 @@ Plan make_plan(const GemmProblem& p) {
         const long items = tiles * splits;
         const long slots = (long)ncu * per_cu;
         const long waves = (items + slots - 1) / slots;
-        const double t_item = (ks / kBK) * t_it + (splits > 1 ? part_tile : epi_tile);
-        double cost = (double)waves * per_cu * t_item;
+        double cost = (double)waves * per_cu * ((ks / kBK) * t_it + (splits > 1 ? part_tile : epi_tile));
         if (splits > 1) cost += ((double)splits * p.M * p.N * 4.0 + (double)p.M * p.N * eb) / bw + 4.0;
-        if (tput && splits == 1) {  // CU-microseconds of the tiles, within kTputSlack of the duration
-          tput_plans[n_tput++] = {Plan{c, tc.bm, tc.bn, lds, 1, ks, (int)tiles, 0, ipt, (int)items, cost},
-                                  (double)items * t_item};
-        }
         if (cost < best.cost * 0.98)
           best = Plan{c, tc.bm, tc.bn, lds, splits, ks, (int)tiles, 0, ipt, (int)items, cost};
       }
@@ -1154,14 +1137,6 @@ Plan make_plan(const GemmProblem& p) {
       if (cost < best.cost * 0.98)
         best = Plan{c, tc.bm, tc.bn, lds, 1, ipt * kt, (int)dp, (int)sk, ipt, (int)grid, cost};
     }
-  }
-  if (tput && n_tput > 0) {
-    const TputPlan* pick = nullptr;
-    for (int i = 0; i < n_tput; ++i)
-      if (tput_plans[i].plan.cost <= kTputSlack * best.cost &&
-          (!pick || tput_plans[i].cu_us < pick->cu_us * 0.98))
-        pick = &tput_plans[i];
-    if (pick) return pick->plan;
   }
   return best;
 }

@@ -205,10 +205,6 @@ struct GemmProblem {
   // runs beside work on another stream: the default plan then takes whole tiles only (persistent
   // stream-K grids and K-split waves would hold every CU the other stream could use)
   bool concurrent;
-  // with `concurrent`: runs beside longer work on the other stream, so the plan minimises the CU
-  // time its tiles take (the GEMM's own duration may grow; the CUs it leaves idle serve the other
-  // stream) instead of its duration
-  bool throughput;
 };
 // Work decomposition of the bf16 GEMMs: 0 = cost model, 1 = whole tiles and K-splits only,
 // 2 = stream-K wherever the direct-to-LDS kernel applies, 3 = whole tiles only.

@@ -292,12 +292,6 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
   // same plan in single-stream mode, so per-kernel timings measure the kernels the layer runs)
   GemmProblem* gl[] = {&g_dA, &g_dw2, &g_dXmid, &g_dwmid, &g_dO, &g_dwo, &g_dXin, &g_dwqkv, &g_dwfc1};
   for (GemmProblem* p : gl) p->concurrent = true;
-  // the side stream's weight-gradient GEMMs that run beside longer work on `s` (dA, the dX chain,
-  // attention) take the plan with the fewest CU-microseconds; those after attention (qkv, fc1)
-  // end the layer beside the last dX GEMM and keep the fastest plan
-  g_dw2.throughput = true;
-  g_dwmid.throughput = true;
-  g_dwo.throughput = true;
   size_t gemm_need = 0, gemm_need2 = 0;
   for (const GemmProblem* p : gl) {
     if (p->M <= 0) continue;
