@@ -121,7 +121,8 @@ collider_status collider_scatter_rows(const void* src, int64_t ld_src, void* dst
  *   db = colsum(dy)    [N] float32 (optional, NULL to skip; same accumulate rule)
  * x [M_kept, K] (row stride ld_x), dy [M_kept, N] (ld_dy), w [N, K] dense, all of dtype dt
  * (COLLIDER_BF16: bf16 operands, fp32 accumulation; COLLIDER_F32: fp32 throughout).
- * M_kept = 0 gives dw = 0, db = 0.
+ * M_kept = 0 gives dw = 0, db = 0.  With COLLIDER_BF16 the workspace also holds x transposed
+ * (K x M_kept rounded up to 64, bf16), which the dw GEMM reads along the token reduction.
  * ------------------------------------------------------------------------------------------- */
 size_t collider_linear_workspace_bytes(collider_dtype dt, int32_t M_kept, int32_t K, int32_t N);
 collider_status collider_linear_bwd_reduced(collider_dtype dt, int32_t M_kept, int32_t K, int32_t N,

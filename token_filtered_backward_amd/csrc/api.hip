@@ -177,14 +177,31 @@ static void linear_problems(collider_dtype dt, int32_t Mk, int32_t K, int32_t N,
   pdw->name = "linear_dw";
 }
 
+// bf16: x' is copied transposed ([K, ldT], tokens contiguous, zero columns up to a multiple of 64)
+// into the workspace, so that the weight-gradient GEMM reads it with 16-byte LDS reads along the
+// reduction, as the layer's weight-gradient GEMMs read their transposed operands
+static int linear_ldT(int32_t M_kept) { return (M_kept + 63) / 64 * 64; }
+
+static void linear_use_xT(GemmProblem* pdw, const void* xT, int32_t M_kept) {
+  pdw->B0 = xT;
+  pdw->ldb = linear_ldT(M_kept);
+  pdw->b_kmajor = true;
+  pdw->b_kpad = true;
+}
+
 size_t collider_linear_workspace_bytes(collider_dtype dt, int32_t M_kept, int32_t K, int32_t N) {
   if (M_kept < 0 || K < 1 || N < 1) return 0;
   GemmProblem a, b;
   linear_problems(dt, M_kept, K, N, nullptr, K, nullptr, N, nullptr, nullptr, nullptr, 0, &a, &b);
   Carver cv(nullptr);
   cv.take<float>((size_t)colsum_parts_count(M_kept) * N);  // bias column-sum partials
-  if (dt == COLLIDER_BF16)
+  if (dt == COLLIDER_BF16) {
+    if (M_kept > 0) {
+      cv.take<uint16_t>((size_t)K * linear_ldT(M_kept));  // x' transposed
+      linear_use_xT(&b, nullptr, M_kept);
+    }
     cv.take<char>(std::max(gemm_bf16_workspace_bytes(a), gemm_bf16_workspace_bytes(b)));
+  }
   return cv.bytes();
 }
 
@@ -207,6 +224,8 @@ collider_status collider_linear_bwd_reduced(collider_dtype dt, int32_t M_kept, i
   linear_problems(dt, M_kept, K, N, x, ld_x, dy, ld_dy, w, dx, dw, accumulate, &pdx, &pdw);
   Carver cv(ws);
   float* parts = cv.take<float>((size_t)colsum_parts_count(M_kept) * N);
+  uint16_t* xT = (dt == COLLIDER_BF16 && M_kept > 0) ? cv.take<uint16_t>((size_t)K * linear_ldT(M_kept))
+                                                     : nullptr;
   char* gws = cv.take<char>(0);
   const size_t gws_bytes = ws_bytes > (size_t)(gws - (char*)ws) ? ws_bytes - (gws - (char*)ws) : 0;
   collider_status st = COLLIDER_OK;
@@ -214,7 +233,12 @@ collider_status collider_linear_bwd_reduced(collider_dtype dt, int32_t M_kept, i
     if (dx) st = gemm_f32(pdx, stream);
     if (st == COLLIDER_OK) st = gemm_f32(pdw, stream);
   } else {
-    if (dx) st = gemm_bf16(pdx, gws, gws_bytes, stream);
+    if (xT) {
+      st = launch_cols_recompute(COL_COPY, (const uint16_t*)x, ld_x, nullptr, nullptr, nullptr, nullptr,
+                                 nullptr, nullptr, M_kept, K, xT, linear_ldT(M_kept), stream);
+      linear_use_xT(&pdw, xT, M_kept);
+    }
+    if (st == COLLIDER_OK && dx) st = gemm_bf16(pdx, gws, gws_bytes, stream);
     if (st == COLLIDER_OK) st = gemm_bf16(pdw, gws, gws_bytes, stream);
   }
   if (st == COLLIDER_OK && db) {

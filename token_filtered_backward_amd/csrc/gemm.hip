@@ -1034,7 +1034,7 @@ struct TileCfg {
   double t_k, t_mn;
 };
 constexpr TileCfg kCfgs[] = {{256, 256, 1.62, 1.80}, {256, 128, 1.01, 1.45}, {128, 256, 1.14, 1.37},
-                             {128, 128, 0.69, 0.91}, {160, 256, 1.43, 0.0},  {192, 256, 1.44, 0.0},
+                             {128, 128, 0.69, 0.91}, {160, 256, 1.21, 0.0},  {192, 256, 1.44, 0.0},
                              {224, 256, 1.54, 0.0}};
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
@@ -1131,7 +1131,12 @@ Plan make_plan(const GemmProblem& p) {
       const long n_it = sk * ipt;
       const long grid = n_it < ncu ? n_it : ncu;
       const double per_wg = (double)((n_it + grid - 1) / grid) * kt / kBK;
-      const double cost = (double)dp / grid * ((double)ipt * kt / kBK * t_it + epi_tile) + per_wg * t_it +
+      // A stream-K k-tile costs kSkSlow times a whole tile's: measured on MI355X with 256 x 256
+      // tiles, the dX GEMM of the TinyLlama gate/up projection (M' 4916, K 11264) took 273 us + a
+      // 57 us fix-up as stream-K (110 k-tiles per workgroup: 2.5 us each) against 186 us in whole
+      // 160-row tiles, and the LM head's dh' (K 32000) 0.73 ms against 0.55 ms.
+      constexpr double kSkSlow = 1.6;
+      const double cost = (double)dp / grid * ((double)ipt * kt / kBK * t_it + epi_tile) + per_wg * t_it * kSkSlow +
                           (double)sk / grid * epi_tile + 2.0 * part_tile +
                           2.0 * grid * tc.bm * tc.bn * 4.0 / bw + 4.0;
       if (cost < best.cost * 0.98)
