@@ -16,7 +16,8 @@
 //     the P / dS accumulators are directly the A operands of P^T dO and dS^T Q.  A workgroup sums
 //     over a slice of the query heads sharing its KV head; slices go to fp32 partial buffers.
 //  3. attn_dkv_finalize: sums the slices in a fixed order, applies the rotary backward to dK and
-//     stores bf16 dk, dv.
+//     stores bf16 dk, dv.  With a single slice (one query head per KV head, or few keys) the dK/dV
+//     kernel does this itself from an LDS copy of its tile, and writes no partials.
 // Token tiles [64 rows x D] live in LDS once, row-major (XOR-swizzled chunks for D = 64, padded
 // rows for D = 128).  Operands that need the token index as the MFMA reduction index (K in dS K;
 // Q and dO in P^T dO and dS^T Q) are read with
@@ -432,7 +433,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_dkv_kernel(AttnPara
   constexpr int BKV = 128, BQ = 64, KK = D / 16, DT = D / 32;
   constexpr int TB = TokTile<D>::BYTES;
   constexpr int BUF = 2 * TB + 2 * BQ * 4;  // Q tile, dO tile, lse*log2e, D
-  __shared__ __align__(16) char smem[2 * BUF];
+  // with a single head slice the epilogue stages the fp32 dK and dV tiles ([BKV][LDF] each) here
+  constexpr int LDF = D + 4;
+  constexpr int STAGE = 2 * BKV * LDF * 4;
+  __shared__ __align__(16) char smem[2 * BUF > STAGE ? 2 * BUF : STAGE];
   // grid (kv head x head slice, sequence, key block): the first key blocks, which see the most
   // queries, are dispatched first
   const int b = blockIdx.y, g = blockIdx.x / p.HS, hs = blockIdx.x % p.HS;
@@ -597,6 +601,50 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_dkv_kernel(AttnPara
     if (it + 1 < n_iter) put((it + 1) & 1);
     __syncthreads();
   }
+  if (p.HS == 1) {
+    // the whole dK / dV of these keys: scale, rotary backward and bf16 stores here, through LDS
+    // (each thread then takes 4 consecutive columns of a row, as the finalize kernel does)
+    __syncthreads();  // every wavefront is done with the Q / dO tiles
+    float* Ek = (float*)smem;
+    float* Ev = Ek + BKV * LDF;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wave * 32 + acc_row(r, lane);
+        Ek[row * LDF + t * 32 + l32] = dka[t][r] * p.scale;
+        Ev[row * LDF + t * 32 + l32] = dva[t][r];
+      }
+    __syncthreads();
+    const int half = p.rot >> 1;
+    for (int q = threadIdx.x; q < BKV * (D / 4); q += 256) {
+      const int row = q / (D / 4), m0 = (q % (D / 4)) * 4;
+      const int j = k0 + row;
+      if (j >= nb) continue;
+      const float* ek = Ek + row * LDF;
+      const float4 x4 = *(const float4*)(ek + m0);
+      const float4 v4 = *(const float4*)(Ev + row * LDF + m0);
+      const float xk[4] = {x4.x, x4.y, x4.z, x4.w};
+      float out[4] = {x4.x, x4.y, x4.z, x4.w};
+      if (m0 < p.rot) {
+        const int pos = (p.idx ? p.idx[cs + j] : cs + j) % p.S;
+        const float2* tab = p.rope + (int64_t)pos * half;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = m0 + e;
+          if (m >= p.rot) continue;
+          const bool lower = m < half;
+          const float2 r = tab[lower ? m : m - half];
+          const float y = ek[lower ? m + half : m - half];
+          out[e] = lower ? xk[e] * r.x + y * r.y : xk[e] * r.x - y * r.y;
+        }
+      }
+      const int64_t o = (int64_t)(cs + j);
+      *(uint2*)(p.dk + o * p.ld_dk + g * D + m0) = make_uint2(pack2bf(out[0], out[1]), pack2bf(out[2], out[3]));
+      *(uint2*)(p.dv + o * p.ld_dv + g * D + m0) = make_uint2(pack2bf(v4.x, v4.y), pack2bf(v4.z, v4.w));
+    }
+    return;
+  }
   // partial slices: [HS][M_kept][nkv][D]
 #pragma unroll
   for (int t = 0; t < DT; ++t)
@@ -722,8 +770,10 @@ static AttnWs carve_attn(const collider_attn_cfg& c, int B, int S, int M_kept, v
   AttnWs w;
   const int hs = choose_hs(c, B, S, M_kept);
   w.D = cv.take<float>((size_t)M_kept * c.n_q_heads);
-  w.dkp = cv.take<float>((size_t)hs * M_kept * c.n_kv_heads * c.head_dim);
-  w.dvp = cv.take<float>((size_t)hs * M_kept * c.n_kv_heads * c.head_dim);
+  // partial dK / dV slices (a single slice is finished inside the dK / dV kernel)
+  const size_t part = hs > 1 ? (size_t)hs * M_kept * c.n_kv_heads * c.head_dim : 0;
+  w.dkp = cv.take<float>(part);
+  w.dvp = cv.take<float>(part);
   w.rope = cv.take<float>((size_t)S * (c.rot_dims > 0 ? c.rot_dims : 2));
   w.bytes = cv.bytes();
   return w;
@@ -798,16 +848,18 @@ collider_status attn_bwd(const collider_attn_cfg& c, const collider_index& ix,
     else
       COLLIDER_LAUNCH("attn_dq", s, hipLaunchKernelGGL((attn_dq_kernel<64, false>), gq, dim3(256), 0, s, p));
     COLLIDER_LAUNCH("attn_dkv", s, hipLaunchKernelGGL(attn_dkv_kernel<64>, gk, dim3(256), 0, s, p));
-    COLLIDER_LAUNCH("attn_dkv_finalize", s,
-                    hipLaunchKernelGGL(attn_dkv_finalize_kernel<64>, dim3(fin_blocks), dim3(256), 0, s, p));
+    if (p.HS > 1)
+      COLLIDER_LAUNCH("attn_dkv_finalize", s,
+                      hipLaunchKernelGGL(attn_dkv_finalize_kernel<64>, dim3(fin_blocks), dim3(256), 0, s, p));
   } else {
     if (full)
       COLLIDER_LAUNCH("attn_dq", s, hipLaunchKernelGGL((attn_dq_kernel<128, true>), gq, dim3(256), 0, s, p));
     else
       COLLIDER_LAUNCH("attn_dq", s, hipLaunchKernelGGL((attn_dq_kernel<128, false>), gq, dim3(256), 0, s, p));
     COLLIDER_LAUNCH("attn_dkv", s, hipLaunchKernelGGL(attn_dkv_kernel<128>, gk, dim3(256), 0, s, p));
-    COLLIDER_LAUNCH("attn_dkv_finalize", s,
-                    hipLaunchKernelGGL(attn_dkv_finalize_kernel<128>, dim3(fin_blocks), dim3(256), 0, s, p));
+    if (p.HS > 1)
+      COLLIDER_LAUNCH("attn_dkv_finalize", s,
+                      hipLaunchKernelGGL(attn_dkv_finalize_kernel<128>, dim3(fin_blocks), dim3(256), 0, s, p));
   }
   return last_hip_status();
 }
