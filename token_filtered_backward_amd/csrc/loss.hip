@@ -9,6 +9,8 @@
 #include <atomic>
 #include <mutex>
 
+#include <algorithm>
+
 #include "internal.h"
 
 namespace collider {
@@ -185,22 +187,25 @@ __global__ __launch_bounds__(256) void ce_grad_kernel(const uint16_t* __restrict
   __shared__ MaxSum s_ms[4];
   const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t = rowmap ? rowmap[c] : c;
-  const int y = labels[t];
   const int nvec = V >> 3;
   const uint4* src = (const uint4*)(logits + t * ld);
   uint4* dst = (uint4*)(dl + (int64_t)c * ldd);
-  if (y < 0 || y >= V) {  // no target: no loss, no gradient
-    for (int i = tid; i < nvec; i += 256) dst[i] = make_uint4(0, 0, 0, 0);
-    return;
-  }
   MaxSum ms{-INFINITY, 0.f};
   uint4 row[RV > 0 ? RV : 1];
   if constexpr (RV > 0) {
+    // the row's loads go out before the label is looked at, so that they need not wait for it
 #pragma unroll
     for (int j = 0; j < RV; ++j) {
       const int i = tid + 256 * j;
       row[j] = i < nvec ? src[i] : make_uint4(0, 0, 0, 0);
     }
+  }
+  const int y = labels[t];
+  if (y < 0 || y >= V) {  // no target: no loss, no gradient
+    for (int i = tid; i < nvec; i += 256) dst[i] = make_uint4(0, 0, 0, 0);
+    return;
+  }
+  if constexpr (RV > 0) {
 #pragma unroll
     for (int j = 0; j < RV; ++j)
       if (tid + 256 * j < nvec) ms = ms_add8(ms, row[j]);
@@ -274,24 +279,27 @@ __global__ __launch_bounds__(256) void ce_loss_kernel(const uint16_t* __restrict
   __shared__ MaxSum s_ms[4];
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int y = labels[t];
-  if (y < 0 || y >= V) {
-    if (tid == 0) loss[t] = 0.f;
-    return;
-  }
   const int nvec = V >> 3;
   const uint16_t* row = logits + t * ld;
   const uint4* src = (const uint4*)row;
-  float zy = 0.f;
-  if (tid == 0) zy = bf2f(row[y]);
   MaxSum ms{-INFINITY, 0.f};
+  uint4 v[NV > 0 ? NV : 1];
   if constexpr (NV > 0) {
-    uint4 v[NV];
+    // the row's loads go out before the label is looked at, so that they need not wait for it
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       v[u] = make_uint4(0, 0, 0, 0);
       if (tid + 256 * u < nvec) v[u] = src[tid + 256 * u];
     }
+  }
+  const int y = labels[t];
+  if (y < 0 || y >= V) {
+    if (tid == 0) loss[t] = 0.f;
+    return;
+  }
+  float zy = 0.f;
+  if (tid == 0) zy = bf2f(row[y]);
+  if constexpr (NV > 0) {
 #pragma unroll
     for (int u = 0; u < NV; ++u)
       if (tid + 256 * u < nvec) ms = ms_add8(ms, v[u]);
@@ -513,8 +521,9 @@ __global__ __launch_bounds__(kEmbChunk) void embed_place_chunks_kernel(
 }
 
 // dE[v, :] (+)= sum over j < off[v+1] - off[v] of dx[row(sorted[off[v] + j]), :]; one wavefront per
-// vocabulary row, 8 columns per lane per step; rows with no kept token are written as zeros
-// (or left as they are when accumulating).
+// vocabulary row, 8 columns per lane per step; rows with no kept token are skipped (zeroed before
+// by embed_zero_kernel, or left as they are when accumulating).  Writing the zero rows here, a few
+// KB per wavefront, took the TinyLlama-vocabulary gradient (32000 x 2048 fp32) 80 us.
 __global__ __launch_bounds__(256) void embed_rowsum_kernel(const uint16_t* __restrict__ dx,
                                                            int64_t ld, const int32_t* __restrict__ idx,
                                                            const int32_t* __restrict__ off,
@@ -524,21 +533,34 @@ __global__ __launch_bounds__(256) void embed_rowsum_kernel(const uint16_t* __res
   const int v = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (v >= V) return;
   const int b = off[v], n = off[v + 1] - b;
-  if (n == 0 && accumulate) return;
+  if (n == 0) return;  // the row is zero already (or keeps its value when accumulating)
   float* out = dE + (int64_t)v * H;
-  for (int col = lane * 8; col < H; col += 512) {
+  for (int c0 = 0; c0 < H; c0 += 512) {  // uniform over the wavefront (the shuffles below)
+    const int col = c0 + lane * 8;
+    const bool on = col < H;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < n; ++j) {
-      const int c = sorted[b + j];
-      const int64_t r = idx ? idx[c] : c;
-      const uint4 u = *(const uint4*)(dx + r * ld + col);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    for (int j0 = 0; j0 < n; j0 += 64) {
+      // the source rows of up to 64 tokens, looked up by the lanes together rather than one
+      // token after another; then added in token order
+      const int nj = min(64, n - j0);
+      int rl = 0;
+      if (lane < nj) {
+        const int c = sorted[b + j0 + lane];
+        rl = idx ? idx[c] : c;
+      }
+      for (int j = 0; j < nj; ++j) {
+        const int64_t r = __shfl(rl, j, 64);
+        if (!on) continue;
+        const uint4 u = *(const uint4*)(dx + r * ld + col);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] += bflo(w[e]);
-        acc[2 * e + 1] += bfhi(w[e]);
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += bflo(w[e]);
+          acc[2 * e + 1] += bfhi(w[e]);
+        }
       }
     }
+    if (!on) continue;
     float4* o = (float4*)(out + col);
     float4 a = make_float4(acc[0], acc[1], acc[2], acc[3]), c4 = make_float4(acc[4], acc[5], acc[6], acc[7]);
     if (accumulate) {
@@ -549,6 +571,13 @@ __global__ __launch_bounds__(256) void embed_rowsum_kernel(const uint16_t* __res
     o[0] = a;
     o[1] = c4;
   }
+}
+
+// dE = 0 in 16-byte stores (the rows of ids no token has stay so; embed_rowsum_kernel writes the
+// others)
+__global__ __launch_bounds__(256) void embed_zero_kernel(float4* __restrict__ p, int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 // Raises embed_place_kernel<true>'s dynamic-LDS limit to the cursor array's size, once per device.
@@ -638,6 +667,13 @@ collider_status launch_embedding_bwd(const uint16_t* dx, int64_t ld, int dx_comp
     COLLIDER_LAUNCH("embed_place", s,
                     hipLaunchKernelGGL(embed_place_kernel<false>, dim3(1), dim3(1024), 0, s, ids, idx,
                                        rows, V, off, cursor, sorted));
+  }
+  if (!accumulate) {
+    const int64_t n4 = (int64_t)V * H / 4;
+    const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 8192);
+    COLLIDER_LAUNCH("embed_zero", s,
+                    hipLaunchKernelGGL(embed_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                                       (float4*)dE, n4));
   }
   COLLIDER_LAUNCH("embed_rowsum", s,
                   hipLaunchKernelGGL(embed_rowsum_kernel, dim3((V + 3) / 4), dim3(256), 0, s, dx, ld,
