@@ -279,27 +279,24 @@ __global__ __launch_bounds__(256) void ce_loss_kernel(const uint16_t* __restrict
   __shared__ MaxSum s_ms[4];
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nvec = V >> 3;
-  const uint16_t* row = logits + t * ld;
-  const uint4* src = (const uint4*)row;
-  MaxSum ms{-INFINITY, 0.f};
-  uint4 v[NV > 0 ? NV : 1];
-  if constexpr (NV > 0) {
-    // the row's loads go out before the label is looked at, so that they need not wait for it
-#pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      v[u] = make_uint4(0, 0, 0, 0);
-      if (tid + 256 * u < nvec) v[u] = src[tid + 256 * u];
-    }
-  }
   const int y = labels[t];
   if (y < 0 || y >= V) {
     if (tid == 0) loss[t] = 0.f;
     return;
   }
+  const int nvec = V >> 3;
+  const uint16_t* row = logits + t * ld;
+  const uint4* src = (const uint4*)row;
   float zy = 0.f;
   if (tid == 0) zy = bf2f(row[y]);
+  MaxSum ms{-INFINITY, 0.f};
   if constexpr (NV > 0) {
+    uint4 v[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (tid + 256 * u < nvec) v[u] = src[tid + 256 * u];
+    }
 #pragma unroll
     for (int u = 0; u < NV; ++u)
       if (tid + 256 * u < nvec) ms = ms_add8(ms, v[u]);
