@@ -33,10 +33,17 @@ constexpr int kSelThreads = 1024;
 // Four passes pick the threshold key byte by byte from the top (a 256-bin histogram of the keys
 // that match the bytes chosen so far); a last pass keeps every key above the threshold and the
 // first `need` keys equal to it in token order (a block-wide running count).
+// CACHE: the scores of M <= kSelThreads * kSelCached tokens are loaded once, all loads in flight,
+// and kept in registers through the passes (re-reading them each pass cost a memory round trip per
+// score and thread: 24 us for 8192 tokens).
+constexpr int kSelCached = 8;
+template <bool CACHE>
 __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* __restrict__ score,
                                                                   int M, int n_keep,
                                                                   uint8_t* __restrict__ keep) {
-  __shared__ uint32_t hist[256];
+  // a histogram per wavefront (atomics of different wavefronts never collide; most keys share
+  // their top bytes, and one shared histogram serialised every atomic of the pass on a few bins)
+  __shared__ uint32_t hist[kSelThreads / 64][256];
   __shared__ uint32_t s_sel[2];
   __shared__ uint32_t s_wsum[kSelThreads / 64];
   __shared__ uint32_t s_carry;
@@ -46,13 +53,44 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* _
     for (int t = tid; t < M; t += kSelThreads) keep[t] = v;
     return;
   }
+  uint32_t kc[CACHE ? kSelCached : 1];
+  if constexpr (CACHE) {
+#pragma unroll
+    for (int q = 0; q < kSelCached; ++q) {
+      const int t = tid + kSelThreads * q;
+      kc[q] = t < M ? score_key(score[t]) : 0u;
+    }
+  }
   uint32_t prefix = 0, pmask = 0, need = (uint32_t)n_keep;
   for (int d = 3; d >= 0; --d) {
-    for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+    for (int i = tid; i < 256 * (kSelThreads / 64); i += kSelThreads) (&hist[0][0])[i] = 0;
     __syncthreads();
-    for (int t = tid; t < M; t += kSelThreads) {
-      const uint32_t k = score_key(score[t]);
-      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> (8 * d)) & 255u], 1u);
+    // a thread adds its run of equal bins with one atomic (a wavefront's lanes still share bins)
+    uint32_t cur = 0u, run = 0u;
+    auto count = [&](uint32_t k) {
+      if ((k & pmask) != prefix) return;
+      const uint32_t b = (k >> (8 * d)) & 255u;
+      if (run && b != cur) {
+        atomicAdd(&hist[wave][cur], run);
+        run = 0u;
+      }
+      cur = b;
+      ++run;
+    };
+    if constexpr (CACHE) {
+#pragma unroll
+      for (int q = 0; q < kSelCached; ++q)
+        if (tid + kSelThreads * q < M) count(kc[q]);
+    } else {
+      for (int t = tid; t < M; t += kSelThreads) count(score_key(score[t]));
+    }
+    if (run) atomicAdd(&hist[wave][cur], run);
+    __syncthreads();
+    if (tid < 256) {  // the wavefronts' histograms summed into the first
+      uint32_t tot = 0;
+#pragma unroll
+      for (int w = 0; w < kSelThreads / 64; ++w) tot += hist[w][tid];
+      hist[0][tid] = tot;
     }
     __syncthreads();
     if (wave == 0) {
@@ -60,7 +98,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* _
       uint32_t loc[4], sum = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        loc[q] = hist[255 - 4 * lane - q];
+        loc[q] = hist[0][255 - 4 * lane - q];
         sum += loc[q];
       }
       uint32_t incl = sum;
@@ -135,9 +173,14 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* _
 collider_status launch_select_topk(const float* score, int M, int n_keep, uint8_t* keep,
                                    hipStream_t s) {
   if (M <= 0) return COLLIDER_OK;
-  COLLIDER_LAUNCH("select_topk", s,
-                  hipLaunchKernelGGL(select_topk_kernel, dim3(1), dim3(kSelThreads), 0, s, score, M,
-                                     n_keep, keep));
+  if (M <= kSelThreads * kSelCached)
+    COLLIDER_LAUNCH("select_topk", s,
+                    hipLaunchKernelGGL(select_topk_kernel<true>, dim3(1), dim3(kSelThreads), 0, s, score,
+                                       M, n_keep, keep));
+  else
+    COLLIDER_LAUNCH("select_topk", s,
+                    hipLaunchKernelGGL(select_topk_kernel<false>, dim3(1), dim3(kSelThreads), 0, s, score,
+                                       M, n_keep, keep));
   return last_hip_status();
 }
 
