@@ -1039,8 +1039,10 @@ constexpr TileCfg kCfgs[] = {{256, 256, 1.62, 1.80}, {256, 128, 1.01, 1.45}, {12
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
 // Direct-to-LDS pipeline of each tile shape: k-tile depth KT and stage count NS, within the
-// 160 KB of LDS a workgroup may hold (NS * (BM + BN) * KT * 2 bytes).  Deeper pipelines hide more
-// memory latency; 32-deep k-tiles buy the extra stages for the large tiles.
+// 160 KB of LDS a workgroup may hold (NS * (BM + BN) * KT * 2 bytes).  Every shape keeps 64-deep
+// k-tiles: 32-deep ones with four stages for the 192- and 256-row tiles (the same prefetch distance
+// in bytes, finer grained) measured 5-15% slower on MI355X, the extra barrier and loop overhead per
+// MFMA outweighing the deeper pipeline.
 constexpr int lds_kt(int, int) { return 64; }
 constexpr int lds_ns(int bm, int bn) {
   return (bn == 256 && (bm == 256 || bm == 224 || bm == 192)) ? 2 : 3;
