@@ -338,9 +338,12 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
   } while (0)
 
   // Weight-gradient GEMMs, the operands only they read (normalised / activated / copied saved
-  // tensors, written transposed) and the gain gradients run on a side stream, forked from and
-  // joined back to the caller's stream with events: that work fills what the dX chain leaves idle,
-  // and the critical path dA -> dX -> norm bwd -> dO -> attention -> dX -> norm bwd stays on `s`.
+  // tensors, written transposed) and the gain gradient of the inner norm run on a side stream,
+  // forked from and joined back to the caller's stream with events: that work fills what the dX
+  // chain leaves idle, and the critical path dA -> dX -> norm bwd -> dO -> attention -> dX -> norm
+  // bwd stays on `s`.  The gain (and bias) gradient of the last norm follows its backward on `s`,
+  // which would otherwise sit idle while the side stream finishes its last weight-gradient GEMMs:
+  // queued behind those GEMMs it made the tail of the step (0.4-0.9% of the layer on MI355X).
   SideLease lease;
   CHECK(side_acquire(&lease.sd));
   Side* side = lease.sd;
@@ -419,12 +422,13 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
                                 w->gamma1, nullptr, idx, Mk, H, b.xnT, ldT, s1));
     CHECK(gemm_bf16(g_dwqkv, b.gemm_ws2, b.gemm_ws2_bytes, s1));
     CHECK(gemm_bf16(g_dXin, b.gemm_ws, b.gemm_ws_bytes, s));
-    CHECK(handoff(7, s, s1));  // dXn1 ready: the gain gradient on the side stream
-    CHECK(launch_norm_grad_parts(b.dxn1, (const uint16_t*)sv->x, nullptr, sv->rstd1, idx, Mk, H,
-                                 b.part_g, nullptr, parts, s1));
-    CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dgamma1, c.accumulate, s1));
     CHECK(launch_norm_bwd(b.dxn1, b.dh, (const uint16_t*)sv->x, nullptr, sv->rstd1, w->gamma1, idx, Mk,
                           H, b.dx_c, dx_full, s, dx_full ? ix.count : nullptr));
+    // partial rows in part_b, which RMSNorm leaves unused: part_g may still be read by the side
+    // stream's column sums of the second norm's gain gradient
+    CHECK(launch_norm_grad_parts(b.dxn1, (const uint16_t*)sv->x, nullptr, sv->rstd1, idx, Mk, H,
+                                 b.part_b, nullptr, parts, s));
+    CHECK(launch_colsum_parts(b.part_b, Mk > 0 ? parts : 0, H, gr->dgamma1, c.accumulate, s));
   } else {
     CHECK(launch_cols_recompute(COL_GELU, (const uint16_t*)sv->f, I, nullptr, nullptr, nullptr,
                                 nullptr, nullptr, idx, Mk, I, b.actT, ldT, s1));
@@ -443,13 +447,12 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
     CHECK(gemm_bf16(g_dwqkv, b.gemm_ws2, b.gemm_ws2_bytes, s1));
     CHECK(gemm_bf16(g_dwfc1, b.gemm_ws2, b.gemm_ws2_bytes, s1));
     CHECK(gemm_bf16(g_dXin, b.gemm_ws, b.gemm_ws_bytes, s));
-    CHECK(handoff(7, s, s1));  // dXn ready: the gain and bias gradients on the side stream
-    CHECK(launch_norm_grad_parts(b.dxn, (const uint16_t*)sv->x, sv->mean, sv->rstd1, idx, Mk, H,
-                                 b.part_g, b.part_b, parts, s1));
-    CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dln_gamma, c.accumulate, s1));
-    CHECK(launch_colsum_parts(b.part_b, Mk > 0 ? parts : 0, H, gr->dln_beta, c.accumulate, s1));
     CHECK(launch_norm_bwd(b.dxn, b.dy_c, (const uint16_t*)sv->x, sv->mean, sv->rstd1, w->ln_gamma,
                           idx, Mk, H, b.dx_c, dx_full, s, dx_full ? ix.count : nullptr));
+    CHECK(launch_norm_grad_parts(b.dxn, (const uint16_t*)sv->x, sv->mean, sv->rstd1, idx, Mk, H,
+                                 b.part_g, b.part_b, parts, s));
+    CHECK(launch_colsum_parts(b.part_g, Mk > 0 ? parts : 0, H, gr->dln_gamma, c.accumulate, s));
+    CHECK(launch_colsum_parts(b.part_b, Mk > 0 ? parts : 0, H, gr->dln_beta, c.accumulate, s));
   }
   CHECK(handoff(4, s1, s));  // join: every weight gradient is complete on the caller's stream
 #undef CHECK
