@@ -83,8 +83,13 @@ collider_status side_acquire(Side** out) {
   Side* sd = new Side;
   sd->dev = dev;
   bool ok = hipStreamCreateWithFlags(&sd->s, hipStreamNonBlocking) == hipSuccess;
+  // The events only order the two streams (hipStreamWaitEvent); the host never queries or waits on
+  // them, so they go without the system-scope fence that host inspection needs.  Eager layer calls
+  // on MI355X: TinyLlama 1.109 -> 1.094 ms, Phi-1.5 1.169 -> 1.163 ms (the fence sat between the
+  // producing kernel and the next one on the recording stream).
   for (hipEvent_t& e : sd->ev)
-    ok = ok && hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&e, hipEventDisableTiming | hipEventDisableSystemFence) ==
+                   hipSuccess;
   if (!ok) {
     side_destroy(sd);
     return COLLIDER_ERR_HIP;
