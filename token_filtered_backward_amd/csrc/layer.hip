@@ -464,9 +464,10 @@ collider_status layer_run(const collider_layer_cfg& c, const collider_layer_weig
       if (side && hipEventRecord(side->ev[2], s) != hipSuccess) return COLLIDER_ERR_HIP;  // dF ready
       CHECK(gemm_bf16(g_dO, b.gemm_ws, b.gemm_ws_bytes, s));
     }
-    // dW_fc1 needs only dF (the dA GEMM's output) and xn': it runs beside attention, which leaves
-    // most of the MFMA throughput idle, instead of behind dW_qkv at the end of the side stream (Phi-1.5
-    // layer 1.282 -> 1.263 ms with eager launches, 1.313 -> 1.271 replayed as a graph, MI355X)
+    // dW_fc1 needs only dF (the dA GEMM's output) and xn': it runs while attention holds the
+    // caller's stream and the side stream would otherwise wait, instead of behind dW_qkv at the
+    // end of the step (Phi-1.5 layer on MI355X: 1.282 -> 1.263 ms with eager launches, 1.313 ->
+    // 1.271 replayed as a graph)
     if (side && hipStreamWaitEvent(s1, side->ev[2], 0) != hipSuccess) return COLLIDER_ERR_HIP;
     CHECK(gemm_bf16(g_dwfc1, b.gemm_ws2, b.gemm_ws2_bytes, s1));
     if (side && hipStreamWaitEvent(s, side->ev[6], 0) != hipSuccess) return COLLIDER_ERR_HIP;
