@@ -435,6 +435,41 @@ def test_layer_every_token_kept_is_the_dense_path(name):
         assert torch.equal(g_c[k], g_dense[k]), k
 
 
+@pytest.mark.parametrize("name,layout", [("small_llama", 0), ("small_llama", 1), ("small_phi", 0),
+                                         ("small_phi", 1)])
+def test_layer_accumulate_adds_onto_weight_and_gain_gradients(name, layout):
+    """accumulate != 0 adds every weight, gain and bias gradient onto what its buffer holds (one
+    fp32 addition: bit for bit the old value plus the gradient of a call without accumulate) and
+    writes dx as that call does."""
+    cfg = synth.get_config(name)
+    inp = synth.make_layer_inputs(cfg, seed=2)
+    weights, saved, dy = _upload_layer(inp)
+    if layout == tfb.WEIGHTS_IN_OUT:
+        weights = tfb.to_in_out(weights)
+    ix = tfb.build_index(_dev_keep(inp["keep"]), cfg.B, cfg.S)
+    lcfg = tfb.layer_cfg(cfg, weight_layout=layout)
+    fresh = tfb.make_grads(lcfg, cfg.M, ix.M_kept, "cuda")
+    tfb.layer_bwd(lcfg, weights, saved, dy, ix, fresh)
+    acfg = tfb.layer_cfg(cfg, accumulate=True, weight_layout=layout)
+    acc = tfb.make_grads(acfg, cfg.M, ix.M_kept, "cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    prior = {}
+    for k, g in acc.items():
+        if g.dtype == torch.float32:
+            g.copy_(torch.randn(g.shape, generator=gen, device="cuda"))
+        else:
+            g.fill_(float("nan"))
+        prior[k] = g.clone()
+    tfb.layer_bwd(acfg, weights, saved, dy, ix, acc)
+    torch.cuda.synchronize()
+    for k in fresh:
+        if k == "dx":
+            assert torch.equal(acc[k].view(torch.int16), fresh[k].view(torch.int16)), k
+        else:
+            assert torch.equal(acc[k], prior[k] + fresh[k]), k
+
+
 @pytest.mark.parametrize("name", ["small_llama", "small_phi"])
 def test_stack_of_layers(name):
     """Three layers from one consistent forward, chained top to bottom with compact gradients
