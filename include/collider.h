@@ -287,11 +287,26 @@ collider_status collider_ce_loss(const void* logits, int64_t ld_logits, const in
  * equal scores keep the lower position first; -0.0 ranks as +0.0; NaN ranks below every number.
  * n_keep <= 0 keeps nothing, n_keep >= M keeps every token.  keep is uint8 [M] (the mask
  * collider_build_index takes).  One workgroup, five passes over the scores: meant for per-batch
- * token counts (M <= 2^30 accepted; time grows linearly with M).  Bit-exact, deterministic.
+ * token counts (M <= 2^30 accepted; time grows linearly with M; collider_select_keep_ws below
+ * spreads large counts over the GPU).  Bit-exact, deterministic.
  * Errors: NULL pointer, M < 1 or M > 2^30.
  * ------------------------------------------------------------------------------------------- */
 collider_status collider_select_keep(const float* score, int32_t M, int32_t n_keep, uint8_t* keep,
                                      hipStream_t stream);
+
+/* collider_select_keep_ws: the same selection, bit for bit, spread over many workgroups for large
+ * token counts: four radix passes, each a histogram launch over contiguous chunks of the scores
+ * and a one-workgroup launch that picks the next key byte, then a count of the threshold-equal
+ * keys per chunk and the mask launch.  ws: 16-byte aligned device memory of
+ * collider_select_workspace_bytes(M) bytes (0 for M <= 8192, where the one-workgroup kernel of
+ * collider_select_keep runs; about 1 KB per 4096 tokens above it, at most 2 MB plus 8 KB), owned
+ * by the caller, not kept after the call's work on `stream` ends; calls that share it must be
+ * ordered.  Errors: NULL score or keep, M < 1 or M > 2^30, ws NULL or smaller than required,
+ * ws not 16-byte aligned.
+ * ------------------------------------------------------------------------------------------- */
+size_t collider_select_workspace_bytes(int32_t M);
+collider_status collider_select_keep_ws(const float* score, int32_t M, int32_t n_keep, uint8_t* keep,
+                                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* collider_lm_head_bwd: per-token cross-entropy backward through the LM head, over kept tokens.
  * The forward computed logits = h @ w_lm^T (w_lm [V, H] bf16, [out, in]) and kept them, bf16

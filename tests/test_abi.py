@@ -155,6 +155,15 @@ def test_loss_side_validation():
     p = ctypes.c_void_p(0x10000)
     assert L.collider_select_keep(None, 8, 4, p, None) == 1
     assert L.collider_select_keep(p, 0, 4, p, None) == 2
+    # the many-workgroup selection: no workspace up to 8192 tokens, one histogram per chunk above
+    assert L.collider_select_workspace_bytes(8192) == 0
+    assert L.collider_select_workspace_bytes(8193) == (4 + 4 * 257) * 4
+    assert L.collider_select_workspace_bytes(1 << 30) == (4 + 2048 * 257) * 4
+    assert L.collider_select_keep_ws(p, 9000, 4, ctypes.c_void_p(0x10004), ctypes.c_void_p(0x10004), 1 << 20, None) == 3
+    assert L.collider_select_keep_ws(None, 9000, 4, p, p, 1 << 20, None) == 1
+    assert L.collider_select_keep_ws(p, 0, 4, p, p, 1 << 20, None) == 2
+    assert L.collider_select_keep_ws(p, 9000, 4, p, None, 0, None) == 5
+    assert L.collider_select_keep_ws(p, 9000, 4, p, p, 16, None) == 5
     ix = tfb.CollIndex(p, p, p, p, 2, 64, 77)
     # V not a multiple of 8, then a missing workspace
     assert L.collider_lm_head_bwd(p, 1004, p, p, 256, p, ctypes.byref(ix), 256, 1004, 1.0, p, 0, p, 0,

@@ -44,6 +44,31 @@ def test_select_keep_bit_exact(M, kind):
         assert np.array_equal(got, ref), (M, kind, n_keep, int(np.sum(got != ref)))
 
 
+@pytest.mark.parametrize("M,kind", [(8193, "ties"), (300007, "lognormal"), (300007, "ties"),
+                                    ((1 << 20) + 3, "normal"), (9000011, "ties")])
+def test_select_keep_multi_workgroup_bit_exact(M, kind):
+    """The selection spread over many workgroups (token counts above 8192; past 2048 x 4096 tokens
+    each workgroup walks several 4096-token steps) keeps the same tokens as the oracle, ties in
+    token order across chunk boundaries included, and as the one-workgroup kernel."""
+    score = _scores(M, kind, M)
+    dev = torch.from_numpy(score).cuda()
+    need = tfb.collider_select_workspace_bytes(M)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for n_keep in sorted({1, M // 3, M - M // 5, M - 1}):
+        keep = torch.empty(M, dtype=torch.uint8, device="cuda")
+        tfb.collider_select_keep_ws(dev, n_keep, keep, ws)
+        got = keep.cpu().numpy()
+        ref = oracle.select_topk(score, n_keep)
+        assert np.array_equal(got, ref), (M, kind, n_keep, int(np.sum(got != ref)))
+    if M < 400000:
+        one = torch.empty(M, dtype=torch.uint8, device="cuda")
+        tfb.collider_select_keep(dev, M // 3, one)
+        keep = torch.empty(M, dtype=torch.uint8, device="cuda")
+        tfb.collider_select_keep_ws(dev, M // 3, keep, ws)
+        assert torch.equal(one, keep)
+
+
 def test_select_keep_matches_the_layer_inputs_mask():
     """On the generator's LogNormal scores (as float32) the device selection gives the 40% mask the
     layer benchmarks use."""

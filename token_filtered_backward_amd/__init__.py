@@ -100,6 +100,8 @@ def lib():
         "collider_gemm_describe_plan": (st, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_i32)]),
         "collider_profile_collect": (_i32, [ctypes.c_char_p, _i32, P(ctypes.c_double), P(_i32), _i32]),
         "collider_select_keep": (st, [_c_p, _i32, _i32, _c_p, _c_p]),
+        "collider_select_workspace_bytes": (sz, [_i32]),
+        "collider_select_keep_ws": (st, [_c_p, _i32, _i32, _c_p, _c_p, sz, _c_p]),
         "collider_ce_loss": (st, [_c_p, _i64, _c_p, _i32, _i32, _c_p, _c_p]),
         "collider_side_streams_live": (_i32, []),
         "collider_release_resources": (st, []),
@@ -230,6 +232,19 @@ def collider_select_keep(score, n_keep, keep, stream=None):
                                       _stream(stream)), "collider_select_keep")
 
 
+def collider_select_workspace_bytes(M) -> int:
+    return int(lib().collider_select_workspace_bytes(int(M)))
+
+
+def collider_select_keep_ws(score, n_keep, keep, ws, stream=None):
+    """collider_select_keep over many workgroups (same mask); ws: uint8 device tensor of at least
+    collider_select_workspace_bytes(M) bytes (may be None when that is 0)."""
+    _check(lib().collider_select_keep_ws(_ptr(score), score.numel(), int(n_keep), _ptr(keep),
+                                         _ptr(ws) if ws is not None else None,
+                                         ws.numel() if ws is not None else 0, _stream(stream)),
+           "collider_select_keep_ws")
+
+
 def collider_ce_loss(logits, labels, loss, stream=None):
     """loss[t] = logsumexp(logits[t]) - logits[t, labels[t]] (0 for a label outside [0, V)) for
     every token: logits bf16 [M, V], labels int32 [M], loss float32 [M]."""
@@ -262,7 +277,12 @@ def select_keep(score: torch.Tensor, n_keep: int, stream=None) -> torch.Tensor:
     if score.dtype != torch.float32 or not score.is_contiguous():
         raise TypeError("score must be a contiguous float32 tensor")
     keep = torch.empty(score.numel(), dtype=torch.uint8, device=score.device)
-    collider_select_keep(score, n_keep, keep, stream)
+    need = collider_select_workspace_bytes(score.numel())
+    if need:  # large token counts: the selection spread over the GPU
+        ws = torch.empty(need, dtype=torch.uint8, device=score.device)
+        collider_select_keep_ws(score, n_keep, keep, ws, stream)
+    else:
+        collider_select_keep(score, n_keep, keep, stream)
     return keep
 
 

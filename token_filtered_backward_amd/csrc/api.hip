@@ -453,6 +453,20 @@ collider_status collider_select_keep(const float* score, int32_t M, int32_t n_ke
   return launch_select_topk(score, M, n_keep, keep, stream);
 }
 
+size_t collider_select_workspace_bytes(int32_t M) {
+  return M < 1 || M > (1 << 30) ? 0 : select_workspace_bytes(M);
+}
+
+collider_status collider_select_keep_ws(const float* score, int32_t M, int32_t n_keep, uint8_t* keep,
+                                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!score || !keep) return COLLIDER_ERR_NULL;
+  if (M < 1 || M > (1 << 30)) return COLLIDER_ERR_SHAPE;
+  const size_t need = select_workspace_bytes(M);
+  if (need > 0 && (!ws || ws_bytes < need)) return COLLIDER_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return COLLIDER_ERR_ALIGN;
+  return launch_select_topk_multi(score, M, n_keep, keep, (uint32_t*)ws, stream);
+}
+
 }  // extern "C"
 
 namespace {

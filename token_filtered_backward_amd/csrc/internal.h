@@ -97,6 +97,11 @@ collider_status launch_build_index(const uint8_t* keep, int B, int S, int32_t* i
 // loss.hip
 collider_status launch_select_topk(const float* score, int M, int n_keep, uint8_t* keep,
                                    hipStream_t s);
+// the same selection over many workgroups, for large token counts (M above 8192); ws holds
+// select_workspace_bytes(M) bytes (0 when the single-workgroup kernel serves M)
+size_t select_workspace_bytes(int M);
+collider_status launch_select_topk_multi(const float* score, int M, int n_keep, uint8_t* keep,
+                                         uint32_t* ws, hipStream_t s);
 collider_status launch_ce_loss(const uint16_t* logits, int64_t ld, const int32_t* labels, int M, int V,
                                float* loss, hipStream_t s);
 collider_status launch_ce_grad(const uint16_t* logits, int64_t ld, const int32_t* labels,

@@ -185,6 +185,248 @@ collider_status launch_select_topk(const float* score, int M, int n_keep, uint8_
 }
 
 // ------------------------------------------------------------------------------------------
+// top-k selection over many workgroups (large token counts): the same radix select, the same
+// result bit for bit.  Each pass is two launches: every workgroup histograms the keys of its
+// contiguous chunk of tokens that match the bytes chosen so far (sel_hist_kernel), then one
+// workgroup adds the histograms in workgroup order and picks the next byte (sel_choose_kernel).
+// After the fourth pass every workgroup counts the keys equal to the threshold in its chunk
+// (sel_eqcount_kernel), and the last launch writes the mask: keys above the threshold, and the
+// first `need` equal keys in token order, each workgroup starting from the equal keys of the
+// chunks before its own (sel_mark_kernel).  Workspace (uint32, 16-byte aligned): the state
+// {prefix, byte mask, need} in 4 words, Gp words of equal-key counts (one per workgroup; Gp = the
+// workgroup count rounded up to 4), then the histograms bin-major ([256][Gp]), so that the
+// choosing workgroup reads each bin's counts with 16-byte loads, four threads per bin.  (Workgroup-major histograms read one count per load and
+// per thread made the four choosing launches take most of the selection's time.)
+// ------------------------------------------------------------------------------------------
+constexpr int kSelMT = 256;          // threads per workgroup
+constexpr int kSelSub = 4096;        // tokens per workgroup and step (16 per thread)
+constexpr int kSelMaxGroups = 2048;  // chunks grow past M / 2048 tokens instead
+
+struct SelPlan {
+  int groups, chunk;  // workgroups, tokens per workgroup (a multiple of kSelSub)
+};
+SelPlan sel_plan(int M) {
+  const int64_t subs = ((int64_t)M + kSelSub - 1) / kSelSub;
+  const int64_t per = (subs + kSelMaxGroups - 1) / kSelMaxGroups;  // sub-chunks per workgroup
+  const int chunk = (int)(per * kSelSub);
+  return SelPlan{(int)(((int64_t)M + chunk - 1) / chunk), chunk};
+}
+
+__global__ __launch_bounds__(kSelMT) void sel_hist_kernel(const float* __restrict__ score, int M,
+                                                          int chunk, int d,
+                                                          uint32_t* __restrict__ ws, int G) {
+  __shared__ uint32_t hist[kSelMT / 64][256];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  // the bytes chosen by the earlier passes (none before the first)
+  const uint32_t prefix = d == 3 ? 0u : ws[0], pmask = d == 3 ? 0u : ws[1];
+  for (int i = tid; i < 256 * (kSelMT / 64); i += kSelMT) (&hist[0][0])[i] = 0;
+  __syncthreads();
+  const int64_t t0 = (int64_t)blockIdx.x * chunk;
+  const int64_t t1 = min((int64_t)M, t0 + chunk);
+  uint32_t cur = 0u, run = 0u;  // a run of equal bins is added with one atomic
+  for (int64_t base = t0; base < t1; base += kSelSub) {
+    uint32_t k[kSelSub / kSelMT];
+#pragma unroll
+    for (int q = 0; q < kSelSub / kSelMT; ++q) {
+      const int64_t t = base + tid + kSelMT * q;
+      k[q] = t < t1 ? score_key(score[t]) : 0u;
+    }
+#pragma unroll
+    for (int q = 0; q < kSelSub / kSelMT; ++q) {
+      if (base + tid + kSelMT * q >= t1 || (k[q] & pmask) != prefix) continue;
+      const uint32_t b = (k[q] >> (8 * d)) & 255u;
+      if (run && b != cur) {
+        atomicAdd(&hist[wave][cur], run);
+        run = 0u;
+      }
+      cur = b;
+      ++run;
+    }
+  }
+  if (run) atomicAdd(&hist[wave][cur], run);
+  __syncthreads();
+  uint32_t tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSelMT / 64; ++w) tot += hist[w][tid];
+  const int Gp = (G + 3) & ~3;
+  ws[4 + Gp + (int64_t)tid * Gp + blockIdx.x] = tot;
+}
+
+__global__ __launch_bounds__(1024) void sel_choose_kernel(uint32_t* __restrict__ ws, int G, int d,
+                                                          int n_keep) {
+  __shared__ uint32_t part[4][256];
+  __shared__ uint32_t tot[256];
+  __shared__ uint32_t s_sel[2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  {  // bin tid / 4: its counts summed by four threads, 4 workgroups per 16-byte load
+    const int bin = tid >> 2, q = tid & 3, Gp = (G + 3) & ~3;
+    const uint32_t* row = ws + 4 + Gp + (int64_t)bin * Gp;  // 16-byte aligned (Gp = 0 mod 4)
+    uint32_t t = 0;
+#pragma unroll 8
+    for (int v = q; v < Gp / 4; v += 4) {
+      const uint4 c = *(const uint4*)(row + 4 * v);
+      const int g = 4 * v;
+      t += c.x + (g + 1 < G ? c.y : 0u) + (g + 2 < G ? c.z : 0u) + (g + 3 < G ? c.w : 0u);
+    }
+    part[q][bin] = t;
+  }
+  const uint32_t need = d == 3 ? (uint32_t)n_keep : ws[2];
+  __syncthreads();
+  if (tid < 256) tot[tid] = part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid];
+  __syncthreads();
+  if (tid < 64) {
+    // lane l holds bins 255 - 4l - q (q = 0..3), i.e. the bins in descending order
+    uint32_t loc[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      loc[q] = tot[255 - 4 * lane - q];
+      sum += loc[q];
+    }
+    uint32_t incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    const uint32_t excl = incl - sum;
+    if (excl < need && need <= incl) {  // exactly one lane: the total is at least `need`
+      uint32_t acc = excl;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (acc + loc[q] >= need) {
+          s_sel[0] = (uint32_t)(255 - 4 * lane - q);
+          s_sel[1] = need - acc;
+          break;
+        }
+        acc += loc[q];
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prefix = d == 3 ? 0u : ws[0], pmask = d == 3 ? 0u : ws[1];
+    ws[0] = prefix | (s_sel[0] << (8 * d));
+    ws[1] = pmask | (255u << (8 * d));
+    ws[2] = s_sel[1];
+  }
+}
+
+// keys equal to the threshold in each workgroup's chunk
+__global__ __launch_bounds__(kSelMT) void sel_eqcount_kernel(const float* __restrict__ score, int M,
+                                                             int chunk, uint32_t* __restrict__ ws) {
+  __shared__ uint32_t s_w[kSelMT / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t T = ws[0];
+  const int64_t t0 = (int64_t)blockIdx.x * chunk;
+  const int64_t t1 = min((int64_t)M, t0 + chunk);
+  uint32_t n = 0;
+  for (int64_t t = t0 + tid; t < t1; t += kSelMT) n += score_key(score[t]) == T ? 1u : 0u;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off, 64);
+  if (lane == 0) s_w[wave] = n;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t tot = 0;
+#pragma unroll
+    for (int w = 0; w < kSelMT / 64; ++w) tot += s_w[w];
+    ws[4 + blockIdx.x] = tot;
+  }
+}
+
+__global__ __launch_bounds__(kSelMT) void sel_mark_kernel(const float* __restrict__ score, int M,
+                                                          int chunk, const uint32_t* __restrict__ ws,
+                                                          uint8_t* __restrict__ keep) {
+  constexpr int PER = kSelSub / kSelMT;  // consecutive tokens per thread and step
+  __shared__ uint32_t s_w[kSelMT / 64];
+  __shared__ uint32_t s_carry;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t T = ws[0], need = ws[2];
+  // equal keys in the chunks before this one, summed in a fixed order
+  uint32_t before_g = 0;
+  for (int g = tid; g < (int)blockIdx.x; g += kSelMT) before_g += ws[4 + g];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) before_g += __shfl_xor(before_g, off, 64);
+  if (lane == 0) s_w[wave] = before_g;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int w = 0; w < kSelMT / 64; ++w) c += s_w[w];
+    s_carry = c;
+  }
+  __syncthreads();
+  const int64_t t0 = (int64_t)blockIdx.x * chunk;
+  const int64_t t1 = min((int64_t)M, t0 + chunk);
+  for (int64_t base = t0; base < t1; base += kSelSub) {
+    const int64_t tb = base + (int64_t)tid * PER;
+    uint32_t kk[PER], eq = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      kk[q] = tb + q < t1 ? score_key(score[tb + q]) : 0u;
+      eq += (tb + q < t1 && kk[q] == T) ? 1u : 0u;
+    }
+    uint32_t incl = eq;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    __syncthreads();  // s_w is rewritten
+    if (lane == 63) s_w[wave] = incl;
+    __syncthreads();
+    uint32_t before = s_carry + incl - eq;
+    for (int w = 0; w < wave; ++w) before += s_w[w];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      if (tb + q >= t1) break;
+      bool kp = kk[q] > T;
+      if (kk[q] == T) {
+        kp = before < need;
+        ++before;
+      }
+      keep[tb + q] = kp ? 1 : 0;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t tot = 0;
+#pragma unroll
+      for (int w = 0; w < kSelMT / 64; ++w) tot += s_w[w];
+      s_carry += tot;
+    }
+  }
+}
+
+size_t select_workspace_bytes(int M) {
+  if (M <= kSelThreads * kSelCached) return 0;
+  const SelPlan pl = sel_plan(M);
+  const int64_t Gp = (pl.groups + 3) & ~3;
+  return (size_t)(4 + Gp + Gp * 256) * sizeof(uint32_t);
+}
+
+collider_status launch_select_topk_multi(const float* score, int M, int n_keep, uint8_t* keep,
+                                         uint32_t* ws, hipStream_t s) {
+  if (M <= 0) return COLLIDER_OK;
+  if (M <= kSelThreads * kSelCached || n_keep <= 0 || n_keep >= M)
+    return launch_select_topk(score, M, n_keep, keep, s);
+  const SelPlan pl = sel_plan(M);
+  for (int d = 3; d >= 0; --d) {
+    COLLIDER_LAUNCH("select_hist", s,
+                    hipLaunchKernelGGL(sel_hist_kernel, dim3(pl.groups), dim3(kSelMT), 0, s, score, M,
+                                       pl.chunk, d, ws, pl.groups));
+    COLLIDER_LAUNCH("select_choose", s,
+                    hipLaunchKernelGGL(sel_choose_kernel, dim3(1), dim3(1024), 0, s, ws, pl.groups, d,
+                                       n_keep));
+  }
+  COLLIDER_LAUNCH("select_eqcount", s,
+                  hipLaunchKernelGGL(sel_eqcount_kernel, dim3(pl.groups), dim3(kSelMT), 0, s, score, M,
+                                     pl.chunk, ws));
+  COLLIDER_LAUNCH("select_mark", s,
+                  hipLaunchKernelGGL(sel_mark_kernel, dim3(pl.groups), dim3(kSelMT), 0, s, score, M,
+                                     pl.chunk, ws, keep));
+  return last_hip_status();
+}
+
+// ------------------------------------------------------------------------------------------
 // cross-entropy gradient over the kept rows: one workgroup per row
 // ------------------------------------------------------------------------------------------
 constexpr float kLog2eF = 1.4426950408889634f;
