@@ -226,7 +226,10 @@ def loss_side_bench(args, cfg, emit=True):
     h = torch.randn((M, H), generator=g, device=dev).to(torch.bfloat16)
     w_lm = (torch.randn((V, H), generator=g, device=dev) * 0.02).to(torch.bfloat16)
     labels = torch.from_numpy(rng.integers(0, V, M).astype(np.int32)).to(dev)
-    ids = torch.from_numpy(rng.integers(0, V, M).astype(np.int32)).to(dev)
+    # token ids of text follow Zipf's law: id v (by frequency rank) with probability ~ 1 / (v+1)^1.1,
+    # so that a few ids carry many tokens (the most frequent one about a tenth of the batch)
+    zipf_p = 1.0 / np.arange(1, V + 1, dtype=np.float64) ** 1.1
+    ids = torch.from_numpy(rng.choice(V, size=M, p=zipf_p / zipf_p.sum()).astype(np.int32)).to(dev)
     dx = torch.randn((n_keep, H), generator=g, device=dev).to(torch.bfloat16)
     dx_full = torch.randn((M, H), generator=g, device=dev).to(torch.bfloat16)
     keep = torch.empty(M, dtype=torch.uint8, device=dev)
