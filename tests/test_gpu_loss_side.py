@@ -160,7 +160,7 @@ def test_lm_head_bwd_all_filtered_and_accumulate():
 
 
 @pytest.mark.parametrize("B,S,H,V,r", [(2, 200, 256, 1000, 40), (1, 3000, 64, 50, 20), (4, 2048, 128, 32000, 40),
-                                       (2, 1500, 64, 50000, 40),
+                                       (2, 1500, 64, 50000, 40), (2, 600, 896, 3000, 40),
                                        (1, 77, 64, 16, 100)])
 @pytest.mark.parametrize("dx_compact", [False, True])
 def test_embedding_bwd_parity(B, S, H, V, r, dx_compact):
