@@ -45,7 +45,7 @@ def test_select_keep_bit_exact(M, kind):
 
 
 @pytest.mark.parametrize("M,kind", [(8193, "ties"), (300007, "lognormal"), (300007, "ties"),
-                                    ((1 << 20) + 3, "normal"), (9000011, "ties")])
+                                    (300007, "const"), ((1 << 20) + 3, "normal"), (9000011, "ties")])
 def test_select_keep_multi_workgroup_bit_exact(M, kind):
     """The selection spread over many workgroups (token counts above 8192; past 2048 x 4096 tokens
     each workgroup walks several 4096-token steps) keeps the same tokens as the oracle, ties in
