@@ -397,6 +397,13 @@ __global__ __launch_bounds__(kSelMT) void sel_mark_kernel(const float* __restric
   }
 }
 
+// keep[t] = v for every t (nothing or everything kept)
+__global__ __launch_bounds__(256) void sel_fill_kernel(uint8_t* __restrict__ keep, int64_t M,
+                                                       uint8_t v) {
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < M; t += (int64_t)gridDim.x * 256)
+    keep[t] = v;
+}
+
 size_t select_workspace_bytes(int M) {
   if (M <= kSelThreads * kSelCached) return 0;
   const SelPlan pl = sel_plan(M);
@@ -407,8 +414,14 @@ size_t select_workspace_bytes(int M) {
 collider_status launch_select_topk_multi(const float* score, int M, int n_keep, uint8_t* keep,
                                          uint32_t* ws, hipStream_t s) {
   if (M <= 0) return COLLIDER_OK;
-  if (M <= kSelThreads * kSelCached || n_keep <= 0 || n_keep >= M)
-    return launch_select_topk(score, M, n_keep, keep, s);
+  if (M <= kSelThreads * kSelCached) return launch_select_topk(score, M, n_keep, keep, s);
+  if (n_keep <= 0 || n_keep >= M) {
+    const int blocks = (int)std::min<int64_t>(((int64_t)M + 255) / 256, 4096);
+    COLLIDER_LAUNCH("select_fill", s,
+                    hipLaunchKernelGGL(sel_fill_kernel, dim3(blocks), dim3(256), 0, s, keep, (int64_t)M,
+                                       (uint8_t)(n_keep <= 0 ? 0 : 1)));
+    return last_hip_status();
+  }
   const SelPlan pl = sel_plan(M);
   for (int d = 3; d >= 0; --d) {
     COLLIDER_LAUNCH("select_hist", s,
