@@ -14,11 +14,13 @@ namespace collider {
 // ------------------------------------------------------------------------------------------
 // gather: dst[c] = src[idx[c]], several tensors per launch (blockIdx.y = descriptor)
 // ------------------------------------------------------------------------------------------
-// Each workgroup moves up to kChunks 16-byte chunks (64 KB): the row indices of its rows are
+// Each workgroup moves up to kChunks 16-byte chunks (32 KB): the row indices of its rows are
 // staged in LDS first, then every thread issues all of its loads before any store, so that many
 // loads are in flight per thread.  One launch covers up to 8 tensors; their workgroups are laid
-// out one tensor after another (blk0[i] = first workgroup of tensor i).
-static constexpr int kPerThread = 16;
+// out one tensor after another (blk0[i] = first workgroup of tensor i).  (64 KB per workgroup
+// gave the 20 MB dY gather of the TinyLlama layer 308 workgroups, 1.2 per CU, so a second round
+// of a few; 32 KB took it from 13.4 to 12.7 us and the zero fill from 11.0 to 8.8 us.)
+static constexpr int kPerThread = 8;
 static constexpr int kChunks = 256 * kPerThread;
 
 struct GatherBatch {
