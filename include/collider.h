@@ -397,7 +397,9 @@ int32_t collider_profile_collect(char* names, int32_t name_cap, double* total_ms
                                  int32_t max_kernels);
 
 /* Library-held HIP objects.  collider_layer_bwd forks part of its work onto a side stream (default
- * priority) and joins it back with events; it leases the stream and its events from a per-device
+ * priority) and joins it back to the caller's stream with events (created without the system-scope
+ * fence: they only order the two streams; the host sees the results after synchronizing the
+ * caller's stream, as for any work on it); it leases the stream and its events from a per-device
  * pool for the duration of one call and returns them when its launches are enqueued, so the pool
  * holds as many sets as calls have ever run at once on a device, however many host threads call
  * (a set still part of an open graph capture is not leased again until that capture ends).
